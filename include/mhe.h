@@ -1,0 +1,229 @@
+/*
+ * mhe.h -- C ABI of libmhe, the MI355X (gfx950) prefill of the Qwen3-VL text
+ * decoder that the MiniMax H3 text/vision encoder truncates at layer 50.
+ *
+ * Source of the computation: the vllm-omni page
+ * "vllm_omni/diffusion/models/minimax_h3/encoder.py" (MiniMax H3 Qwen3-VL
+ * layer-50 text/vision encoder), referred to below as the H3 encoder page,
+ * and its rendered API documentation page.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense row-major device buffers. "bf16" means IEEE bfloat16
+ *    stored as uint16; the library rounds to nearest-even wherever it
+ *    produces bf16. Linear weights follow y = x W^T with W stored [out, in].
+ *  - The caller owns every device buffer, the workspace and the stream. The
+ *    library allocates and frees nothing; host pointer arrays (layer weight
+ *    tables, DeepStack feature tables) are read only during the call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls enqueue work and return without synchronising the host; results
+ *    are valid once the caller synchronises the stream.
+ *  - Return value: MHE_OK (0) or an mhe_status code. All argument checks run
+ *    on the host before anything is enqueued, so a failed call has launched
+ *    nothing. MHE_ERR_HIP reports a launch error returned by the HIP runtime
+ *    (work enqueued earlier in the same call may then have run).
+ *    mhe_last_error() returns a message for the calling thread's last failure.
+ *  - Entry points keep no state between calls; concurrent calls are safe when
+ *    each has its own workspace and output buffers.
+ */
+#ifndef MHE_H
+#define MHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MHE_ABI_VERSION 1
+
+typedef enum mhe_status {
+  MHE_OK = 0,
+  MHE_ERR_NULL = 1,        /* a required pointer is NULL */
+  MHE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  MHE_ERR_MISMATCH = 3,    /* visual-mask popcount differs from n_vis (checked mode only) */
+  MHE_ERR_UNSUPPORTED = 4, /* valid but not built for (head_dim, K multiple, group size) */
+  MHE_ERR_WORKSPACE = 5,   /* workspace too small or misaligned */
+  MHE_ERR_HIP = 6          /* the HIP runtime reported an error */
+} mhe_status;
+
+/*
+ * Model constants. H3 encoder page: hidden size 5120 and 50 retained layers
+ * are module constants; head counts, head_dim, intermediate size, rms eps,
+ * rope theta and the multimodal rotary section come from the Qwen3-VL config
+ * (MiniMaxH3Qwen3VLTextAttention, MiniMaxH3Qwen3VLTextMLP,
+ * MiniMaxH3Qwen3VLTextRotaryEmbedding; section default [24, 20, 20]).
+ * Supported: head_dim 64 or 128; n_heads a multiple of n_kv_heads with 1, 2, 4 or 8 query heads per key/value head; hidden, n_heads*head_dim and
+ * intermediate multiples of 64; hidden <= 8192; seq <= 131072.
+ */
+typedef struct mhe_config {
+  int32_t hidden;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t intermediate;
+  float rms_eps;
+  float rope_theta;
+  int32_t mrope_section[3];
+} mhe_config;
+
+/*
+ * One decoder layer's weights, all bf16 device pointers (H3 encoder page,
+ * MiniMaxH3Qwen3VLTextDecoderLayer and its attention/MLP):
+ *   ln_in  [hidden]                input_layernorm gain
+ *   w_q    [n_heads*head_dim, hidden]   rows 0.. of the fused qkv weight
+ *   w_k    [n_kv_heads*head_dim, hidden]
+ *   w_v    [n_kv_heads*head_dim, hidden]
+ *   q_norm [head_dim], k_norm [head_dim]  per-head RMSNorm gains
+ *   w_o    [hidden, n_heads*head_dim]
+ *   ln_post[hidden]                post_attention_layernorm gain
+ *   w_gate [intermediate, hidden], w_up [intermediate, hidden]
+ *                                  the two halves of the fused gate_up weight
+ *   w_down [hidden, intermediate]
+ */
+typedef struct mhe_layer_weights {
+  const void* ln_in;
+  const void* w_q;
+  const void* w_k;
+  const void* w_v;
+  const void* q_norm;
+  const void* k_norm;
+  const void* w_o;
+  const void* ln_post;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+} mhe_layer_weights;
+
+int32_t mhe_abi_version(void);
+const char* mhe_status_string(int32_t status);
+/* Message for the calling thread's last failed call ("" if none). */
+const char* mhe_last_error(void);
+
+/*
+ * Bytes of device workspace that mhe_layer_forward / mhe_encode need for
+ * `seq` tokens (256-byte aligned base required). Returns 0 for an invalid
+ * config or seq <= 0 (mhe_last_error says why).
+ */
+size_t mhe_workspace_bytes(const mhe_config* cfg, int32_t seq);
+
+/*
+ * One decoder layer in place: hidden [seq, hidden] bf16 is read and
+ * overwritten with the layer output. H3 encoder page,
+ * MiniMaxH3Qwen3VLTextDecoderLayer.forward: residual + attention(RMSNorm(x)),
+ * then residual + MLP(RMSNorm(x)); attention is per-head q/k RMSNorm,
+ * multimodal rotary from `positions`, causal GQA attention with scale
+ * 1/sqrt(head_dim) and the O projection (MiniMaxH3Qwen3VLTextAttention.forward);
+ * the MLP is down(silu(gate(x)) * up(x)) (MiniMaxH3Qwen3VLTextMLP.forward).
+ * positions: device int32 [3, seq], rows (T, H, W) (the page's [3, 1, seq]
+ * int64 position ids, narrowed). The rotary angles are recomputed per call.
+ * Errors: NULL pointers, seq <= 0, unsupported config, workspace too small.
+ */
+int32_t mhe_layer_forward(const mhe_config* cfg, const mhe_layer_weights* w, void* hidden,
+                          const int32_t* positions, int32_t seq, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * DeepStack injection in place (H3 encoder page,
+ * MiniMaxH3Qwen3VLTextModel._deepstack_process): for r < n_vis,
+ * hidden[t_r, :] += feature[r, :] where t_r is the r-th token (ascending)
+ * whose visual_mask byte is non-zero; the sum is rounded to bf16 once.
+ * hidden [seq, hidden_dim] bf16, visual_mask device uint8 [seq], feature
+ * [n_vis, hidden_dim] bf16. n_vis == 0 is a no-op. If the mask has fewer set
+ * bytes than n_vis the extra feature rows are ignored; if it has more, only
+ * the first n_vis visual tokens are updated (never out of bounds).
+ * workspace: at least seq*4 + 256 bytes.
+ */
+int32_t mhe_deepstack_inject(void* hidden, int32_t seq, int32_t hidden_dim,
+                             const uint8_t* visual_mask, int32_t n_vis, const void* feature,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The whole prefill (H3 encoder page, MiniMaxH3Qwen3VLTextModel.forward):
+ * out = hidden state after n_layers decoder layers, unnormalised, bf16
+ * [seq, hidden]. inputs_embeds [seq, hidden] bf16 is not written (it is
+ * copied to `out`, which is then updated in place). layers: host array of
+ * n_layers weight tables. After layer l, for l < min(n_ds, n_layers),
+ * DeepStack level l (deepstack[l], device bf16 [n_vis, hidden]) is added to
+ * the visual rows as in mhe_deepstack_inject; levels beyond n_layers are
+ * unused. visual_mask/deepstack may be NULL only when n_ds == 0 or
+ * n_vis == 0. `out` must not overlap inputs_embeds or the workspace.
+ */
+int32_t mhe_encode(const mhe_config* cfg, const mhe_layer_weights* layers, int32_t n_layers,
+                   const void* inputs_embeds, const int32_t* positions,
+                   const uint8_t* visual_mask, int32_t n_vis, const void* const* deepstack,
+                   int32_t n_ds, int32_t seq, void* out, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * Count the non-zero bytes of visual_mask [seq] into *count_host (host
+ * int32). Synchronises `stream`. For callers that want the pages' feature /
+ * token count check (H3 encoder page, _get_placeholder_mask) before
+ * mhe_encode; workspace needs seq*4 + 256 bytes.
+ */
+int32_t mhe_count_visual(const uint8_t* visual_mask, int32_t seq, int32_t* count_host,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- single steps of the layer, each one kernel (used for per-step checks) ---- */
+
+/*
+ * y[r, :] = gamma * x[r, :] / sqrt(mean(x[r, :]^2) + eps), fp32 reduction,
+ * one bf16 rounding (H3 encoder page, MiniMaxH3Qwen3VLRMSNorm). x, y
+ * [rows, dim] bf16 (may alias), gamma [dim] bf16. dim % 8 == 0, dim <= 8192.
+ */
+int32_t mhe_rms_norm(const void* x, const void* gamma, void* y, int32_t rows, int32_t dim,
+                     float eps, void* stream);
+
+/*
+ * c[m, n] = sum_k a[m, k] w[n, k] (+ residual[m, n]) with fp32 accumulation
+ * and one bf16 rounding (the F.linear calls of the H3 encoder page; the
+ * residual form is the decoder layer's residual add fused into the O and
+ * down projections). a [m, k], w [n, k], c and residual [m, n] bf16;
+ * residual may be NULL or equal to c (in-place), c must not overlap a or w.
+ * k % 64 == 0, n % 32 == 0.
+ */
+int32_t mhe_linear(const void* a, const void* w, void* c, const void* residual, int32_t m,
+                   int32_t n, int32_t k, void* stream);
+
+/*
+ * c[m, j] = silu(sum_k a[m,k] w_gate[j,k]) * sum_k a[m,k] w_up[j,k] in fp32,
+ * one bf16 rounding (H3 encoder page, MiniMaxH3Qwen3VLTextMLP.forward up to
+ * the down projection). a [m, k], w_gate and w_up [n, k], c [m, n].
+ * k % 64 == 0, n % 32 == 0.
+ */
+int32_t mhe_linear_swiglu(const void* a, const void* w_gate, const void* w_up, void* c,
+                          int32_t m, int32_t n, int32_t k, void* stream);
+
+/*
+ * Per-head q/k RMSNorm and multimodal rotary (H3 encoder page,
+ * MiniMaxH3Qwen3VLTextAttention.forward up to SDPA, with
+ * MiniMaxH3Qwen3VLTextRotaryEmbedding and _apply_interleaved_mrope).
+ * qkv [seq, (n_heads + 2 n_kv_heads) head_dim] bf16 holds q | k | v
+ * projections per token; q_norm, k_norm [head_dim] bf16 are the per-head
+ * gains; positions device int32 [3, seq]. Outputs, in the layouts the attention step reads:
+ *   q_out [seq, n_heads, head_dim]
+ *   k_out [n_kv_heads, seq_pad, head_dim]
+ *   vt_out[n_kv_heads, head_dim, seq_pad]: V transposed, and within each
+ *         aligned group of 16 tokens stored in the order
+ *         0 1 2 3 8 9 10 11 4 5 6 7 12 13 14 15
+ * with seq_pad = seq rounded up to 64; rows/columns past seq are zero.
+ */
+int32_t mhe_qk_norm_rope(const mhe_config* cfg, const void* qkv, const void* q_norm,
+                         const void* k_norm, const int32_t* positions, int32_t seq, void* q_out,
+                         void* k_out, void* vt_out, void* stream);
+
+/*
+ * Causal GQA attention (H3 encoder page, MiniMaxH3Qwen3VLTextAttention.forward:
+ * query head h uses key/value head h / (n_heads / n_kv_heads), key j visible
+ * to query i iff j <= i, scale 1/sqrt(head_dim), softmax in fp32).
+ * q, k, vt in the layouts mhe_qk_norm_rope writes; o [seq, n_heads*head_dim]
+ * bf16 with column h*head_dim + d.
+ */
+int32_t mhe_attention(const void* q, const void* k, const void* vt, void* o, int32_t seq,
+                      int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MHE_H */

@@ -1,0 +1,222 @@
+"""ctypes binding of libmhe (the C ABI declared in ``include/mhe.h``).
+
+Argument marshalling only: every function here forwards device pointers,
+sizes and a HIP stream to the library of the same name, which does all of the
+computation. Arguments may be torch tensors (their ``data_ptr()`` is passed)
+or plain integers (raw device addresses). The stream defaults to torch's
+current stream on the current device.
+
+The library is loaded on first use; if ``libmhe.so`` has not been built the
+call fails loudly (there is no fallback path).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmhe.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "mhe.h")
+
+MHE_OK = 0
+STATUS_NAMES = {0: "MHE_OK", 1: "MHE_ERR_NULL", 2: "MHE_ERR_SHAPE", 3: "MHE_ERR_MISMATCH",
+                4: "MHE_ERR_UNSUPPORTED", 5: "MHE_ERR_WORKSPACE", 6: "MHE_ERR_HIP"}
+
+
+class MheError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        self.fn, self.status, self.message = fn, status, message
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)}: {message}")
+
+
+class MheConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("intermediate", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_float), ("mrope_section", ctypes.c_int32 * 3)]
+
+
+WEIGHT_FIELDS = ("ln_in", "w_q", "w_k", "w_v", "q_norm", "k_norm", "w_o", "ln_post",
+                 "w_gate", "w_up", "w_down")
+
+
+class MheLayerWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in WEIGHT_FIELDS]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_SIGNATURES = {
+    "mhe_abi_version": (_i32, []),
+    "mhe_status_string": (ctypes.c_char_p, [_i32]),
+    "mhe_last_error": (ctypes.c_char_p, []),
+    "mhe_workspace_bytes": (_sz, [ctypes.POINTER(MheConfig), _i32]),
+    "mhe_layer_forward": (_i32, [ctypes.POINTER(MheConfig), ctypes.POINTER(MheLayerWeights), _vp,
+                                 _vp, _i32, _vp, _sz, _vp]),
+    "mhe_deepstack_inject": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "mhe_encode": (_i32, [ctypes.POINTER(MheConfig), ctypes.POINTER(MheLayerWeights), _i32, _vp,
+                          _vp, _vp, _i32, ctypes.POINTER(_vp), _i32, _i32, _vp, _vp, _sz, _vp]),
+    "mhe_count_visual": (_i32, [_vp, _i32, ctypes.POINTER(_i32), _vp, _sz, _vp]),
+    "mhe_rms_norm": (_i32, [_vp, _vp, _vp, _i32, _i32, _f32, _vp]),
+    "mhe_linear": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
+    "mhe_linear_swiglu": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
+    "mhe_qk_norm_rope": (_i32, [ctypes.POINTER(MheConfig), _vp, _vp, _vp, _vp, _i32, _vp, _vp,
+                                _vp, _vp]),
+    "mhe_attention": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m multimodal_encoder_prefill_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def header_entry_points() -> list:
+    """Names of the functions that include/mhe.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mhe_[a-z_]+)\s*\(", text)))
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != MHE_OK:
+        msg = lib().mhe_last_error().decode(errors="replace")
+        raise MheError(fn, rc, msg)
+
+
+def make_config(hidden, n_heads, n_kv_heads, head_dim, intermediate, rms_eps=1e-6,
+                rope_theta=5e6, mrope_section=(24, 20, 20)) -> MheConfig:
+    c = MheConfig()
+    c.hidden, c.n_heads, c.n_kv_heads, c.head_dim = hidden, n_heads, n_kv_heads, head_dim
+    c.intermediate, c.rms_eps, c.rope_theta = intermediate, rms_eps, rope_theta
+    for i in range(3):
+        c.mrope_section[i] = int(mrope_section[i])
+    return c
+
+
+def config_from_dims(d) -> MheConfig:
+    return make_config(d.hidden, d.n_heads, d.n_kv_heads, d.head_dim, d.intermediate,
+                       d.rms_eps, d.rope_theta, d.mrope_section)
+
+
+def layer_table(weights) -> MheLayerWeights:
+    """Weight table from a mapping name -> tensor (or device address)."""
+    t = MheLayerWeights()
+    for name in WEIGHT_FIELDS:
+        setattr(t, name, _ptr(weights[name]))
+    return t
+
+
+def abi_version() -> int:
+    return lib().mhe_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().mhe_status_string(status).decode()
+
+
+def workspace_bytes(cfg: MheConfig, seq: int) -> int:
+    n = lib().mhe_workspace_bytes(ctypes.byref(cfg), seq)
+    if n == 0:
+        raise MheError("mhe_workspace_bytes", 2, lib().mhe_last_error().decode())
+    return n
+
+
+def layer_forward(cfg, weights, hidden, positions, seq, workspace, workspace_bytes, stream=None):
+    table = weights if isinstance(weights, MheLayerWeights) else layer_table(weights)
+    _check("mhe_layer_forward", lib().mhe_layer_forward(
+        ctypes.byref(cfg), ctypes.byref(table), _ptr(hidden), _ptr(positions), seq,
+        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def deepstack_inject(hidden, seq, hidden_dim, visual_mask, n_vis, feature, workspace,
+                     workspace_bytes, stream=None):
+    _check("mhe_deepstack_inject", lib().mhe_deepstack_inject(
+        _ptr(hidden), seq, hidden_dim, _ptr(visual_mask), n_vis, _ptr(feature),
+        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def encode(cfg, layers: Sequence, inputs_embeds, positions, seq, out, workspace,
+           workspace_bytes, visual_mask=None, n_vis=0, deepstack: Optional[Sequence] = None,
+           stream=None):
+    n_layers = len(layers)
+    tables = (MheLayerWeights * max(n_layers, 1))()
+    for i, w in enumerate(layers):
+        tables[i] = w if isinstance(w, MheLayerWeights) else layer_table(w)
+    n_ds = 0 if deepstack is None else len(deepstack)
+    ds = (ctypes.c_void_p * max(n_ds, 1))()
+    for i in range(n_ds):
+        ds[i] = _ptr(deepstack[i])
+    _check("mhe_encode", lib().mhe_encode(
+        ctypes.byref(cfg), tables if n_layers else None, n_layers, _ptr(inputs_embeds),
+        _ptr(positions), _ptr(visual_mask), n_vis, ds if n_ds else None, n_ds, seq, _ptr(out),
+        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def count_visual(visual_mask, seq, workspace, workspace_bytes, stream=None) -> int:
+    n = ctypes.c_int32(-1)
+    _check("mhe_count_visual", lib().mhe_count_visual(
+        _ptr(visual_mask), seq, ctypes.byref(n), _ptr(workspace), workspace_bytes,
+        _stream(stream)))
+    return n.value
+
+
+def rms_norm(x, gamma, y, rows, dim, eps, stream=None):
+    _check("mhe_rms_norm", lib().mhe_rms_norm(_ptr(x), _ptr(gamma), _ptr(y), rows, dim, eps,
+                                              _stream(stream)))
+
+
+def linear(a, w, c, m, n, k, residual=None, stream=None):
+    _check("mhe_linear", lib().mhe_linear(_ptr(a), _ptr(w), _ptr(c), _ptr(residual), m, n, k,
+                                          _stream(stream)))
+
+
+def linear_swiglu(a, w_gate, w_up, c, m, n, k, stream=None):
+    _check("mhe_linear_swiglu", lib().mhe_linear_swiglu(_ptr(a), _ptr(w_gate), _ptr(w_up),
+                                                        _ptr(c), m, n, k, _stream(stream)))
+
+
+def qk_norm_rope(cfg, qkv, q_norm, k_norm, positions, seq, q_out, k_out, vt_out, stream=None):
+    _check("mhe_qk_norm_rope", lib().mhe_qk_norm_rope(
+        ctypes.byref(cfg), _ptr(qkv), _ptr(q_norm), _ptr(k_norm), _ptr(positions), seq,
+        _ptr(q_out), _ptr(k_out), _ptr(vt_out), _stream(stream)))
+
+
+def attention(q, k, vt, o, seq, n_heads, n_kv_heads, head_dim, stream=None):
+    _check("mhe_attention", lib().mhe_attention(_ptr(q), _ptr(k), _ptr(vt), _ptr(o), seq,
+                                                n_heads, n_kv_heads, head_dim, _stream(stream)))
+
+
+def seq_pad(seq: int) -> int:
+    """Padded token count of the K / V^T layouts (multiple of 64)."""
+    return (seq + 63) // 64 * 64

@@ -1,0 +1,411 @@
+// C ABI of libmhe (declared in include/mhe.h): argument checks, workspace
+// carving and the launch sequence of one decoder layer and of the whole
+// prefill. Every check runs on the host before the first launch of a call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/mhe.h"
+#include "internal.h"
+
+using mhe::bf16_t;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int32_t hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MHE_OK;
+  return fail(MHE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxSeq = 1 << 17;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int32_t check_config(const mhe_config* c) {
+  if (!c) return fail(MHE_ERR_NULL, "config is NULL");
+  if (c->hidden <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->intermediate <= 0)
+    return fail(MHE_ERR_SHAPE, "config sizes must be positive");
+  if (c->n_heads % c->n_kv_heads != 0)
+    return fail(MHE_ERR_SHAPE, "n_heads (%d) is not a multiple of n_kv_heads (%d)", c->n_heads,
+                c->n_kv_heads);
+  if (c->head_dim % 2 != 0) return fail(MHE_ERR_SHAPE, "head_dim must be even");
+  if (!(c->rms_eps >= 0.f) || !std::isfinite(c->rms_eps))
+    return fail(MHE_ERR_SHAPE, "rms_eps must be finite and >= 0");
+  if (!(c->rope_theta > 0.f) || !std::isfinite(c->rope_theta))
+    return fail(MHE_ERR_SHAPE, "rope_theta must be finite and > 0");
+  for (int i = 0; i < 3; ++i)
+    if (c->mrope_section[i] < 0) return fail(MHE_ERR_SHAPE, "mrope_section must be >= 0");
+  if (!mhe::attention_supported(c->n_heads, c->n_kv_heads, c->head_dim))
+    return fail(MHE_ERR_UNSUPPORTED,
+                "attention built for head_dim 64/128 and 1, 2, 4 or 8 query heads per kv head "
+                "(got head_dim %d, %d/%d heads)",
+                c->head_dim, c->n_heads, c->n_kv_heads);
+  if (!mhe::rmsnorm_supported(c->hidden))
+    return fail(MHE_ERR_UNSUPPORTED, "hidden %d: must be a multiple of 8 and <= 8192", c->hidden);
+  const int qw = c->n_heads * c->head_dim;
+  const int qkvw = (c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
+  if (!mhe::gemm_supported(qkvw, c->hidden) || !mhe::gemm_supported(c->hidden, qw) ||
+      !mhe::gemm_supported(c->intermediate, c->hidden) ||
+      !mhe::gemm_supported(c->hidden, c->intermediate))
+    return fail(MHE_ERR_UNSUPPORTED,
+                "GEMM needs hidden, n_heads*head_dim and intermediate to be multiples of 64");
+  return MHE_OK;
+}
+
+struct Workspace {
+  bf16_t* hn;    // [S, H]
+  bf16_t* qkv;   // [S, (Hq + 2 Hkv) D]
+  bf16_t* qn;    // [S, Hq, D]
+  bf16_t* kn;    // [Hkv, Sp, D]
+  bf16_t* vt;    // [Hkv, D, Sp]
+  bf16_t* ao;    // [S, Hq D]
+  bf16_t* act;   // [S, I], aliases qkv..ao (used after attention)
+  int32_t* vis;  // [S]
+  int32_t* cnt;  // [1]
+  size_t total;
+};
+
+Workspace carve(const mhe_config& c, int seq, char* base) {
+  const size_t S = static_cast<size_t>(seq);
+  const size_t sp = static_cast<size_t>(mhe::seq_pad(seq));
+  const size_t D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
+  Workspace w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  w.hn = reinterpret_cast<bf16_t*>(take(S * c.hidden * 2));
+  const size_t region_start = off;
+  w.qkv = reinterpret_cast<bf16_t*>(take(S * (Hq + 2 * Hkv) * D * 2));
+  w.qn = reinterpret_cast<bf16_t*>(take(S * Hq * D * 2));
+  w.kn = reinterpret_cast<bf16_t*>(take(Hkv * sp * D * 2));
+  w.vt = reinterpret_cast<bf16_t*>(take(Hkv * D * sp * 2));
+  w.ao = reinterpret_cast<bf16_t*>(take(S * Hq * D * 2));
+  const size_t attn_bytes = off - region_start;
+  const size_t act_bytes = align_up(S * c.intermediate * 2);
+  w.act = reinterpret_cast<bf16_t*>(base ? base + region_start : nullptr);
+  if (act_bytes > attn_bytes) off = region_start + act_bytes;
+  w.vis = reinterpret_cast<int32_t*>(take(S * 4));
+  w.cnt = reinterpret_cast<int32_t*>(take(4));
+  w.total = off;
+  return w;
+}
+
+int32_t check_weights(const mhe_layer_weights* w, int layer) {
+  if (!w) return fail(MHE_ERR_NULL, "layer %d weights table is NULL", layer);
+  const void* p[] = {w->ln_in, w->w_q, w->w_k, w->w_v, w->q_norm, w->k_norm,
+                     w->w_o, w->ln_post, w->w_gate, w->w_up, w->w_down};
+  const char* names[] = {"ln_in", "w_q", "w_k", "w_v", "q_norm", "k_norm",
+                         "w_o", "ln_post", "w_gate", "w_up", "w_down"};
+  for (int i = 0; i < 11; ++i)
+    if (!p[i]) return fail(MHE_ERR_NULL, "layer %d: %s is NULL", layer, names[i]);
+  return MHE_OK;
+}
+
+int32_t check_seq(int32_t seq) {
+  if (seq <= 0 || seq > kMaxSeq) return fail(MHE_ERR_SHAPE, "seq %d out of range [1, %d]", seq, kMaxSeq);
+  return MHE_OK;
+}
+
+int32_t check_ws(const void* ws, size_t have, size_t need) {
+  if (!ws) return fail(MHE_ERR_NULL, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
+    return fail(MHE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(MHE_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+  return MHE_OK;
+}
+
+// The launch sequence of one decoder layer (arguments already checked).
+int32_t run_layer(const mhe_config& c, const mhe_layer_weights& w, bf16_t* x, const int32_t* pos,
+                  int seq, const Workspace& ws, hipStream_t st) {
+  const int H = c.hidden, D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
+  const int qw = Hq * D, kvw = Hkv * D;
+  int32_t rc;
+  // input RMSNorm
+  if ((rc = hip_check(mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_in), ws.hn, seq, H,
+                                          c.rms_eps, st),
+                      "input rmsnorm")))
+    return rc;
+  // q | k | v projections in one launch
+  mhe::BSegments qkv{{static_cast<const bf16_t*>(w.w_q), static_cast<const bf16_t*>(w.w_k),
+                      static_cast<const bf16_t*>(w.w_v)},
+                     {qw, kvw, kvw},
+                     3};
+  if ((rc = hip_check(mhe::launch_gemm(mhe::Epilogue::kStore, ws.hn, qkv, ws.qkv, nullptr, seq,
+                                       qw + 2 * kvw, H, st),
+                      "qkv projection")))
+    return rc;
+  // q/k norm + rotary, K and V relayout
+  mhe::RopeParams rp{Hq, Hkv, D, c.rms_eps, c.rope_theta,
+                     {c.mrope_section[0], c.mrope_section[1], c.mrope_section[2]}};
+  if ((rc = hip_check(mhe::launch_qk_norm_rope(rp, ws.qkv, static_cast<const bf16_t*>(w.q_norm),
+                                               static_cast<const bf16_t*>(w.k_norm), pos, seq,
+                                               ws.qn, ws.kn, ws.vt, st),
+                      "q/k norm + rotary")))
+    return rc;
+  if ((rc = hip_check(mhe::launch_attention(ws.qn, ws.kn, ws.vt, ws.ao, seq, Hq, Hkv, D, st),
+                      "attention")))
+    return rc;
+  // O projection + residual, in place on x
+  mhe::BSegments wo{{static_cast<const bf16_t*>(w.w_o), nullptr, nullptr}, {H, 0, 0}, 1};
+  if ((rc = hip_check(mhe::launch_gemm(mhe::Epilogue::kResidual, ws.ao, wo, x, x, seq, H, qw, st),
+                      "o projection")))
+    return rc;
+  if ((rc = hip_check(mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_post), ws.hn, seq, H,
+                                          c.rms_eps, st),
+                      "post-attention rmsnorm")))
+    return rc;
+  mhe::BSegments gu{{static_cast<const bf16_t*>(w.w_gate), static_cast<const bf16_t*>(w.w_up),
+                     nullptr},
+                    {c.intermediate, c.intermediate, 0},
+                    2};
+  if ((rc = hip_check(mhe::launch_gemm(mhe::Epilogue::kSwiGLU, ws.hn, gu, ws.act, nullptr, seq,
+                                       c.intermediate, H, st),
+                      "gate/up projection")))
+    return rc;
+  mhe::BSegments wd{{static_cast<const bf16_t*>(w.w_down), nullptr, nullptr}, {H, 0, 0}, 1};
+  return hip_check(mhe::launch_gemm(mhe::Epilogue::kResidual, ws.act, wd, x, x, seq, H,
+                                    c.intermediate, st),
+                   "down projection");
+}
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const char* pa = static_cast<const char*>(a);
+  const char* pb = static_cast<const char*>(b);
+  return pa < pb + bn && pb < pa + an;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mhe_abi_version(void) { return MHE_ABI_VERSION; }
+
+const char* mhe_status_string(int32_t s) {
+  switch (s) {
+    case MHE_OK: return "ok";
+    case MHE_ERR_NULL: return "null pointer";
+    case MHE_ERR_SHAPE: return "invalid shape";
+    case MHE_ERR_MISMATCH: return "visual token count mismatch";
+    case MHE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MHE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MHE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* mhe_last_error(void) { return g_last_error.c_str(); }
+
+size_t mhe_workspace_bytes(const mhe_config* cfg, int32_t seq) {
+  if (check_config(cfg) || check_seq(seq)) return 0;
+  return carve(*cfg, seq, nullptr).total;
+}
+
+int32_t mhe_layer_forward(const mhe_config* cfg, const mhe_layer_weights* w, void* hidden,
+                          const int32_t* positions, int32_t seq, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  int32_t rc;
+  if ((rc = check_config(cfg))) return rc;
+  if ((rc = check_weights(w, 0))) return rc;
+  if (!hidden) return fail(MHE_ERR_NULL, "hidden is NULL");
+  if (!positions) return fail(MHE_ERR_NULL, "positions is NULL");
+  if ((rc = check_seq(seq))) return rc;
+  const Workspace need = carve(*cfg, seq, nullptr);
+  if ((rc = check_ws(workspace, workspace_bytes, need.total))) return rc;
+  const Workspace ws = carve(*cfg, seq, static_cast<char*>(workspace));
+  return run_layer(*cfg, *w, static_cast<bf16_t*>(hidden), positions, seq, ws,
+                   static_cast<hipStream_t>(stream));
+}
+
+int32_t mhe_deepstack_inject(void* hidden, int32_t seq, int32_t hidden_dim,
+                             const uint8_t* visual_mask, int32_t n_vis, const void* feature,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t rc;
+  if ((rc = check_seq(seq))) return rc;
+  if (hidden_dim <= 0 || hidden_dim % 8 != 0)
+    return fail(MHE_ERR_SHAPE, "hidden_dim %d must be a positive multiple of 8", hidden_dim);
+  if (n_vis < 0 || n_vis > seq) return fail(MHE_ERR_SHAPE, "n_vis %d out of range [0, %d]", n_vis, seq);
+  if (n_vis == 0) return MHE_OK;
+  if (!hidden || !visual_mask || !feature) return fail(MHE_ERR_NULL, "hidden, visual_mask and feature are required");
+  if ((rc = check_ws(workspace, workspace_bytes, align_up(static_cast<size_t>(seq) * 4) + 256))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* idx = static_cast<int32_t*>(workspace);
+  int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align_up(static_cast<size_t>(seq) * 4));
+  if ((rc = hip_check(mhe::launch_visual_index(visual_mask, seq, n_vis, idx, cnt, st), "visual index")))
+    return rc;
+  return hip_check(mhe::launch_deepstack_add(static_cast<bf16_t*>(hidden), hidden_dim, idx, n_vis,
+                                             static_cast<const bf16_t*>(feature), st),
+                   "deepstack add");
+}
+
+int32_t mhe_encode(const mhe_config* cfg, const mhe_layer_weights* layers, int32_t n_layers,
+                   const void* inputs_embeds, const int32_t* positions,
+                   const uint8_t* visual_mask, int32_t n_vis, const void* const* deepstack,
+                   int32_t n_ds, int32_t seq, void* out, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  int32_t rc;
+  if ((rc = check_config(cfg))) return rc;
+  if ((rc = check_seq(seq))) return rc;
+  if (n_layers < 0) return fail(MHE_ERR_SHAPE, "n_layers %d < 0", n_layers);
+  if (n_ds < 0) return fail(MHE_ERR_SHAPE, "n_ds %d < 0", n_ds);
+  if (n_vis < 0 || n_vis > seq) return fail(MHE_ERR_SHAPE, "n_vis %d out of range [0, %d]", n_vis, seq);
+  if (!inputs_embeds || !out) return fail(MHE_ERR_NULL, "inputs_embeds and out are required");
+  if (!positions) return fail(MHE_ERR_NULL, "positions is NULL");
+  if (n_layers > 0 && !layers) return fail(MHE_ERR_NULL, "layers is NULL");
+  for (int l = 0; l < n_layers; ++l)
+    if ((rc = check_weights(&layers[l], l))) return rc;
+  const int used_ds = (n_vis > 0) ? (n_ds < n_layers ? n_ds : n_layers) : 0;
+  if (used_ds > 0) {
+    if (!visual_mask) return fail(MHE_ERR_NULL, "visual_mask is NULL with DeepStack levels");
+    if (!deepstack) return fail(MHE_ERR_NULL, "deepstack table is NULL");
+    for (int l = 0; l < used_ds; ++l)
+      if (!deepstack[l]) return fail(MHE_ERR_NULL, "deepstack[%d] is NULL", l);
+  }
+  const size_t act_bytes = static_cast<size_t>(seq) * cfg->hidden * 2;
+  if (overlaps(out, act_bytes, inputs_embeds, act_bytes))
+    return fail(MHE_ERR_SHAPE, "out overlaps inputs_embeds");
+  const Workspace need = carve(*cfg, seq, nullptr);
+  if ((rc = check_ws(workspace, workspace_bytes, need.total))) return rc;
+  if (overlaps(out, act_bytes, workspace, need.total))
+    return fail(MHE_ERR_SHAPE, "out overlaps the workspace");
+
+  const Workspace ws = carve(*cfg, seq, static_cast<char*>(workspace));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  bf16_t* x = static_cast<bf16_t*>(out);
+  if ((rc = hip_check(hipMemcpyAsync(x, inputs_embeds, act_bytes, hipMemcpyDeviceToDevice, st),
+                      "copy inputs_embeds")))
+    return rc;
+  if (used_ds > 0 &&
+      (rc = hip_check(mhe::launch_visual_index(visual_mask, seq, n_vis, ws.vis, ws.cnt, st),
+                      "visual index")))
+    return rc;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((rc = run_layer(*cfg, layers[l], x, positions, seq, ws, st))) return rc;
+    if (l < used_ds &&
+        (rc = hip_check(mhe::launch_deepstack_add(x, cfg->hidden, ws.vis, n_vis,
+                                                  static_cast<const bf16_t*>(deepstack[l]), st),
+                        "deepstack add")))
+      return rc;
+  }
+  return MHE_OK;
+}
+
+int32_t mhe_count_visual(const uint8_t* visual_mask, int32_t seq, int32_t* count_host,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t rc;
+  if ((rc = check_seq(seq))) return rc;
+  if (!visual_mask || !count_host) return fail(MHE_ERR_NULL, "visual_mask and count_host are required");
+  if ((rc = check_ws(workspace, workspace_bytes, align_up(static_cast<size_t>(seq) * 4) + 256))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* idx = static_cast<int32_t*>(workspace);
+  int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align_up(static_cast<size_t>(seq) * 4));
+  if ((rc = hip_check(mhe::launch_visual_index(visual_mask, seq, 0, idx, cnt, st), "visual index")))
+    return rc;
+  if ((rc = hip_check(hipMemcpyAsync(count_host, cnt, 4, hipMemcpyDeviceToHost, st), "count copy")))
+    return rc;
+  return hip_check(hipStreamSynchronize(st), "stream synchronize");
+}
+
+int32_t mhe_rms_norm(const void* x, const void* gamma, void* y, int32_t rows, int32_t dim,
+                     float eps, void* stream) {
+  if (!x || !gamma || !y) return fail(MHE_ERR_NULL, "x, gamma and y are required");
+  if (rows <= 0) return fail(MHE_ERR_SHAPE, "rows %d must be > 0", rows);
+  if (!mhe::rmsnorm_supported(dim)) return fail(MHE_ERR_UNSUPPORTED, "dim %d: multiple of 8, <= 8192", dim);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MHE_ERR_SHAPE, "eps must be finite and >= 0");
+  return hip_check(mhe::launch_rmsnorm(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(gamma),
+                                       static_cast<bf16_t*>(y), rows, dim, eps,
+                                       static_cast<hipStream_t>(stream)),
+                   "rmsnorm");
+}
+
+int32_t mhe_linear(const void* a, const void* w, void* c, const void* residual, int32_t m,
+                   int32_t n, int32_t k, void* stream) {
+  if (!a || !w || !c) return fail(MHE_ERR_NULL, "a, w and c are required");
+  if (m <= 0 || n <= 0 || k <= 0) return fail(MHE_ERR_SHAPE, "m, n, k must be > 0");
+  if (!mhe::gemm_supported(n, k)) return fail(MHE_ERR_UNSUPPORTED, "needs n %% 32 == 0 and k %% 64 == 0 (n=%d, k=%d)", n, k);
+  const size_t cb = static_cast<size_t>(m) * n * 2;
+  if (overlaps(c, cb, a, static_cast<size_t>(m) * k * 2) || overlaps(c, cb, w, static_cast<size_t>(n) * k * 2))
+    return fail(MHE_ERR_SHAPE, "c overlaps an operand");
+  if (residual && residual != c && overlaps(c, cb, residual, cb))
+    return fail(MHE_ERR_SHAPE, "residual partially overlaps c");
+  mhe::BSegments b{{static_cast<const bf16_t*>(w), nullptr, nullptr}, {n, 0, 0}, 1};
+  return hip_check(mhe::launch_gemm(residual ? mhe::Epilogue::kResidual : mhe::Epilogue::kStore,
+                                    static_cast<const bf16_t*>(a), b, static_cast<bf16_t*>(c),
+                                    static_cast<const bf16_t*>(residual), m, n, k,
+                                    static_cast<hipStream_t>(stream)),
+                   "linear");
+}
+
+int32_t mhe_linear_swiglu(const void* a, const void* w_gate, const void* w_up, void* c,
+                          int32_t m, int32_t n, int32_t k, void* stream) {
+  if (!a || !w_gate || !w_up || !c) return fail(MHE_ERR_NULL, "a, w_gate, w_up and c are required");
+  if (m <= 0 || n <= 0 || k <= 0) return fail(MHE_ERR_SHAPE, "m, n, k must be > 0");
+  if (!mhe::gemm_supported(n, k)) return fail(MHE_ERR_UNSUPPORTED, "needs n %% 32 == 0 and k %% 64 == 0 (n=%d, k=%d)", n, k);
+  const size_t cb = static_cast<size_t>(m) * n * 2;
+  if (overlaps(c, cb, a, static_cast<size_t>(m) * k * 2))
+    return fail(MHE_ERR_SHAPE, "c overlaps a");
+  mhe::BSegments b{{static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(w_up), nullptr},
+                   {n, n, 0},
+                   2};
+  return hip_check(mhe::launch_gemm(mhe::Epilogue::kSwiGLU, static_cast<const bf16_t*>(a), b,
+                                    static_cast<bf16_t*>(c), nullptr, m, n, k,
+                                    static_cast<hipStream_t>(stream)),
+                   "linear_swiglu");
+}
+
+int32_t mhe_qk_norm_rope(const mhe_config* cfg, const void* qkv, const void* q_norm,
+                         const void* k_norm, const int32_t* positions, int32_t seq, void* q_out,
+                         void* k_out, void* vt_out, void* stream) {
+  int32_t rc;
+  if ((rc = check_config(cfg))) return rc;
+  if ((rc = check_seq(seq))) return rc;
+  if (!qkv || !q_norm || !k_norm || !positions || !q_out || !k_out || !vt_out)
+    return fail(MHE_ERR_NULL, "all buffers are required");
+  mhe::RopeParams rp{cfg->n_heads, cfg->n_kv_heads, cfg->head_dim, cfg->rms_eps, cfg->rope_theta,
+                     {cfg->mrope_section[0], cfg->mrope_section[1], cfg->mrope_section[2]}};
+  return hip_check(mhe::launch_qk_norm_rope(rp, static_cast<const bf16_t*>(qkv),
+                                            static_cast<const bf16_t*>(q_norm),
+                                            static_cast<const bf16_t*>(k_norm), positions, seq,
+                                            static_cast<bf16_t*>(q_out), static_cast<bf16_t*>(k_out),
+                                            static_cast<bf16_t*>(vt_out),
+                                            static_cast<hipStream_t>(stream)),
+                   "q/k norm + rotary");
+}
+
+int32_t mhe_attention(const void* q, const void* k, const void* vt, void* o, int32_t seq,
+                      int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, void* stream) {
+  int32_t rc;
+  if ((rc = check_seq(seq))) return rc;
+  if (!q || !k || !vt || !o) return fail(MHE_ERR_NULL, "q, k, vt and o are required");
+  if (n_heads <= 0 || n_kv_heads <= 0 || n_heads % n_kv_heads != 0)
+    return fail(MHE_ERR_SHAPE, "n_heads must be a positive multiple of n_kv_heads");
+  if (!mhe::attention_supported(n_heads, n_kv_heads, head_dim))
+    return fail(MHE_ERR_UNSUPPORTED, "head_dim 64/128 and 1, 2, 4 or 8 query heads per kv head");
+  return hip_check(mhe::launch_attention(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                                         static_cast<const bf16_t*>(vt), static_cast<bf16_t*>(o), seq,
+                                         n_heads, n_kv_heads, head_dim,
+                                         static_cast<hipStream_t>(stream)),
+                   "attention");
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Launchers of the libmhe kernels (host side, called by api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mhe {
+
+typedef uint16_t bf16_t;
+
+// rmsnorm.hip
+bool rmsnorm_supported(int dim);
+hipError_t launch_rmsnorm(const bf16_t* x, const bf16_t* gamma, bf16_t* y, int rows, int dim,
+                          float eps, hipStream_t stream);
+
+// gemm.hip: C[m, n] = A[m, :] . B[n, :] with one of three epilogues.
+enum class Epilogue { kStore = 0, kResidual = 1, kSwiGLU = 2 };
+
+// Up to three row segments that together form the B operand (e.g. w_q | w_k | w_v).
+struct BSegments {
+  const bf16_t* ptr[3];
+  int rows[3];
+  int count;
+};
+
+bool gemm_supported(int n, int k);
+// kStore / kResidual: B is the concatenation of the segments (n = total rows).
+// kSwiGLU: seg 0 = gate, seg 1 = up, each n rows; C has n columns.
+hipError_t launch_gemm(Epilogue epi, const bf16_t* a, const BSegments& b, bf16_t* c,
+                       const bf16_t* residual, int m, int n, int k, hipStream_t stream);
+
+// qk_norm_rope.hip
+struct RopeParams {
+  int n_heads, n_kv_heads, head_dim;
+  float eps, theta;
+  int section[3];
+};
+int seq_pad(int seq);
+hipError_t launch_qk_norm_rope(const RopeParams& p, const bf16_t* qkv, const bf16_t* q_norm,
+                               const bf16_t* k_norm, const int32_t* positions, int seq,
+                               bf16_t* q_out, bf16_t* k_out, bf16_t* vt_out, hipStream_t stream);
+
+// attention.hip
+bool attention_supported(int n_heads, int n_kv_heads, int head_dim);
+hipError_t launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o,
+                            int seq, int n_heads, int n_kv_heads, int head_dim,
+                            hipStream_t stream);
+
+// deepstack.hip
+hipError_t launch_visual_index(const uint8_t* mask, int seq, int n_vis, int32_t* idx,
+                               int32_t* count, hipStream_t stream);
+hipError_t launch_deepstack_add(bf16_t* hidden, int hidden_dim, const int32_t* idx, int n_vis,
+                                const bf16_t* feature, hipStream_t stream);
+
+}  // namespace mhe

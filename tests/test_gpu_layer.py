@@ -1,0 +1,160 @@
+"""Decoder layer and whole-prefill parity of the HIP path against the CPU oracle.
+
+Bars (fixed by the decoder's own accuracy target): one layer, fed the GPU's
+bf16 hidden state (teacher-forced), agrees with the float64 oracle to
+rel-L2 <= 2e-2; the free-running stack agrees at its last layer to
+rel-L2 <= 5e-2. Max-abs is printed beside every rel-L2.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from multimodal_encoder_prefill_amd import binding as b
+from multimodal_encoder_prefill_amd import synth
+from helpers import f64, report, oracle_dims, oracle_layer
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _setup(wl, n_layers=None):
+    n_layers = wl.n_layers if n_layers is None else n_layers
+    layers = [synth.layer_weights(wl, l, DEV) for l in range(n_layers)]
+    emb = synth.embeddings(wl, DEV)
+    pos_np = synth.positions(wl)
+    pos = torch.from_numpy(pos_np).to(DEV)
+    mask_np = synth.visual_mask(wl)
+    mask = torch.from_numpy(mask_np).to(DEV)
+    ds = [synth.deepstack_features(wl, i, DEV) for i in range(wl.n_ds)]
+    cfg = b.config_from_dims(wl.dims)
+    nbytes = b.workspace_bytes(cfg, wl.seq)
+    ws = torch.empty(nbytes, device=DEV, dtype=torch.uint8)
+    return dict(layers=layers, emb=emb, pos=pos, pos_np=pos_np, mask=mask, mask_np=mask_np,
+                ds=ds, cfg=cfg, ws=ws, nbytes=nbytes)
+
+
+def _gpu_states(wl, s):
+    """hidden_states[0..L] from the GPU, one layer (and DeepStack level) per call."""
+    h = s["emb"].clone()
+    states = [h.clone()]
+    for l, w in enumerate(s["layers"]):
+        b.layer_forward(s["cfg"], w, h, s["pos"], wl.seq, s["ws"], s["nbytes"])
+        if l < len(s["ds"]) and wl.n_vis > 0:
+            b.deepstack_inject(h, wl.seq, wl.dims.hidden, s["mask"], wl.n_vis, s["ds"][l],
+                               s["ws"], s["nbytes"])
+        states.append(h.clone())
+    torch.cuda.synchronize()
+    return states
+
+
+def _teacher_forced(wl, s, states, rows=None, layers=None):
+    dims = oracle_dims(wl.dims)
+    cos, sin = oracle.rope_cos_sin(s["pos_np"], dims.head_dim, dims.rope_theta, dims.mrope_section)
+    idx = np.flatnonzero(s["mask_np"])
+    worst = 0.0
+    for l in (range(len(s["layers"])) if layers is None else layers):
+        h_in = f64(states[l])
+        r = np.arange(wl.seq) if rows is None else rows
+        ref = oracle.decoder_layer(h_in, oracle_layer(s["layers"][l]), cos, sin, dims, rows=r)
+        if l < len(s["ds"]) and wl.n_vis > 0:
+            feat = f64(s["ds"][l])
+            pos_in_vis = np.searchsorted(idx, r)
+            is_vis = s["mask_np"][r] != 0
+            ref[is_vis] += feat[pos_in_vis[is_vis]]
+        got = f64(states[l + 1])[r]
+        rel, _ = report(f"{wl.key} layer {l} (teacher-forced)", got, ref)
+        worst = max(worst, rel)
+    return worst
+
+
+def test_layer_tiny_teacher_forced():
+    wl = synth.WORKLOADS["tiny"]
+    s = _setup(wl)
+    states = _gpu_states(wl, s)
+    assert _teacher_forced(wl, s, states) <= 2e-2
+
+
+def test_layer_full_width_s512_teacher_forced():
+    wl = synth.WORKLOADS["layer1_s512"]
+    s = _setup(wl)
+    states = _gpu_states(wl, s)
+    rows = np.unique(np.concatenate([np.arange(0, 512, 17), [1, 255, 256, 510, 511]]))
+    assert _teacher_forced(wl, s, states, rows=rows) <= 2e-2
+
+
+def _run_encode(wl, s, n_layers=None):
+    layers = s["layers"] if n_layers is None else s["layers"][:n_layers]
+    out = torch.empty_like(s["emb"])
+    b.encode(s["cfg"], layers, s["emb"], s["pos"], wl.seq, out, s["ws"], s["nbytes"],
+             visual_mask=s["mask"] if wl.n_vis else None, n_vis=wl.n_vis,
+             deepstack=s["ds"] if wl.n_vis else None)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_encode_tiny_free_running():
+    wl = synth.WORKLOADS["tiny"]
+    s = _setup(wl)
+    emb0 = s["emb"].clone()
+    out = _run_encode(wl, s)
+    assert torch.equal(s["emb"], emb0)                       # input not written
+    ref = oracle.encode(f64(s["emb"]), s["pos_np"], [oracle_layer(w) for w in s["layers"]],
+                        oracle_dims(wl.dims))
+    assert report("tiny layer-2 free-running", f64(out), ref)[0] <= 5e-2
+
+
+def _narrow_stack(n_layers, seq, grid, n_ds):
+    dims = synth.Dims(hidden=512, n_heads=8, n_kv_heads=1, head_dim=64, intermediate=1536,
+                      rms_eps=1e-6, rope_theta=1e6)
+    text = (seq - int(np.prod(grid))) // 2
+    segs = (("text", text), ("visual", grid), ("text", seq - text - int(np.prod(grid))))
+    return synth.custom_workload(dims, seq, n_layers, segs, n_ds, key="narrow50", index=50)
+
+
+def test_encode_50_layers_narrow_free_running():
+    """50 layers free-running, every DeepStack level, image segment: the error at
+    hidden_states[50] stays within the end-to-end bar."""
+    wl = _narrow_stack(50, 300, (1, 8, 16), 3)
+    s = _setup(wl)
+    out = _run_encode(wl, s)
+    states = oracle.encode(f64(s["emb"]), s["pos_np"], [oracle_layer(w) for w in s["layers"]],
+                           oracle_dims(wl.dims), visual_mask=s["mask_np"],
+                           deepstack=[f64(d) for d in s["ds"]], return_all=True)
+    assert report("narrow hidden_states[50] free-running", f64(out), states[-1])[0] <= 5e-2
+    gpu_states = _gpu_states(wl, s)
+    assert torch.equal(gpu_states[-1], out)                  # encode == layer-by-layer calls
+    assert _teacher_forced(wl, s, gpu_states, layers=[0, 1, 2, 3, 25, 49]) <= 2e-2
+
+
+def test_encode_image_s2048_l4_deepstack():
+    wl = synth.WORKLOADS["image_s2048_l4"]
+    s = _setup(wl)
+    out = _run_encode(wl, s)
+    states = _gpu_states(wl, s)
+    assert torch.equal(states[-1], out)
+    rows = np.unique(np.concatenate([np.arange(0, wl.seq, 97), [511, 512, 1535, 1536, wl.seq - 1]]))
+    assert _teacher_forced(wl, s, states, rows=rows) <= 2e-2
+
+
+def test_encode_causal_bitwise():
+    wl = _narrow_stack(3, 200, (1, 4, 8), 2)
+    s = _setup(wl)
+    out1 = _run_encode(wl, s)
+    cut = 120
+    s["emb"][cut:] += 1.0
+    out2 = _run_encode(wl, s)
+    assert torch.equal(out1[:cut], out2[:cut])
+    assert not torch.equal(out1[cut:], out2[cut:])
+
+
+def test_encode_no_deepstack_when_no_visual_tokens():
+    wl = synth.WORKLOADS["tiny"]
+    s = _setup(wl)
+    out = _run_encode(wl, s)
+    out2 = torch.empty_like(out)
+    b.encode(s["cfg"], s["layers"], s["emb"], s["pos"], wl.seq, out2, s["ws"], s["nbytes"],
+             visual_mask=None, n_vis=0, deepstack=None)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
