@@ -165,6 +165,34 @@ int32_t mhe_encode(const mhe_config* cfg, const mhe_layer_weights* layers, int32
 int32_t mhe_count_visual(const uint8_t* visual_mask, int32_t seq, int32_t* count_host,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- optional launch timing -------------------------------------------------- */
+
+/* Steps of one decoder layer (plus the DeepStack add), as trace bit positions. */
+enum {
+  MHE_STEP_INPUT_NORM = 0, /* input RMSNorm */
+  MHE_STEP_QKV = 1,        /* q | k | v projections */
+  MHE_STEP_QK_ROPE = 2,    /* q/k RMSNorm + rotary + K/V relayout */
+  MHE_STEP_ATTENTION = 3,  /* causal GQA attention */
+  MHE_STEP_O_PROJ = 4,     /* O projection + residual */
+  MHE_STEP_POST_NORM = 5,  /* post-attention RMSNorm */
+  MHE_STEP_GATE_UP = 6,    /* gate/up projections + SiLU*mul */
+  MHE_STEP_DOWN = 7,       /* down projection + residual */
+  MHE_STEP_DEEPSTACK = 8,  /* DeepStack scatter-add */
+  MHE_STEP_COUNT = 9
+};
+
+/*
+ * Process-wide, opt-in launch timing (the one piece of library state). With
+ * bit s of `step_mask` set, every later launch of step s made by
+ * mhe_layer_forward / mhe_encode is bracketed by a pair of HIP events on the
+ * call's stream; mask 0 turns recording off (the default). mhe_trace_read
+ * waits for the recorded events of `step`, writes the summed kernel time in
+ * milliseconds and the number of launches, and clears that step's record.
+ * Calls that overlap on several host threads share one record.
+ */
+int32_t mhe_trace_enable(uint32_t step_mask);
+int32_t mhe_trace_read(int32_t step, double* total_ms, int64_t* launches);
+
 /* ---- single steps of the layer, each one kernel (used for per-step checks) ---- */
 
 /*

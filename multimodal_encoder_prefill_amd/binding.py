@@ -67,7 +67,13 @@ _SIGNATURES = {
     "mhe_qk_norm_rope": (_i32, [ctypes.POINTER(MheConfig), _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                                 _vp, _vp]),
     "mhe_attention": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "mhe_trace_enable": (_i32, [ctypes.c_uint32]),
+    "mhe_trace_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
 }
+
+# step ids of the trace facility (MHE_STEP_* in include/mhe.h)
+STEPS = ("input_norm", "qkv", "qk_rope", "attention", "o_proj", "post_norm", "gate_up", "down",
+         "deepstack")
 
 
 def lib() -> ctypes.CDLL:
@@ -215,6 +221,22 @@ def qk_norm_rope(cfg, qkv, q_norm, k_norm, positions, seq, q_out, k_out, vt_out,
 def attention(q, k, vt, o, seq, n_heads, n_kv_heads, head_dim, stream=None):
     _check("mhe_attention", lib().mhe_attention(_ptr(q), _ptr(k), _ptr(vt), _ptr(o), seq,
                                                 n_heads, n_kv_heads, head_dim, _stream(stream)))
+
+
+def trace_enable(steps) -> None:
+    """Record launch times of the named steps (an iterable of STEPS names; empty = off)."""
+    mask = 0
+    for name in steps:
+        mask |= 1 << STEPS.index(name)
+    _check("mhe_trace_enable", lib().mhe_trace_enable(mask))
+
+
+def trace_read(step: str):
+    """(total milliseconds, launches) recorded for `step` since the last read."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    _check("mhe_trace_read", lib().mhe_trace_read(STEPS.index(step), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def seq_pad(seq: int) -> int:

@@ -3,11 +3,14 @@
 // prefill. Every check runs on the host before the first launch of a call.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/mhe.h"
 #include "internal.h"
@@ -135,58 +138,105 @@ int32_t check_ws(const void* ws, size_t have, size_t need) {
   return MHE_OK;
 }
 
+// ---- opt-in launch timing: event pairs around the launches of chosen steps ----
+struct EventPair {
+  hipEvent_t start, stop;
+};
+struct StepTrace {
+  std::vector<EventPair> pending;
+  double done_ms = 0.0;
+  int64_t launches = 0;
+};
+std::atomic<uint32_t> g_trace_mask{0};
+std::mutex g_trace_mu;
+StepTrace g_trace[MHE_STEP_COUNT];
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t pooled_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` (returning hipError_t); when the step is traced, brackets it
+// with two events recorded on `st`.
+template <typename F>
+int32_t traced(int step, hipStream_t st, const char* what, F&& launch) {
+  if (!(g_trace_mask.load(std::memory_order_relaxed) & (1u << step))) return hip_check(launch(), what);
+  EventPair ev{nullptr, nullptr};
+  {
+    std::lock_guard<std::mutex> lk(g_trace_mu);
+    ev.start = pooled_event();
+    ev.stop = pooled_event();
+  }
+  if (!ev.start || !ev.stop) return fail(MHE_ERR_HIP, "%s: could not create trace events", what);
+  int32_t rc;
+  if ((rc = hip_check(hipEventRecord(ev.start, st), "trace event"))) return rc;
+  if ((rc = hip_check(launch(), what))) return rc;
+  if ((rc = hip_check(hipEventRecord(ev.stop, st), "trace event"))) return rc;
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  g_trace[step].pending.push_back(ev);
+  return MHE_OK;
+}
+
 // The launch sequence of one decoder layer (arguments already checked).
 int32_t run_layer(const mhe_config& c, const mhe_layer_weights& w, bf16_t* x, const int32_t* pos,
                   int seq, const Workspace& ws, hipStream_t st) {
   const int H = c.hidden, D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
   const int qw = Hq * D, kvw = Hkv * D;
   int32_t rc;
-  // input RMSNorm
-  if ((rc = hip_check(mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_in), ws.hn, seq, H,
-                                          c.rms_eps, st),
-                      "input rmsnorm")))
+  if ((rc = traced(MHE_STEP_INPUT_NORM, st, "input rmsnorm", [&] {
+         return mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_in), ws.hn, seq, H, c.rms_eps, st);
+       })))
     return rc;
   // q | k | v projections in one launch
-  mhe::BSegments qkv{{static_cast<const bf16_t*>(w.w_q), static_cast<const bf16_t*>(w.w_k),
-                      static_cast<const bf16_t*>(w.w_v)},
-                     {qw, kvw, kvw},
-                     3};
-  if ((rc = hip_check(mhe::launch_gemm(mhe::Epilogue::kStore, ws.hn, qkv, ws.qkv, nullptr, seq,
-                                       qw + 2 * kvw, H, st),
-                      "qkv projection")))
+  const mhe::BSegments qkv{{static_cast<const bf16_t*>(w.w_q), static_cast<const bf16_t*>(w.w_k),
+                            static_cast<const bf16_t*>(w.w_v)},
+                           {qw, kvw, kvw},
+                           3};
+  if ((rc = traced(MHE_STEP_QKV, st, "qkv projection", [&] {
+         return mhe::launch_gemm(mhe::Epilogue::kStore, ws.hn, qkv, ws.qkv, nullptr, seq, qw + 2 * kvw, H, st);
+       })))
     return rc;
   // q/k norm + rotary, K and V relayout
-  mhe::RopeParams rp{Hq, Hkv, D, c.rms_eps, c.rope_theta,
-                     {c.mrope_section[0], c.mrope_section[1], c.mrope_section[2]}};
-  if ((rc = hip_check(mhe::launch_qk_norm_rope(rp, ws.qkv, static_cast<const bf16_t*>(w.q_norm),
-                                               static_cast<const bf16_t*>(w.k_norm), pos, seq,
-                                               ws.qn, ws.kn, ws.vt, st),
-                      "q/k norm + rotary")))
+  const mhe::RopeParams rp{Hq, Hkv, D, c.rms_eps, c.rope_theta,
+                           {c.mrope_section[0], c.mrope_section[1], c.mrope_section[2]}};
+  if ((rc = traced(MHE_STEP_QK_ROPE, st, "q/k norm + rotary", [&] {
+         return mhe::launch_qk_norm_rope(rp, ws.qkv, static_cast<const bf16_t*>(w.q_norm),
+                                         static_cast<const bf16_t*>(w.k_norm), pos, seq, ws.qn, ws.kn,
+                                         ws.vt, st);
+       })))
     return rc;
-  if ((rc = hip_check(mhe::launch_attention(ws.qn, ws.kn, ws.vt, ws.ao, seq, Hq, Hkv, D, st),
-                      "attention")))
+  if ((rc = traced(MHE_STEP_ATTENTION, st, "attention", [&] {
+         return mhe::launch_attention(ws.qn, ws.kn, ws.vt, ws.ao, seq, Hq, Hkv, D, st);
+       })))
     return rc;
   // O projection + residual, in place on x
-  mhe::BSegments wo{{static_cast<const bf16_t*>(w.w_o), nullptr, nullptr}, {H, 0, 0}, 1};
-  if ((rc = hip_check(mhe::launch_gemm(mhe::Epilogue::kResidual, ws.ao, wo, x, x, seq, H, qw, st),
-                      "o projection")))
+  const mhe::BSegments wo{{static_cast<const bf16_t*>(w.w_o), nullptr, nullptr}, {H, 0, 0}, 1};
+  if ((rc = traced(MHE_STEP_O_PROJ, st, "o projection", [&] {
+         return mhe::launch_gemm(mhe::Epilogue::kResidual, ws.ao, wo, x, x, seq, H, qw, st);
+       })))
     return rc;
-  if ((rc = hip_check(mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_post), ws.hn, seq, H,
-                                          c.rms_eps, st),
-                      "post-attention rmsnorm")))
+  if ((rc = traced(MHE_STEP_POST_NORM, st, "post-attention rmsnorm", [&] {
+         return mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_post), ws.hn, seq, H, c.rms_eps, st);
+       })))
     return rc;
-  mhe::BSegments gu{{static_cast<const bf16_t*>(w.w_gate), static_cast<const bf16_t*>(w.w_up),
-                     nullptr},
-                    {c.intermediate, c.intermediate, 0},
-                    2};
-  if ((rc = hip_check(mhe::launch_gemm(mhe::Epilogue::kSwiGLU, ws.hn, gu, ws.act, nullptr, seq,
-                                       c.intermediate, H, st),
-                      "gate/up projection")))
+  const mhe::BSegments gu{{static_cast<const bf16_t*>(w.w_gate), static_cast<const bf16_t*>(w.w_up), nullptr},
+                          {c.intermediate, c.intermediate, 0},
+                          2};
+  if ((rc = traced(MHE_STEP_GATE_UP, st, "gate/up projection", [&] {
+         return mhe::launch_gemm(mhe::Epilogue::kSwiGLU, ws.hn, gu, ws.act, nullptr, seq, c.intermediate, H, st);
+       })))
     return rc;
-  mhe::BSegments wd{{static_cast<const bf16_t*>(w.w_down), nullptr, nullptr}, {H, 0, 0}, 1};
-  return hip_check(mhe::launch_gemm(mhe::Epilogue::kResidual, ws.act, wd, x, x, seq, H,
-                                    c.intermediate, st),
-                   "down projection");
+  const mhe::BSegments wd{{static_cast<const bf16_t*>(w.w_down), nullptr, nullptr}, {H, 0, 0}, 1};
+  return traced(MHE_STEP_DOWN, st, "down projection", [&] {
+    return mhe::launch_gemm(mhe::Epilogue::kResidual, ws.act, wd, x, x, seq, H, c.intermediate, st);
+  });
 }
 
 bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
@@ -215,6 +265,39 @@ const char* mhe_status_string(int32_t s) {
 }
 
 const char* mhe_last_error(void) { return g_last_error.c_str(); }
+
+int32_t mhe_trace_enable(uint32_t step_mask) {
+  if (step_mask >> MHE_STEP_COUNT) return fail(MHE_ERR_SHAPE, "trace mask 0x%x has unknown step bits", step_mask);
+  g_trace_mask.store(step_mask);
+  return MHE_OK;
+}
+
+int32_t mhe_trace_read(int32_t step, double* total_ms, int64_t* launches) {
+  if (step < 0 || step >= MHE_STEP_COUNT) return fail(MHE_ERR_SHAPE, "unknown step %d", step);
+  if (!total_ms || !launches) return fail(MHE_ERR_NULL, "total_ms and launches are required");
+  std::lock_guard<std::mutex> lk(g_trace_mu);
+  StepTrace& t = g_trace[step];
+  int32_t rc = MHE_OK;
+  for (const EventPair& ev : t.pending) {
+    float ms = 0.f;
+    if (rc == MHE_OK) {
+      rc = hip_check(hipEventSynchronize(ev.stop), "trace event synchronize");
+      if (rc == MHE_OK) rc = hip_check(hipEventElapsedTime(&ms, ev.start, ev.stop), "trace elapsed time");
+      if (rc == MHE_OK) {
+        t.done_ms += ms;
+        t.launches += 1;
+      }
+    }
+    g_event_pool.push_back(ev.start);
+    g_event_pool.push_back(ev.stop);
+  }
+  t.pending.clear();
+  *total_ms = t.done_ms;
+  *launches = t.launches;
+  t.done_ms = 0.0;
+  t.launches = 0;
+  return rc;
+}
 
 size_t mhe_workspace_bytes(const mhe_config* cfg, int32_t seq) {
   if (check_config(cfg) || check_seq(seq)) return 0;
@@ -301,10 +384,10 @@ int32_t mhe_encode(const mhe_config* cfg, const mhe_layer_weights* layers, int32
     return rc;
   for (int l = 0; l < n_layers; ++l) {
     if ((rc = run_layer(*cfg, layers[l], x, positions, seq, ws, st))) return rc;
-    if (l < used_ds &&
-        (rc = hip_check(mhe::launch_deepstack_add(x, cfg->hidden, ws.vis, n_vis,
-                                                  static_cast<const bf16_t*>(deepstack[l]), st),
-                        "deepstack add")))
+    if (l < used_ds && (rc = traced(MHE_STEP_DEEPSTACK, st, "deepstack add", [&] {
+                          return mhe::launch_deepstack_add(x, cfg->hidden, ws.vis, n_vis,
+                                                           static_cast<const bf16_t*>(deepstack[l]), st);
+                        })))
       return rc;
   }
   return MHE_OK;

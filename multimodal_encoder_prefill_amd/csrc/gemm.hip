@@ -11,12 +11,19 @@
 //                                              MLP activation, MiniMaxH3Qwen3VLTextMLP)
 //
 // Tiling: a 256 (m) x 256 (n) output tile per workgroup of 4 wavefronts, each
-// wavefront owning 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16. The
-// weight rows are the MFMA "A" operand and the activation rows the "B"
-// operand, so every lane ends up with 4 consecutive output columns (8-byte
-// stores). K advances 64 at a time through an LDS double buffer (2 x 64 KB);
-// rows are 128 bytes and their 16-byte chunks are XOR-swizzled so the
-// ds_read_b128 operand fetches of 8 or 16 consecutive lanes hit distinct banks.
+// wavefront owning 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 with
+// the accumulators in AGPRs. The weight rows are the MFMA "A" operand and the
+// activation rows the "B" operand, so every lane ends up with 4 consecutive
+// output columns (8-byte stores).
+//
+// K advances BK at a time through a ring of STAGES LDS buffers. Operand rows
+// are BK*2 bytes and their 16-byte chunks are XOR-swizzled so the ds_read_b128
+// operand fetches of 8 (or 16) consecutive lanes hit distinct banks. Tiles are
+// fetched either straight into LDS (buffer_load_dwordx4 ... lds) with up to
+// STAGES-1 k-steps in flight, or through registers (one k-step in flight)
+// then ds_write_b128. All loads use scalar buffer resources over 32- or
+// 64-row blocks, so rows past M or N read as zero without per-lane checks.
+//
 // Workgroups are remapped so that each XCD (workgroups are dealt round-robin
 // over the 8 XCDs) receives a contiguous run of tiles, ordered in groups of m
 // tiles so tiles running together on one XCD share A and B panels in its L2.
@@ -29,11 +36,14 @@ namespace {
 
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 64;
 constexpr int kThreads = 256;
-constexpr int kTileElems = BM * BK;  // per operand per stage (BM == BN)
-constexpr int kGroupM = 4;           // m tiles per ordering group
+constexpr int kGroupM = 8;  // m tiles per ordering group
 constexpr int kXcds = 8;
+
+// Pipeline configuration used by launch_gemm.
+constexpr int kBK = 64;
+constexpr int kStages = 2;
+constexpr bool kDma = true;
 
 struct GemmArgs {
   const bf16_t* a;
@@ -45,7 +55,15 @@ struct GemmArgs {
   int tiles_m, tiles_n;
 };
 
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// Chunk swizzle of an LDS operand row (16-byte chunks). For 128-byte rows
+// (BK 64) rows r..r+7 and r..r+15 map one logical chunk to distinct 16-byte
+// bank groups; for 64-byte rows (BK 32) two rows share a 128-byte bank window
+// and the swizzle keeps 8 (16) consecutive rows distinct as well.
+template <int BK>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (BK == 64) return (row & 7) ^ ((row >> 3) & 1);
+  else return ((row >> 1) ^ (row >> 2)) & 3;
+}
 
 // Buffer resource over [p, p + bytes); the pointer and size are wave-uniform
 // and are pinned to scalar registers so loads need no per-lane descriptor.
@@ -58,11 +76,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const bf16_t* p, i
                                            __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-template <int EPI>
+// Wait until at most N vector-memory operations of this wavefront are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier that orders LDS traffic only: it waits for this
+// wavefront's LDS operations but leaves global loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int EPI, int BK, int STAGES, bool DMA>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) {
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(DMA || STAGES == 2, "register staging keeps one k-step in flight");
+  static_assert(STAGES >= 2 && STAGES <= 5, "stages");
+  constexpr int kTileElems = BM * BK;               // one operand, one stage
+  constexpr int kRowBytes = BK * 2;
+  constexpr int kChunks = BK / 8;                   // 16-byte chunks per row
+  constexpr int kRowsPerBlk = 4096 / kRowBytes;     // rows one load instruction covers
+  constexpr int kBlks = 256 / kRowsPerBlk;          // load instructions per operand per stage
+  constexpr int kLoadsPerStage = 2 * kBlks;
+
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
-  bf16_t* As = smem;                   // [2][BM][BK]
-  bf16_t* Bs = smem + 2 * kTileElems;  // [2][BN][BK]
+  bf16_t* As = smem;                          // [STAGES][BM][BK]
+  bf16_t* Bs = smem + STAGES * kTileElems;    // [STAGES][BN][BK]
 
   const int M = args.m, N = args.n, K = args.k;
   const int tid = threadIdx.x;
@@ -86,48 +127,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   const int tile_n = in_group / gm;
   const int m0 = tile_m * BM;
 
-  // ---- global -> LDS: each operand tile is 8 blocks of 32 rows; block i of
-  //      A is rows m0+32i.., block i of B a 32-row slice of one weight
-  //      segment. Every block gets its own buffer resource (scalar), bounded
-  //      to the rows that exist, so rows past M read as zero. The loads go
-  //      straight to LDS (buffer_load_dwordx4 ... lds): lane L of wave w fills
-  //      16 bytes at LDS row w*8 + L/8 of the block, physical chunk L%8, so it
-  //      fetches the logical chunk that the swizzle puts there.
-  const int fill_row = wave * 8 + (lane >> 3);
-  const int fill_chunk = (lane & 7) ^ swz(fill_row);
-  const int voff = fill_row * K * 2 + fill_chunk * 16;
-
-  __amdgpu_buffer_rsrc_t a_rsrc[8], b_rsrc[8];
+  // ---- per-block buffer resources (row blocks of kRowsPerBlk) ----
+  __amdgpu_buffer_rsrc_t a_rsrc[kBlks], b_rsrc[kBlks];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row0 = m0 + 32 * i;
-    const int nrows = max(0, min(32, M - row0));
+  for (int i = 0; i < kBlks; ++i) {
+    const int row0 = m0 + kRowsPerBlk * i;
+    const int nrows = max(0, min(kRowsPerBlk, M - row0));
     a_rsrc[i] = scalar_rsrc(args.a + static_cast<size_t>(min(row0, M - 1)) * K, nrows * K * 2);
     const bf16_t* base;
-    int v;
-    bool ok;
+    int v, avail;
     if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
-      // block i: wave half i/4, slot i%4; slots 0,1 gate rows, 2,3 up rows
-      const int j = tile_n * (BN / 2) + (i >> 2) * 64 + (i & 1) * 32;
-      ok = j < N;
-      base = ((i & 3) < 2) ? args.bptr[0] : args.bptr[1];
-      v = ok ? j : 0;
+      // virtual B rows of the tile, in 32-row slots s: wave half s/4 covers
+      // output columns j0 + 64 (s/4) .., slots s%4 = 0,1 gate rows, 2,3 up rows
+      const int s = i * (kRowsPerBlk / 32);
+      const int j = tile_n * (BN / 2) + (s >> 2) * 64 + (s & 1) * 32;
+      base = ((s & 3) < 2) ? args.bptr[0] : args.bptr[1];
+      v = min(j, N - 1);
+      avail = N - j;
     } else {
-      const int row = tile_n * BN + 32 * i;
-      ok = row < N;
-      const int rr = ok ? row : 0;
+      const int row = tile_n * BN + kRowsPerBlk * i;
+      const int rr = min(row, N - 1);
       if (rr < args.brows[0]) {
         base = args.bptr[0];
         v = rr;
+        avail = args.brows[0] - row;
       } else if (rr < args.brows[0] + args.brows[1]) {
         base = args.bptr[1];
         v = rr - args.brows[0];
+        avail = args.brows[0] + args.brows[1] - row;
       } else {
         base = args.bptr[2];
         v = rr - args.brows[0] - args.brows[1];
+        avail = N - row;
       }
     }
-    b_rsrc[i] = scalar_rsrc(base + static_cast<size_t>(v) * K, ok ? 32 * K * 2 : 0);
+    const int brows = max(0, min(kRowsPerBlk, avail));
+    b_rsrc[i] = scalar_rsrc(base + static_cast<size_t>(v) * K, brows * K * 2);
   }
 
   f32x16 acc[4][4];
@@ -138,37 +173,63 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  // ---- load paths ----
+  // DMA: lane L of wave w fills 16 bytes at block row w*(1024/kRowBytes) + L/kChunks,
+  // physical chunk L%kChunks, and so fetches the logical chunk the swizzle puts there.
+  const int dma_row = wave * (1024 / kRowBytes) + lane / kChunks;
+  const int dma_voff = dma_row * K * 2 + (((lane % kChunks) ^ swz<BK>(dma_row)) * 16);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue_tile = [&](int kt, int stage) {
+  auto issue_dma = [&](int kt, int stage) {
+#if __HIP_DEVICE_COMPILE__  // the LDS-DMA builtin exists only in the device pass
     const int soff = kt * BK * 2;
-    bf16_t* as = As + stage * kTileElems + wave_u * 8 * BK;
-    bf16_t* bs = Bs + stage * kTileElems + wave_u * 8 * BK;
+    bf16_t* as = As + stage * kTileElems + wave_u * 512;
+    bf16_t* bs = Bs + stage * kTileElems + wave_u * 512;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kBlks; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          a_rsrc[i], (__attribute__((address_space(3))) void*)(as + i * 32 * BK), 16, voff, soff, 0, 0);
+          a_rsrc[i], (__attribute__((address_space(3))) void*)(as + i * kRowsPerBlk * BK), 16,
+          dma_voff, soff, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          b_rsrc[i], (__attribute__((address_space(3))) void*)(bs + i * 32 * BK), 16, voff, soff, 0, 0);
+          b_rsrc[i], (__attribute__((address_space(3))) void*)(bs + i * kRowsPerBlk * BK), 16,
+          dma_voff, soff, 0, 0);
+    }
+#endif
+  };
+  // Registers: thread t loads row t/kChunks of each block, chunk t%kChunks.
+  const int reg_row = tid / kChunks;
+  const int reg_chunk = tid % kChunks;
+  const int reg_voff = reg_row * K * 2 + reg_chunk * 16;
+  const int reg_lds = reg_row * BK + ((reg_chunk ^ swz<BK>(reg_row)) << 3);
+  u32x4 ra[DMA ? 1 : kBlks], rb[DMA ? 1 : kBlks];
+  auto load_regs = [&](int kt) {
+    if constexpr (!DMA) {
+      const int soff = kt * BK * 2;
+#pragma unroll
+      for (int i = 0; i < kBlks; ++i) {
+        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc[i], reg_voff, soff, 0));
+        rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc[i], reg_voff, soff, 0));
+      }
+    }
+  };
+  auto store_regs = [&](int stage) {
+    if constexpr (!DMA) {
+#pragma unroll
+      for (int i = 0; i < kBlks; ++i) {
+        *reinterpret_cast<u32x4*>(As + stage * kTileElems + i * kRowsPerBlk * BK + reg_lds) = ra[i];
+        *reinterpret_cast<u32x4*>(Bs + stage * kTileElems + i * kRowsPerBlk * BK + reg_lds) = rb[i];
+      }
     }
   };
 
-  // operand fetch offsets inside a stage
+  // ---- compute one k-step from LDS stage `stage` ----
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
-  const int lswz = swz(lrow);
+  const int lswz = swz<BK>(lrow);
   const int a_base = (wm * 128 + lrow) * BK;  // activation rows (MFMA B operand)
   const int b_base = (wn * 128 + lrow) * BK;  // weight rows (MFMA A operand)
-
-  const int nk = K / BK;
-  issue_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) issue_tile(kt + 1, cur ^ 1);
-    const bf16_t* as = As + cur * kTileElems;
-    const bf16_t* bs = Bs + cur * kTileElems;
+  auto compute = [&](int stage) {
+    const bf16_t* as = As + stage * kTileElems;
+    const bf16_t* bs = Bs + stage * kTileElems;
     // operands of substep s+1 are fetched while substep s's 16 MFMAs run
     bf16x8 wop[2][4], xop[2][4];
     auto fetch = [&](int s, int slot) {
@@ -199,10 +260,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // the next stage's loads have landed in LDS, and every wave is done
-    // reading this stage before it is refilled
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  };
+
+  const int nk = K / BK;
+  if constexpr (DMA) {
+    // Ring of STAGES buffers; k-step kt lives in stage kt % STAGES and is
+    // fetched STAGES-1 steps ahead of its use.
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+      if (p < nk) issue_dma(p, p);
+    for (int kt = 0; kt < nk; ++kt) {
+      // this wavefront's loads for k-step kt are done once at most the
+      // loads of the k-steps issued after it are still in flight
+      const int ahead = min(STAGES - 2, nk - 1 - kt);
+      if (ahead >= 3) wait_vmcnt<(STAGES >= 5 ? 3 : 0) * kLoadsPerStage>();
+      else if (ahead == 2) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * kLoadsPerStage>();
+      else if (ahead == 1) wait_vmcnt<(STAGES >= 3 ? 1 : 0) * kLoadsPerStage>();
+      else wait_vmcnt<0>();
+      // every wavefront's loads for kt have landed, and every wavefront is
+      // done with k-step kt-1, whose stage is refilled next
+      lds_barrier();
+      if (kt + STAGES - 1 < nk) issue_dma(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+      compute(kt % STAGES);
+    }
+  } else {
+    load_regs(0);
+    store_regs(0);
+    if (nk > 1) load_regs(1);
+    lds_barrier();
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) {
+        // stage (kt+1)%2 was last read in k-step kt-1, before the barrier
+        store_regs((kt + 1) & 1);
+        if (kt + 2 < nk) load_regs(kt + 2);
+      }
+      compute(kt & 1);
+      lds_barrier();
+    }
   }
 
   // ---- epilogue: lane holds column m = lrow of each 32x32 block and rows
@@ -259,29 +353,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   }
 }
 
-constexpr size_t kSmemBytes = 4 * kTileElems * sizeof(bf16_t);  // 128 KB
-
 template <int EPI>
 hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
+  constexpr size_t smem = static_cast<size_t>(kStages) * 2 * BM * kBK * sizeof(bf16_t);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<EPI>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(kSmemBytes));
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_kernel<EPI, kBK, kStages, kDma>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(gemm_kernel<EPI>, dim3(grid), dim3(kThreads), kSmemBytes, stream, args);
+  hipLaunchKernelGGL((gemm_kernel<EPI, kBK, kStages, kDma>), dim3(grid), dim3(kThreads), smem,
+                     stream, args);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool gemm_supported(int n, int k) { return n > 0 && k > 0 && n % 32 == 0 && k % BK == 0; }
+int gemm_segment_rows() { return 4096 / (kBK * 2); }
+
+bool gemm_supported(int n, int k) { return n > 0 && k > 0 && n % 32 == 0 && k % kBK == 0; }
 
 hipError_t launch_gemm(Epilogue epi, const bf16_t* a, const BSegments& b, bf16_t* c,
                        const bf16_t* residual, int m, int n, int k, hipStream_t stream) {
   if (m <= 0) return hipSuccess;
+  // a load block never straddles two weight segments
+  if (epi != Epilogue::kSwiGLU && b.count > 1)
+    for (int i = 0; i < b.count; ++i)
+      if (b.rows[i] % gemm_segment_rows() != 0) return hipErrorInvalidValue;
   GemmArgs args{};
   args.a = a;
   for (int i = 0; i < 3; ++i) {

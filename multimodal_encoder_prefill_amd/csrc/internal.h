@@ -24,6 +24,8 @@ struct BSegments {
 };
 
 bool gemm_supported(int n, int k);
+// Rows of one load block; each segment of a multi-segment B must be a multiple.
+int gemm_segment_rows();
 // kStore / kResidual: B is the concatenation of the segments (n = total rows).
 // kSwiGLU: seg 0 = gate, seg 1 = up, each n rows; C has n columns.
 hipError_t launch_gemm(Epilogue epi, const bf16_t* a, const BSegments& b, bf16_t* c,
