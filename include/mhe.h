@@ -204,24 +204,36 @@ int32_t mhe_rms_norm(const void* x, const void* gamma, void* y, int32_t rows, in
                      float eps, void* stream);
 
 /*
+ * Bytes of fp32 scratch with which mhe_linear / mhe_linear_swiglu can balance
+ * their last wave of output tiles (split along k, partials summed in a fixed
+ * order). Independent of the shape.
+ */
+size_t mhe_linear_workspace_bytes(void);
+
+/*
  * c[m, n] = sum_k a[m, k] w[n, k] (+ residual[m, n]) with fp32 accumulation
  * and one bf16 rounding (the F.linear calls of the H3 encoder page; the
  * residual form is the decoder layer's residual add fused into the O and
  * down projections). a [m, k], w [n, k], c and residual [m, n] bf16;
  * residual may be NULL or equal to c (in-place), c must not overlap a or w.
- * k % 64 == 0, n % 32 == 0.
+ * k % 64 == 0, n % 32 == 0. workspace (256-byte aligned, may be NULL):
+ * scratch for the k-split of the last wave of tiles; with NULL or fewer than
+ * mhe_linear_workspace_bytes() bytes fewer (or no) tiles are split. The
+ * result does not depend on whether a tile is split beyond fp32 summation
+ * order.
  */
 int32_t mhe_linear(const void* a, const void* w, void* c, const void* residual, int32_t m,
-                   int32_t n, int32_t k, void* stream);
+                   int32_t n, int32_t k, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * c[m, j] = silu(sum_k a[m,k] w_gate[j,k]) * sum_k a[m,k] w_up[j,k] in fp32,
  * one bf16 rounding (H3 encoder page, MiniMaxH3Qwen3VLTextMLP.forward up to
  * the down projection). a [m, k], w_gate and w_up [n, k], c [m, n].
- * k % 64 == 0, n % 32 == 0.
+ * k % 64 == 0, n % 32 == 0. workspace as for mhe_linear.
  */
 int32_t mhe_linear_swiglu(const void* a, const void* w_gate, const void* w_up, void* c,
-                          int32_t m, int32_t n, int32_t k, void* stream);
+                          int32_t m, int32_t n, int32_t k, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * Per-head q/k RMSNorm and multimodal rotary (H3 encoder page,

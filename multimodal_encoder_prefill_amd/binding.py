@@ -62,8 +62,9 @@ _SIGNATURES = {
                           _vp, _vp, _i32, ctypes.POINTER(_vp), _i32, _i32, _vp, _vp, _sz, _vp]),
     "mhe_count_visual": (_i32, [_vp, _i32, ctypes.POINTER(_i32), _vp, _sz, _vp]),
     "mhe_rms_norm": (_i32, [_vp, _vp, _vp, _i32, _i32, _f32, _vp]),
-    "mhe_linear": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
-    "mhe_linear_swiglu": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp]),
+    "mhe_linear_workspace_bytes": (_sz, []),
+    "mhe_linear": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "mhe_linear_swiglu": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "mhe_qk_norm_rope": (_i32, [ctypes.POINTER(MheConfig), _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                                 _vp, _vp]),
     "mhe_attention": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
@@ -202,14 +203,28 @@ def rms_norm(x, gamma, y, rows, dim, eps, stream=None):
                                               _stream(stream)))
 
 
-def linear(a, w, c, m, n, k, residual=None, stream=None):
+def linear_workspace_bytes() -> int:
+    return lib().mhe_linear_workspace_bytes()
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    if isinstance(workspace, tuple):
+        return workspace
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+def linear(a, w, c, m, n, k, residual=None, workspace=None, stream=None):
+    wp, wb = _ws(workspace)
     _check("mhe_linear", lib().mhe_linear(_ptr(a), _ptr(w), _ptr(c), _ptr(residual), m, n, k,
-                                          _stream(stream)))
+                                          wp, wb, _stream(stream)))
 
 
-def linear_swiglu(a, w_gate, w_up, c, m, n, k, stream=None):
+def linear_swiglu(a, w_gate, w_up, c, m, n, k, workspace=None, stream=None):
+    wp, wb = _ws(workspace)
     _check("mhe_linear_swiglu", lib().mhe_linear_swiglu(_ptr(a), _ptr(w_gate), _ptr(w_up),
-                                                        _ptr(c), m, n, k, _stream(stream)))
+                                                        _ptr(c), m, n, k, wp, wb, _stream(stream)))
 
 
 def qk_norm_rope(cfg, qkv, q_norm, k_norm, positions, seq, q_out, k_out, vt_out, stream=None):

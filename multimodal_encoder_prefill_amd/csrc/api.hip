@@ -83,6 +83,8 @@ struct Workspace {
   bf16_t* act;   // [S, I], aliases qkv..ao (used after attention)
   int32_t* vis;  // [S]
   int32_t* cnt;  // [1]
+  float* partial;  // split-K partial tiles of the GEMMs' last wave
+  size_t partial_bytes;
   size_t total;
 };
 
@@ -110,6 +112,8 @@ Workspace carve(const mhe_config& c, int seq, char* base) {
   if (act_bytes > attn_bytes) off = region_start + act_bytes;
   w.vis = reinterpret_cast<int32_t*>(take(S * 4));
   w.cnt = reinterpret_cast<int32_t*>(take(4));
+  w.partial_bytes = mhe::gemm_partial_bytes();
+  w.partial = reinterpret_cast<float*>(take(w.partial_bytes));
   w.total = off;
   return w;
 }
@@ -200,7 +204,8 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights& w, bf16_t* x, co
                            {qw, kvw, kvw},
                            3};
   if ((rc = traced(MHE_STEP_QKV, st, "qkv projection", [&] {
-         return mhe::launch_gemm(mhe::Epilogue::kStore, ws.hn, qkv, ws.qkv, nullptr, seq, qw + 2 * kvw, H, st);
+         return mhe::launch_gemm(mhe::Epilogue::kStore, ws.hn, qkv, ws.qkv, nullptr, seq, qw + 2 * kvw, H,
+                                ws.partial, ws.partial_bytes, st);
        })))
     return rc;
   // q/k norm + rotary, K and V relayout
@@ -219,7 +224,8 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights& w, bf16_t* x, co
   // O projection + residual, in place on x
   const mhe::BSegments wo{{static_cast<const bf16_t*>(w.w_o), nullptr, nullptr}, {H, 0, 0}, 1};
   if ((rc = traced(MHE_STEP_O_PROJ, st, "o projection", [&] {
-         return mhe::launch_gemm(mhe::Epilogue::kResidual, ws.ao, wo, x, x, seq, H, qw, st);
+         return mhe::launch_gemm(mhe::Epilogue::kResidual, ws.ao, wo, x, x, seq, H, qw, ws.partial,
+                                ws.partial_bytes, st);
        })))
     return rc;
   if ((rc = traced(MHE_STEP_POST_NORM, st, "post-attention rmsnorm", [&] {
@@ -230,12 +236,14 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights& w, bf16_t* x, co
                           {c.intermediate, c.intermediate, 0},
                           2};
   if ((rc = traced(MHE_STEP_GATE_UP, st, "gate/up projection", [&] {
-         return mhe::launch_gemm(mhe::Epilogue::kSwiGLU, ws.hn, gu, ws.act, nullptr, seq, c.intermediate, H, st);
+         return mhe::launch_gemm(mhe::Epilogue::kSwiGLU, ws.hn, gu, ws.act, nullptr, seq, c.intermediate, H,
+                                ws.partial, ws.partial_bytes, st);
        })))
     return rc;
   const mhe::BSegments wd{{static_cast<const bf16_t*>(w.w_down), nullptr, nullptr}, {H, 0, 0}, 1};
   return traced(MHE_STEP_DOWN, st, "down projection", [&] {
-    return mhe::launch_gemm(mhe::Epilogue::kResidual, ws.act, wd, x, x, seq, H, c.intermediate, st);
+    return mhe::launch_gemm(mhe::Epilogue::kResidual, ws.act, wd, x, x, seq, H, c.intermediate,
+                            ws.partial, ws.partial_bytes, st);
   });
 }
 
@@ -421,8 +429,17 @@ int32_t mhe_rms_norm(const void* x, const void* gamma, void* y, int32_t rows, in
                    "rmsnorm");
 }
 
+size_t mhe_linear_workspace_bytes(void) { return mhe::gemm_partial_bytes(); }
+
+static int32_t check_gemm_ws(const void* ws, size_t ws_bytes) {
+  if (!ws) return MHE_OK;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
+    return fail(MHE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return MHE_OK;
+}
+
 int32_t mhe_linear(const void* a, const void* w, void* c, const void* residual, int32_t m,
-                   int32_t n, int32_t k, void* stream) {
+                   int32_t n, int32_t k, void* workspace, size_t workspace_bytes, void* stream) {
   if (!a || !w || !c) return fail(MHE_ERR_NULL, "a, w and c are required");
   if (m <= 0 || n <= 0 || k <= 0) return fail(MHE_ERR_SHAPE, "m, n, k must be > 0");
   if (!mhe::gemm_supported(n, k)) return fail(MHE_ERR_UNSUPPORTED, "needs n %% 32 == 0 and k %% 64 == 0 (n=%d, k=%d)", n, k);
@@ -431,27 +448,38 @@ int32_t mhe_linear(const void* a, const void* w, void* c, const void* residual, 
     return fail(MHE_ERR_SHAPE, "c overlaps an operand");
   if (residual && residual != c && overlaps(c, cb, residual, cb))
     return fail(MHE_ERR_SHAPE, "residual partially overlaps c");
+  int32_t rc;
+  if ((rc = check_gemm_ws(workspace, workspace_bytes))) return rc;
+  if (workspace && (overlaps(workspace, workspace_bytes, c, cb) || overlaps(workspace, workspace_bytes, a, static_cast<size_t>(m) * k * 2)))
+    return fail(MHE_ERR_SHAPE, "workspace overlaps an operand");
   mhe::BSegments b{{static_cast<const bf16_t*>(w), nullptr, nullptr}, {n, 0, 0}, 1};
   return hip_check(mhe::launch_gemm(residual ? mhe::Epilogue::kResidual : mhe::Epilogue::kStore,
                                     static_cast<const bf16_t*>(a), b, static_cast<bf16_t*>(c),
                                     static_cast<const bf16_t*>(residual), m, n, k,
+                                    static_cast<float*>(workspace), workspace ? workspace_bytes : 0,
                                     static_cast<hipStream_t>(stream)),
                    "linear");
 }
 
 int32_t mhe_linear_swiglu(const void* a, const void* w_gate, const void* w_up, void* c,
-                          int32_t m, int32_t n, int32_t k, void* stream) {
+                          int32_t m, int32_t n, int32_t k, void* workspace,
+                          size_t workspace_bytes, void* stream) {
   if (!a || !w_gate || !w_up || !c) return fail(MHE_ERR_NULL, "a, w_gate, w_up and c are required");
   if (m <= 0 || n <= 0 || k <= 0) return fail(MHE_ERR_SHAPE, "m, n, k must be > 0");
   if (!mhe::gemm_supported(n, k)) return fail(MHE_ERR_UNSUPPORTED, "needs n %% 32 == 0 and k %% 64 == 0 (n=%d, k=%d)", n, k);
   const size_t cb = static_cast<size_t>(m) * n * 2;
   if (overlaps(c, cb, a, static_cast<size_t>(m) * k * 2))
     return fail(MHE_ERR_SHAPE, "c overlaps a");
+  int32_t rc;
+  if ((rc = check_gemm_ws(workspace, workspace_bytes))) return rc;
+  if (workspace && overlaps(workspace, workspace_bytes, c, cb))
+    return fail(MHE_ERR_SHAPE, "workspace overlaps c");
   mhe::BSegments b{{static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(w_up), nullptr},
                    {n, n, 0},
                    2};
   return hip_check(mhe::launch_gemm(mhe::Epilogue::kSwiGLU, static_cast<const bf16_t*>(a), b,
                                     static_cast<bf16_t*>(c), nullptr, m, n, k,
+                                    static_cast<float*>(workspace), workspace ? workspace_bytes : 0,
                                     static_cast<hipStream_t>(stream)),
                    "linear_swiglu");
 }

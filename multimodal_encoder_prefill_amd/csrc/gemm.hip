@@ -53,7 +53,24 @@ struct GemmArgs {
   const bf16_t* r;
   int m, n, k;
   int tiles_m, tiles_n;
+  // work units of this launch: tiles [tile_begin, tile_begin + units / ksplit),
+  // each split into ksplit k-ranges of kt_per_split k-steps. With ksplit > 1 the
+  // raw fp32 accumulators go to partial[unit] ([256][256] floats per unit).
+  int tile_begin, units, ksplit, kt_per_split;
+  float* partial;
 };
+
+// Output tile (m, n) of logical tile t: groups of kGroupM m-tiles, n-major
+// inside a group, so consecutive tiles share B panels and A panels.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int group_size = kGroupM * tiles_n;
+  const int group = t / group_size;
+  const int first_m = group * kGroupM;
+  const int gm = min(tiles_m - first_m, kGroupM);
+  const int in_group = t - group * group_size;
+  tm = first_m + in_group % gm;
+  tn = in_group / gm;
+}
 
 // Chunk swizzle of an LDS operand row (16-byte chunks). For 128-byte rows
 // (BK 64) rows r..r+7 and r..r+15 map one logical chunk to distinct 16-byte
@@ -112,20 +129,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   const int wm = wave & 1;
   const int wn = wave >> 1;
 
-  // ---- tile id: contiguous per XCD, then grouped-m ordering ----
-  const int total = args.tiles_m * args.tiles_n;
+  // ---- work unit: contiguous per XCD, then tile and k-range ----
+  const int total = args.units;
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds;
   const int q = total / kXcds, rmd = total % kXcds;
-  const int logical = xcd * q + min(xcd, rmd) + bid / kXcds;
-  const int group_size = kGroupM * args.tiles_n;
-  const int group = logical / group_size;
-  const int first_m = group * kGroupM;
-  const int gm = min(args.tiles_m - first_m, kGroupM);
-  const int in_group = logical - group * group_size;
-  const int tile_m = first_m + in_group % gm;
-  const int tile_n = in_group / gm;
+  const int unit = xcd * q + min(xcd, rmd) + bid / kXcds;
+  int tile_m, tile_n;
+  tile_coords(args.tile_begin + unit / args.ksplit, args.tiles_m, args.tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM;
+  const int kt_begin = (unit % args.ksplit) * args.kt_per_split;
+  const int kt_end = min(kt_begin + args.kt_per_split, K / BK);
 
   // ---- per-block buffer resources (row blocks of kRowsPerBlk) ----
   __amdgpu_buffer_rsrc_t a_rsrc[kBlks], b_rsrc[kBlks];
@@ -193,6 +207,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
           b_rsrc[i], (__attribute__((address_space(3))) void*)(bs + i * kRowsPerBlk * BK), 16,
           dma_voff, soff, 0, 0);
     }
+#else
+    (void)kt, (void)stage, (void)dma_voff, (void)wave_u;
 #endif
   };
   // Registers: thread t loads row t/kChunks of each block, chunk t%kChunks.
@@ -262,13 +278,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     }
   };
 
-  const int nk = K / BK;
+  const int nk = kt_end - kt_begin;  // k-steps of this unit; k-step i is kt_begin + i
   if constexpr (DMA) {
     // Ring of STAGES buffers; k-step kt lives in stage kt % STAGES and is
     // fetched STAGES-1 steps ahead of its use.
 #pragma unroll
     for (int p = 0; p < STAGES - 1; ++p)
-      if (p < nk) issue_dma(p, p);
+      if (p < nk) issue_dma(kt_begin + p, p);
     for (int kt = 0; kt < nk; ++kt) {
       // this wavefront's loads for k-step kt are done once at most the
       // loads of the k-steps issued after it are still in flight
@@ -280,23 +296,45 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       // every wavefront's loads for kt have landed, and every wavefront is
       // done with k-step kt-1, whose stage is refilled next
       lds_barrier();
-      if (kt + STAGES - 1 < nk) issue_dma(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+      if (kt + STAGES - 1 < nk) issue_dma(kt_begin + kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
       compute(kt % STAGES);
     }
   } else {
-    load_regs(0);
-    store_regs(0);
-    if (nk > 1) load_regs(1);
+    if (nk > 0) {
+      load_regs(kt_begin);
+      store_regs(0);
+    }
+    if (nk > 1) load_regs(kt_begin + 1);
     lds_barrier();
     for (int kt = 0; kt < nk; ++kt) {
       if (kt + 1 < nk) {
         // stage (kt+1)%2 was last read in k-step kt-1, before the barrier
         store_regs((kt + 1) & 1);
-        if (kt + 2 < nk) load_regs(kt + 2);
+        if (kt + 2 < nk) load_regs(kt_begin + kt + 2);
       }
       compute(kt & 1);
       lds_barrier();
     }
+  }
+
+  // ---- split-K unit: raw accumulators to the unit's partial tile, laid out
+  //      [m_local][virtual n] so 4 consecutive n are one 16-byte store ----
+  if (args.ksplit > 1) {
+    float* dst = args.partial + static_cast<size_t>(unit) * BM * BN;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ml = wm * 128 + j * 32 + lrow;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+          *reinterpret_cast<f32x4*>(dst + ml * BN + wn * 128 + i * 32 + 8 * g + 4 * lhalf) = v;
+        }
+    }
+    return;
   }
 
   // ---- epilogue: lane holds column m = lrow of each 32x32 block and rows
@@ -353,6 +391,57 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   }
 }
 
+// Sums the ksplit partial tiles of each split tile in a fixed order and
+// applies the epilogue. Block (t, y) handles rows 4y..4y+3 of split tile t;
+// each thread 4 consecutive virtual columns.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args) {
+  const int t = blockIdx.x;
+  const int ml = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int vn = (threadIdx.x & 63) * 4;
+  int tile_m, tile_n;
+  tile_coords(args.tile_begin + t, args.tiles_m, args.tiles_n, tile_m, tile_n);
+  const int m = tile_m * BM + ml;
+  if (m >= args.m) return;
+  const float* src = args.partial + static_cast<size_t>(t) * args.ksplit * BM * BN + ml * BN + vn;
+  f32x4 sum = *reinterpret_cast<const f32x4*>(src);
+  for (int sidx = 1; sidx < args.ksplit; ++sidx)
+    sum += *reinterpret_cast<const f32x4*>(src + static_cast<size_t>(sidx) * BM * BN);
+  const int N = args.n;
+  float o[4];
+  int n;
+  if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+    // virtual column vn: wave half vn/128, 32-wide slot (vn%128)/32; slots 0,1
+    // are gate columns whose up partner sits 64 virtual columns later
+    const int slot = (vn & 127) >> 5;
+    if (slot >= 2) return;
+    const f32x4 up = *reinterpret_cast<const f32x4*>(src + 64);
+    f32x4 upsum = up;
+    for (int sidx = 1; sidx < args.ksplit; ++sidx)
+      upsum += *reinterpret_cast<const f32x4*>(src + 64 + static_cast<size_t>(sidx) * BM * BN);
+    n = tile_n * (BN / 2) + (vn >> 7) * 64 + slot * 32 + (vn & 31);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = sum[e] / (1.f + __expf(-sum[e])) * upsum[e];
+  } else {
+    n = tile_n * BN + vn;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = sum[e];
+  }
+  if (n >= N) return;
+  const size_t off = static_cast<size_t>(m) * N + n;
+  if (EPI == static_cast<int>(Epilogue::kResidual)) {
+    const u32x2 rv = *reinterpret_cast<const u32x2*>(args.r + off);
+    o[0] += __uint_as_float(rv[0] << 16);
+    o[1] += __uint_as_float(rv[0] & 0xffff0000u);
+    o[2] += __uint_as_float(rv[1] << 16);
+    o[3] += __uint_as_float(rv[1] & 0xffff0000u);
+  }
+  u32x2 pk;
+  pk[0] = pack_bf16x2(o[0], o[1]);
+  pk[1] = pack_bf16x2(o[2], o[3]);
+  *reinterpret_cast<u32x2*>(args.c + off) = pk;
+}
+
 template <int EPI>
 hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
   constexpr size_t smem = static_cast<size_t>(kStages) * 2 * BM * kBK * sizeof(bf16_t);
@@ -375,8 +464,65 @@ int gemm_segment_rows() { return 4096 / (kBK * 2); }
 
 bool gemm_supported(int n, int k) { return n > 0 && k > 0 && n % 32 == 0 && k % kBK == 0; }
 
+namespace {
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+template <int EPI>
+hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t stream) {
+  // One workgroup fills a CU (128 KB of LDS), so a launch of T tiles runs in
+  // ceil(T / CUs) waves. Full waves run whole tiles; when the last wave would
+  // leave more than half the CUs idle, its R tiles are cut into ksplit k-ranges
+  // (ksplit * R <= CUs) whose fp32 partials are summed by a small reduction.
+  const int tiles = args.tiles_m * args.tiles_n;
+  const int nk = args.k / kBK;
+  static const int cus = device_cus();
+  const int rem = tiles % cus;
+  int ksplit = 1;
+  if (partial && rem > 0 && rem <= cus / 2) {
+    ksplit = min(cus / rem, 16);
+    ksplit = min(ksplit, nk / 4);
+    const size_t cap = partial_bytes / (static_cast<size_t>(BM) * BN * sizeof(float));
+    while (ksplit > 1 && static_cast<size_t>(ksplit) * rem > cap) --ksplit;
+  }
+  const int full = ksplit > 1 ? tiles - rem : tiles;
+  hipError_t e;
+  if (full > 0) {
+    GemmArgs a = args;
+    a.tile_begin = 0;
+    a.units = full;
+    a.ksplit = 1;
+    a.kt_per_split = nk;
+    a.partial = nullptr;
+    if ((e = launch_epi<EPI>(a, full, stream)) != hipSuccess) return e;
+  }
+  if (ksplit > 1) {
+    GemmArgs a = args;
+    a.tile_begin = full;
+    a.units = rem * ksplit;
+    a.ksplit = ksplit;
+    a.kt_per_split = (nk + ksplit - 1) / ksplit;
+    a.partial = partial;
+    if ((e = launch_epi<EPI>(a, a.units, stream)) != hipSuccess) return e;
+    hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(rem, BM / 4), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t gemm_partial_bytes() { return static_cast<size_t>(320) * BM * BN * sizeof(float); }
+
 hipError_t launch_gemm(Epilogue epi, const bf16_t* a, const BSegments& b, bf16_t* c,
-                       const bf16_t* residual, int m, int n, int k, hipStream_t stream) {
+                       const bf16_t* residual, int m, int n, int k, float* partial,
+                       size_t partial_bytes, hipStream_t stream) {
   if (m <= 0) return hipSuccess;
   // a load block never straddles two weight segments
   if (epi != Epilogue::kSwiGLU && b.count > 1)
@@ -395,11 +541,10 @@ hipError_t launch_gemm(Epilogue epi, const bf16_t* a, const BSegments& b, bf16_t
   args.k = k;
   args.tiles_m = (m + BM - 1) / BM;
   args.tiles_n = epi == Epilogue::kSwiGLU ? (n + BN / 2 - 1) / (BN / 2) : (n + BN - 1) / BN;
-  const int grid = args.tiles_m * args.tiles_n;
   switch (epi) {
-    case Epilogue::kStore: return launch_epi<0>(args, grid, stream);
-    case Epilogue::kResidual: return launch_epi<1>(args, grid, stream);
-    case Epilogue::kSwiGLU: return launch_epi<2>(args, grid, stream);
+    case Epilogue::kStore: return run<0>(args, partial, partial_bytes, stream);
+    case Epilogue::kResidual: return run<1>(args, partial, partial_bytes, stream);
+    case Epilogue::kSwiGLU: return run<2>(args, partial, partial_bytes, stream);
   }
   return hipErrorInvalidValue;
 }

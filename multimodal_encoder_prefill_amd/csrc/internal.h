@@ -28,8 +28,12 @@ bool gemm_supported(int n, int k);
 int gemm_segment_rows();
 // kStore / kResidual: B is the concatenation of the segments (n = total rows).
 // kSwiGLU: seg 0 = gate, seg 1 = up, each n rows; C has n columns.
+// `partial` (may be NULL) is fp32 scratch for split-K units of the last wave;
+// gemm_partial_bytes() is enough for every shape.
+size_t gemm_partial_bytes();
 hipError_t launch_gemm(Epilogue epi, const bf16_t* a, const BSegments& b, bf16_t* c,
-                       const bf16_t* residual, int m, int n, int k, hipStream_t stream);
+                       const bf16_t* residual, int m, int n, int k, float* partial,
+                       size_t partial_bytes, hipStream_t stream);
 
 // qk_norm_rope.hip
 struct RopeParams {

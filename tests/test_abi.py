@@ -27,13 +27,14 @@ def test_status_strings_and_version():
 
 def test_workspace_bytes_scales_and_validates():
     cfg = b.config_from_dims(synth.FULL)
+    part = b.linear_workspace_bytes()          # fixed split-K scratch
     w1 = b.workspace_bytes(cfg, 512)
     w2 = b.workspace_bytes(cfg, 4096)
-    assert w2 > 7 * w1
+    assert w2 - part > 7 * (w1 - part)
     # hidden + max(attention buffers, MLP activation) + index list, 256-byte aligned pieces
     S = 4096
     attn = S * 10240 * 2 + S * 8192 * 2 + 2 * 8 * 4096 * 128 * 2 + S * 8192 * 2
-    assert w2 >= S * 5120 * 2 + max(attn, S * 25600 * 2) + S * 4
+    assert w2 >= S * 5120 * 2 + max(attn, S * 25600 * 2) + S * 4 + part
     with pytest.raises(b.MheError):
         b.workspace_bytes(cfg, 0)
     bad = b.config_from_dims(synth.FULL)
@@ -101,10 +102,12 @@ def test_step_entry_points_reject_before_launch():
     lib = b.lib()
     assert lib.mhe_rms_norm(None, 0x10, 0x20, 4, 256, 1e-6, None) == 1
     assert lib.mhe_rms_norm(0x10, 0x10, 0x20, 4, 20000, 1e-6, None) == 4
-    assert lib.mhe_linear(0x10, 0x20, 0x30, None, 4, 100, 64, None) == 4   # n % 32
-    assert lib.mhe_linear(0x10, 0x20, 0x30, None, 4, 64, 48, None) == 4    # k % 64
-    assert lib.mhe_linear(0x1000, 0x900000, 0x1000, None, 4, 64, 64, None) == 2  # c aliases a
-    assert lib.mhe_linear_swiglu(0x10, None, 0x20, 0x30, 4, 64, 64, None) == 1
+    assert lib.mhe_linear(0x10, 0x20, 0x30, None, 4, 100, 64, None, 0, None) == 4   # n % 32
+    assert lib.mhe_linear(0x10, 0x20, 0x30, None, 4, 64, 48, None, 0, None) == 4    # k % 64
+    assert lib.mhe_linear(0x1000, 0x900000, 0x1000, None, 4, 64, 64, None, 0, None) == 2  # c aliases a
+    assert lib.mhe_linear(0x1000, 0x900000, 0x100000, None, 4, 64, 64, 0x200010, 1 << 20, None) == 5
+    assert lib.mhe_linear_swiglu(0x10, None, 0x20, 0x30, 4, 64, 64, None, 0, None) == 1
+    assert b.linear_workspace_bytes() >= 256 * 256 * 256 * 4
     assert lib.mhe_attention(0x10, 0x20, 0x30, 0x40, 64, 12, 1, 128, None) == 4  # group 12
     assert lib.mhe_attention(0x10, 0x20, 0x30, 0x40, 0, 8, 1, 128, None) == 2
     assert lib.mhe_deepstack_inject(0x10, 64, 256, 0x20, 65, 0x30, 0x40, 1 << 20, None) == 2

@@ -96,6 +96,50 @@ def test_linear_swiglu(m, n, k):
     assert mx <= 2.0 ** -7 * np.max(np.abs(ref))
 
 
+def _gemm_ws():
+    return torch.empty(b.linear_workspace_bytes(), device=DEV, dtype=torch.uint8)
+
+
+@pytest.mark.parametrize("m,n,k,residual", [
+    (512, 5120, 8192, True),      # 40 tiles: all split 6 ways along k
+    (300, 96, 1024, False),       # ragged m, one partial n tile, 4-way split
+    (1000, 2048, 1024, True),     # 32 tiles
+    (4096, 5120, 25600, True),    # down projection: 256 whole tiles + 64 tiles split 4 ways
+])
+def test_linear_split_k(m, n, k, residual):
+    """The last wave of tiles is split along k into fp32 partials and reduced."""
+    print(f"linear split-k m={m} n={n} k={k} residual={residual}", flush=True)
+    a = _randn((m, k), 12 + m)
+    w = _randn((n, k), 13 + n, 0.02)
+    c = _randn((m, n), 14) if residual else torch.empty((m, n), device=DEV, dtype=torch.bfloat16)
+    r0 = f64(c) if residual else 0.0
+    c_plain = c.clone()
+    b.linear(a, w, c, m, n, k, residual=c if residual else None, workspace=_gemm_ws())
+    b.linear(a, w, c_plain, m, n, k, residual=c_plain if residual else None)
+    torch.cuda.synchronize()
+    rows = np.unique(np.linspace(0, m - 1, 40).astype(int))
+    ref = (r0[rows] if residual else 0.0) + f64(a[rows]) @ f64(w).T
+    assert report("linear split-k", f64(c)[rows], ref)[0] <= 4e-3
+    # split and unsplit differ only by fp32 summation order before one bf16 rounding
+    r, mx = report("split vs unsplit", f64(c), f64(c_plain))
+    assert r <= 2e-3 and mx <= 2.0 ** -6 * np.max(np.abs(f64(c_plain)))
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 1056, 1024), (4096, 25600, 5120)])
+def test_linear_swiglu_split_k(m, n, k):
+    print(f"swiglu split-k m={m} n={n} k={k}", flush=True)
+    a = _randn((m, k), 43)
+    wg = _randn((n, k), 44, 0.05)
+    wu = _randn((n, k), 45, 0.05)
+    c = torch.empty((m, n), device=DEV, dtype=torch.bfloat16)
+    b.linear_swiglu(a, wg, wu, c, m, n, k, workspace=_gemm_ws())
+    torch.cuda.synchronize()
+    rows = np.unique(np.linspace(0, m - 1, 24).astype(int))
+    ar = f64(a[rows])
+    ref = oracle.silu(ar @ f64(wg).T) * (ar @ f64(wu).T)
+    assert report("swiglu split-k", f64(c)[rows], ref)[0] <= 4e-3
+
+
 @pytest.mark.parametrize("name,m,n,k", [("o_proj", 4096, 5120, 8192), ("down", 4096, 5120, 25600),
                                          ("qkv", 4096, 10240, 5120)])
 def test_linear_full_size_sampled_rows(name, m, n, k):
