@@ -37,6 +37,10 @@ int32_t hip_check(hipError_t e, const char* what) {
 }
 
 constexpr int kMaxSeq = 1 << 17;
+// Activation buffers that feed a GEMM as its A operand get this many extra
+// elements per row: row strides that are multiples of 2 KB make the 128-byte
+// row pieces a GEMM k-step loads collide in the same L2 channels.
+constexpr int kActPad = 128;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -74,13 +78,14 @@ int32_t check_config(const mhe_config* c) {
 }
 
 struct Workspace {
-  bf16_t* hn;    // [S, H]
+  int ld_h, ld_o, ld_i;  // row strides of hn, ao, act
+  bf16_t* hn;    // [S, H] with row stride ld_h
   bf16_t* qkv;   // [S, (Hq + 2 Hkv) D]
   bf16_t* qn;    // [S, Hq, D]
   bf16_t* kn;    // [Hkv, Sp, D]
   bf16_t* vt;    // [Hkv, D, Sp]
-  bf16_t* ao;    // [S, Hq D]
-  bf16_t* act;   // [S, I], aliases qkv..ao (used after attention)
+  bf16_t* ao;    // [S, Hq D] with row stride ld_o
+  bf16_t* act;   // [S, I] with row stride ld_i, aliases qkv..ao (used after attention)
   int32_t* vis;  // [S]
   int32_t* cnt;  // [1]
   float* partial;  // split-K partial tiles of the GEMMs' last wave
@@ -93,21 +98,24 @@ Workspace carve(const mhe_config& c, int seq, char* base) {
   const size_t sp = static_cast<size_t>(mhe::seq_pad(seq));
   const size_t D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
   Workspace w{};
+  w.ld_h = c.hidden + kActPad;
+  w.ld_o = c.n_heads * c.head_dim + kActPad;
+  w.ld_i = c.intermediate + kActPad;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     char* p = base ? base + off : nullptr;
     off += align_up(bytes);
     return p;
   };
-  w.hn = reinterpret_cast<bf16_t*>(take(S * c.hidden * 2));
+  w.hn = reinterpret_cast<bf16_t*>(take(S * w.ld_h * 2));
   const size_t region_start = off;
   w.qkv = reinterpret_cast<bf16_t*>(take(S * (Hq + 2 * Hkv) * D * 2));
   w.qn = reinterpret_cast<bf16_t*>(take(S * Hq * D * 2));
   w.kn = reinterpret_cast<bf16_t*>(take(Hkv * sp * D * 2));
   w.vt = reinterpret_cast<bf16_t*>(take(Hkv * D * sp * 2));
-  w.ao = reinterpret_cast<bf16_t*>(take(S * Hq * D * 2));
+  w.ao = reinterpret_cast<bf16_t*>(take(S * w.ld_o * 2));
   const size_t attn_bytes = off - region_start;
-  const size_t act_bytes = align_up(S * c.intermediate * 2);
+  const size_t act_bytes = align_up(S * w.ld_i * 2);
   w.act = reinterpret_cast<bf16_t*>(base ? base + region_start : nullptr);
   if (act_bytes > attn_bytes) off = region_start + act_bytes;
   w.vis = reinterpret_cast<int32_t*>(take(S * 4));
@@ -195,7 +203,8 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights& w, bf16_t* x, co
   const int qw = Hq * D, kvw = Hkv * D;
   int32_t rc;
   if ((rc = traced(MHE_STEP_INPUT_NORM, st, "input rmsnorm", [&] {
-         return mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_in), ws.hn, seq, H, c.rms_eps, st);
+         return mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_in), ws.hn, ws.ld_h, seq, H,
+                                    c.rms_eps, st);
        })))
     return rc;
   // q | k | v projections in one launch
@@ -204,7 +213,7 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights& w, bf16_t* x, co
                            {qw, kvw, kvw},
                            3};
   if ((rc = traced(MHE_STEP_QKV, st, "qkv projection", [&] {
-         return mhe::launch_gemm(mhe::Epilogue::kStore, ws.hn, qkv, ws.qkv, nullptr, seq, qw + 2 * kvw, H,
+         return mhe::launch_gemm(mhe::Epilogue::kStore, ws.hn, ws.ld_h, qkv, H, ws.qkv, qw + 2 * kvw, nullptr, seq, qw + 2 * kvw, H,
                                 ws.partial, ws.partial_bytes, st);
        })))
     return rc;
@@ -218,31 +227,32 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights& w, bf16_t* x, co
        })))
     return rc;
   if ((rc = traced(MHE_STEP_ATTENTION, st, "attention", [&] {
-         return mhe::launch_attention(ws.qn, ws.kn, ws.vt, ws.ao, seq, Hq, Hkv, D, st);
+         return mhe::launch_attention(ws.qn, ws.kn, ws.vt, ws.ao, ws.ld_o, seq, Hq, Hkv, D, st);
        })))
     return rc;
   // O projection + residual, in place on x
   const mhe::BSegments wo{{static_cast<const bf16_t*>(w.w_o), nullptr, nullptr}, {H, 0, 0}, 1};
   if ((rc = traced(MHE_STEP_O_PROJ, st, "o projection", [&] {
-         return mhe::launch_gemm(mhe::Epilogue::kResidual, ws.ao, wo, x, x, seq, H, qw, ws.partial,
+         return mhe::launch_gemm(mhe::Epilogue::kResidual, ws.ao, ws.ld_o, wo, qw, x, H, x, seq, H, qw, ws.partial,
                                 ws.partial_bytes, st);
        })))
     return rc;
   if ((rc = traced(MHE_STEP_POST_NORM, st, "post-attention rmsnorm", [&] {
-         return mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_post), ws.hn, seq, H, c.rms_eps, st);
+         return mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_post), ws.hn, ws.ld_h, seq, H,
+                                    c.rms_eps, st);
        })))
     return rc;
   const mhe::BSegments gu{{static_cast<const bf16_t*>(w.w_gate), static_cast<const bf16_t*>(w.w_up), nullptr},
                           {c.intermediate, c.intermediate, 0},
                           2};
   if ((rc = traced(MHE_STEP_GATE_UP, st, "gate/up projection", [&] {
-         return mhe::launch_gemm(mhe::Epilogue::kSwiGLU, ws.hn, gu, ws.act, nullptr, seq, c.intermediate, H,
+         return mhe::launch_gemm(mhe::Epilogue::kSwiGLU, ws.hn, ws.ld_h, gu, H, ws.act, ws.ld_i, nullptr, seq, c.intermediate, H,
                                 ws.partial, ws.partial_bytes, st);
        })))
     return rc;
   const mhe::BSegments wd{{static_cast<const bf16_t*>(w.w_down), nullptr, nullptr}, {H, 0, 0}, 1};
   return traced(MHE_STEP_DOWN, st, "down projection", [&] {
-    return mhe::launch_gemm(mhe::Epilogue::kResidual, ws.act, wd, x, x, seq, H, c.intermediate,
+    return mhe::launch_gemm(mhe::Epilogue::kResidual, ws.act, ws.ld_i, wd, c.intermediate, x, H, x, seq, H, c.intermediate,
                             ws.partial, ws.partial_bytes, st);
   });
 }
@@ -424,7 +434,7 @@ int32_t mhe_rms_norm(const void* x, const void* gamma, void* y, int32_t rows, in
   if (!mhe::rmsnorm_supported(dim)) return fail(MHE_ERR_UNSUPPORTED, "dim %d: multiple of 8, <= 8192", dim);
   if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(MHE_ERR_SHAPE, "eps must be finite and >= 0");
   return hip_check(mhe::launch_rmsnorm(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(gamma),
-                                       static_cast<bf16_t*>(y), rows, dim, eps,
+                                       static_cast<bf16_t*>(y), dim, rows, dim, eps,
                                        static_cast<hipStream_t>(stream)),
                    "rmsnorm");
 }
@@ -454,7 +464,7 @@ int32_t mhe_linear(const void* a, const void* w, void* c, const void* residual, 
     return fail(MHE_ERR_SHAPE, "workspace overlaps an operand");
   mhe::BSegments b{{static_cast<const bf16_t*>(w), nullptr, nullptr}, {n, 0, 0}, 1};
   return hip_check(mhe::launch_gemm(residual ? mhe::Epilogue::kResidual : mhe::Epilogue::kStore,
-                                    static_cast<const bf16_t*>(a), b, static_cast<bf16_t*>(c),
+                                    static_cast<const bf16_t*>(a), k, b, k, static_cast<bf16_t*>(c), n,
                                     static_cast<const bf16_t*>(residual), m, n, k,
                                     static_cast<float*>(workspace), workspace ? workspace_bytes : 0,
                                     static_cast<hipStream_t>(stream)),
@@ -477,8 +487,8 @@ int32_t mhe_linear_swiglu(const void* a, const void* w_gate, const void* w_up, v
   mhe::BSegments b{{static_cast<const bf16_t*>(w_gate), static_cast<const bf16_t*>(w_up), nullptr},
                    {n, n, 0},
                    2};
-  return hip_check(mhe::launch_gemm(mhe::Epilogue::kSwiGLU, static_cast<const bf16_t*>(a), b,
-                                    static_cast<bf16_t*>(c), nullptr, m, n, k,
+  return hip_check(mhe::launch_gemm(mhe::Epilogue::kSwiGLU, static_cast<const bf16_t*>(a), k, b, k,
+                                    static_cast<bf16_t*>(c), n, nullptr, m, n, k,
                                     static_cast<float*>(workspace), workspace ? workspace_bytes : 0,
                                     static_cast<hipStream_t>(stream)),
                    "linear_swiglu");
@@ -513,7 +523,7 @@ int32_t mhe_attention(const void* q, const void* k, const void* vt, void* o, int
   if (!mhe::attention_supported(n_heads, n_kv_heads, head_dim))
     return fail(MHE_ERR_UNSUPPORTED, "head_dim 64/128 and 1, 2, 4 or 8 query heads per kv head");
   return hip_check(mhe::launch_attention(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                                         static_cast<const bf16_t*>(vt), static_cast<bf16_t*>(o), seq,
+                                         static_cast<const bf16_t*>(vt), static_cast<bf16_t*>(o), n_heads * head_dim, seq,
                                          n_heads, n_kv_heads, head_dim,
                                          static_cast<hipStream_t>(stream)),
                    "attention");

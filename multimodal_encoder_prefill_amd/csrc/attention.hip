@@ -38,8 +38,8 @@ template <int D, int G>
 __global__ __launch_bounds__(64 * G) void attention_kernel(const bf16_t* __restrict__ q,
                                                           const bf16_t* __restrict__ k,
                                                           const bf16_t* __restrict__ vt,
-                                                          bf16_t* __restrict__ o, int seq,
-                                                          int n_heads, int n_kv_heads,
+                                                          bf16_t* __restrict__ o, int ldo,
+                                                          int seq, int n_heads, int n_kv_heads,
                                                           float scale_log2) {
   constexpr int KCH = D / 8;         // 16-byte chunks per K row
   constexpr int NTH = 64 * G;
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(64 * G) void attention_kernel(const bf16_t* __restr
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (qi < seq) {
     const float inv = 1.f / l_tot;
-    bf16_t* dst = o + static_cast<size_t>(qi) * n_heads * D + h * D + lhalf * 4;
+    bf16_t* dst = o + static_cast<size_t>(qi) * ldo + h * D + lhalf * 4;
 #pragma unroll
     for (int b = 0; b < DB; ++b)
 #pragma unroll
@@ -227,8 +227,8 @@ __global__ __launch_bounds__(64 * G) void attention_kernel(const bf16_t* __restr
 }
 
 template <int D>
-hipError_t launch_d(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o, int seq,
-                    int n_heads, int n_kv_heads, hipStream_t stream) {
+hipError_t launch_d(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o, int ldo,
+                    int seq, int n_heads, int n_kv_heads, hipStream_t stream) {
   const int G = n_heads / n_kv_heads;
   const int n_qb = (seq + QB - 1) / QB;
   const dim3 grid(n_qb * n_kv_heads);
@@ -237,7 +237,7 @@ hipError_t launch_d(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* 
 #define MHE_ATTN_CASE(GG)                                                                      \
   case GG:                                                                                     \
     hipLaunchKernelGGL((attention_kernel<D, GG>), grid, dim3(64 * GG), 0, stream, q, k, vt, o, \
-                       seq, n_heads, n_kv_heads, scale_log2);                                  \
+                       ldo, seq, n_heads, n_kv_heads, scale_log2);                             \
     break;
     MHE_ATTN_CASE(1)
     MHE_ATTN_CASE(2)
@@ -259,11 +259,12 @@ bool attention_supported(int n_heads, int n_kv_heads, int head_dim) {
 }
 
 hipError_t launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o,
-                            int seq, int n_heads, int n_kv_heads, int head_dim,
+                            int ldo, int seq, int n_heads, int n_kv_heads, int head_dim,
                             hipStream_t stream) {
   if (seq <= 0) return hipSuccess;
-  if (head_dim == 128) return launch_d<128>(q, k, vt, o, seq, n_heads, n_kv_heads, stream);
-  if (head_dim == 64) return launch_d<64>(q, k, vt, o, seq, n_heads, n_kv_heads, stream);
+  if (ldo < n_heads * head_dim || ldo % 4 != 0) return hipErrorInvalidValue;
+  if (head_dim == 128) return launch_d<128>(q, k, vt, o, ldo, seq, n_heads, n_kv_heads, stream);
+  if (head_dim == 64) return launch_d<64>(q, k, vt, o, ldo, seq, n_heads, n_kv_heads, stream);
   return hipErrorInvalidValue;
 }
 

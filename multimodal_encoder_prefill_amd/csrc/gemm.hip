@@ -52,6 +52,8 @@ struct GemmArgs {
   bf16_t* c;
   const bf16_t* r;
   int m, n, k;
+  int lda, ldb;  // row strides (elements) of A and of every B segment
+  int ldc;       // row stride of C and of the residual
   int tiles_m, tiles_n;
   // work units of this launch: tiles [tile_begin, tile_begin + units / ksplit),
   // each split into ksplit k-ranges of kt_per_split k-steps. With ksplit > 1 the
@@ -123,6 +125,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   bf16_t* Bs = smem + STAGES * kTileElems;    // [STAGES][BN][BK]
 
   const int M = args.m, N = args.n, K = args.k;
+  const int lda = args.lda, ldb = args.ldb;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -147,7 +150,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   for (int i = 0; i < kBlks; ++i) {
     const int row0 = m0 + kRowsPerBlk * i;
     const int nrows = max(0, min(kRowsPerBlk, M - row0));
-    a_rsrc[i] = scalar_rsrc(args.a + static_cast<size_t>(min(row0, M - 1)) * K, nrows * K * 2);
+    a_rsrc[i] = scalar_rsrc(args.a + static_cast<size_t>(min(row0, M - 1)) * lda,
+                            nrows > 0 ? ((nrows - 1) * lda + K) * 2 : 0);
     const bf16_t* base;
     int v, avail;
     if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
@@ -176,7 +180,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       }
     }
     const int brows = max(0, min(kRowsPerBlk, avail));
-    b_rsrc[i] = scalar_rsrc(base + static_cast<size_t>(v) * K, brows * K * 2);
+    b_rsrc[i] = scalar_rsrc(base + static_cast<size_t>(v) * ldb,
+                            brows > 0 ? ((brows - 1) * ldb + K) * 2 : 0);
   }
 
   f32x16 acc[4][4];
@@ -191,7 +196,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   // DMA: lane L of wave w fills 16 bytes at block row w*(1024/kRowBytes) + L/kChunks,
   // physical chunk L%kChunks, and so fetches the logical chunk the swizzle puts there.
   const int dma_row = wave * (1024 / kRowBytes) + lane / kChunks;
-  const int dma_voff = dma_row * K * 2 + (((lane % kChunks) ^ swz<BK>(dma_row)) * 16);
+  const int dma_chunk = ((lane % kChunks) ^ swz<BK>(dma_row)) * 16;
+  const int dma_voff_a = dma_row * lda * 2 + dma_chunk;
+  const int dma_voff_b = dma_row * ldb * 2 + dma_chunk;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   auto issue_dma = [&](int kt, int stage) {
 #if __HIP_DEVICE_COMPILE__  // the LDS-DMA builtin exists only in the device pass
@@ -202,19 +209,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     for (int i = 0; i < kBlks; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           a_rsrc[i], (__attribute__((address_space(3))) void*)(as + i * kRowsPerBlk * BK), 16,
-          dma_voff, soff, 0, 0);
+          dma_voff_a, soff, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           b_rsrc[i], (__attribute__((address_space(3))) void*)(bs + i * kRowsPerBlk * BK), 16,
-          dma_voff, soff, 0, 0);
+          dma_voff_b, soff, 0, 0);
     }
 #else
-    (void)kt, (void)stage, (void)dma_voff, (void)wave_u;
+    (void)kt, (void)stage, (void)dma_voff_a, (void)dma_voff_b, (void)wave_u;
 #endif
   };
   // Registers: thread t loads row t/kChunks of each block, chunk t%kChunks.
   const int reg_row = tid / kChunks;
   const int reg_chunk = tid % kChunks;
-  const int reg_voff = reg_row * K * 2 + reg_chunk * 16;
+  const int reg_voff_a = reg_row * lda * 2 + reg_chunk * 16;
+  const int reg_voff_b = reg_row * ldb * 2 + reg_chunk * 16;
   const int reg_lds = reg_row * BK + ((reg_chunk ^ swz<BK>(reg_row)) << 3);
   u32x4 ra[DMA ? 1 : kBlks], rb[DMA ? 1 : kBlks];
   auto load_regs = [&](int kt) {
@@ -222,8 +230,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       const int soff = kt * BK * 2;
 #pragma unroll
       for (int i = 0; i < kBlks; ++i) {
-        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc[i], reg_voff, soff, 0));
-        rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc[i], reg_voff, soff, 0));
+        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc[i], reg_voff_a, soff, 0));
+        rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc[i], reg_voff_b, soff, 0));
       }
     }
   };
@@ -360,7 +368,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
           u32x2 pk;
           pk[0] = pack_bf16x2(o[0], o[1]);
           pk[1] = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<u32x2*>(args.c + static_cast<size_t>(m) * N + jb + 8 * g + 4 * lhalf) = pk;
+          *reinterpret_cast<u32x2*>(args.c + static_cast<size_t>(m) * args.ldc + jb + 8 * g + 4 * lhalf) = pk;
         }
       }
     } else {
@@ -370,7 +378,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
         if (nb >= N) continue;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const size_t off = static_cast<size_t>(m) * N + nb + 8 * g + 4 * lhalf;
+          const size_t off = static_cast<size_t>(m) * args.ldc + nb + 8 * g + 4 * lhalf;
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * g + e];
@@ -428,7 +436,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args)
     for (int e = 0; e < 4; ++e) o[e] = sum[e];
   }
   if (n >= N) return;
-  const size_t off = static_cast<size_t>(m) * N + n;
+  const size_t off = static_cast<size_t>(m) * args.ldc + n;
   if (EPI == static_cast<int>(Epilogue::kResidual)) {
     const u32x2 rv = *reinterpret_cast<const u32x2*>(args.r + off);
     o[0] += __uint_as_float(rv[0] << 16);
@@ -520,9 +528,11 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
 
 size_t gemm_partial_bytes() { return static_cast<size_t>(320) * BM * BN * sizeof(float); }
 
-hipError_t launch_gemm(Epilogue epi, const bf16_t* a, const BSegments& b, bf16_t* c,
-                       const bf16_t* residual, int m, int n, int k, float* partial,
-                       size_t partial_bytes, hipStream_t stream) {
+hipError_t launch_gemm(Epilogue epi, const bf16_t* a, int lda, const BSegments& b, int ldb,
+                       bf16_t* c, int ldc, const bf16_t* residual, int m, int n, int k,
+                       float* partial, size_t partial_bytes, hipStream_t stream) {
+  if (lda < k || ldb < k || ldc < n || lda % 8 != 0 || ldb % 8 != 0 || ldc % 4 != 0)
+    return hipErrorInvalidValue;
   if (m <= 0) return hipSuccess;
   // a load block never straddles two weight segments
   if (epi != Epilogue::kSwiGLU && b.count > 1)
@@ -539,6 +549,9 @@ hipError_t launch_gemm(Epilogue epi, const bf16_t* a, const BSegments& b, bf16_t
   args.m = m;
   args.n = n;
   args.k = k;
+  args.lda = lda;
+  args.ldb = ldb;
+  args.ldc = ldc;
   args.tiles_m = (m + BM - 1) / BM;
   args.tiles_n = epi == Epilogue::kSwiGLU ? (n + BN / 2 - 1) / (BN / 2) : (n + BN - 1) / BN;
   switch (epi) {

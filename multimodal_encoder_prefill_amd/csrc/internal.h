@@ -10,8 +10,9 @@ typedef uint16_t bf16_t;
 
 // rmsnorm.hip
 bool rmsnorm_supported(int dim);
-hipError_t launch_rmsnorm(const bf16_t* x, const bf16_t* gamma, bf16_t* y, int rows, int dim,
-                          float eps, hipStream_t stream);
+// y rows are ldy elements apart (>= dim, multiple of 8); x is dense.
+hipError_t launch_rmsnorm(const bf16_t* x, const bf16_t* gamma, bf16_t* y, int ldy, int rows,
+                          int dim, float eps, hipStream_t stream);
 
 // gemm.hip: C[m, n] = A[m, :] . B[n, :] with one of three epilogues.
 enum class Epilogue { kStore = 0, kResidual = 1, kSwiGLU = 2 };
@@ -31,9 +32,11 @@ int gemm_segment_rows();
 // `partial` (may be NULL) is fp32 scratch for split-K units of the last wave;
 // gemm_partial_bytes() is enough for every shape.
 size_t gemm_partial_bytes();
-hipError_t launch_gemm(Epilogue epi, const bf16_t* a, const BSegments& b, bf16_t* c,
-                       const bf16_t* residual, int m, int n, int k, float* partial,
-                       size_t partial_bytes, hipStream_t stream);
+// lda / ldb: row strides in elements (>= k, multiples of 8) of A and of B;
+// ldc: row stride of C and of the residual (>= n, multiple of 4).
+hipError_t launch_gemm(Epilogue epi, const bf16_t* a, int lda, const BSegments& b, int ldb,
+                       bf16_t* c, int ldc, const bf16_t* residual, int m, int n, int k,
+                       float* partial, size_t partial_bytes, hipStream_t stream);
 
 // qk_norm_rope.hip
 struct RopeParams {
@@ -48,8 +51,9 @@ hipError_t launch_qk_norm_rope(const RopeParams& p, const bf16_t* qkv, const bf1
 
 // attention.hip
 bool attention_supported(int n_heads, int n_kv_heads, int head_dim);
+// o rows are ldo elements apart (>= n_heads * head_dim, multiple of 4).
 hipError_t launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o,
-                            int seq, int n_heads, int n_kv_heads, int head_dim,
+                            int ldo, int seq, int n_heads, int n_kv_heads, int head_dim,
                             hipStream_t stream);
 
 // deepstack.hip

@@ -41,7 +41,6 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
     int n_heads, int n_kv_heads, float eps, float theta, int sec1, int sec2,
     bf16_t* __restrict__ q_out, bf16_t* __restrict__ k_out, bf16_t* __restrict__ vt_out) {
   constexpr int HALF = D / 2;
-  constexpr int RPW = 64 / HALF;  // head rows per wavefront pass
   const int s0 = blockIdx.x * kTok;
   const int width = (n_heads + 2 * n_kv_heads) * D;
   const int n_chunks = (n_heads + n_kv_heads + kHeadsPerBlock - 1) / kHeadsPerBlock;
@@ -87,47 +86,60 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
   }
   __syncthreads();
 
+  // ---- q / k head rows: D/8 lanes per row, 8 consecutive elements per lane;
+  //      element d pairs with d +- D/2, which sits D/16 lanes away ----
+  constexpr int LPR = D / 8;           // lanes per head row
+  constexpr int ROWS_PER_PASS = 64 / LPR;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int sub = lane / HALF;   // which row of the wavefront pass
-  const int j = lane % HALF;     // this lane owns elements j and j + HALF
+  const int sub = lane / LPR;
+  const int chunk = lane % LPR;
+  const bool first_half = chunk < LPR / 2;
+  const int j0 = (chunk % (LPR / 2)) * 8;   // rotary slot of this lane's first element
   const int h_first = blockIdx.y * kHeadsPerBlock;
   const int h_count = min(kHeadsPerBlock, n_heads + n_kv_heads - h_first);
   const int rows = kTok * h_count;
-  for (int r0 = wave * RPW; r0 < rows; r0 += 4 * RPW) {
+  for (int r0 = wave * ROWS_PER_PASS; r0 < rows; r0 += 4 * ROWS_PER_PASS) {
     const int r = r0 + sub;
     const bool active = r < rows;
     const int t = active ? r / h_count : 0;
     const int h = h_first + (active ? r % h_count : 0);
     const int s = s0 + t;
     const bool is_q = h < n_heads;
-    float x0 = 0.f, x1 = 0.f;
+    float x[8];
     if (active && s < seq) {
-      const bf16_t* src = qkv + static_cast<size_t>(s) * width + h * D;
-      x0 = bf16_to_f32(src[j]);
-      x1 = bf16_to_f32(src[j + HALF]);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qkv + static_cast<size_t>(s) * width + h * D + chunk * 8);
+      unpack8(v, x);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = 0.f;
     }
-    float ss = group_sum<HALF>(x0 * x0 + x1 * x1);
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+    ss = group_sum<LPR>(ss);
     const float rinv = rsqrtf(ss / static_cast<float>(D) + eps);
-    const bf16_t* gain = is_q ? q_gain : k_gain;
-    const float y0 = x0 * rinv * bf16_to_f32(gain[j]);
-    const float y1 = x1 * rinv * bf16_to_f32(gain[j + HALF]);
-    const float c = cs[t][j][0], sn = cs[t][j][1];
-    const float o0 = y0 * c - y1 * sn;
-    const float o1 = y1 * c + y0 * sn;
+    float gn[8];
+    unpack8(*reinterpret_cast<const u32x4*>((is_q ? q_gain : k_gain) + chunk * 8), gn);
+    float y[8], o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = x[i] * rinv * gn[i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float partner = __shfl_xor(y[i], LPR / 2, 64);
+      const float c = cs[t][j0 + i][0], sn = cs[t][j0 + i][1];
+      // first half: x cos - x_partner sin; second half: x cos + x_partner sin
+      o[i] = first_half ? y[i] * c - partner * sn : y[i] * c + partner * sn;
+    }
     if (!active) continue;
     if (is_q) {
-      if (s < seq) {
-        bf16_t* dst = q_out + (static_cast<size_t>(s) * n_heads + h) * D;
-        dst[j] = f32_to_bf16(o0);
-        dst[j + HALF] = f32_to_bf16(o1);
-      }
+      if (s < seq)
+        *reinterpret_cast<u32x4*>(q_out + (static_cast<size_t>(s) * n_heads + h) * D + chunk * 8) = pack8(o);
     } else if (s < seq_pad) {
       const int g = h - n_heads;
-      bf16_t* dst = k_out + (static_cast<size_t>(g) * seq_pad + s) * D;
-      const bool live = s < seq;
-      dst[j] = live ? f32_to_bf16(o0) : static_cast<bf16_t>(0);
-      dst[j + HALF] = live ? f32_to_bf16(o1) : static_cast<bf16_t>(0);
+      u32x4 v = pack8(o);
+      if (s >= seq) v = u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(k_out + (static_cast<size_t>(g) * seq_pad + s) * D + chunk * 8) = v;
     }
   }
 }

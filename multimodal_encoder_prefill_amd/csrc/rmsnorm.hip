@@ -11,10 +11,12 @@ namespace {
 constexpr int kRowsPerBlock = 4;   // 4 waves, one row each
 constexpr int kMaxChunks = 16;     // 16-byte chunks per lane -> dim <= 64*8*16 = 8192
 
-// x and y may alias: every lane loads its whole row slice before any store.
+// x and y may alias (with ldy == dim): every lane loads its whole row slice
+// before any store.
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const bf16_t* x,
                                                       const bf16_t* __restrict__ gamma,
-                                                      bf16_t* y, int rows, int dim, float eps) {
+                                                      bf16_t* y, int ldy, int rows, int dim,
+                                                      float eps) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
@@ -36,7 +38,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const bf16_t* x,
   ss = wave_sum(ss);
   const float r = rsqrtf(ss / static_cast<float>(dim) + eps);
   const u32x4* gr = reinterpret_cast<const u32x4*>(gamma);
-  u32x4* yr = reinterpret_cast<u32x4*>(y + static_cast<size_t>(row) * dim);
+  u32x4* yr = reinterpret_cast<u32x4*>(y + static_cast<size_t>(row) * ldy);
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int c = lane + 64 * i;
@@ -53,11 +55,12 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const bf16_t* x,
 
 }  // namespace
 
-hipError_t launch_rmsnorm(const bf16_t* x, const bf16_t* gamma, bf16_t* y, int rows, int dim,
-                          float eps, hipStream_t stream) {
+hipError_t launch_rmsnorm(const bf16_t* x, const bf16_t* gamma, bf16_t* y, int ldy, int rows,
+                          int dim, float eps, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
+  if (ldy < dim || ldy % 8 != 0) return hipErrorInvalidValue;
   dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock);
-  hipLaunchKernelGGL(rmsnorm_kernel, grid, dim3(256), 0, stream, x, gamma, y, rows, dim, eps);
+  hipLaunchKernelGGL(rmsnorm_kernel, grid, dim3(256), 0, stream, x, gamma, y, ldy, rows, dim, eps);
   return hipGetLastError();
 }
 
