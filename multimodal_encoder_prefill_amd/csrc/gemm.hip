@@ -486,14 +486,15 @@ template <int EPI>
 hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t stream) {
   // One workgroup fills a CU (128 KB of LDS), so a launch of T tiles runs in
   // ceil(T / CUs) waves. Full waves run whole tiles; when the last wave would
-  // leave more than half the CUs idle, its R tiles are cut into ksplit k-ranges
+  // leave at least half the CUs idle and is a sizeable part of the launch (at
+  // most 4 full waves before it), its R tiles are cut into ksplit k-ranges
   // (ksplit * R <= CUs) whose fp32 partials are summed by a small reduction.
   const int tiles = args.tiles_m * args.tiles_n;
   const int nk = args.k / kBK;
   static const int cus = device_cus();
   const int rem = tiles % cus;
   int ksplit = 1;
-  if (partial && rem > 0 && rem <= cus / 2) {
+  if (partial && rem > 0 && rem <= cus / 2 && tiles / cus <= 4) {
     ksplit = min(cus / rem, 16);
     ksplit = min(ksplit, nk / 4);
     const size_t cap = partial_bytes / (static_cast<size_t>(BM) * BN * sizeof(float));
