@@ -5,11 +5,12 @@
 // repeat_interleave; here the expansion is an index map and K/V are read once
 // per group), key j is visible to query i iff j <= i (is_causal with an
 // all-ones padding mask), the scale is 1/sqrt(D) (the SDPA default). Softmax is
-// computed online in fp32 (running max and sum, exp2 with a log2(e) pre-scale)
-// and the output is rounded to bf16 once.
+// computed online in fp32 (running max and sum, exp2 with a log2(e) pre-scale,
+// the max raised lazily) and the output is rounded to bf16 once.
 //
-// One workgroup = one key/value head g and 32 query rows; its G wavefronts are
-// the G query heads of the group, so every K/V tile staged in LDS serves all G
+// One workgroup = one key/value head g and 32 query rows; its wavefronts each
+// take two query heads of the group, so every K/V tile staged in LDS serves
+// all G heads and every K or V operand read from LDS feeds the MFMAs of two
 // heads. Each wavefront computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 // (keys are the MFMA rows, queries the columns), so a lane holds 16 scores of
 // a single query per 32-key block and the row max needs only one exchange
@@ -34,21 +35,24 @@ constexpr int KT = 64;   // keys per tile
 
 __device__ __forceinline__ int swz8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-template <int D, int G>
-__global__ __launch_bounds__(64 * G) void attention_kernel(const bf16_t* __restrict__ q,
-                                                          const bf16_t* __restrict__ k,
-                                                          const bf16_t* __restrict__ vt,
-                                                          bf16_t* __restrict__ o, int ldo,
-                                                          int seq, int n_heads, int n_kv_heads,
-                                                          float scale_log2) {
-  constexpr int KCH = D / 8;         // 16-byte chunks per K row
-  constexpr int NTH = 64 * G;
-  constexpr int K_CHUNKS = KT * KCH;  // per tile
-  constexpr int V_CHUNKS = D * (KT / 8);
-  constexpr int K_PER_T = (K_CHUNKS + NTH - 1) / NTH;
-  constexpr int V_PER_T = (V_CHUNKS + NTH - 1) / NTH;
-  constexpr int DS = D / 16;         // MFMA k-steps over head_dim
-  constexpr int DB = D / 32;         // 32-row blocks of O^T
+// Buffer resource over [p, p + bytes) held in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const bf16_t* p, int bytes) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+  const uint64_t s = (static_cast<uint64_t>(hi) << 32) | lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(s), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+template <int D, int G, int HPW>
+__global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
+    bf16_t* __restrict__ o, int ldo, int seq, int n_heads, int n_kv_heads, float scale_log2) {
+  constexpr int WAVES = G / HPW;
+  constexpr int KCH = D / 8;          // 16-byte chunks per K row
+  constexpr int DS = D / 16;          // MFMA k-steps over head_dim
+  constexpr int DB = D / 32;          // 32-row blocks of O^T
 
   __shared__ __attribute__((aligned(16))) bf16_t k_lds[2][KT * D];
   __shared__ __attribute__((aligned(16))) bf16_t v_lds[2][D * KT];
@@ -61,20 +65,21 @@ __global__ __launch_bounds__(64 * G) void attention_kernel(const bf16_t* __restr
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int h = g * G + wave;
+  const int h0 = g * G + wave * HPW;   // this wavefront's first query head
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
+  const int qi = q0 + lrow;
 
-  // ---- Q rows as the MFMA B operand, kept in registers ----
-  bf16x8 qreg[DS];
-  {
-    const int qi = q0 + lrow;
-    const bf16_t* src = q + (static_cast<size_t>(min(qi, seq - 1)) * n_heads + h) * D + lhalf * 8;
+  // ---- Q rows of the wavefront's heads as MFMA B operands, kept in registers ----
+  bf16x8 qreg[HPW][DS];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    const bf16_t* src = q + (static_cast<size_t>(min(qi, seq - 1)) * n_heads + h0 + hh) * D + lhalf * 8;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       u32x4 v = *reinterpret_cast<const u32x4*>(src + s * 16);
       if (qi >= seq) v = u32x4{0, 0, 0, 0};
-      qreg[s] = __builtin_bit_cast(bf16x8, v);
+      qreg[hh][s] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
@@ -83,117 +88,142 @@ __global__ __launch_bounds__(64 * G) void attention_kernel(const bf16_t* __restr
   const int last_key = min(q0 + QB - 1, seq - 1);
   const int n_tiles = last_key / KT + 1;
 
-  u32x4 kst[K_PER_T], vst[V_PER_T];
-  auto load_tile = [&](int t) {
+  // ---- K / V^T tiles go straight to LDS (buffer_load_dwordx4 ... lds). In
+  //      load instruction i, lane L of wavefront w fills the 16 LDS bytes at
+  //      offset ((i*WAVES + w)*64 + L)*16 of the tile, i.e. some row and
+  //      physical chunk, and fetches the logical chunk the swizzle puts there.
+  //      Tiles never extend past seq_pad, so every load is in bounds. ----
+  constexpr int K_ROW_BYTES = D * 2;
+  constexpr int V_ROW_BYTES = KT * 2;
+  constexpr int K_INSTR = KT * K_ROW_BYTES / (WAVES * 1024);
+  constexpr int V_INSTR = D * V_ROW_BYTES / (WAVES * 1024);
+  const __amdgpu_buffer_rsrc_t k_rsrc = scalar_rsrc(kg, sp * D * 2);
+  const __amdgpu_buffer_rsrc_t v_rsrc = scalar_rsrc(vg, D * sp * 2);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto issue_tile = [&](int t, int stage) {
+#if __HIP_DEVICE_COMPILE__  // the LDS-DMA builtin exists only in the device pass
 #pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + i * NTH;
-      if (c < K_CHUNKS) kst[i] = *reinterpret_cast<const u32x4*>(kg + static_cast<size_t>(t * KT) * D + c * 8);
+    for (int i = 0; i < K_INSTR; ++i) {
+      const int off = ((i * WAVES + wave) * 64 + lane) * 16;
+      const int row = off / K_ROW_BYTES, phys = (off % K_ROW_BYTES) / 16;
+      const int ch = (KCH == 16) ? (phys ^ (row & 15)) : (phys ^ swz8(row));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          k_rsrc, (__attribute__((address_space(3))) void*)(&k_lds[stage][0] + (i * WAVES + wave_u) * 512),
+          16, row * K_ROW_BYTES + ch * 16, t * KT * K_ROW_BYTES, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int c = tid + i * NTH;
-      if (c < V_CHUNKS) {
-        const int d = c / (KT / 8), ch = c % (KT / 8);
-        vst[i] = *reinterpret_cast<const u32x4*>(vg + static_cast<size_t>(d) * sp + t * KT + ch * 8);
-      }
+    for (int i = 0; i < V_INSTR; ++i) {
+      const int off = ((i * WAVES + wave) * 64 + lane) * 16;
+      const int row = off / V_ROW_BYTES, phys = (off % V_ROW_BYTES) / 16;
+      const int ch = phys ^ swz8(row);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          v_rsrc, (__attribute__((address_space(3))) void*)(&v_lds[stage][0] + (i * WAVES + wave_u) * 512),
+          16, row * sp * 2 + ch * 16, t * KT * 2, 0, 0);
     }
-  };
-  auto store_tile = [&](int stage) {
-#pragma unroll
-    for (int i = 0; i < K_PER_T; ++i) {
-      const int c = tid + i * NTH;
-      if (c < K_CHUNKS) {
-        const int row = c / KCH, ch = c % KCH;
-        const int phys = (KCH == 16) ? (ch ^ (row & 15)) : (ch ^ swz8(row));
-        *reinterpret_cast<u32x4*>(&k_lds[stage][row * D + phys * 8]) = kst[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < V_PER_T; ++i) {
-      const int c = tid + i * NTH;
-      if (c < V_CHUNKS) {
-        const int d = c / (KT / 8), ch = c % (KT / 8);
-        *reinterpret_cast<u32x4*>(&v_lds[stage][d * KT + ((ch ^ swz8(d)) * 8)]) = vst[i];
-      }
-    }
+#else
+    (void)t, (void)stage, (void)wave_u;
+#endif
   };
 
-  f32x16 oacc[DB];
+  f32x16 oacc[HPW][DB];
 #pragma unroll
-  for (int b = 0; b < DB; ++b)
+  for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[b][e] = 0.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  const int qi = q0 + lrow;
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[hh][b][e] = 0.f;
+  float m_run[HPW], l_run[HPW];
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh) {
+    m_run[hh] = -INFINITY;
+    l_run[hh] = 0.f;
+  }
 
-  load_tile(0);
-  store_tile(0);
+  issue_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
     const int cur = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    if (t + 1 < n_tiles) issue_tile(t + 1, cur ^ 1);
     const bf16_t* kl = k_lds[cur];
     const bf16_t* vl = v_lds[cur];
 
-    // ---- S^T for 64 keys: two 32-key blocks ----
-    f32x16 sacc[2];
+    // ---- S^T for 64 keys (two 32-key blocks), every K operand used by all heads ----
+    f32x16 sacc[HPW][2];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[hh][kb][e] = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
       const int row = kb * 32 + lrow;
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
         const int ch = 2 * s + lhalf;
         const int phys = (KCH == 16) ? (ch ^ (row & 15)) : (ch ^ swz8(row));
         const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + row * D + phys * 8));
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[s], sacc[kb], 0, 0, 0);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+          sacc[hh][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[hh][s], sacc[hh][kb], 0, 0, 0);
       }
     }
 
-    // ---- online softmax (log2 domain); lane's query is qi, keys per register ----
+    // ---- online softmax per head. Scores stay raw; the running max m is kept
+    //      in the scaled log2 domain and p = exp2(s * scale_log2 - m) is one
+    //      FMA plus one exp. m is only raised when a tile's max exceeds it by
+    //      more than 8 (p <= 2^8 meanwhile, exact once divided by the sum), so
+    //      the O rescale is skipped for the whole wavefront on most tiles. ----
     const bool diag = (t * KT + KT - 1) > q0;  // tile may hold keys past some query
-    float tmax = -INFINITY;
+    bf16x8 pop[HPW][4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int hh = 0; hh < HPW; ++hh) {
+      if (diag) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = sacc[kb][e] * scale_log2;
-        if (diag) {
-          const int key = t * KT + kb * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
-          if (key > qi) x = -INFINITY;
-        }
-        sacc[kb][e] = x;
-        tmax = fmaxf(tmax, x);
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = t * KT + kb * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
+            if (key > qi) sacc[hh][kb][e] = -INFINITY;
+          }
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);   // 0 on the first tile (m_run = -inf)
-    m_run = m_new;
-    float psum = 0.f;
-    bf16x8 pop[4];
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = exp2f(sacc[kb][hh * 8 + e] - m_new);
-          psum += pv[e];
-        }
-        pop[kb * 2 + hh] = __builtin_bit_cast(bf16x8, pack8(pv));
+        for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(sacc[hh][kb][e], sacc[hh][kb][e + 1]));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
+      float alpha = 1.f;
+      if (tmax > m_run[hh] + 8.f) {
+        alpha = __builtin_amdgcn_exp2f(m_run[hh] - tmax);  // 0 on the first tile
+        m_run[hh] = tmax;
       }
-    l_run = l_run * alpha + psum;
+      const float neg_m = -m_run[hh];
+      float psum = 0.f;
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[b][e] *= alpha;
+        for (int half = 0; half < 2; ++half) {
+          float pv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[hh][kb][half * 8 + e], scale_log2, neg_m));
+            psum += pv[e];
+          }
+          pop[hh][kb * 2 + half] = __builtin_bit_cast(bf16x8, pack8(pv));
+        }
+      l_run[hh] = l_run[hh] * alpha + psum;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int b = 0; b < DB; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[hh][b][e] *= alpha;
+      }
+    }
 
-    // ---- O^T += V^T P^T: 4 steps of 16 keys ----
+    // ---- O^T += V^T P^T: 4 steps of 16 keys, every V operand used by all heads ----
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
       const int d = b * 32 + lrow;
@@ -201,28 +231,34 @@ __global__ __launch_bounds__(64 * G) void attention_kernel(const bf16_t* __restr
       for (int s = 0; s < KT / 16; ++s) {
         const int ch = 2 * s + lhalf;
         const bf16x8 vop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vl + d * KT + ((ch ^ swz8(d)) * 8)));
-        oacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[s], oacc[b], 0, 0, 0);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh)
+          oacc[hh][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[hh][s], oacc[hh][b], 0, 0, 0);
       }
     }
 
-    if (t + 1 < n_tiles) store_tile(cur ^ 1);
+    // the next tile has landed, and every wavefront is done with this one
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
   // ---- normalise and store: lane holds query lrow, d = 32b + 8(e/4) + 4 lhalf + e%4 ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (qi < seq) {
-    const float inv = 1.f / l_tot;
-    bf16_t* dst = o + static_cast<size_t>(qi) * ldo + h * D + lhalf * 4;
 #pragma unroll
-    for (int b = 0; b < DB; ++b)
+  for (int hh = 0; hh < HPW; ++hh) {
+    const float l_tot = l_run[hh] + __shfl_xor(l_run[hh], 32, 64);
+    if (qi < seq) {
+      const float inv = 1.f / l_tot;
+      bf16_t* dst = o + static_cast<size_t>(qi) * ldo + (h0 + hh) * D + lhalf * 4;
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        u32x2 pk;
-        pk[0] = pack_bf16x2(oacc[b][gq * 4 + 0] * inv, oacc[b][gq * 4 + 1] * inv);
-        pk[1] = pack_bf16x2(oacc[b][gq * 4 + 2] * inv, oacc[b][gq * 4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(dst + b * 32 + gq * 8) = pk;
-      }
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(oacc[hh][b][gq * 4 + 0] * inv, oacc[hh][b][gq * 4 + 1] * inv);
+          pk[1] = pack_bf16x2(oacc[hh][b][gq * 4 + 2] * inv, oacc[hh][b][gq * 4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(dst + b * 32 + gq * 8) = pk;
+        }
+    }
   }
 }
 
@@ -234,15 +270,15 @@ hipError_t launch_d(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* 
   const dim3 grid(n_qb * n_kv_heads);
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
   switch (G) {
-#define MHE_ATTN_CASE(GG)                                                                      \
-  case GG:                                                                                     \
-    hipLaunchKernelGGL((attention_kernel<D, GG>), grid, dim3(64 * GG), 0, stream, q, k, vt, o, \
-                       ldo, seq, n_heads, n_kv_heads, scale_log2);                             \
+#define MHE_ATTN_CASE(GG, HH)                                                                 \
+  case GG:                                                                                    \
+    hipLaunchKernelGGL((attention_kernel<D, GG, HH>), grid, dim3(64 * (GG / HH)), 0, stream, \
+                       q, k, vt, o, ldo, seq, n_heads, n_kv_heads, scale_log2);               \
     break;
-    MHE_ATTN_CASE(1)
-    MHE_ATTN_CASE(2)
-    MHE_ATTN_CASE(4)
-    MHE_ATTN_CASE(8)
+    MHE_ATTN_CASE(1, 1)
+    MHE_ATTN_CASE(2, 1)
+    MHE_ATTN_CASE(4, 1)
+    MHE_ATTN_CASE(8, 1)
 #undef MHE_ATTN_CASE
     default:
       return hipErrorInvalidValue;
