@@ -200,13 +200,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   const int dma_voff_a = dma_row * lda * 2 + dma_chunk;
   const int dma_voff_b = dma_row * ldb * 2 + dma_chunk;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue_dma = [&](int kt, int stage) {
+  auto issue_dma = [&](int kt, int stage, int i0, int i1) {
 #if __HIP_DEVICE_COMPILE__  // the LDS-DMA builtin exists only in the device pass
     const int soff = kt * BK * 2;
     bf16_t* as = As + stage * kTileElems + wave_u * 512;
     bf16_t* bs = Bs + stage * kTileElems + wave_u * 512;
 #pragma unroll
-    for (int i = 0; i < kBlks; ++i) {
+    for (int i = i0; i < i1; ++i) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           a_rsrc[i], (__attribute__((address_space(3))) void*)(as + i * kRowsPerBlk * BK), 16,
           dma_voff_a, soff, 0, 0);
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
           dma_voff_b, soff, 0, 0);
     }
 #else
-    (void)kt, (void)stage, (void)dma_voff_a, (void)dma_voff_b, (void)wave_u;
+    (void)kt, (void)stage, (void)i0, (void)i1, (void)dma_voff_a, (void)dma_voff_b, (void)wave_u;
 #endif
   };
   // Registers: thread t loads row t/kChunks of each block, chunk t%kChunks.
@@ -251,10 +251,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   const int lswz = swz<BK>(lrow);
   const int a_base = (wm * 128 + lrow) * BK;  // activation rows (MFMA B operand)
   const int b_base = (wn * 128 + lrow) * BK;  // weight rows (MFMA A operand)
-  auto compute = [&](int stage) {
+  auto compute = [&](int stage, int next_kt, int next_stage) {
     const bf16_t* as = As + stage * kTileElems;
     const bf16_t* bs = Bs + stage * kTileElems;
-    // operands of substep s+1 are fetched while substep s's 16 MFMAs run
+    // Operands of substep s+1 are fetched while substep s's 16 MFMAs run, and
+    // the global->LDS loads of the k-step `next_kt` (into `next_stage`) are
+    // issued over the first three substeps, between the MFMAs, rather than in
+    // one burst that would hold up MFMA issue (-1: no loads).
     bf16x8 wop[2][4], xop[2][4];
     auto fetch = [&](int s, int slot) {
       const int chunk = ((2 * s + lhalf) ^ lswz) << 3;
@@ -269,17 +272,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     for (int s = 0; s < BK / 16; ++s) {
       __builtin_amdgcn_sched_barrier(0);
       if (s + 1 < BK / 16) fetch(s + 1, (s + 1) & 1);
+      constexpr int nsub = 3;  // substeps that carry global->LDS loads
+      constexpr int per = (kBlks + nsub - 1) / nsub;
+      if (next_kt >= 0 && s < nsub) issue_dma(next_kt, next_stage, s * per, min((s + 1) * per, kBlks));
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[s & 1][i], xop[s & 1][j], acc[i][j], 0, 0, 0);
       if (s + 1 < BK / 16) {
-        // spread the 8 operand reads between the 16 MFMAs
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          if (s < nsub && g < 2 * per) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global->LDS load
           __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < (s < nsub ? 2 * per : 0); ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -292,7 +304,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     // fetched STAGES-1 steps ahead of its use.
 #pragma unroll
     for (int p = 0; p < STAGES - 1; ++p)
-      if (p < nk) issue_dma(kt_begin + p, p);
+      if (p < nk) issue_dma(kt_begin + p, p, 0, kBlks);
     for (int kt = 0; kt < nk; ++kt) {
       // this wavefront's loads for k-step kt are done once at most the
       // loads of the k-steps issued after it are still in flight
@@ -304,8 +316,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       // every wavefront's loads for kt have landed, and every wavefront is
       // done with k-step kt-1, whose stage is refilled next
       lds_barrier();
-      if (kt + STAGES - 1 < nk) issue_dma(kt_begin + kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-      compute(kt % STAGES);
+      const bool more = kt + STAGES - 1 < nk;
+      compute(kt % STAGES, more ? kt_begin + kt + STAGES - 1 : -1, (kt + STAGES - 1) % STAGES);
     }
   } else {
     if (nk > 0) {
@@ -320,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
         store_regs((kt + 1) & 1);
         if (kt + 2 < nk) load_regs(kt_begin + kt + 2);
       }
-      compute(kt & 1);
+      compute(kt & 1, -1, 0);
       lds_barrier();
     }
   }
