@@ -247,7 +247,7 @@ int32_t mhe_linear_swiglu(const void* a, const void* w_gate, const void* w_up, v
  *   vt_out[n_kv_heads, head_dim, seq_pad]: V transposed, and within each
  *         aligned group of 16 tokens stored in the order
  *         0 1 2 3 8 9 10 11 4 5 6 7 12 13 14 15
- * with seq_pad = seq rounded up to 64; rows/columns past seq are zero.
+ * with seq_pad = seq rounded up to 128; rows/columns past seq are zero.
  */
 int32_t mhe_qk_norm_rope(const mhe_config* cfg, const void* qkv, const void* q_norm,
                          const void* k_norm, const int32_t* positions, int32_t seq, void* q_out,

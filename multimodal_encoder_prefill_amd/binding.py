@@ -255,5 +255,5 @@ def trace_read(step: str):
 
 
 def seq_pad(seq: int) -> int:
-    """Padded token count of the K / V^T layouts (multiple of 64)."""
-    return (seq + 63) // 64 * 64
+    """Padded token count of the K / V^T layouts (multiple of 128)."""
+    return (seq + 127) // 128 * 128

@@ -31,7 +31,7 @@ namespace mhe {
 namespace {
 
 constexpr int QB = 32;   // query rows per workgroup
-constexpr int KT = 64;   // keys per tile
+constexpr int KT = 128;  // keys per tile (the K / V^T layouts are padded to a multiple)
 
 __device__ __forceinline__ int swz8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
@@ -53,11 +53,14 @@ __global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
   constexpr int KCH = D / 8;          // 16-byte chunks per K row
   constexpr int DS = D / 16;          // MFMA k-steps over head_dim
   constexpr int DB = D / 32;          // 32-row blocks of O^T
+  constexpr int KB = KT / 32;         // 32-key blocks of S^T per tile
+  constexpr int PS = KT / 16;         // 16-key MFMA steps of O^T += V^T P^T
+  constexpr int VCH = KT / 8;         // 16-byte chunks per V^T row
 
   __shared__ __attribute__((aligned(16))) bf16_t k_lds[2][KT * D];
   __shared__ __attribute__((aligned(16))) bf16_t v_lds[2][D * KT];
 
-  const int sp = (seq + 63) / 64 * 64;
+  const int sp = seq_pad(seq);
   const int n_qb = (seq + QB - 1) / QB;
   const int g = blockIdx.x % n_kv_heads;
   const int qb = n_qb - 1 - static_cast<int>(blockIdx.x / n_kv_heads);
@@ -92,7 +95,7 @@ __global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
   //      load instruction i, lane L of wavefront w fills the 16 LDS bytes at
   //      offset ((i*WAVES + w)*64 + L)*16 of the tile, i.e. some row and
   //      physical chunk, and fetches the logical chunk the swizzle puts there.
-  //      Tiles never extend past seq_pad, so every load is in bounds. ----
+  //      seq_pad is a multiple of the tile, so every load is in bounds. ----
   constexpr int K_ROW_BYTES = D * 2;
   constexpr int V_ROW_BYTES = KT * 2;
   constexpr int K_INSTR = KT * K_ROW_BYTES / (WAVES * 1024);
@@ -115,13 +118,13 @@ __global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
     for (int i = 0; i < V_INSTR; ++i) {
       const int off = ((i * WAVES + wave) * 64 + lane) * 16;
       const int row = off / V_ROW_BYTES, phys = (off % V_ROW_BYTES) / 16;
-      const int ch = phys ^ swz8(row);
+      const int ch = (VCH == 16) ? (phys ^ (row & 15)) : (phys ^ swz8(row));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           v_rsrc, (__attribute__((address_space(3))) void*)(&v_lds[stage][0] + (i * WAVES + wave_u) * 512),
           16, row * sp * 2 + ch * 16, t * KT * 2, 0, 0);
     }
 #else
-    (void)t, (void)stage, (void)wave_u;
+    (void)t, (void)stage, (void)wave_u, (void)k_rsrc, (void)v_rsrc, (void)K_INSTR, (void)V_INSTR;
 #endif
   };
 
@@ -150,15 +153,15 @@ __global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
     const bf16_t* vl = v_lds[cur];
 
     // ---- S^T for 64 keys (two 32-key blocks), every K operand used by all heads ----
-    f32x16 sacc[HPW][2];
+    f32x16 sacc[HPW][KB];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[hh][kb][e] = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       const int row = kb * 32 + lrow;
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
@@ -177,12 +180,12 @@ __global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
     //      more than 8 (p <= 2^8 meanwhile, exact once divided by the sum), so
     //      the O rescale is skipped for the whole wavefront on most tiles. ----
     const bool diag = (t * KT + KT - 1) > q0;  // tile may hold keys past some query
-    bf16x8 pop[HPW][4];
+    bf16x8 pop[HPW][PS];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       if (diag) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = t * KT + kb * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
       }
       float tmax = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(sacc[hh][kb][e], sacc[hh][kb][e + 1]));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
       const float neg_m = -m_run[hh];
       float psum = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           float pv[8];
@@ -230,7 +233,8 @@ __global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
 #pragma unroll
       for (int s = 0; s < KT / 16; ++s) {
         const int ch = 2 * s + lhalf;
-        const bf16x8 vop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vl + d * KT + ((ch ^ swz8(d)) * 8)));
+        const int vphys = (VCH == 16) ? (ch ^ (d & 15)) : (ch ^ swz8(d));
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vl + d * KT + vphys * 8));
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh)
           oacc[hh][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[hh][s], oacc[hh][b], 0, 0, 0);

@@ -44,7 +44,8 @@ struct RopeParams {
   float eps, theta;
   int section[3];
 };
-int seq_pad(int seq);
+// tokens of the K / V^T layouts: seq rounded up to a multiple of 128
+__host__ __device__ inline int seq_pad(int seq) { return (seq + 127) / 128 * 128; }
 hipError_t launch_qk_norm_rope(const RopeParams& p, const bf16_t* qkv, const bf16_t* q_norm,
                                const bf16_t* k_norm, const int32_t* positions, int seq,
                                bf16_t* q_out, bf16_t* k_out, bf16_t* vt_out, hipStream_t stream);

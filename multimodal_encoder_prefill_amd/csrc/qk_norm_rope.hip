@@ -14,8 +14,9 @@
 // [kv_head][D][seq_pad] with tokens permuted inside every aligned group of 16
 // (0 1 2 3 8 9 10 11 4 5 6 7 12 13 14 15), which is the order in which one
 // 32x32x16 MFMA step of the attention kernel consumes probabilities, so the
-// attention kernel reads both K and V with plain 16-byte LDS loads. Padding
-// tokens (seq <= s < seq_pad) are written as zeros.
+// attention kernel reads both K and V with plain 16-byte LDS loads. seq_pad
+// is seq rounded up to 128 (the attention key tile); padding tokens
+// (seq <= s < seq_pad) are written as zeros.
 //
 // HBM-bound: per token it reads and writes (n_heads + 2 n_kv_heads) * D bf16.
 #include "common.h"
@@ -145,8 +146,6 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
 }
 
 }  // namespace
-
-int seq_pad(int seq) { return (seq + 63) / 64 * 64; }
 
 hipError_t launch_qk_norm_rope(const RopeParams& p, const bf16_t* qkv, const bf16_t* q_norm,
                                const bf16_t* k_norm, const int32_t* positions, int seq,
