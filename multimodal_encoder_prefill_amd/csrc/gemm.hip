@@ -16,13 +16,14 @@
 // activation rows the "B" operand, so every lane ends up with 4 consecutive
 // output columns (8-byte stores).
 //
-// K advances BK at a time through a ring of STAGES LDS buffers. Operand rows
-// are BK*2 bytes and their 16-byte chunks are XOR-swizzled so the ds_read_b128
-// operand fetches of 8 (or 16) consecutive lanes hit distinct banks. Tiles are
-// fetched either straight into LDS (buffer_load_dwordx4 ... lds) with up to
-// STAGES-1 k-steps in flight, or through registers (one k-step in flight)
-// then ds_write_b128. All loads use scalar buffer resources over 32- or
-// 64-row blocks, so rows past M or N read as zero without per-lane checks.
+// K advances 64 at a time through two LDS stages of 2 x 32 KB. Operand rows
+// are 128 bytes and their 16-byte chunks are XOR-swizzled so the ds_read_b128
+// operand fetches of 8 (or 16) consecutive lanes hit distinct banks. Tiles go
+// straight from global memory into LDS (buffer_load_dwordx4 ... lds) through
+// scalar buffer resources over 32-row blocks, so rows past M or N read as zero
+// without per-lane checks. One workgroup barrier per k-step, placed before its
+// last k-substep: that substep's operands are already in registers, so its
+// MFMAs hide the barrier and the first operand reads of the next k-step.
 //
 // Workgroups are remapped so that each XCD (workgroups are dealt round-robin
 // over the 8 XCDs) receives a contiguous run of tiles, ordered in groups of m
@@ -40,10 +41,7 @@ constexpr int kThreads = 256;
 constexpr int kGroupM = 8;  // m tiles per ordering group
 constexpr int kXcds = 8;
 
-// Pipeline configuration used by launch_gemm.
-constexpr int kBK = 64;
-constexpr int kStages = 2;
-constexpr bool kDma = true;
+constexpr int BK = 64;  // k elements per pipeline step (one 128-byte row piece)
 
 struct GemmArgs {
   const bf16_t* a;
@@ -74,15 +72,9 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
   tn = in_group / gm;
 }
 
-// Chunk swizzle of an LDS operand row (16-byte chunks). For 128-byte rows
-// (BK 64) rows r..r+7 and r..r+15 map one logical chunk to distinct 16-byte
-// bank groups; for 64-byte rows (BK 32) two rows share a 128-byte bank window
-// and the swizzle keeps 8 (16) consecutive rows distinct as well.
-template <int BK>
-__device__ __forceinline__ int swz(int row) {
-  if constexpr (BK == 64) return (row & 7) ^ ((row >> 3) & 1);
-  else return ((row >> 1) ^ (row >> 2)) & 3;
-}
+// Chunk swizzle of a 128-byte LDS operand row (8 chunks of 16 bytes): rows
+// r..r+7 and r..r+15 map one logical chunk to distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 // Buffer resource over [p, p + bytes); the pointer and size are wave-uniform
 // and are pinned to scalar registers so loads need no per-lane descriptor.
@@ -108,21 +100,23 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int EPI, int BK, int STAGES, bool DMA>
+template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) {
-  static_assert(BK == 32 || BK == 64, "BK");
-  static_assert(DMA || STAGES == 2, "register staging keeps one k-step in flight");
-  static_assert(STAGES >= 2 && STAGES <= 5, "stages");
-  constexpr int kTileElems = BM * BK;               // one operand, one stage
+  constexpr int kTileElems = BM * BK;           // one operand, one stage
   constexpr int kRowBytes = BK * 2;
-  constexpr int kChunks = BK / 8;                   // 16-byte chunks per row
-  constexpr int kRowsPerBlk = 4096 / kRowBytes;     // rows one load instruction covers
-  constexpr int kBlks = 256 / kRowsPerBlk;          // load instructions per operand per stage
-  constexpr int kLoadsPerStage = 2 * kBlks;
+  constexpr int kChunks = BK / 8;               // 16-byte chunks per row
+  constexpr int kRowsPerBlk = 4096 / kRowBytes; // rows one load instruction of the 4 waves covers
+  constexpr int kBlks = 256 / kRowsPerBlk;      // load instructions per operand per k-step
+  // The 2 kBlks loads of k-step kt+1 are issued in three parts: loads
+  // [0, kL0) during the last substep of k-step kt-1, the next kL1 and the rest
+  // during substeps 0 and 1 of k-step kt, each spread one per MFMA pair.
+  constexpr int kL0 = 6, kL1 = 5;
+  constexpr int kWarm = 4;  // warm-up distance in k-steps
+  static_assert(BK == 64 && kL0 <= 8 && kL1 <= 8 && 2 * kBlks - kL0 - kL1 <= 8, "pipeline shape");
 
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
-  bf16_t* As = smem;                          // [STAGES][BM][BK]
-  bf16_t* Bs = smem + STAGES * kTileElems;    // [STAGES][BN][BK]
+  bf16_t* As = smem;                  // [2][BM][BK]
+  bf16_t* Bs = smem + 2 * kTileElems; // [2][BN][BK], then 4 KB of warm-up scratch
 
   const int M = args.m, N = args.n, K = args.k;
   const int lda = args.lda, ldb = args.ldb;
@@ -142,16 +136,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   tile_coords(args.tile_begin + unit / args.ksplit, args.tiles_m, args.tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM;
   const int kt_begin = (unit % args.ksplit) * args.kt_per_split;
-  const int kt_end = min(kt_begin + args.kt_per_split, K / BK);
+  const int nk = min(kt_begin + args.kt_per_split, K / BK) - kt_begin;  // k-steps of this unit
 
-  // ---- per-block buffer resources (row blocks of kRowsPerBlk) ----
-  __amdgpu_buffer_rsrc_t a_rsrc[kBlks], b_rsrc[kBlks];
-#pragma unroll
-  for (int i = 0; i < kBlks; ++i) {
-    const int row0 = m0 + kRowsPerBlk * i;
-    const int nrows = max(0, min(kRowsPerBlk, M - row0));
-    a_rsrc[i] = scalar_rsrc(args.a + static_cast<size_t>(min(row0, M - 1)) * lda,
-                            nrows > 0 ? ((nrows - 1) * lda + K) * 2 : 0);
+  // ---- buffer resources over row blocks of kRowsPerBlk rows ----
+  // A rows m0 + row0 .. (row0 + rows) of the tile
+  auto a_block = [&](int row0, int rows) {
+    const int r = m0 + row0;
+    const int nrows = max(0, min(rows, M - r));
+    return scalar_rsrc(args.a + static_cast<size_t>(min(r, M - 1)) * lda,
+                       nrows > 0 ? ((nrows - 1) * lda + K) * 2 : 0);
+  };
+  // B row block i of the tile
+  auto b_block = [&](int i) {
     const bf16_t* base;
     int v, avail;
     if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
@@ -180,9 +176,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       }
     }
     const int brows = max(0, min(kRowsPerBlk, avail));
-    b_rsrc[i] = scalar_rsrc(base + static_cast<size_t>(v) * ldb,
-                            brows > 0 ? ((brows - 1) * ldb + K) * 2 : 0);
+    return scalar_rsrc(base + static_cast<size_t>(v) * ldb,
+                       brows > 0 ? ((brows - 1) * ldb + K) * 2 : 0);
+  };
+  __amdgpu_buffer_rsrc_t a_rsrc[kBlks], b_rsrc[kBlks];
+#pragma unroll
+  for (int i = 0; i < kBlks; ++i) {
+    a_rsrc[i] = a_block(kRowsPerBlk * i, kRowsPerBlk);
+    b_rsrc[i] = b_block(i);
   }
+  // empty range: loads through it touch no memory and return zeros
+  const __amdgpu_buffer_rsrc_t null_rsrc = scalar_rsrc(args.a, 0);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -192,149 +196,147 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // ---- load paths ----
-  // DMA: lane L of wave w fills 16 bytes at block row w*(1024/kRowBytes) + L/kChunks,
-  // physical chunk L%kChunks, and so fetches the logical chunk the swizzle puts there.
+  // ---- global -> LDS: lane L of wave w fills 16 bytes at block row
+  //      w*(1024/kRowBytes) + L/kChunks, physical chunk L%kChunks, and so
+  //      fetches the logical chunk the swizzle puts there. Blocks [b0, b1) of
+  //      both operands of k-step kt (unit-relative) go to LDS stage `stage`;
+  //      a k-step past the unit's range is loaded through the empty resource
+  //      (its zeros land in a stage that is no longer read). ----
   const int dma_row = wave * (1024 / kRowBytes) + lane / kChunks;
-  const int dma_chunk = ((lane % kChunks) ^ swz<BK>(dma_row)) * 16;
+  const int dma_chunk = ((lane % kChunks) ^ swz(dma_row)) * 16;
   const int dma_voff_a = dma_row * lda * 2 + dma_chunk;
   const int dma_voff_b = dma_row * ldb * 2 + dma_chunk;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  auto issue_dma = [&](int kt, int stage, int i0, int i1) {
-#if __HIP_DEVICE_COMPILE__  // the LDS-DMA builtin exists only in the device pass
-    const int soff = kt * BK * 2;
-    bf16_t* as = As + stage * kTileElems + wave_u * 512;
-    bf16_t* bs = Bs + stage * kTileElems + wave_u * 512;
+  // ---- L2 warm-up. The tiles running together on one XCD share operand
+  //      blocks (tile_coords: 8 m-tiles x 4 n-tiles), so without help the
+  //      first request for every k-step block of A and B misses the L2 for all
+  //      of its sharers at once. Each tile therefore loads, kWarm k-steps
+  //      ahead, its share of the blocks it shares (64 A rows chosen by
+  //      tile_n % 4, 32 B rows by tile_m % 8) into a scratch corner of LDS:
+  //      96 of the 512 rows, three 8-row loads per wavefront. ----
+  const __amdgpu_buffer_rsrc_t warm_a = a_block(64 * (tile_n & 3), 64);
+  const __amdgpu_buffer_rsrc_t warm_b = b_block(tile_m & 7);
+  int warm_voff[3];
 #pragma unroll
-    for (int i = i0; i < i1; ++i) {
+  for (int j = 0; j < 3; ++j) {
+    const int line = 24 * wave + 8 * j + lane / 8;  // 0..63 A rows, 64..95 B rows
+    warm_voff[j] = (line < 64 ? line * lda : (line - 64) * ldb) * 2 + (lane % 8) * 16;
+  }
+  auto issue_warm = [&](int kt) {
+#if __HIP_DEVICE_COMPILE__
+    const bool live = kt < nk;
+    const int soff = (kt_begin + kt) * BK * 2;
+    bf16_t* scratch = smem + 4 * kTileElems + wave_u * 512;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const bool is_a = 24 * wave_u + 8 * j < 64;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          a_rsrc[i], (__attribute__((address_space(3))) void*)(as + i * kRowsPerBlk * BK), 16,
-          dma_voff_a, soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          b_rsrc[i], (__attribute__((address_space(3))) void*)(bs + i * kRowsPerBlk * BK), 16,
-          dma_voff_b, soff, 0, 0);
+          live ? (is_a ? warm_a : warm_b) : null_rsrc,
+          (__attribute__((address_space(3))) void*)scratch, 16, warm_voff[j], soff, 0, 0);
     }
 #else
-    (void)kt, (void)stage, (void)i0, (void)i1, (void)dma_voff_a, (void)dma_voff_b, (void)wave_u;
+    (void)kt, (void)warm_a, (void)warm_b, (void)warm_voff;
 #endif
   };
-  // Registers: thread t loads row t/kChunks of each block, chunk t%kChunks.
-  const int reg_row = tid / kChunks;
-  const int reg_chunk = tid % kChunks;
-  const int reg_voff_a = reg_row * lda * 2 + reg_chunk * 16;
-  const int reg_voff_b = reg_row * ldb * 2 + reg_chunk * 16;
-  const int reg_lds = reg_row * BK + ((reg_chunk ^ swz<BK>(reg_row)) << 3);
-  u32x4 ra[DMA ? 1 : kBlks], rb[DMA ? 1 : kBlks];
-  auto load_regs = [&](int kt) {
-    if constexpr (!DMA) {
-      const int soff = kt * BK * 2;
-#pragma unroll
-      for (int i = 0; i < kBlks; ++i) {
-        ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(a_rsrc[i], reg_voff_a, soff, 0));
-        rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b_rsrc[i], reg_voff_b, soff, 0));
-      }
-    }
+
+  // load number l of a k-step: operand l % 2 (0: A, 1: B) of row block l / 2
+  auto issue_load = [&](int kt, int stage, int l) {
+#if __HIP_DEVICE_COMPILE__  // the LDS-DMA builtin exists only in the device pass
+    const bool live = kt < nk;
+    const int soff = (kt_begin + kt) * BK * 2;
+    const int i = l >> 1;
+    bf16_t* dst = ((l & 1) ? Bs : As) + stage * kTileElems + wave_u * 512 + i * kRowsPerBlk * BK;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        live ? ((l & 1) ? b_rsrc[i] : a_rsrc[i]) : null_rsrc,
+        (__attribute__((address_space(3))) void*)dst, 16, (l & 1) ? dma_voff_b : dma_voff_a, soff, 0, 0);
+#else
+    (void)kt, (void)stage, (void)l, (void)dma_voff_a, (void)dma_voff_b, (void)wave_u;
+    (void)null_rsrc;
+#endif
   };
-  auto store_regs = [&](int stage) {
-    if constexpr (!DMA) {
+  auto issue_dma = [&](int kt, int stage, int b0, int b1) {
 #pragma unroll
-      for (int i = 0; i < kBlks; ++i) {
-        *reinterpret_cast<u32x4*>(As + stage * kTileElems + i * kRowsPerBlk * BK + reg_lds) = ra[i];
-        *reinterpret_cast<u32x4*>(Bs + stage * kTileElems + i * kRowsPerBlk * BK + reg_lds) = rb[i];
-      }
-    }
+    for (int l = 2 * b0; l < 2 * b1; ++l) issue_load(kt, stage, l);
   };
 
-  // ---- compute one k-step from LDS stage `stage` ----
+  // ---- LDS -> registers and MFMA: substep s of a k-step covers k 16s..16s+15;
+  //      operands are double-buffered in two register slots ----
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
-  const int lswz = swz<BK>(lrow);
+  const int lswz = swz(lrow);
   const int a_base = (wm * 128 + lrow) * BK;  // activation rows (MFMA B operand)
   const int b_base = (wn * 128 + lrow) * BK;  // weight rows (MFMA A operand)
-  auto compute = [&](int stage, int next_kt, int next_stage) {
+  bf16x8 wop[2][4], xop[2][4];
+  auto fetch = [&](int stage, int s, int slot) {
     const bf16_t* as = As + stage * kTileElems;
     const bf16_t* bs = Bs + stage * kTileElems;
-    // Operands of substep s+1 are fetched while substep s's 16 MFMAs run, and
-    // the global->LDS loads of the k-step `next_kt` (into `next_stage`) are
-    // issued over the first three substeps, between the MFMAs, rather than in
-    // one burst that would hold up MFMA issue (-1: no loads).
-    bf16x8 wop[2][4], xop[2][4];
-    auto fetch = [&](int s, int slot) {
-      const int chunk = ((2 * s + lhalf) ^ lswz) << 3;
+    const int chunk = ((2 * s + lhalf) ^ lswz) << 3;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + chunk));
-        xop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + chunk));
-      }
-    };
-    fetch(0, 0);
+    for (int i = 0; i < 4; ++i) {
+      wop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + chunk));
+      xop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + chunk));
+    }
+  };
+  // blocks in order of max(i, j), so the MFMAs that need the operands read
+  // last come last
+  auto mfma_one = [&](int slot, int q) {
+    // q-th block in that order: q = d*d + e for d = 0..3, e = 0..2d
+    const int d = q < 1 ? 0 : q < 4 ? 1 : q < 9 ? 2 : 3;
+    const int e = q - d * d;
+    const int i = e <= d ? e : d, j = e <= d ? d : 2 * d - e;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[slot][i], xop[slot][j], acc[i][j], 0, 0, 0);
+  };
+  auto mfma = [&](int slot) {
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (s + 1 < BK / 16) fetch(s + 1, (s + 1) & 1);
-      constexpr int nsub = 3;  // substeps that carry global->LDS loads
-      constexpr int per = (kBlks + nsub - 1) / nsub;
-      if (next_kt >= 0 && s < nsub) issue_dma(next_kt, next_stage, s * per, min((s + 1) * per, kBlks));
+    for (int q = 0; q < 16; ++q) mfma_one(slot, q);
+  };
+  // the 16 MFMAs of a substep with loads [l0, l1) of k-step kt placed one
+  // after each pair of MFMAs
+  auto mfma_loads = [&](int slot, int kt, int stage, int l0, int l1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[s & 1][i], xop[s & 1][j], acc[i][j], 0, 0, 0);
-      if (s + 1 < BK / 16) {
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-          if (s < nsub && g < 2 * per) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global->LDS load
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
-        }
-      } else {
-#pragma unroll
-        for (int g = 0; g < (s < nsub ? 2 * per : 0); ++g) {
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        }
-      }
+    for (int g = 0; g < 8; ++g) {
+      mfma_one(slot, 2 * g);
+      mfma_one(slot, 2 * g + 1);
+      if (l0 + g < l1) issue_load(kt, stage, l0 + g);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  const int nk = kt_end - kt_begin;  // k-steps of this unit; k-step i is kt_begin + i
-  if constexpr (DMA) {
-    // Ring of STAGES buffers; k-step kt lives in stage kt % STAGES and is
-    // fetched STAGES-1 steps ahead of its use.
-#pragma unroll
-    for (int p = 0; p < STAGES - 1; ++p)
-      if (p < nk) issue_dma(kt_begin + p, p, 0, kBlks);
-    for (int kt = 0; kt < nk; ++kt) {
-      // this wavefront's loads for k-step kt are done once at most the
-      // loads of the k-steps issued after it are still in flight
-      const int ahead = min(STAGES - 2, nk - 1 - kt);
-      if (ahead >= 3) wait_vmcnt<(STAGES >= 5 ? 3 : 0) * kLoadsPerStage>();
-      else if (ahead == 2) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * kLoadsPerStage>();
-      else if (ahead == 1) wait_vmcnt<(STAGES >= 3 ? 1 : 0) * kLoadsPerStage>();
-      else wait_vmcnt<0>();
-      // every wavefront's loads for kt have landed, and every wavefront is
-      // done with k-step kt-1, whose stage is refilled next
-      lds_barrier();
-      const bool more = kt + STAGES - 1 < nk;
-      compute(kt % STAGES, more ? kt_begin + kt + STAGES - 1 : -1, (kt + STAGES - 1) % STAGES);
-    }
-  } else {
-    if (nk > 0) {
-      load_regs(kt_begin);
-      store_regs(0);
-    }
-    if (nk > 1) load_regs(kt_begin + 1);
+  // ---- pipeline over a two-stage LDS ring. The one workgroup barrier per
+  //      k-step sits before its last substep, whose operands are already in
+  //      registers: the MFMAs of that substep cover the reads of the next
+  //      k-step's first operands, and the stage just finished is refilled
+  //      from there on. ----
+  if (nk > 0) {
+    issue_dma(0, 0, 0, kBlks);
+    wait_vmcnt<0>();
     lds_barrier();
+    fetch(0, 0, 0);
+    for (int l = 0; l < kL0; ++l) issue_load(1, 1, l);
     for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) {
-        // stage (kt+1)%2 was last read in k-step kt-1, before the barrier
-        store_regs((kt + 1) & 1);
-        if (kt + 2 < nk) load_regs(kt_begin + kt + 2);
-      }
-      compute(kt & 1, -1, 0);
+      const int st = kt & 1;
+      __builtin_amdgcn_sched_barrier(0);
+      fetch(st, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_loads(0, kt + 1, st ^ 1, kL0, kL0 + kL1);
+      fetch(st, 2, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_loads(1, kt + 1, st ^ 1, kL0 + kL1, 2 * kBlks);
+      fetch(st, 3, 1);
+      issue_warm(kt + kWarm);
+      mfma(0);
+      __builtin_amdgcn_sched_barrier(0);
+      // k-step kt+1 is complete in LDS (only the three warm-up loads just
+      // issued may still be in flight) and no wavefront reads stage st any more
+      wait_vmcnt<3>();
       lds_barrier();
+      fetch(st ^ 1, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_loads(1, kt + 2, st, 0, kL0);
     }
+    // the trailing loads (empty resources) and reads have completed
+    wait_vmcnt<0>();
+    lds_barrier();
   }
 
   // ---- split-K unit: raw accumulators to the unit's partial tile, laid out
@@ -464,25 +466,25 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args)
 
 template <int EPI>
 hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
-  constexpr size_t smem = static_cast<size_t>(kStages) * 2 * BM * kBK * sizeof(bf16_t);
+  constexpr size_t smem = static_cast<size_t>(2) * 2 * BM * BK * sizeof(bf16_t) + 4096;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_kernel<EPI, kBK, kStages, kDma>),
+        reinterpret_cast<const void*>(&gemm_kernel<EPI>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<EPI, kBK, kStages, kDma>), dim3(grid), dim3(kThreads), smem,
+  hipLaunchKernelGGL((gemm_kernel<EPI>), dim3(grid), dim3(kThreads), smem,
                      stream, args);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int gemm_segment_rows() { return 4096 / (kBK * 2); }
+int gemm_segment_rows() { return 4096 / (BK * 2); }
 
-bool gemm_supported(int n, int k) { return n > 0 && k > 0 && n % 32 == 0 && k % kBK == 0; }
+bool gemm_supported(int n, int k) { return n > 0 && k > 0 && n % 32 == 0 && k % BK == 0; }
 
 namespace {
 
@@ -502,7 +504,7 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
   // most 4 full waves before it), its R tiles are cut into ksplit k-ranges
   // (ksplit * R <= CUs) whose fp32 partials are summed by a small reduction.
   const int tiles = args.tiles_m * args.tiles_n;
-  const int nk = args.k / kBK;
+  const int nk = args.k / BK;
   static const int cus = device_cus();
   const int rem = tiles % cus;
   int ksplit = 1;
