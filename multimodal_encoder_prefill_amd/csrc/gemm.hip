@@ -28,6 +28,8 @@
 // Workgroups are remapped so that each XCD (workgroups are dealt round-robin
 // over the 8 XCDs) receives a contiguous run of tiles, ordered in groups of m
 // tiles so tiles running together on one XCD share A and B panels in its L2.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -107,12 +109,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   constexpr int kChunks = BK / 8;               // 16-byte chunks per row
   constexpr int kRowsPerBlk = 4096 / kRowBytes; // rows one load instruction of the 4 waves covers
   constexpr int kBlks = 256 / kRowsPerBlk;      // load instructions per operand per k-step
-  // The 2 kBlks loads of k-step kt+1 are issued in three parts: loads
+  // The 2 kBlks loads of k-step kt+1 are issued in up to three parts: loads
   // [0, kL0) during the last substep of k-step kt-1, the next kL1 and the rest
-  // during substeps 0 and 1 of k-step kt, each spread one per MFMA pair.
-  constexpr int kL0 = 6, kL1 = 5;
+  // during substeps 0 and 1 of k-step kt, each part spread evenly over the
+  // substep's MFMAs. (Issuing all of them in one substep is slower, and so is
+  // issuing the last ones late in substep 1.)
+  constexpr int kL0 = 8, kL1 = 8;
   constexpr int kWarm = 4;  // warm-up distance in k-steps
-  static_assert(BK == 64 && kL0 <= 8 && kL1 <= 8 && 2 * kBlks - kL0 - kL1 <= 8, "pipeline shape");
+  static_assert(BK == 64 && kL0 + kL1 <= 2 * kBlks, "pipeline shape");
 
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
   bf16_t* As = smem;                  // [2][BM][BK]
@@ -209,33 +213,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // ---- L2 warm-up. The tiles running together on one XCD share operand
   //      blocks (tile_coords: 8 m-tiles x 4 n-tiles), so without help the
-  //      first request for every k-step block of A and B misses the L2 for all
-  //      of its sharers at once. Each tile therefore loads, kWarm k-steps
-  //      ahead, its share of the blocks it shares (64 A rows chosen by
-  //      tile_n % 4, 32 B rows by tile_m % 8) into a scratch corner of LDS:
-  //      96 of the 512 rows, three 8-row loads per wavefront. ----
-  const __amdgpu_buffer_rsrc_t warm_a = a_block(64 * (tile_n & 3), 64);
-  const __amdgpu_buffer_rsrc_t warm_b = b_block(tile_m & 7);
-  int warm_voff[3];
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const int line = 24 * wave + 8 * j + lane / 8;  // 0..63 A rows, 64..95 B rows
-    warm_voff[j] = (line < 64 ? line * lda : (line - 64) * ldb) * 2 + (lane % 8) * 16;
-  }
+  //      first request for a k-step block misses the L2 for all of its sharers
+  //      at once. For the weight rows, which come from HBM, each tile
+  //      therefore loads its share of its B block (32 rows, chosen by
+  //      tile_m % 8) kWarm k-steps ahead into a scratch corner of LDS, one
+  //      8-row load per wavefront. (Activation rows are hits in the last-level
+  //      cache and gain nothing from this.) ----
+  const __amdgpu_buffer_rsrc_t warm_b = b_block((tile_m & 7) * (32 / kRowsPerBlk));
+  const int warm_voff = (8 * wave + lane / 8) * ldb * 2 + (lane % 8) * 16;
   auto issue_warm = [&](int kt) {
 #if __HIP_DEVICE_COMPILE__
-    const bool live = kt < nk;
     const int soff = (kt_begin + kt) * BK * 2;
     bf16_t* scratch = smem + 4 * kTileElems + wave_u * 512;
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const bool is_a = 24 * wave_u + 8 * j < 64;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          live ? (is_a ? warm_a : warm_b) : null_rsrc,
-          (__attribute__((address_space(3))) void*)scratch, 16, warm_voff[j], soff, 0, 0);
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        kt < nk ? warm_b : null_rsrc, (__attribute__((address_space(3))) void*)scratch, 16,
+        warm_voff, soff, 0, 0);
 #else
-    (void)kt, (void)warm_a, (void)warm_b, (void)warm_voff;
+    (void)kt, (void)warm_b, (void)warm_voff;
 #endif
   };
 
@@ -290,14 +284,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 #pragma unroll
     for (int q = 0; q < 16; ++q) mfma_one(slot, q);
   };
-  // the 16 MFMAs of a substep with loads [l0, l1) of k-step kt placed one
-  // after each pair of MFMAs
-  auto mfma_loads = [&](int slot, int kt, int stage, int l0, int l1) {
+  // the 16 MFMAs of a substep with loads [L0, L1) of k-step kt spread evenly
+  // between them (L0, L1 compile-time: std::integral_constant)
+  auto mfma_loads = [&](int slot, int kt, int stage, auto L0, auto L1) {
+    constexpr int l0 = decltype(L0)::value, n = decltype(L1)::value - l0;
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      mfma_one(slot, 2 * g);
-      mfma_one(slot, 2 * g + 1);
-      if (l0 + g < l1) issue_load(kt, stage, l0 + g);
+    for (int q = 0; q < 16; ++q) {
+      mfma_one(slot, q);
+      if constexpr (n > 0) {
+#pragma unroll
+        for (int j = 0; j < n; ++j)
+          if (j * 16 / n == q) issue_load(kt, stage, l0 + j);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -318,21 +316,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       __builtin_amdgcn_sched_barrier(0);
       fetch(st, 1, 1);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_loads(0, kt + 1, st ^ 1, kL0, kL0 + kL1);
+      mfma_loads(0, kt + 1, st ^ 1, std::integral_constant<int, kL0>(), std::integral_constant<int, kL0 + kL1>());
       fetch(st, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_loads(1, kt + 1, st ^ 1, kL0 + kL1, 2 * kBlks);
+      mfma_loads(1, kt + 1, st ^ 1, std::integral_constant<int, kL0 + kL1>(), std::integral_constant<int, 2 * kBlks>());
       fetch(st, 3, 1);
       issue_warm(kt + kWarm);
       mfma(0);
       __builtin_amdgcn_sched_barrier(0);
-      // k-step kt+1 is complete in LDS (only the three warm-up loads just
-      // issued may still be in flight) and no wavefront reads stage st any more
-      wait_vmcnt<3>();
+      // k-step kt+1 is complete in LDS (only the warm-up load just issued may
+      // still be in flight) and no wavefront reads stage st any more
+      wait_vmcnt<1>();
       lds_barrier();
       fetch(st ^ 1, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_loads(1, kt + 2, st, 0, kL0);
+      mfma_loads(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, kL0>());
     }
     // the trailing loads (empty resources) and reads have completed
     wait_vmcnt<0>();
