@@ -16,6 +16,10 @@ page and the class/function on it whose computation it follows:
 * "vLLM Qwen3-VL page" = ``vllm/model_executor/models/qwen3_vl.py``;
 * "SGLang Qwen3-VL page" = ``python/sglang/srt/models/qwen3_vl.py``.
 
+``oracle.frontend`` holds the token-level front end of the same page
+(token types, embedding gather with visual placeholder scatter, the joint
+DeepStack order and the multimodal rotary position ids).
+
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, invariants, hand-derived fixtures under
 ``tests/golden/`` and independent library routines (torch's ``rms_norm`` and
@@ -40,3 +44,4 @@ from .qwen3vl_text import (  # noqa: F401
     layer_param_count,
 )
 from .positions import text_and_grid_positions  # noqa: F401
+from . import frontend  # noqa: F401

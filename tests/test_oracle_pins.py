@@ -420,3 +420,111 @@ def test_positions_worked_examples_and_synth_recipe():
             if r[0] == key:
                 tok = int(r[1])
                 assert ref[:, tok].tolist() == [int(x) for x in r[2].split()], (key, tok)
+
+
+# ---------------------------------------------------------------- token front end
+
+IMG_ID, VID_ID = 151655, 151656
+
+
+def _ids_from_types(types, seed=0):
+    """Token ids of the given types: text ids drawn below the special ids."""
+    rng = np.random.default_rng(seed)
+    types = np.asarray(types)
+    ids = rng.integers(0, 151000, size=len(types))
+    ids[types == 1] = IMG_ID
+    ids[types == 2] = VID_ID
+    return ids
+
+
+def test_rope_index_worked_example():
+    rows = {k: v for k, v in (ln.split("|") for ln in _lines("rope_index_mixed.txt"))}
+    rows = {k.strip(): v.split() for k, v in rows.items()}
+    types = [int(x) for x in rows["types"]]
+    ids = _ids_from_types(types)
+    pos, delta = oracle.frontend.rope_index(ids, IMG_ID, VID_ID,
+                                            [[int(x) for x in rows["image_grid"]]],
+                                            [[int(x) for x in rows["video_grid"]]],
+                                            int(rows["merge"][0]))
+    want = np.array([[int(x) for x in rows[a]] for a in ("t", "h", "w")])
+    assert np.array_equal(pos, want)
+    assert delta == int(rows["delta"][0])
+
+
+def test_rope_index_text_only_is_a_ramp():
+    ids = _ids_from_types(np.zeros(37, dtype=int), seed=3)
+    pos, delta = oracle.frontend.rope_index(ids, IMG_ID, VID_ID, None, None, 2)
+    assert np.array_equal(pos, np.tile(np.arange(37), (3, 1)))
+    assert delta == 0
+
+
+def test_rope_index_agrees_with_segment_rule_on_workloads():
+    # two formulations of the page's rule: from token ids (runs of equal
+    # type) and from the workloads' segment lists
+    from multimodal_encoder_prefill_amd import synth
+    for name in ("image_s2048_l4", "image_s4096_l50", "video_s16384_l50"):
+        wl = synth.WORKLOADS[name]
+        types, igrids = [], []
+        for kind, spec in wl.segments:
+            if kind == "text":
+                types += [0] * int(spec)
+            else:
+                t, h, w = (int(x) for x in spec)
+                types += [1] * (t * h * w)
+                igrids.append((t, 2 * h, 2 * w))
+        ids = _ids_from_types(types, seed=5)
+        pos, delta = oracle.frontend.rope_index(ids, IMG_ID, VID_ID, igrids, None, 2)
+        ref = oracle.text_and_grid_positions(wl.segments)
+        assert np.array_equal(pos, ref)
+        assert delta == int(ref.max()) + 1 - ref.shape[1]
+
+
+def test_rope_index_rejects_runs_that_do_not_fit_a_grid():
+    ids = _ids_from_types([0, 1, 1, 1, 0])
+    with pytest.raises(ValueError):  # 3 tokens, grid holds 4
+        oracle.frontend.rope_index(ids, IMG_ID, VID_ID, [[1, 4, 4]], None, 2)
+    with pytest.raises(ValueError):  # no grid at all
+        oracle.frontend.rope_index(ids, IMG_ID, VID_ID, None, None, 2)
+    # adjacent frames with no text between them are one run: it holds two
+    # frames' tokens, more than the one-frame grid it takes
+    ids = _ids_from_types([0] + [2] * 8 + [0])
+    with pytest.raises(ValueError):
+        oracle.frontend.rope_index(ids, IMG_ID, VID_ID, None, [[2, 4, 4]], 2)
+
+
+def test_embed_and_scatter_places_rows():
+    # a table whose row i is filled with i identifies every gathered row
+    vocab, hid = 151936, 8
+    table = np.repeat(np.arange(vocab, dtype=np.float64)[:, None], hid, axis=1)
+    types = [0, 1, 1, 0, 2, 0, 1]
+    ids = _ids_from_types(types, seed=7)
+    img = -1.0 - np.arange(3 * hid, dtype=np.float64).reshape(3, hid)
+    vid = -100.0 - np.arange(hid, dtype=np.float64)[None, :]
+    out = oracle.frontend.embed_and_scatter(table, ids, IMG_ID, VID_ID, img, vid)
+    for t in (0, 3, 5):
+        assert np.all(out[t] == ids[t])
+    np.testing.assert_array_equal(out[[1, 2, 6]], img)
+    np.testing.assert_array_equal(out[4], vid[0])
+    with pytest.raises(ValueError):
+        oracle.frontend.embed_and_scatter(table, ids, IMG_ID, VID_ID, img[:2], None)
+
+
+def test_aggregate_deepstack_joint_order():
+    S, hid = 12, 4
+    image_mask = np.zeros(S, bool)
+    video_mask = np.zeros(S, bool)
+    image_mask[[1, 2, 7]] = True
+    video_mask[[4, 5, 9, 10]] = True
+    rng = np.random.default_rng(11)
+    img = [rng.normal(size=(3, hid)) for _ in range(3)]
+    vid = [rng.normal(size=(4, hid)) for _ in range(3)]
+    vis, levels = oracle.frontend.aggregate_deepstack(image_mask, video_mask, img, vid)
+    assert np.array_equal(np.nonzero(vis)[0], [1, 2, 4, 5, 7, 9, 10])
+    for l in range(3):
+        # the joint rows, put back on their tokens, give each modality's rows
+        full = np.zeros((S, hid))
+        full[vis] = levels[l]
+        np.testing.assert_array_equal(full[image_mask], img[l])
+        np.testing.assert_array_equal(full[video_mask], vid[l])
+    m, lv = oracle.frontend.aggregate_deepstack(image_mask, None, img, None)
+    assert np.array_equal(m, image_mask) and lv is img
