@@ -263,6 +263,85 @@ int32_t mhe_qk_norm_rope(const mhe_config* cfg, const void* qkv, const void* q_n
 int32_t mhe_attention(const void* q, const void* k, const void* vt, void* o, int32_t seq,
                       int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, void* stream);
 
+/* ---- token-level front end (from token ids to mhe_encode's inputs) ---------- */
+
+/*
+ * Multimodal rotary position ids from token ids (H3 encoder page,
+ * _get_rope_index with _get_vision_position_ids, and the token types that
+ * _encode assigns). HOST function: every pointer is host memory, nothing is
+ * enqueued and no GPU is needed.
+ *   ids [seq] int32. A token equal to image_token_id is an image placeholder,
+ *   equal to video_token_id a video placeholder, anything else text.
+ *   image_grid_thw [n_images, 3], video_grid_thw [n_videos, 3]: int32 (t, h, w)
+ *   patch grids as the vision tower reports them; spatial_merge is its merge
+ *   size (2 for Qwen3-VL). A video of t frames counts as t one-frame grids.
+ * The tokens are cut into runs of one type. A text run of n tokens takes
+ * positions cur .. cur+n-1 on all three axes and advances cur by n; a visual
+ * run takes the next grid of its type and must hold its t * (h/m) * (w/m)
+ * tokens; its token at frame f, row r, column c gets (cur+f, cur+r, cur+c) and
+ * cur advances by max(h, w)/m.
+ * Outputs: positions [3, seq] int32 (rows T, H, W), the layout mhe_encode
+ * takes; optional (may be NULL) image_mask, video_mask, visual_mask [seq]
+ * uint8 (1 on image / video / either placeholder tokens) and *delta = max
+ * position + 1 - seq (the page's rope delta).
+ * Errors: NULL ids/positions or grid arrays, seq out of range, equal token
+ * ids, a non-positive grid or h, w not multiples of spatial_merge
+ * (MHE_ERR_SHAPE); a visual run with no grid left or of another length than
+ * its grid (MHE_ERR_MISMATCH; the page's processor brackets every image and
+ * video frame with text). Grids left over are ignored, as on the page. On
+ * error the outputs are partly written.
+ */
+int32_t mhe_rope_index(const int32_t* ids, int32_t seq, int32_t image_token_id,
+                       int32_t video_token_id, const int32_t* image_grid_thw, int32_t n_images,
+                       const int32_t* video_grid_thw, int32_t n_videos, int32_t spatial_merge,
+                       int32_t* positions, uint8_t* image_mask, uint8_t* video_mask,
+                       uint8_t* visual_mask, int32_t* delta);
+
+/*
+ * Token embedding gather (H3 encoder page, _encode: text_model.embed_tokens;
+ * the vocab-parallel embedding of the same page for a table shard):
+ * out[s, :] = table[ids[s] - row_begin, :] when row_begin <= ids[s] <
+ * row_begin + rows, else a zero row, which is also added to *n_outside
+ * (device int32, may be NULL; the caller zeroes it). ids device int32 [seq],
+ * table device bf16 [rows, hidden_dim], out [seq, hidden_dim] bf16.
+ * hidden_dim % 8 == 0.
+ */
+int32_t mhe_embed_tokens(const int32_t* ids, int32_t seq, const void* table, int32_t row_begin,
+                         int32_t rows, int32_t hidden_dim, void* out, int32_t* n_outside,
+                         void* stream);
+
+/*
+ * Visual placeholder scatter in place (H3 encoder page, _encode:
+ * inputs_embeds.masked_scatter(mask, embeds)): for r < n, hidden[t_r, :] =
+ * feature[r, :] where t_r is the r-th token (ascending) whose mask byte is
+ * set. Same shapes, bounds behaviour and workspace (seq*4 + 256 bytes) as
+ * mhe_deepstack_inject; the page's count check is mhe_count_visual.
+ */
+int32_t mhe_scatter_visual(void* hidden, int32_t seq, int32_t hidden_dim, const uint8_t* mask,
+                           int32_t n, const void* feature, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of mhe_join_visual for `seq` tokens (0 if seq is out of range). */
+size_t mhe_join_visual_workspace_bytes(int32_t seq);
+
+/*
+ * One DeepStack level for a prompt with both images and videos (H3 encoder
+ * page, _aggregate_deepstack): joint[r, :] is the feature row of the r-th
+ * visual token (ascending over tokens set in image_mask or video_mask):
+ * image_feature[i] if it is the i-th image token, else video_feature[v] if it
+ * is the v-th video token. image_mask, video_mask device uint8 [seq]
+ * (disjoint); image_feature [n_image, hidden_dim], video_feature [n_video,
+ * hidden_dim], joint [n_image + n_video, hidden_dim], bf16. Rows with no
+ * matching feature (masks with fewer set bytes than n_image / n_video) are
+ * zero, as in the page's zero-initialised joint array. Pass joint with
+ * visual_mask = image_mask | video_mask (mhe_rope_index writes it) to
+ * mhe_encode.
+ */
+int32_t mhe_join_visual(const uint8_t* image_mask, const uint8_t* video_mask, int32_t seq,
+                        int32_t hidden_dim, const void* image_feature, int32_t n_image,
+                        const void* video_feature, int32_t n_video, void* joint, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -70,7 +70,17 @@ _SIGNATURES = {
     "mhe_attention": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "mhe_trace_enable": (_i32, [ctypes.c_uint32]),
     "mhe_trace_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
+    "mhe_rope_index": (_i32, [_vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp,
+                              _vp, ctypes.POINTER(_i32)]),
+    "mhe_embed_tokens": (_i32, [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "mhe_scatter_visual": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "mhe_join_visual_workspace_bytes": (_sz, [_i32]),
+    "mhe_join_visual": (_i32, [_vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
 }
+
+# placeholder token ids of Qwen3-VL (H3 encoder page, MiniMaxH3Qwen3VLEncoder defaults)
+IMAGE_TOKEN_ID = 151655
+VIDEO_TOKEN_ID = 151656
 
 # step ids of the trace facility (MHE_STEP_* in include/mhe.h)
 STEPS = ("input_norm", "qkv", "qk_rope", "attention", "o_proj", "post_norm", "gate_up", "down",
@@ -257,3 +267,109 @@ def trace_read(step: str):
 def seq_pad(seq: int) -> int:
     """Padded token count of the K / V^T layouts (multiple of 128)."""
     return (seq + 127) // 128 * 128
+
+
+# ---- token-level front end ----
+
+def rope_index(ids, image_token_id=IMAGE_TOKEN_ID, video_token_id=VIDEO_TOKEN_ID,
+               image_grid_thw=None, video_grid_thw=None, spatial_merge=2):
+    """Host call: (positions int32 [3, S], image_mask, video_mask, visual_mask uint8 [S], delta).
+
+    ids: host token ids (sequence, numpy array or CPU tensor); grids: [n, 3] (t, h, w).
+    """
+    import numpy as np
+    ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+    seq = int(ids.shape[0])
+    ig = np.ascontiguousarray(np.asarray(image_grid_thw if image_grid_thw is not None else
+                                         np.zeros((0, 3)), dtype=np.int32).reshape(-1, 3))
+    vg = np.ascontiguousarray(np.asarray(video_grid_thw if video_grid_thw is not None else
+                                         np.zeros((0, 3)), dtype=np.int32).reshape(-1, 3))
+    pos = np.empty((3, max(seq, 1)), dtype=np.int32)
+    masks = [np.empty(max(seq, 1), dtype=np.uint8) for _ in range(3)]
+    delta = ctypes.c_int32(0)
+    _check("mhe_rope_index", lib().mhe_rope_index(
+        ids.ctypes.data, seq, image_token_id, video_token_id,
+        ig.ctypes.data if len(ig) else None, len(ig), vg.ctypes.data if len(vg) else None, len(vg),
+        spatial_merge, pos.ctypes.data, masks[0].ctypes.data, masks[1].ctypes.data,
+        masks[2].ctypes.data, ctypes.byref(delta)))
+    return pos, masks[0], masks[1], masks[2], delta.value
+
+
+def embed_tokens(ids, seq, table, row_begin, rows, hidden_dim, out, n_outside=None, stream=None):
+    _check("mhe_embed_tokens", lib().mhe_embed_tokens(
+        _ptr(ids), seq, _ptr(table), row_begin, rows, hidden_dim, _ptr(out), _ptr(n_outside),
+        _stream(stream)))
+
+
+def scatter_visual(hidden, seq, hidden_dim, mask, n, feature, workspace, workspace_bytes,
+                   stream=None):
+    _check("mhe_scatter_visual", lib().mhe_scatter_visual(
+        _ptr(hidden), seq, hidden_dim, _ptr(mask), n, _ptr(feature), _ptr(workspace),
+        workspace_bytes, _stream(stream)))
+
+
+def join_visual_workspace_bytes(seq: int) -> int:
+    return lib().mhe_join_visual_workspace_bytes(seq)
+
+
+def join_visual(image_mask, video_mask, seq, hidden_dim, image_feature, n_image, video_feature,
+                n_video, joint, workspace, workspace_bytes, stream=None):
+    _check("mhe_join_visual", lib().mhe_join_visual(
+        _ptr(image_mask), _ptr(video_mask), seq, hidden_dim, _ptr(image_feature), n_image,
+        _ptr(video_feature), n_video, _ptr(joint), _ptr(workspace), workspace_bytes,
+        _stream(stream)))
+
+
+def encode_ids(cfg, layers: Sequence, ids, embed_table, out, workspace, workspace_bytes, *,
+               image_embeds=None, image_grid_thw=None, video_embeds=None, video_grid_thw=None,
+               deepstack_image: Optional[Sequence] = None,
+               deepstack_video: Optional[Sequence] = None,
+               image_token_id=IMAGE_TOKEN_ID, video_token_id=VIDEO_TOKEN_ID, spatial_merge=2,
+               stream=None):
+    """The page's encode_ids from token ids and vision-tower outputs, as libmhe calls.
+
+    ids: host token ids [S]; embed_table device bf16 [vocab, hidden]; image / video
+    embeds device bf16 [n, hidden] (rows in placeholder order) with their grids;
+    deepstack_* lists of device bf16 [n, hidden] per level. `out` [S, hidden] receives
+    the layer output. Raises ValueError when feature and placeholder counts differ
+    (H3 encoder page, _get_placeholder_mask).
+    """
+    import numpy as np
+    import torch
+    pos, img_m, vid_m, vis_m, _ = rope_index(ids, image_token_id, video_token_id,
+                                             image_grid_thw, video_grid_thw, spatial_merge)
+    seq = pos.shape[1] if len(np.asarray(ids)) else 0
+    n_img, n_vid = int(img_m[:seq].sum()), int(vid_m[:seq].sum())
+    for name, feats, n in (("image", image_embeds, n_img), ("video", video_embeds, n_vid)):
+        if feats is not None and feats.shape[0] != n:
+            raise ValueError(f"{name} features and tokens do not match: tokens {n}, features {feats.shape[0]}")
+    dev = out.device
+    hidden = cfg.hidden
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a[..., :seq])).to(dev)
+    ids_dev = up(np.asarray(ids, dtype=np.int32))
+    pos_dev, img_dev, vid_dev, vis_dev = up(pos), up(img_m), up(vid_m), up(vis_m)
+    embeds = torch.empty(seq, hidden, dtype=torch.bfloat16, device=dev)
+    embed_tokens(ids_dev, seq, embed_table, 0, embed_table.shape[0], hidden, embeds, stream=stream)
+    small = torch.empty(join_visual_workspace_bytes(seq), dtype=torch.uint8, device=dev)
+    nb = small.numel()
+    if image_embeds is not None:
+        scatter_visual(embeds, seq, hidden, img_dev, n_img, image_embeds, small, nb, stream)
+    if video_embeds is not None:
+        scatter_visual(embeds, seq, hidden, vid_dev, n_vid, video_embeds, small, nb, stream)
+    # DeepStack rows in token order over every visual token (_aggregate_deepstack)
+    levels, mask, n_vis = None, None, 0
+    if deepstack_image is not None and deepstack_video is not None:
+        levels = []
+        for di, dv in zip(deepstack_image, deepstack_video):
+            joint = torch.empty(n_img + n_vid, hidden, dtype=torch.bfloat16, device=dev)
+            join_visual(img_dev, vid_dev, seq, hidden, di, n_img, dv, n_vid, joint, small, nb,
+                        stream)
+            levels.append(joint)
+        mask, n_vis = vis_dev, n_img + n_vid
+    elif deepstack_image is not None:
+        levels, mask, n_vis = list(deepstack_image), img_dev, n_img
+    elif deepstack_video is not None:
+        levels, mask, n_vis = list(deepstack_video), vid_dev, n_vid
+    encode(cfg, layers, embeds, pos_dev, seq, out, workspace, workspace_bytes,
+           visual_mask=mask, n_vis=n_vis, deepstack=levels, stream=stream)
+    return pos

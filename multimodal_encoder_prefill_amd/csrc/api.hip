@@ -529,4 +529,112 @@ int32_t mhe_attention(const void* q, const void* k, const void* vt, void* o, int
                    "attention");
 }
 
+// ---- token-level front end ----
+
+int32_t mhe_rope_index(const int32_t* ids, int32_t seq, int32_t image_token_id,
+                       int32_t video_token_id, const int32_t* image_grid_thw, int32_t n_images,
+                       const int32_t* video_grid_thw, int32_t n_videos, int32_t spatial_merge,
+                       int32_t* positions, uint8_t* image_mask, uint8_t* video_mask,
+                       uint8_t* visual_mask, int32_t* delta) {
+  int32_t rc;
+  if ((rc = check_seq(seq))) return rc;
+  if (!ids || !positions) return fail(MHE_ERR_NULL, "ids and positions are required");
+  if (n_images < 0 || n_videos < 0) return fail(MHE_ERR_SHAPE, "negative grid count");
+  if ((n_images > 0 && !image_grid_thw) || (n_videos > 0 && !video_grid_thw))
+    return fail(MHE_ERR_NULL, "grid array is NULL");
+  if (spatial_merge <= 0) return fail(MHE_ERR_SHAPE, "spatial_merge %d must be > 0", spatial_merge);
+  if (image_token_id == video_token_id)
+    return fail(MHE_ERR_SHAPE, "image and video token ids must differ");
+  for (int i = 0; i < n_videos; ++i)
+    if (video_grid_thw[3 * i] <= 0 || video_grid_thw[3 * i] > kMaxSeq)
+      return fail(MHE_ERR_SHAPE, "video %d has %d frames", i, video_grid_thw[3 * i]);
+  std::string err;
+  rc = mhe::rope_index_host(ids, seq, image_token_id, video_token_id, image_grid_thw, n_images,
+                            video_grid_thw, n_videos, spatial_merge, positions, image_mask,
+                            video_mask, visual_mask, delta, &err);
+  if (rc != MHE_OK) return fail(rc, "%s", err.c_str());
+  return MHE_OK;
+}
+
+int32_t mhe_embed_tokens(const int32_t* ids, int32_t seq, const void* table, int32_t row_begin,
+                         int32_t rows, int32_t hidden_dim, void* out, int32_t* n_outside,
+                         void* stream) {
+  int32_t rc;
+  if ((rc = check_seq(seq))) return rc;
+  if (!ids || !table || !out) return fail(MHE_ERR_NULL, "ids, table and out are required");
+  if (rows <= 0 || row_begin < 0)
+    return fail(MHE_ERR_SHAPE, "table rows [%d, %d + %d) out of range", row_begin, row_begin, rows);
+  if (hidden_dim <= 0 || hidden_dim % 8 != 0)
+    return fail(MHE_ERR_SHAPE, "hidden_dim %d must be a positive multiple of 8", hidden_dim);
+  return hip_check(mhe::launch_embed_gather(ids, seq, static_cast<const bf16_t*>(table), row_begin,
+                                            rows, hidden_dim, static_cast<bf16_t*>(out), n_outside,
+                                            static_cast<hipStream_t>(stream)),
+                   "embedding gather");
+}
+
+int32_t mhe_scatter_visual(void* hidden, int32_t seq, int32_t hidden_dim, const uint8_t* mask,
+                           int32_t n, const void* feature, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int32_t rc;
+  if ((rc = check_seq(seq))) return rc;
+  if (hidden_dim <= 0 || hidden_dim % 8 != 0)
+    return fail(MHE_ERR_SHAPE, "hidden_dim %d must be a positive multiple of 8", hidden_dim);
+  if (n < 0 || n > seq) return fail(MHE_ERR_SHAPE, "n %d out of range [0, %d]", n, seq);
+  if (n == 0) return MHE_OK;
+  if (!hidden || !mask || !feature) return fail(MHE_ERR_NULL, "hidden, mask and feature are required");
+  if ((rc = check_ws(workspace, workspace_bytes, align_up(static_cast<size_t>(seq) * 4) + 256))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* idx = static_cast<int32_t*>(workspace);
+  int32_t* cnt = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + align_up(static_cast<size_t>(seq) * 4));
+  if ((rc = hip_check(mhe::launch_visual_index(mask, seq, n, idx, cnt, st), "visual index"))) return rc;
+  return hip_check(mhe::launch_row_scatter(static_cast<bf16_t*>(hidden), hidden_dim, idx, n,
+                                           static_cast<const bf16_t*>(feature), st),
+                   "placeholder scatter");
+}
+
+size_t mhe_join_visual_workspace_bytes(int32_t seq) {
+  if (seq <= 0 || seq > kMaxSeq) return 0;
+  return 3 * align_up(static_cast<size_t>(seq) * 4) + 256;
+}
+
+int32_t mhe_join_visual(const uint8_t* image_mask, const uint8_t* video_mask, int32_t seq,
+                        int32_t hidden_dim, const void* image_feature, int32_t n_image,
+                        const void* video_feature, int32_t n_video, void* joint, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int32_t rc;
+  if ((rc = check_seq(seq))) return rc;
+  if (hidden_dim <= 0 || hidden_dim % 8 != 0)
+    return fail(MHE_ERR_SHAPE, "hidden_dim %d must be a positive multiple of 8", hidden_dim);
+  if (n_image < 0 || n_video < 0 || static_cast<int64_t>(n_image) + n_video > seq)
+    return fail(MHE_ERR_SHAPE, "n_image %d + n_video %d out of range [0, %d]", n_image, n_video, seq);
+  if (n_image + n_video == 0) return MHE_OK;
+  if (!image_mask || !video_mask || !joint)
+    return fail(MHE_ERR_NULL, "image_mask, video_mask and joint are required");
+  if ((n_image > 0 && !image_feature) || (n_video > 0 && !video_feature))
+    return fail(MHE_ERR_NULL, "feature array is NULL");
+  if ((rc = check_ws(workspace, workspace_bytes, mhe_join_visual_workspace_bytes(seq)))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const size_t list = align_up(static_cast<size_t>(seq) * 4);
+  int32_t* vis_idx = reinterpret_cast<int32_t*>(ws);
+  int32_t* img_idx = reinterpret_cast<int32_t*>(ws + list);
+  int32_t* vid_idx = reinterpret_cast<int32_t*>(ws + 2 * list);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + 3 * list);
+  const int n_total = n_image + n_video;
+  if ((rc = hip_check(mhe::launch_visual_index(image_mask, seq, n_total, vis_idx, cnt, st, video_mask),
+                      "visual index")))
+    return rc;
+  if ((rc = hip_check(mhe::launch_visual_index(image_mask, seq, n_image, img_idx, cnt + 1, st),
+                      "image index")))
+    return rc;
+  if ((rc = hip_check(mhe::launch_visual_index(video_mask, seq, n_video, vid_idx, cnt + 2, st),
+                      "video index")))
+    return rc;
+  return hip_check(mhe::launch_join_visual(vis_idx, n_total, image_mask, img_idx, n_image,
+                                           static_cast<const bf16_t*>(image_feature), vid_idx,
+                                           n_video, static_cast<const bf16_t*>(video_feature),
+                                           hidden_dim, static_cast<bf16_t*>(joint), st),
+                   "visual join");
+}
+
 }  // extern "C"

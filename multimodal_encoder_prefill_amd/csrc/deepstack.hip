@@ -1,6 +1,7 @@
 // DeepStack injection (H3 encoder page, MiniMaxH3Qwen3VLTextModel._deepstack_process):
 // hidden[t_r] += feature[r] for the r-th visual token t_r in ascending token
-// order, summed in fp32 and rounded to bf16 once.
+// order, summed in fp32 and rounded to bf16 once. The same row kernel without
+// the add is the placeholder scatter of _encode (masked_scatter).
 //
 // visual_index_kernel turns the uint8 mask into the ascending list of visual
 // token indices with one workgroup-wide scan (run once per encode); entries
@@ -19,6 +20,7 @@ namespace {
 constexpr int kScanThreads = 1024;
 
 __global__ __launch_bounds__(kScanThreads) void visual_index_kernel(const uint8_t* __restrict__ mask,
+                                                                   const uint8_t* __restrict__ mask2,
                                                                    int seq, int n_vis,
                                                                    int32_t* __restrict__ idx,
                                                                    int32_t* __restrict__ count) {
@@ -27,7 +29,9 @@ __global__ __launch_bounds__(kScanThreads) void visual_index_kernel(const uint8_
   const int per = (seq + kScanThreads - 1) / kScanThreads;
   const int beg = min(tid * per, seq), end = min(beg + per, seq);
   int local = 0;
-  for (int s = beg; s < end; ++s) local += mask[s] != 0;
+  // a token counts when its byte in mask (or, if given, in mask2) is set
+  auto set = [&](int s) { return mask[s] != 0 || (mask2 && mask2[s] != 0); };
+  for (int s = beg; s < end; ++s) local += set(s);
   // inclusive scan over the workgroup: within wavefronts, then across them
   const int lane = tid & 63, wave = tid >> 6;
   int incl = local;
@@ -42,7 +46,7 @@ __global__ __launch_bounds__(kScanThreads) void visual_index_kernel(const uint8_
   for (int w = 0; w < wave; ++w) before += warp_tot[w];
   int rank = before + incl - local;  // exclusive prefix
   for (int s = beg; s < end; ++s) {
-    if (mask[s] != 0) {
+    if (set(s)) {
       if (rank < n_vis) idx[rank] = s;
       ++rank;
     }
@@ -53,6 +57,9 @@ __global__ __launch_bounds__(kScanThreads) void visual_index_kernel(const uint8_
   if (tid == 0) *count = total;
 }
 
+// ADD: hidden[t_r] += feature[r] (fp32 sum, one bf16 rounding); otherwise
+// hidden[t_r] = feature[r] (a plain copy, the placeholder scatter).
+template <bool ADD>
 __global__ __launch_bounds__(256) void deepstack_add_kernel(bf16_t* __restrict__ hidden, int dim,
                                                             const int32_t* __restrict__ idx,
                                                             int n_vis,
@@ -65,6 +72,10 @@ __global__ __launch_bounds__(256) void deepstack_add_kernel(bf16_t* __restrict__
   u32x4* h = reinterpret_cast<u32x4*>(hidden + static_cast<size_t>(t) * dim);
   const u32x4* f = reinterpret_cast<const u32x4*>(feature + static_cast<size_t>(r) * dim);
   for (int c = lane; c < dim / 8; c += 64) {
+    if (!ADD) {
+      h[c] = f[c];
+      continue;
+    }
     float a[8], b[8];
     unpack8(h[c], a);
     unpack8(f[c], b);
@@ -77,17 +88,25 @@ __global__ __launch_bounds__(256) void deepstack_add_kernel(bf16_t* __restrict__
 }  // namespace
 
 hipError_t launch_visual_index(const uint8_t* mask, int seq, int n_vis, int32_t* idx,
-                               int32_t* count, hipStream_t stream) {
-  hipLaunchKernelGGL(visual_index_kernel, dim3(1), dim3(kScanThreads), 0, stream, mask, seq,
-                     n_vis, idx, count);
+                               int32_t* count, hipStream_t stream, const uint8_t* mask2) {
+  hipLaunchKernelGGL(visual_index_kernel, dim3(1), dim3(kScanThreads), 0, stream, mask, mask2,
+                     seq, n_vis, idx, count);
   return hipGetLastError();
 }
 
 hipError_t launch_deepstack_add(bf16_t* hidden, int hidden_dim, const int32_t* idx, int n_vis,
                                 const bf16_t* feature, hipStream_t stream) {
   if (n_vis <= 0) return hipSuccess;
-  hipLaunchKernelGGL(deepstack_add_kernel, dim3((n_vis + 3) / 4), dim3(256), 0, stream, hidden,
-                     hidden_dim, idx, n_vis, feature);
+  hipLaunchKernelGGL(deepstack_add_kernel<true>, dim3((n_vis + 3) / 4), dim3(256), 0, stream,
+                     hidden, hidden_dim, idx, n_vis, feature);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_scatter(bf16_t* hidden, int hidden_dim, const int32_t* idx, int n,
+                              const bf16_t* feature, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(deepstack_add_kernel<false>, dim3((n + 3) / 4), dim3(256), 0, stream, hidden,
+                     hidden_dim, idx, n, feature);
   return hipGetLastError();
 }
 

@@ -210,3 +210,41 @@ def random_positions(seq: int, max_pos: int, seed: int) -> np.ndarray:
     """int32 [3, S] with independent axes (exercises every rotary slot rule)."""
     rng = np.random.default_rng([_BASE_SEED, seed])
     return rng.integers(0, max_pos, size=(3, seq)).astype(np.int32)
+
+
+# ---- token-level inputs (ids, embedding table, vision-tower outputs) ----
+
+_TABLE_ID = 300
+_FEATURE_ID = 400
+
+
+def prompt_ids(runs, image_token_id: int, video_token_id: int, text_vocab: int,
+               seed: int) -> np.ndarray:
+    """int32 token ids for runs ("text" | "image" | "video", token count), in order.
+
+    Text ids are drawn uniformly from [0, text_vocab) (callers keep the
+    placeholder ids outside that range); image / video runs are the
+    placeholder ids."""
+    rng = np.random.default_rng([_BASE_SEED, _TABLE_ID, seed])
+    parts = []
+    for kind, n in runs:
+        if kind == "text":
+            parts.append(rng.integers(0, text_vocab, size=int(n)))
+        else:
+            tok = image_token_id if kind == "image" else video_token_id
+            parts.append(np.full(int(n), tok))
+    return np.concatenate(parts).astype(np.int32)
+
+
+def token_table(vocab: int, hidden: int, seed: int, device="cpu") -> torch.Tensor:
+    """Embedding table [vocab, hidden] bf16 ~ N(0, 1)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(_BASE_SEED * 1000 + _TABLE_ID + seed)
+    return torch.randn(vocab, hidden, generator=g, device=device).to(torch.bfloat16)
+
+
+def feature_rows(n: int, hidden: int, seed: int, device="cpu") -> torch.Tensor:
+    """Vision-tower output rows [n, hidden] bf16 ~ N(0, 1)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(_BASE_SEED * 1000 + _FEATURE_ID + seed)
+    return torch.randn(n, hidden, generator=g, device=device).to(torch.bfloat16)
