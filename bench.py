@@ -18,6 +18,9 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                taken from HIP event pairs the library records around every
                launch of that kernel on its stream during the timed steps
   breakdown    mean milliseconds per encode of each step (a separate traced pass)
+  frontend     token-level front end of the same prompt, outside the encode:
+               host position ids (ms) and the embedding gather, placeholder
+               scatter and joint DeepStack kernels (us, GB/s)
   cpu_baseline the CPU oracle (float64 NumPy) timed on one decoder layer of
                the same workload, scaled to the whole encode
 """
@@ -108,6 +111,73 @@ def cpu_baseline(wl, layer0, emb, pos_np, mask_np, ds0):
             "seconds_measured": round(dt, 3), "finite": bool(np.isfinite(out).all())}
 
 
+def frontend_measure(wl, dev):
+    """Token-level front end of the same workload, timed outside the encode:
+    host position ids from token ids, and the embedding gather (151936-row
+    table), placeholder scatter and joint DeepStack kernels with HIP events
+    over 20 launches each; HBM rates are algorithmic bytes (rows read + rows
+    written) over the mean launch time."""
+    import numpy as np
+    import torch
+    from multimodal_encoder_prefill_amd import binding as b
+    from multimodal_encoder_prefill_amd import synth
+    d = wl.dims
+    S, H, vocab = wl.seq, d.hidden, 151936
+    runs, grids = [], []
+    for kind, spec in wl.segments:
+        if kind == "text":
+            runs.append(("text", int(spec)))
+        else:
+            t, h, w = (int(x) for x in spec)
+            runs.append(("image", t * h * w))
+            grids.append((t, 2 * h, 2 * w))
+    ids = synth.prompt_ids(runs, b.IMAGE_TOKEN_ID, b.VIDEO_TOKEN_ID, 151000, seed=0)
+    t0 = time.perf_counter()
+    for _ in range(5):
+        _, im, _, vis, _ = b.rope_index(ids, image_grid_thw=grids or None)
+    host_ms = (time.perf_counter() - t0) * 1000 / 5
+    table = synth.token_table(vocab, H, seed=0, device=dev)
+    ids_d = torch.from_numpy(ids).to(dev)
+    out = torch.empty(S, H, dtype=torch.bfloat16, device=dev)
+    n = int(im.sum())
+    feat = synth.feature_rows(max(n, 1), H, seed=0, device=dev)
+    # the visual block split in two halves, as if its second half were video
+    half = np.zeros(S, np.uint8)
+    half[np.flatnonzero(im)[n // 2:]] = 1
+    img_m = torch.from_numpy((im & (1 - half)).astype(np.uint8)).to(dev)
+    vid_m = torch.from_numpy(half).to(dev)
+    joint = torch.empty(max(n, 1), H, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(b.join_visual_workspace_bytes(S), dtype=torch.uint8, device=dev)
+    im_d = torch.from_numpy(im).to(dev)
+
+    def timed(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {"rope_index_host_ms": round(host_ms, 3)}
+    cases = [("embed_tokens", lambda: b.embed_tokens(ids_d, S, table, 0, vocab, H, out), 2 * S * H * 2)]
+    if n:
+        cases += [("scatter_visual", lambda: b.scatter_visual(out, S, H, im_d, n, feat, ws, ws.numel()),
+                   2 * n * H * 2),
+                  ("join_visual", lambda: b.join_visual(img_m, vid_m, S, H, feat, n - n // 2,
+                                                        feat, n // 2, joint, ws, ws.numel()),
+                   2 * n * H * 2)]
+    for name, fn, nbytes in cases:
+        ms = timed(fn)
+        gbs = nbytes / (ms / 1000.0) / 1e9
+        res[name] = {"us": round(ms * 1000, 2), "bytes": nbytes, "gb_s": round(gbs, 1),
+                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)}
+    del table
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +186,7 @@ def main():
     ap.add_argument("--workload", default="image_s4096_l50")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
+    ap.add_argument("--no-frontend", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -204,6 +275,11 @@ def main():
         b.trace_enable([])
         log("breakdown ms/encode: " + json.dumps(breakdown))
 
+    frontend = None
+    if not args.no_frontend:
+        frontend = frontend_measure(wl, dev)
+        log("front end: " + json.dumps(frontend))
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one decoder layer ...")
@@ -223,6 +299,7 @@ def main():
         "tflops_per_step": round(flops_step / 1e12, 3),
         "roofline": roofline,
         "breakdown_ms_per_step": breakdown,
+        "frontend": frontend,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
