@@ -16,6 +16,10 @@ page and the class/function on it whose computation it follows:
 * "vLLM Qwen3-VL page" = ``vllm/model_executor/models/qwen3_vl.py``;
 * "SGLang Qwen3-VL page" = ``python/sglang/srt/models/qwen3_vl.py``.
 
+``oracle.vision`` holds the page's Qwen3-VL vision tower (patch embedding,
+interpolated position embeddings, 2-D rotary, non-causal per-frame attention
+blocks, the merger and the DeepStack mergers).
+
 ``oracle.frontend`` holds the token-level front end of the same page
 (token types, embedding gather with visual placeholder scatter, the joint
 DeepStack order and the multimodal rotary position ids).
@@ -45,3 +49,4 @@ from .qwen3vl_text import (  # noqa: F401
 )
 from .positions import text_and_grid_positions  # noqa: F401
 from . import frontend  # noqa: F401
+from . import vision  # noqa: F401
