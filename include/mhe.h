@@ -342,6 +342,111 @@ int32_t mhe_join_visual(const uint8_t* image_mask, const uint8_t* video_mask, in
                         const void* video_feature, int32_t n_video, void* joint, void* workspace,
                         size_t workspace_bytes, void* stream);
 
+/* ---- Qwen3-VL vision tower (produces the visual rows and DeepStack levels) -- */
+
+/*
+ * Vision tower sizes (H3 encoder page, MiniMaxH3Qwen3VLVisionModel; the values
+ * come from the checkpoint's vision config, which the page does not print).
+ * Qwen3-VL: hidden 1152, 16 heads (head_dim 72), MLP width 4304 stored padded
+ * with zero rows / columns to a multiple of 64 (4352: a zero fc1 row with a
+ * zero bias gives gelu(0) = 0, which a zero fc2 column ignores), depth 27,
+ * patch_dim = in_channels 3 * temporal patch 2 * 16 * 16 = 1536, spatial
+ * merge 2, out_hidden 5120 (the text hidden size), pos_side 48 (2304 learned
+ * position embeddings), DeepStack after blocks 8, 16 and 24.
+ * Supported: hidden, intermediate and merge^2 * hidden multiples of 64;
+ * out_hidden a multiple of 32; head_dim = hidden / n_heads a multiple of 4
+ * and <= 128; patch_dim a multiple of 64; merge^2 * hidden <= 8192;
+ * n_deepstack <= 8.
+ */
+typedef struct mhe_vision_config {
+  int32_t hidden;
+  int32_t n_heads;
+  int32_t intermediate;
+  int32_t depth;
+  int32_t patch_dim;
+  int32_t merge;
+  int32_t out_hidden;
+  int32_t pos_side;
+  int32_t n_deepstack;
+  int32_t deepstack_index[8];
+} mhe_vision_config;
+
+/* One vision block (MiniMaxH3Qwen3VLVisionBlock), bf16 device pointers:
+ * norm1/norm2 LayerNorm weight and bias [hidden]; qkv_w [3 hidden, hidden],
+ * qkv_b [3 hidden] (q | k | v, head-major inside each); proj_w [hidden, hidden],
+ * proj_b; fc1_w [intermediate, hidden], fc1_b; fc2_w [hidden, intermediate], fc2_b. */
+typedef struct mhe_vision_block_weights {
+  const void *norm1_w, *norm1_b, *qkv_w, *qkv_b, *proj_w, *proj_b;
+  const void *norm2_w, *norm2_b, *fc1_w, *fc1_b, *fc2_w, *fc2_b;
+} mhe_vision_block_weights;
+
+/* A patch merger (MiniMaxH3Qwen3VLVisionPatchMerger): norm over hidden (main
+ * merger) or over merge^2 * hidden (DeepStack mergers); fc1 [M, M] with
+ * M = merge^2 * hidden; fc2 [out_hidden, M]; biases likewise. */
+typedef struct mhe_vision_merger_weights {
+  const void *norm_w, *norm_b, *fc1_w, *fc1_b, *fc2_w, *fc2_b;
+} mhe_vision_merger_weights;
+
+/* patch_w [hidden, patch_dim]: the Conv3d kernel [hidden, C, T, P, P]
+ * flattened; patch_b [hidden]; pos_table [pos_side^2, hidden]; blocks: host
+ * array [depth]; deepstack: host array [n_deepstack]. */
+typedef struct mhe_vision_weights {
+  const void* patch_w;
+  const void* patch_b;
+  const void* pos_table;
+  const mhe_vision_block_weights* blocks;
+  mhe_vision_merger_weights merger;
+  const mhe_vision_merger_weights* deepstack;
+} mhe_vision_weights;
+
+/* Workspace bytes of the vision entry points for n_patches patches (0 on a
+ * bad config or size). */
+size_t mhe_vision_workspace_bytes(const mhe_vision_config* cfg, int32_t n_patches);
+
+/*
+ * The whole tower (H3 encoder page, MiniMaxH3Qwen3VLVisionModel.forward):
+ * pixels [n_patches, patch_dim] bf16 (the processor's flattened patches, in
+ * its order: images in turn, frames, then merge x merge blocks), grid_thw
+ * HOST int32 [n_grids, 3] (t, h, w in patches; h, w multiples of merge;
+ * n_grids <= 64), n_patches = sum t*h*w. Writes merged [n_patches / merge^2,
+ * out_hidden] (the image / video embeddings mhe_scatter_visual places) and,
+ * for each DeepStack level l, deepstack[l] (host array of device pointers)
+ * [n_patches / merge^2, out_hidden]. Each kernel accumulates in fp32 and
+ * rounds its output to bf16 once.
+ */
+int32_t mhe_vision_forward(const mhe_vision_config* cfg, const mhe_vision_weights* w,
+                           const void* pixels, const int32_t* grid_thw, int32_t n_grids,
+                           void* merged, void* const* deepstack, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Steps of the tower, for per-step checks. hidden [n_patches, hidden] bf16.
+ * mhe_vision_embed: hidden = patch embedding + interpolated position table.
+ * mhe_vision_blocks: blocks [first, first + count) of w->blocks in place.
+ * mhe_vision_merge: one merger on hidden -> out [n_patches / merge^2,
+ * out_hidden]; postshuffle 0 for the main merger, 1 for a DeepStack merger. */
+int32_t mhe_vision_embed(const mhe_vision_config* cfg, const mhe_vision_weights* w,
+                         const void* pixels, const int32_t* grid_thw, int32_t n_grids,
+                         void* hidden, void* workspace, size_t workspace_bytes, void* stream);
+int32_t mhe_vision_blocks(const mhe_vision_config* cfg, const mhe_vision_weights* w,
+                          int32_t first, int32_t count, void* hidden, const int32_t* grid_thw,
+                          int32_t n_grids, void* workspace, size_t workspace_bytes, void* stream);
+int32_t mhe_vision_merge(const mhe_vision_config* cfg, const mhe_vision_merger_weights* m,
+                         int32_t postshuffle, const void* hidden, int32_t n_patches, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* y = LayerNorm(x) * w + b over rows of dim (biased variance, fp32), one
+ * bf16 rounding (nn.LayerNorm of the vision blocks). dim % 8 == 0, <= 8192;
+ * x and y may alias. */
+int32_t mhe_layer_norm(const void* x, const void* w, const void* b, void* y, int32_t rows,
+                       int32_t dim, float eps, void* stream);
+
+/* c = act(a w^T + bias) (+ residual when act == 0), fp32 accumulation, one
+ * bf16 rounding: the biased linears of the vision tower. act: 0 none, 1 GELU
+ * tanh form, 2 GELU erf form. Shapes and workspace as mhe_linear. */
+int32_t mhe_linear_bias(const void* a, const void* w, const void* bias, void* c,
+                        const void* residual, int32_t m, int32_t n, int32_t k, int32_t act,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -47,6 +47,34 @@ class MheLayerWeights(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in WEIGHT_FIELDS]
 
 
+class MheVisionConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("intermediate", ctypes.c_int32), ("depth", ctypes.c_int32),
+                ("patch_dim", ctypes.c_int32), ("merge", ctypes.c_int32),
+                ("out_hidden", ctypes.c_int32), ("pos_side", ctypes.c_int32),
+                ("n_deepstack", ctypes.c_int32), ("deepstack_index", ctypes.c_int32 * 8)]
+
+
+VISION_BLOCK_FIELDS = ("norm1_w", "norm1_b", "qkv_w", "qkv_b", "proj_w", "proj_b", "norm2_w",
+                       "norm2_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")
+VISION_MERGER_FIELDS = ("norm_w", "norm_b", "fc1_w", "fc1_b", "fc2_w", "fc2_b")
+
+
+class MheVisionBlockWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in VISION_BLOCK_FIELDS]
+
+
+class MheVisionMergerWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in VISION_MERGER_FIELDS]
+
+
+class MheVisionWeights(ctypes.Structure):
+    _fields_ = [("patch_w", ctypes.c_void_p), ("patch_b", ctypes.c_void_p),
+                ("pos_table", ctypes.c_void_p), ("blocks", ctypes.POINTER(MheVisionBlockWeights)),
+                ("merger", MheVisionMergerWeights),
+                ("deepstack", ctypes.POINTER(MheVisionMergerWeights))]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -76,6 +104,18 @@ _SIGNATURES = {
     "mhe_scatter_visual": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
     "mhe_join_visual_workspace_bytes": (_sz, [_i32]),
     "mhe_join_visual": (_i32, [_vp, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "mhe_vision_workspace_bytes": (_sz, [ctypes.POINTER(MheVisionConfig), _i32]),
+    "mhe_vision_forward": (_i32, [ctypes.POINTER(MheVisionConfig), ctypes.POINTER(MheVisionWeights),
+                                  _vp, _vp, _i32, _vp, ctypes.POINTER(_vp), _vp, _sz, _vp]),
+    "mhe_vision_embed": (_i32, [ctypes.POINTER(MheVisionConfig), ctypes.POINTER(MheVisionWeights),
+                                _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "mhe_vision_blocks": (_i32, [ctypes.POINTER(MheVisionConfig), ctypes.POINTER(MheVisionWeights),
+                                 _i32, _i32, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "mhe_vision_merge": (_i32, [ctypes.POINTER(MheVisionConfig),
+                                ctypes.POINTER(MheVisionMergerWeights), _i32, _vp, _i32, _vp, _vp,
+                                _sz, _vp]),
+    "mhe_layer_norm": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _f32, _vp]),
+    "mhe_linear_bias": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
 }
 
 # placeholder token ids of Qwen3-VL (H3 encoder page, MiniMaxH3Qwen3VLEncoder defaults)
@@ -373,3 +413,104 @@ def encode_ids(cfg, layers: Sequence, ids, embed_table, out, workspace, workspac
     encode(cfg, layers, embeds, pos_dev, seq, out, workspace, workspace_bytes,
            visual_mask=mask, n_vis=n_vis, deepstack=levels, stream=stream)
     return pos
+
+
+# ---- vision tower ----
+
+def vision_config(vd) -> MheVisionConfig:
+    """From an object with hidden, n_heads, intermediate (stored width), depth,
+    patch_dim, merge, out_hidden, pos_side, deepstack (synth.VisionDims)."""
+    c = MheVisionConfig()
+    c.hidden, c.n_heads, c.intermediate, c.depth = vd.hidden, vd.n_heads, vd.intermediate, vd.depth
+    c.patch_dim, c.merge, c.out_hidden, c.pos_side = vd.patch_dim, vd.merge, vd.out_hidden, vd.pos_side
+    c.n_deepstack = len(vd.deepstack)
+    for i, d in enumerate(vd.deepstack):
+        c.deepstack_index[i] = d
+    return c
+
+
+def _merger_table(m) -> MheVisionMergerWeights:
+    t = MheVisionMergerWeights()
+    for f in VISION_MERGER_FIELDS:
+        setattr(t, f, _ptr(m[f]))
+    return t
+
+
+class VisionTables:
+    """Host tables of a tower's device weights (dict as synth.vision_weights returns);
+    keeps the ctypes arrays alive for the calls that use them."""
+
+    def __init__(self, w):
+        self.blocks = (MheVisionBlockWeights * max(len(w["blocks"]), 1))()
+        for i, b in enumerate(w["blocks"]):
+            for f in VISION_BLOCK_FIELDS:
+                setattr(self.blocks[i], f, _ptr(b[f]))
+        self.ds = (MheVisionMergerWeights * max(len(w["deepstack"]), 1))()
+        for i, m in enumerate(w["deepstack"]):
+            self.ds[i] = _merger_table(m)
+        self.merger = _merger_table(w["merger"])
+        self.table = MheVisionWeights()
+        self.table.patch_w, self.table.patch_b = _ptr(w["patch_w"]), _ptr(w["patch_b"])
+        self.table.pos_table = _ptr(w["pos_table"])
+        self.table.blocks = ctypes.cast(self.blocks, ctypes.POINTER(MheVisionBlockWeights))
+        self.table.merger = self.merger
+        self.table.deepstack = ctypes.cast(self.ds, ctypes.POINTER(MheVisionMergerWeights))
+
+
+def _grids(grid_thw):
+    import numpy as np
+    g = np.ascontiguousarray(np.asarray(grid_thw, dtype=np.int32).reshape(-1, 3))
+    return g, len(g)
+
+
+def vision_workspace_bytes(cfg: MheVisionConfig, n_patches: int) -> int:
+    n = lib().mhe_vision_workspace_bytes(ctypes.byref(cfg), n_patches)
+    if n == 0:
+        raise MheError("mhe_vision_workspace_bytes", 2, lib().mhe_last_error().decode())
+    return n
+
+
+def vision_forward(cfg, tables: VisionTables, pixels, grid_thw, merged, deepstack, workspace,
+                   workspace_bytes, stream=None):
+    g, ng = _grids(grid_thw)
+    ds = (ctypes.c_void_p * max(len(deepstack), 1))(*[_ptr(d) for d in deepstack])
+    _check("mhe_vision_forward", lib().mhe_vision_forward(
+        ctypes.byref(cfg), ctypes.byref(tables.table), _ptr(pixels), g.ctypes.data, ng,
+        _ptr(merged), ds, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def vision_embed(cfg, tables: VisionTables, pixels, grid_thw, hidden, workspace, workspace_bytes,
+                 stream=None):
+    g, ng = _grids(grid_thw)
+    _check("mhe_vision_embed", lib().mhe_vision_embed(
+        ctypes.byref(cfg), ctypes.byref(tables.table), _ptr(pixels), g.ctypes.data, ng,
+        _ptr(hidden), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def vision_blocks(cfg, tables: VisionTables, first, count, hidden, grid_thw, workspace,
+                  workspace_bytes, stream=None):
+    g, ng = _grids(grid_thw)
+    _check("mhe_vision_blocks", lib().mhe_vision_blocks(
+        ctypes.byref(cfg), ctypes.byref(tables.table), first, count, _ptr(hidden), g.ctypes.data,
+        ng, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def vision_merge(cfg, merger, postshuffle, hidden, n_patches, out, workspace, workspace_bytes,
+                 stream=None):
+    t = merger if isinstance(merger, MheVisionMergerWeights) else _merger_table(merger)
+    _check("mhe_vision_merge", lib().mhe_vision_merge(
+        ctypes.byref(cfg), ctypes.byref(t), int(bool(postshuffle)), _ptr(hidden), n_patches,
+        _ptr(out), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def layer_norm(x, w, b, y, rows, dim, eps=1e-6, stream=None):
+    _check("mhe_layer_norm", lib().mhe_layer_norm(_ptr(x), _ptr(w), _ptr(b), _ptr(y), rows, dim,
+                                                  eps, _stream(stream)))
+
+
+def linear_bias(a, w, bias, c, m, n, k, act=0, residual=None, workspace=None, stream=None):
+    """act: 0 none, 1 GELU (tanh form), 2 GELU (erf form)."""
+    wp, wb = _ws(workspace)
+    _check("mhe_linear_bias", lib().mhe_linear_bias(_ptr(a), _ptr(w), _ptr(bias), _ptr(c),
+                                                    _ptr(residual), m, n, k, act, wp, wb,
+                                                    _stream(stream)))

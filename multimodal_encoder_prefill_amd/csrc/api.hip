@@ -3,6 +3,7 @@
 // prefill. Every check runs on the host before the first launch of a call.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -635,6 +636,348 @@ int32_t mhe_join_visual(const uint8_t* image_mask, const uint8_t* video_mask, in
                                            n_video, static_cast<const bf16_t*>(video_feature),
                                            hidden_dim, static_cast<bf16_t*>(joint), st),
                    "visual join");
+}
+
+}  // extern "C"
+
+// ---- vision tower ----
+
+namespace {
+
+int32_t check_vision_config(const mhe_vision_config* c) {
+  if (!c) return fail(MHE_ERR_NULL, "vision config is NULL");
+  if (c->hidden <= 0 || c->n_heads <= 0 || c->intermediate <= 0 || c->depth < 0 ||
+      c->patch_dim <= 0 || c->merge <= 0 || c->out_hidden <= 0 || c->pos_side <= 0)
+    return fail(MHE_ERR_SHAPE, "vision config sizes must be positive");
+  if (c->hidden % c->n_heads != 0) return fail(MHE_ERR_SHAPE, "hidden %% n_heads != 0");
+  const int dh = c->hidden / c->n_heads;
+  if (dh % 4 != 0 || dh > 128)
+    return fail(MHE_ERR_UNSUPPORTED, "vision head_dim %d must be a multiple of 4 and <= 128", dh);
+  const int mh = c->merge * c->merge * c->hidden;
+  if (c->hidden % 64 || c->intermediate % 64 || c->patch_dim % 64 || mh % 64 || c->out_hidden % 32)
+    return fail(MHE_ERR_UNSUPPORTED,
+                "vision GEMMs need hidden, intermediate, patch_dim, merge^2*hidden multiples of 64 "
+                "and out_hidden a multiple of 32");
+  if (!mhe::rmsnorm_supported(mh) || !mhe::rmsnorm_supported(c->hidden))
+    return fail(MHE_ERR_UNSUPPORTED, "merge^2 * hidden %d must be <= 8192", mh);
+  if (c->n_deepstack < 0 || c->n_deepstack > 8)
+    return fail(MHE_ERR_SHAPE, "n_deepstack %d out of range [0, 8]", c->n_deepstack);
+  for (int i = 0; i < c->n_deepstack; ++i)
+    if (c->deepstack_index[i] < 0 || c->deepstack_index[i] >= c->depth)
+      return fail(MHE_ERR_SHAPE, "deepstack_index[%d] = %d not a block", i, c->deepstack_index[i]);
+  return MHE_OK;
+}
+
+// Grid list -> kernel argument; checks the grids and that they hold n patches.
+int32_t make_grids(const mhe_vision_config& c, const int32_t* thw, int n_grids, int n,
+                   mhe::VisionGrids* g) {
+  if (!thw) return fail(MHE_ERR_NULL, "grid_thw is NULL");
+  if (n_grids <= 0 || n_grids > mhe::kMaxVisionGrids)
+    return fail(MHE_ERR_SHAPE, "n_grids %d out of range [1, %d]", n_grids, mhe::kMaxVisionGrids);
+  int64_t total = 0;
+  g->count = n_grids;
+  g->merge = c.merge;
+  for (int i = 0; i < n_grids; ++i) {
+    const int t = thw[3 * i], h = thw[3 * i + 1], w = thw[3 * i + 2];
+    if (t <= 0 || h <= 0 || w <= 0 || h % c.merge || w % c.merge)
+      return fail(MHE_ERR_SHAPE, "grid %d (%d, %d, %d): positive, h and w multiples of %d", i, t,
+                  h, w, c.merge);
+    g->t[i] = t;
+    g->h[i] = h;
+    g->w[i] = w;
+    total += static_cast<int64_t>(t) * h * w;
+  }
+  if (total != n)
+    return fail(MHE_ERR_MISMATCH, "grids hold %lld patches, %d given", static_cast<long long>(total), n);
+  return MHE_OK;
+}
+
+struct VisionWs {
+  int ld_u, ld_o, ld_i, ld_m;
+  mhe::PatchInfo* info;
+  bf16_t* x;    // [n, H] hidden state of mhe_vision_forward
+  bf16_t* u;    // [n, ld_u] norm output (dense [n, H] / [n/m^2, M] for the mergers)
+  bf16_t* qkv;  // [n, 3H]
+  bf16_t* q;    // [n, heads, 128]
+  bf16_t* k;    // [heads, n_pad, 128]
+  bf16_t* vt;   // [heads, 128, n_pad]
+  bf16_t* ao;   // [n, ld_o]
+  bf16_t* act;  // [n, ld_i], aliases qkv..ao
+  bf16_t* m1;   // [n/m^2, ld_m], aliases qkv..ao
+  float* partial;
+  size_t partial_bytes;
+  size_t total;
+};
+
+VisionWs vision_carve(const mhe_vision_config& c, int n, char* base) {
+  const size_t N = n, np = mhe::seq_pad(n), H = c.hidden, heads = c.n_heads;
+  const size_t mh = static_cast<size_t>(c.merge) * c.merge * H, nm = N / (c.merge * c.merge);
+  VisionWs w{};
+  w.ld_u = c.hidden + kActPad;
+  w.ld_o = c.hidden + kActPad;
+  w.ld_i = c.intermediate + kActPad;
+  w.ld_m = static_cast<int>(mh) + kActPad;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  w.info = reinterpret_cast<mhe::PatchInfo*>(take(N * sizeof(mhe::PatchInfo)));
+  w.x = reinterpret_cast<bf16_t*>(take(N * H * 2));
+  w.u = reinterpret_cast<bf16_t*>(take(N * w.ld_u * 2));
+  const size_t region = off;
+  w.qkv = reinterpret_cast<bf16_t*>(take(N * 3 * H * 2));
+  w.q = reinterpret_cast<bf16_t*>(take(N * heads * 128 * 2));
+  w.k = reinterpret_cast<bf16_t*>(take(heads * np * 128 * 2));
+  w.vt = reinterpret_cast<bf16_t*>(take(heads * 128 * np * 2));
+  w.ao = reinterpret_cast<bf16_t*>(take(N * w.ld_o * 2));
+  const size_t attn_end = off;
+  const size_t need_act = align_up(N * w.ld_i * 2), need_m1 = align_up(nm * w.ld_m * 2);
+  w.act = reinterpret_cast<bf16_t*>(base ? base + region : nullptr);
+  w.m1 = reinterpret_cast<bf16_t*>(base ? base + region : nullptr);
+  off = std::max(attn_end, region + std::max(need_act, need_m1));
+  w.partial_bytes = mhe::gemm_partial_bytes();
+  w.partial = reinterpret_cast<float*>(take(w.partial_bytes));
+  w.total = off;
+  (void)mh;
+  return w;
+}
+
+int32_t vision_gemm(mhe::Epilogue epi, const bf16_t* a, int lda, const void* wt, const void* bias,
+                    bf16_t* c, int ldc, const bf16_t* r, int m, int n, int k, const VisionWs& ws,
+                    hipStream_t st, const char* what) {
+  if (!wt || !bias) return fail(MHE_ERR_NULL, "%s: weight or bias is NULL", what);
+  mhe::BSegments b{{static_cast<const bf16_t*>(wt), nullptr, nullptr}, {n, 0, 0}, 1};
+  return hip_check(mhe::launch_gemm(epi, a, lda, b, k, c, ldc, r, m, n, k, ws.partial,
+                                    ws.partial_bytes, st, static_cast<const bf16_t*>(bias)),
+                   what);
+}
+
+int32_t run_vision_block(const mhe_vision_config& c, const mhe_vision_block_weights& p, bf16_t* h,
+                         int n, const VisionWs& ws, hipStream_t st) {
+  const int H = c.hidden, dh = H / c.n_heads;
+  int32_t rc;
+  if (!p.norm1_w || !p.norm1_b || !p.norm2_w || !p.norm2_b)
+    return fail(MHE_ERR_NULL, "vision block norm weights are NULL");
+  if ((rc = hip_check(mhe::launch_layernorm(h, H, static_cast<const bf16_t*>(p.norm1_w),
+                                            static_cast<const bf16_t*>(p.norm1_b), ws.u, ws.ld_u, n,
+                                            H, 1e-6f, st), "layer norm 1")))
+    return rc;
+  if ((rc = vision_gemm(mhe::Epilogue::kBias, ws.u, ws.ld_u, p.qkv_w, p.qkv_b, ws.qkv, 3 * H,
+                        nullptr, n, 3 * H, H, ws, st, "qkv")))
+    return rc;
+  if ((rc = hip_check(mhe::launch_vision_rope(ws.qkv, 3 * H, n, c.n_heads, dh, ws.info, ws.q, ws.k,
+                                              ws.vt, st), "vision rotary")))
+    return rc;
+  if ((rc = hip_check(mhe::launch_segment_attention(ws.q, ws.k, ws.vt, ws.ao, ws.ld_o, n, c.n_heads,
+                                                    dh, ws.info, st), "vision attention")))
+    return rc;
+  if ((rc = vision_gemm(mhe::Epilogue::kBiasResidual, ws.ao, ws.ld_o, p.proj_w, p.proj_b, h, H, h,
+                        n, H, H, ws, st, "proj")))
+    return rc;
+  if ((rc = hip_check(mhe::launch_layernorm(h, H, static_cast<const bf16_t*>(p.norm2_w),
+                                            static_cast<const bf16_t*>(p.norm2_b), ws.u, ws.ld_u, n,
+                                            H, 1e-6f, st), "layer norm 2")))
+    return rc;
+  if ((rc = vision_gemm(mhe::Epilogue::kBiasGeluTanh, ws.u, ws.ld_u, p.fc1_w, p.fc1_b, ws.act,
+                        ws.ld_i, nullptr, n, c.intermediate, H, ws, st, "fc1")))
+    return rc;
+  return vision_gemm(mhe::Epilogue::kBiasResidual, ws.act, ws.ld_i, p.fc2_w, p.fc2_b, h, H, h, n, H,
+                     c.intermediate, ws, st, "fc2");
+}
+
+int32_t run_vision_merge(const mhe_vision_config& c, const mhe_vision_merger_weights& p, bool post,
+                         const bf16_t* h, int n, bf16_t* out, const VisionWs& ws, hipStream_t st) {
+  const int H = c.hidden, mh = c.merge * c.merge * H, nm = n / (c.merge * c.merge);
+  int32_t rc;
+  if (!p.norm_w || !p.norm_b) return fail(MHE_ERR_NULL, "merger norm weights are NULL");
+  // main merger: normalise tokens, then view merge^2 consecutive rows as one;
+  // DeepStack merger: view first, normalise the merged rows
+  hipError_t e = post ? mhe::launch_layernorm(h, mh, static_cast<const bf16_t*>(p.norm_w),
+                                              static_cast<const bf16_t*>(p.norm_b), ws.u, mh, nm,
+                                              mh, 1e-6f, st)
+                      : mhe::launch_layernorm(h, H, static_cast<const bf16_t*>(p.norm_w),
+                                              static_cast<const bf16_t*>(p.norm_b), ws.u, H, n, H,
+                                              1e-6f, st);
+  if ((rc = hip_check(e, "merger norm"))) return rc;
+  if ((rc = vision_gemm(mhe::Epilogue::kBiasGeluErf, ws.u, mh, p.fc1_w, p.fc1_b, ws.m1, ws.ld_m,
+                        nullptr, nm, mh, mh, ws, st, "merger fc1")))
+    return rc;
+  return vision_gemm(mhe::Epilogue::kBias, ws.m1, ws.ld_m, p.fc2_w, p.fc2_b, out, c.out_hidden,
+                     nullptr, nm, c.out_hidden, mh, ws, st, "merger fc2");
+}
+
+int32_t vision_prelude(const mhe_vision_config* cfg, int n, const int32_t* thw, int n_grids,
+                       void* workspace, size_t workspace_bytes, mhe::VisionGrids* g, VisionWs* ws,
+                       hipStream_t st) {
+  int32_t rc;
+  if ((rc = check_vision_config(cfg))) return rc;
+  if ((rc = make_grids(*cfg, thw, n_grids, n, g))) return rc;
+  if ((rc = check_seq(n))) return rc;
+  const VisionWs need = vision_carve(*cfg, n, nullptr);
+  if ((rc = check_ws(workspace, workspace_bytes, need.total))) return rc;
+  *ws = vision_carve(*cfg, n, static_cast<char*>(workspace));
+  return hip_check(mhe::launch_patch_info(*g, n, ws->info, st), "patch info");
+}
+
+// Patches the grids hold (0 when the list is unusable; make_grids reports why).
+int grid_patches(const int32_t* thw, int n_grids) {
+  if (!thw || n_grids <= 0 || n_grids > mhe::kMaxVisionGrids) return 0;
+  int64_t n = 0;
+  for (int i = 0; i < n_grids; ++i) {
+    const int64_t p = static_cast<int64_t>(thw[3 * i]) * thw[3 * i + 1] * thw[3 * i + 2];
+    if (thw[3 * i] <= 0 || thw[3 * i + 1] <= 0 || thw[3 * i + 2] <= 0) return 0;
+    n += p;
+    if (n > kMaxSeq) return 0;
+  }
+  return static_cast<int>(n);
+}
+
+int32_t check_blocks(const mhe_vision_weights* w, int first, int count, int depth) {
+  if (!w) return fail(MHE_ERR_NULL, "vision weights are NULL");
+  if (count > 0 && !w->blocks) return fail(MHE_ERR_NULL, "vision blocks table is NULL");
+  if (first < 0 || count < 0 || first + count > depth)
+    return fail(MHE_ERR_SHAPE, "blocks [%d, %d) outside [0, %d)", first, first + count, depth);
+  return MHE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mhe_vision_workspace_bytes(const mhe_vision_config* cfg, int32_t n_patches) {
+  if (check_vision_config(cfg) || check_seq(n_patches)) return 0;
+  return vision_carve(*cfg, n_patches, nullptr).total;
+}
+
+int32_t mhe_vision_embed(const mhe_vision_config* cfg, const mhe_vision_weights* w,
+                         const void* pixels, const int32_t* grid_thw, int32_t n_grids,
+                         void* hidden, void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t rc;
+  if (!w || !pixels || !hidden) return fail(MHE_ERR_NULL, "weights, pixels and hidden are required");
+  if (!w->patch_w || !w->patch_b || !w->pos_table) return fail(MHE_ERR_NULL, "patch / position weights are NULL");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int n = grid_patches(grid_thw, n_grids);
+  mhe::VisionGrids g;
+  VisionWs ws;
+  if ((rc = vision_prelude(cfg, n, grid_thw, n_grids, workspace, workspace_bytes, &g, &ws, st))) return rc;
+  bf16_t* h = static_cast<bf16_t*>(hidden);
+  if ((rc = vision_gemm(mhe::Epilogue::kBias, static_cast<const bf16_t*>(pixels), cfg->patch_dim,
+                        w->patch_w, w->patch_b, h, cfg->hidden, nullptr, n, cfg->hidden,
+                        cfg->patch_dim, ws, st, "patch embed")))
+    return rc;
+  return hip_check(mhe::launch_pos_embed(h, cfg->hidden, n, cfg->hidden,
+                                         static_cast<const bf16_t*>(w->pos_table), cfg->pos_side,
+                                         ws.info, st), "position embedding");
+}
+
+int32_t mhe_vision_blocks(const mhe_vision_config* cfg, const mhe_vision_weights* w,
+                          int32_t first, int32_t count, void* hidden, const int32_t* grid_thw,
+                          int32_t n_grids, void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t rc;
+  if (!hidden) return fail(MHE_ERR_NULL, "hidden is NULL");
+  if (cfg && (rc = check_blocks(w, first, count, cfg->depth))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int n = grid_patches(grid_thw, n_grids);
+  mhe::VisionGrids g;
+  VisionWs ws;
+  if ((rc = vision_prelude(cfg, n, grid_thw, n_grids, workspace, workspace_bytes, &g, &ws, st))) return rc;
+  for (int b = first; b < first + count; ++b)
+    if ((rc = run_vision_block(*cfg, w->blocks[b], static_cast<bf16_t*>(hidden), n, ws, st))) return rc;
+  return MHE_OK;
+}
+
+int32_t mhe_vision_merge(const mhe_vision_config* cfg, const mhe_vision_merger_weights* m,
+                         int32_t postshuffle, const void* hidden, int32_t n_patches, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t rc;
+  if ((rc = check_vision_config(cfg))) return rc;
+  if ((rc = check_seq(n_patches))) return rc;
+  if (!m || !hidden || !out) return fail(MHE_ERR_NULL, "merger weights, hidden and out are required");
+  if (n_patches % (cfg->merge * cfg->merge))
+    return fail(MHE_ERR_SHAPE, "n_patches %d is not a multiple of merge^2", n_patches);
+  const VisionWs need = vision_carve(*cfg, n_patches, nullptr);
+  if ((rc = check_ws(workspace, workspace_bytes, need.total))) return rc;
+  const VisionWs ws = vision_carve(*cfg, n_patches, static_cast<char*>(workspace));
+  return run_vision_merge(*cfg, *m, postshuffle != 0, static_cast<const bf16_t*>(hidden), n_patches,
+                          static_cast<bf16_t*>(out), ws, static_cast<hipStream_t>(stream));
+}
+
+int32_t mhe_vision_forward(const mhe_vision_config* cfg, const mhe_vision_weights* w,
+                           const void* pixels, const int32_t* grid_thw, int32_t n_grids,
+                           void* merged, void* const* deepstack, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  int32_t rc;
+  if (!w || !pixels || !merged) return fail(MHE_ERR_NULL, "weights, pixels and merged are required");
+  if (!w->patch_w || !w->patch_b || !w->pos_table) return fail(MHE_ERR_NULL, "patch / position weights are NULL");
+  if (cfg && (rc = check_blocks(w, 0, cfg->depth, cfg->depth))) return rc;
+  if (cfg && cfg->n_deepstack > 0) {
+    if (!deepstack || !w->deepstack) return fail(MHE_ERR_NULL, "DeepStack outputs or mergers are NULL");
+    for (int l = 0; l < cfg->n_deepstack; ++l)
+      if (!deepstack[l]) return fail(MHE_ERR_NULL, "deepstack[%d] is NULL", l);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int n = grid_patches(grid_thw, n_grids);
+  mhe::VisionGrids g;
+  VisionWs ws;
+  if ((rc = vision_prelude(cfg, n, grid_thw, n_grids, workspace, workspace_bytes, &g, &ws, st))) return rc;
+  const mhe_vision_config& c = *cfg;
+  if ((rc = vision_gemm(mhe::Epilogue::kBias, static_cast<const bf16_t*>(pixels), c.patch_dim,
+                        w->patch_w, w->patch_b, ws.x, c.hidden, nullptr, n, c.hidden, c.patch_dim,
+                        ws, st, "patch embed")))
+    return rc;
+  if ((rc = hip_check(mhe::launch_pos_embed(ws.x, c.hidden, n, c.hidden,
+                                            static_cast<const bf16_t*>(w->pos_table), c.pos_side,
+                                            ws.info, st), "position embedding")))
+    return rc;
+  for (int b = 0; b < c.depth; ++b) {
+    if ((rc = run_vision_block(c, w->blocks[b], ws.x, n, ws, st))) return rc;
+    for (int l = 0; l < c.n_deepstack; ++l)
+      if (c.deepstack_index[l] == b &&
+          (rc = run_vision_merge(c, w->deepstack[l], true, ws.x, n, static_cast<bf16_t*>(deepstack[l]),
+                                 ws, st)))
+        return rc;
+  }
+  return run_vision_merge(c, w->merger, false, ws.x, n, static_cast<bf16_t*>(merged), ws, st);
+}
+
+int32_t mhe_layer_norm(const void* x, const void* w, const void* b, void* y, int32_t rows,
+                       int32_t dim, float eps, void* stream) {
+  if (!x || !w || !b || !y) return fail(MHE_ERR_NULL, "x, w, b and y are required");
+  if (rows <= 0) return fail(MHE_ERR_SHAPE, "rows must be > 0");
+  if (!mhe::rmsnorm_supported(dim)) return fail(MHE_ERR_UNSUPPORTED, "dim %d: multiple of 8, <= 8192", dim);
+  if (!(eps >= 0.f)) return fail(MHE_ERR_SHAPE, "eps must be >= 0");
+  return hip_check(mhe::launch_layernorm(static_cast<const bf16_t*>(x), dim, static_cast<const bf16_t*>(w),
+                                         static_cast<const bf16_t*>(b), static_cast<bf16_t*>(y), dim,
+                                         rows, dim, eps, static_cast<hipStream_t>(stream)),
+                   "layer norm");
+}
+
+int32_t mhe_linear_bias(const void* a, const void* w, const void* bias, void* c,
+                        const void* residual, int32_t m, int32_t n, int32_t k, int32_t act,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!a || !w || !bias || !c) return fail(MHE_ERR_NULL, "a, w, bias and c are required");
+  if (m <= 0 || n <= 0 || k <= 0) return fail(MHE_ERR_SHAPE, "m, n, k must be > 0");
+  if (act < 0 || act > 2) return fail(MHE_ERR_SHAPE, "act %d not in {0, 1, 2}", act);
+  if (act != 0 && residual) return fail(MHE_ERR_SHAPE, "a residual goes with act 0 only");
+  if (!mhe::gemm_supported(n, k)) return fail(MHE_ERR_UNSUPPORTED, "needs n %% 32 == 0 and k %% 64 == 0 (n=%d, k=%d)", n, k);
+  const size_t cb = static_cast<size_t>(m) * n * 2;
+  if (overlaps(c, cb, a, static_cast<size_t>(m) * k * 2) || overlaps(c, cb, w, static_cast<size_t>(n) * k * 2))
+    return fail(MHE_ERR_SHAPE, "c overlaps an operand");
+  if (residual && residual != c && overlaps(c, cb, residual, cb))
+    return fail(MHE_ERR_SHAPE, "residual partially overlaps c");
+  int32_t rc;
+  if ((rc = check_gemm_ws(workspace, workspace_bytes))) return rc;
+  const mhe::Epilogue epi = act == 1 ? mhe::Epilogue::kBiasGeluTanh
+                          : act == 2 ? mhe::Epilogue::kBiasGeluErf
+                          : residual ? mhe::Epilogue::kBiasResidual : mhe::Epilogue::kBias;
+  mhe::BSegments b{{static_cast<const bf16_t*>(w), nullptr, nullptr}, {n, 0, 0}, 1};
+  return hip_check(mhe::launch_gemm(epi, static_cast<const bf16_t*>(a), k, b, k, static_cast<bf16_t*>(c), n,
+                                    static_cast<const bf16_t*>(residual), m, n, k,
+                                    static_cast<float*>(workspace), workspace ? workspace_bytes : 0,
+                                    static_cast<hipStream_t>(stream), static_cast<const bf16_t*>(bias)),
+                   "linear bias");
 }
 
 }  // extern "C"

@@ -23,6 +23,14 @@
 // with 8 key/value heads, each XCD serves one head and keeps its K/V in its
 // own L2. Query blocks are issued longest-first (causal work grows with the
 // block index).
+//
+// The same kernel serves the vision tower's attention (H3 encoder page,
+// MiniMaxH3Qwen3VLVisionAttention.forward): SEG replaces the causal mask by
+// "key in the query's frame" (a [seg_lo, seg_hi) token range per query), the
+// head_dim of 72 is stored zero-padded to 128 (zero q/k columns add nothing to
+// the scores, zero V rows give output columns that are not stored), and with
+// one query head per key/value head a workgroup takes QW query blocks of one
+// head so that its QW wavefronts share every K/V tile.
 #include "common.h"
 #include "internal.h"
 
@@ -45,11 +53,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const bf16_t* p, i
                                            __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-template <int D, int G, int HPW>
-__global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
+template <int D, int G, int HPW, int QW, bool SEG>
+__global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
-    bf16_t* __restrict__ o, int ldo, int seq, int n_heads, int n_kv_heads, float scale_log2) {
-  constexpr int WAVES = G / HPW;
+    bf16_t* __restrict__ o, int ldo, int seq, int n_heads, int n_kv_heads, float scale_log2,
+    int dout, const PatchInfo* __restrict__ info) {
+  constexpr int HW = G / HPW;        // wavefronts per query block (heads of the group)
+  constexpr int WAVES = HW * QW;
   constexpr int KCH = D / 8;          // 16-byte chunks per K row
   constexpr int DS = D / 16;          // MFMA k-steps over head_dim
   constexpr int DB = D / 32;          // 32-row blocks of O^T
@@ -61,17 +71,17 @@ __global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
   __shared__ __attribute__((aligned(16))) bf16_t v_lds[2][D * KT];
 
   const int sp = seq_pad(seq);
-  const int n_qb = (seq + QB - 1) / QB;
+  const int n_qb = (seq + QB * QW - 1) / (QB * QW);
   const int g = blockIdx.x % n_kv_heads;
   const int qb = n_qb - 1 - static_cast<int>(blockIdx.x / n_kv_heads);
-  const int q0 = qb * QB;
+  const int q0 = qb * QB * QW;         // first query row of the workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int h0 = g * G + wave * HPW;   // this wavefront's first query head
+  const int h0 = g * G + (wave % HW) * HPW;   // this wavefront's first query head
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
-  const int qi = q0 + lrow;
+  const int qi = q0 + (wave / HW) * QB + lrow;
 
   // ---- Q rows of the wavefront's heads as MFMA B operands, kept in registers ----
   bf16x8 qreg[HPW][DS];
@@ -88,8 +98,26 @@ __global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
 
   const bf16_t* kg = k + static_cast<size_t>(g) * sp * D;
   const bf16_t* vg = vt + static_cast<size_t>(g) * D * sp;
-  const int last_key = min(q0 + QB - 1, seq - 1);
-  const int n_tiles = last_key / KT + 1;
+  // key range of the workgroup: [0, last query] (causal) or the union of its
+  // queries' frames (SEG); per-query limits are applied as masks
+  int key_lo = 0, key_hi = min(q0 + QB * QW, seq);
+  int my_lo = 0, my_hi = qi + 1;
+  if constexpr (SEG) {
+    __shared__ int range[2];
+    if (tid == 0) {
+      range[0] = info[q0].seg_lo;
+      range[1] = info[min(q0 + QB * QW, seq) - 1].seg_hi;
+    }
+    if (qi < seq) {
+      my_lo = info[qi].seg_lo;
+      my_hi = info[qi].seg_hi;
+    }
+    __syncthreads();
+    key_lo = range[0];     // frames are contiguous and ascending
+    key_hi = range[1];
+  }
+  const int t_first = key_lo / KT;
+  const int n_tiles = (key_hi - 1) / KT + 1 - t_first;
 
   // ---- K / V^T tiles go straight to LDS (buffer_load_dwordx4 ... lds). In
   //      load instruction i, lane L of wavefront w fills the 16 LDS bytes at
@@ -138,17 +166,19 @@ __global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
   float m_run[HPW], l_run[HPW];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    m_run[hh] = -INFINITY;
+    // finite, so a lane whose keys all lie in later tiles computes exp2(-inf) = 0, never NaN
+    m_run[hh] = -1e30f;
     l_run[hh] = 0.f;
   }
 
-  issue_tile(0, 0);
+  issue_tile(t_first, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < n_tiles) issue_tile(t + 1, cur ^ 1);
+  for (int ti = 0; ti < n_tiles; ++ti) {
+    const int t = t_first + ti;
+    const int cur = ti & 1;
+    if (ti + 1 < n_tiles) issue_tile(t + 1, cur ^ 1);
     const bf16_t* kl = k_lds[cur];
     const bf16_t* vl = v_lds[cur];
 
@@ -179,17 +209,18 @@ __global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
     //      FMA plus one exp. m is only raised when a tile's max exceeds it by
     //      more than 8 (p <= 2^8 meanwhile, exact once divided by the sum), so
     //      the O rescale is skipped for the whole wavefront on most tiles. ----
-    const bool diag = (t * KT + KT - 1) > q0;  // tile may hold keys past some query
+    // tile may hold keys past some query (causal) or outside some frame (SEG)
+    const bool edge = SEG || (t * KT + KT - 1) > q0;
     bf16x8 pop[HPW][PS];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
-      if (diag) {
+      if (edge) {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
             const int key = t * KT + kb * 32 + (e >> 2) * 8 + lhalf * 4 + (e & 3);
-            if (key > qi) sacc[hh][kb][e] = -INFINITY;
+            if (key < my_lo || key >= my_hi) sacc[hh][kb][e] = -INFINITY;
           }
       }
       float tmax = -INFINITY;
@@ -252,15 +283,17 @@ __global__ __launch_bounds__(64 * (G / HPW)) void attention_kernel(
     const float l_tot = l_run[hh] + __shfl_xor(l_run[hh], 32, 64);
     if (qi < seq) {
       const float inv = 1.f / l_tot;
-      bf16_t* dst = o + static_cast<size_t>(qi) * ldo + (h0 + hh) * D + lhalf * 4;
+      bf16_t* dst = o + static_cast<size_t>(qi) * ldo + (h0 + hh) * dout + lhalf * 4;
 #pragma unroll
       for (int b = 0; b < DB; ++b)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(oacc[hh][b][gq * 4 + 0] * inv, oacc[hh][b][gq * 4 + 1] * inv);
-          pk[1] = pack_bf16x2(oacc[hh][b][gq * 4 + 2] * inv, oacc[hh][b][gq * 4 + 3] * inv);
-          *reinterpret_cast<u32x2*>(dst + b * 32 + gq * 8) = pk;
+          if (D != 128 || b * 32 + gq * 8 + lhalf * 4 < dout) {
+            u32x2 pk;
+            pk[0] = pack_bf16x2(oacc[hh][b][gq * 4 + 0] * inv, oacc[hh][b][gq * 4 + 1] * inv);
+            pk[1] = pack_bf16x2(oacc[hh][b][gq * 4 + 2] * inv, oacc[hh][b][gq * 4 + 3] * inv);
+            *reinterpret_cast<u32x2*>(dst + b * 32 + gq * 8) = pk;
+          }
         }
     }
   }
@@ -276,8 +309,9 @@ hipError_t launch_d(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* 
   switch (G) {
 #define MHE_ATTN_CASE(GG, HH)                                                                 \
   case GG:                                                                                    \
-    hipLaunchKernelGGL((attention_kernel<D, GG, HH>), grid, dim3(64 * (GG / HH)), 0, stream, \
-                       q, k, vt, o, ldo, seq, n_heads, n_kv_heads, scale_log2);               \
+    hipLaunchKernelGGL((attention_kernel<D, GG, HH, 1, false>), grid, dim3(64 * (GG / HH)), 0, \
+                       stream, q, k, vt, o, ldo, seq, n_heads, n_kv_heads, scale_log2, D,     \
+                       nullptr);                                                              \
     break;
     MHE_ATTN_CASE(1, 1)
     MHE_ATTN_CASE(2, 1)
@@ -296,6 +330,20 @@ bool attention_supported(int n_heads, int n_kv_heads, int head_dim) {
   if (n_kv_heads <= 0 || n_heads % n_kv_heads != 0) return false;
   const int g = n_heads / n_kv_heads;
   return (head_dim == 64 || head_dim == 128) && (g == 1 || g == 2 || g == 4 || g == 8);
+}
+
+hipError_t launch_segment_attention(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o,
+                                    int ldo, int n, int heads, int head_dim,
+                                    const PatchInfo* info, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (head_dim > 128 || head_dim % 4 != 0 || ldo < heads * head_dim || ldo % 4 != 0)
+    return hipErrorInvalidValue;
+  constexpr int kQW = 4;
+  const int n_qb = (n + QB * kQW - 1) / (QB * kQW);
+  const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(head_dim));
+  hipLaunchKernelGGL((attention_kernel<128, 1, 1, kQW, true>), dim3(n_qb * heads), dim3(64 * kQW),
+                     0, stream, q, k, vt, o, ldo, n, heads, heads, scale_log2, head_dim, info);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o,

@@ -9,6 +9,11 @@
 //                                              decoder layer's residual add)
 //   kSwiGLU   C = silu(A Bg^T) * (A Bu^T)     (gate/up projections and the
 //                                              MLP activation, MiniMaxH3Qwen3VLTextMLP)
+//   kBias, kBiasResidual, kBiasGeluTanh, kBiasGeluErf
+//             C = A B^T + bias, then + R or GELU (the biased linears of the
+//             vision tower: MiniMaxH3Qwen3VLVisionAttention / VisionMLP /
+//             VisionPatchMerger; the MLP's GELU is the tanh form, the
+//             merger's the erf form)
 //
 // Tiling: a 256 (m) x 256 (n) output tile per workgroup of 4 wavefronts, each
 // wavefront owning 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 with
@@ -51,6 +56,7 @@ struct GemmArgs {
   int brows[3];
   bf16_t* c;
   const bf16_t* r;
+  const bf16_t* bias;
   int m, n, k;
   int lda, ldb;  // row strides (elements) of A and of every B segment
   int ldc;       // row stride of C and of the residual
@@ -100,6 +106,50 @@ __device__ __forceinline__ void wait_vmcnt() {
 // wavefront's LDS operations but leaves global loads in flight.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+constexpr bool epi_bias(int e) { return e >= static_cast<int>(Epilogue::kBias); }
+constexpr bool epi_residual(int e) {
+  return e == static_cast<int>(Epilogue::kResidual) || e == static_cast<int>(Epilogue::kBiasResidual);
+}
+
+// GELU, tanh form: x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), with
+// tanh(y) = 1 - 2 / (1 + e^(2y)) (saturates correctly at both ends).
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float y = 0.7978845608028654f * (x + 0.044715f * x * x * x);
+  return 0.5f * x * (2.f - 2.f / (1.f + __expf(2.f * y)));
+}
+__device__ __forceinline__ float gelu_erf(float x) {
+  return 0.5f * x * (1.f + erff(x * 0.7071067811865476f));
+}
+
+// Non-SwiGLU epilogue of four consecutive outputs (columns n..n+3 of the row
+// at element offset `off`), rounded to bf16 once.
+template <int EPI>
+__device__ __forceinline__ u32x2 finish4(float* o, const GemmArgs& args, int n, size_t off) {
+  if constexpr (epi_bias(EPI)) {
+    const u32x2 bv = *reinterpret_cast<const u32x2*>(args.bias + n);
+    o[0] += __uint_as_float(bv[0] << 16);
+    o[1] += __uint_as_float(bv[0] & 0xffff0000u);
+    o[2] += __uint_as_float(bv[1] << 16);
+    o[3] += __uint_as_float(bv[1] & 0xffff0000u);
+  }
+  if constexpr (epi_residual(EPI)) {
+    const u32x2 rv = *reinterpret_cast<const u32x2*>(args.r + off);
+    o[0] += __uint_as_float(rv[0] << 16);
+    o[1] += __uint_as_float(rv[0] & 0xffff0000u);
+    o[2] += __uint_as_float(rv[1] << 16);
+    o[3] += __uint_as_float(rv[1] & 0xffff0000u);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (EPI == static_cast<int>(Epilogue::kBiasGeluTanh)) o[e] = gelu_tanh(o[e]);
+    if constexpr (EPI == static_cast<int>(Epilogue::kBiasGeluErf)) o[e] = gelu_erf(o[e]);
+  }
+  u32x2 pk;
+  pk[0] = pack_bf16x2(o[0], o[1]);
+  pk[1] = pack_bf16x2(o[2], o[3]);
+  return pk;
 }
 
 template <int EPI>
@@ -394,17 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * g + e];
-          if (EPI == static_cast<int>(Epilogue::kResidual)) {
-            const u32x2 rv = *reinterpret_cast<const u32x2*>(args.r + off);
-            o[0] += __uint_as_float(rv[0] << 16);
-            o[1] += __uint_as_float(rv[0] & 0xffff0000u);
-            o[2] += __uint_as_float(rv[1] << 16);
-            o[3] += __uint_as_float(rv[1] & 0xffff0000u);
-          }
-          u32x2 pk;
-          pk[0] = pack_bf16x2(o[0], o[1]);
-          pk[1] = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<u32x2*>(args.c + off) = pk;
+          *reinterpret_cast<u32x2*>(args.c + off) = finish4<EPI>(o, args, nb + 8 * g + 4 * lhalf, off);
         }
       }
     }
@@ -449,17 +489,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args)
   }
   if (n >= N) return;
   const size_t off = static_cast<size_t>(m) * args.ldc + n;
-  if (EPI == static_cast<int>(Epilogue::kResidual)) {
-    const u32x2 rv = *reinterpret_cast<const u32x2*>(args.r + off);
-    o[0] += __uint_as_float(rv[0] << 16);
-    o[1] += __uint_as_float(rv[0] & 0xffff0000u);
-    o[2] += __uint_as_float(rv[1] << 16);
-    o[3] += __uint_as_float(rv[1] & 0xffff0000u);
+  if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+    u32x2 pk;
+    pk[0] = pack_bf16x2(o[0], o[1]);
+    pk[1] = pack_bf16x2(o[2], o[3]);
+    *reinterpret_cast<u32x2*>(args.c + off) = pk;
+  } else {
+    *reinterpret_cast<u32x2*>(args.c + off) = finish4<EPI>(o, args, n, off);
   }
-  u32x2 pk;
-  pk[0] = pack_bf16x2(o[0], o[1]);
-  pk[1] = pack_bf16x2(o[2], o[3]);
-  *reinterpret_cast<u32x2*>(args.c + off) = pk;
 }
 
 template <int EPI>
@@ -543,7 +580,8 @@ size_t gemm_partial_bytes() { return static_cast<size_t>(320) * BM * BN * sizeof
 
 hipError_t launch_gemm(Epilogue epi, const bf16_t* a, int lda, const BSegments& b, int ldb,
                        bf16_t* c, int ldc, const bf16_t* residual, int m, int n, int k,
-                       float* partial, size_t partial_bytes, hipStream_t stream) {
+                       float* partial, size_t partial_bytes, hipStream_t stream,
+                       const bf16_t* bias) {
   if (lda < k || ldb < k || ldc < n || lda % 8 != 0 || ldb % 8 != 0 || ldc % 4 != 0)
     return hipErrorInvalidValue;
   if (m <= 0) return hipSuccess;
@@ -559,6 +597,8 @@ hipError_t launch_gemm(Epilogue epi, const bf16_t* a, int lda, const BSegments& 
   }
   args.c = c;
   args.r = residual;
+  args.bias = bias;
+  if (static_cast<int>(epi) >= static_cast<int>(Epilogue::kBias) && !bias) return hipErrorInvalidValue;
   args.m = m;
   args.n = n;
   args.k = k;
@@ -571,6 +611,10 @@ hipError_t launch_gemm(Epilogue epi, const bf16_t* a, int lda, const BSegments& 
     case Epilogue::kStore: return run<0>(args, partial, partial_bytes, stream);
     case Epilogue::kResidual: return run<1>(args, partial, partial_bytes, stream);
     case Epilogue::kSwiGLU: return run<2>(args, partial, partial_bytes, stream);
+    case Epilogue::kBias: return run<3>(args, partial, partial_bytes, stream);
+    case Epilogue::kBiasResidual: return run<4>(args, partial, partial_bytes, stream);
+    case Epilogue::kBiasGeluTanh: return run<5>(args, partial, partial_bytes, stream);
+    case Epilogue::kBiasGeluErf: return run<6>(args, partial, partial_bytes, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -15,9 +15,19 @@ bool rmsnorm_supported(int dim);
 // y rows are ldy elements apart (>= dim, multiple of 8); x is dense.
 hipError_t launch_rmsnorm(const bf16_t* x, const bf16_t* gamma, bf16_t* y, int ldy, int rows,
                           int dim, float eps, hipStream_t stream);
+// LayerNorm with weight and bias; x rows ldx apart, y rows ldy apart (x and y
+// may alias with ldx == ldy).
+hipError_t launch_layernorm(const bf16_t* x, int ldx, const bf16_t* w, const bf16_t* b, bf16_t* y,
+                            int ldy, int rows, int dim, float eps, hipStream_t stream);
 
-// gemm.hip: C[m, n] = A[m, :] . B[n, :] with one of three epilogues.
-enum class Epilogue { kStore = 0, kResidual = 1, kSwiGLU = 2 };
+// gemm.hip: C[m, n] = A[m, :] . B[n, :] with one of these epilogues:
+//   kStore C = AB^T, kResidual C = R + AB^T, kSwiGLU C = silu(AB_g^T) * AB_u^T,
+//   kBias C = AB^T + b, kBiasResidual C = R + (AB^T + b),
+//   kBiasGeluTanh / kBiasGeluErf C = gelu(AB^T + b) (tanh / erf form).
+enum class Epilogue {
+  kStore = 0, kResidual = 1, kSwiGLU = 2, kBias = 3, kBiasResidual = 4, kBiasGeluTanh = 5,
+  kBiasGeluErf = 6
+};
 
 // Up to three row segments that together form the B operand (e.g. w_q | w_k | w_v).
 struct BSegments {
@@ -36,9 +46,11 @@ int gemm_segment_rows();
 size_t gemm_partial_bytes();
 // lda / ldb: row strides in elements (>= k, multiples of 8) of A and of B;
 // ldc: row stride of C and of the residual (>= n, multiple of 4).
+// bias [n] bf16 for the kBias* epilogues (ignored otherwise).
 hipError_t launch_gemm(Epilogue epi, const bf16_t* a, int lda, const BSegments& b, int ldb,
                        bf16_t* c, int ldc, const bf16_t* residual, int m, int n, int k,
-                       float* partial, size_t partial_bytes, hipStream_t stream);
+                       float* partial, size_t partial_bytes, hipStream_t stream,
+                       const bf16_t* bias = nullptr);
 
 // qk_norm_rope.hip
 struct RopeParams {
@@ -71,6 +83,34 @@ hipError_t launch_deepstack_add(bf16_t* hidden, int hidden_dim, const int32_t* i
 // hidden[idx[r]] = feature[r], r < n
 hipError_t launch_row_scatter(bf16_t* hidden, int hidden_dim, const int32_t* idx, int n,
                               const bf16_t* feature, hipStream_t stream);
+
+// vision.hip
+// Per patch, in the tower's block order: row and column in its image, the
+// image's patch grid (h, w) and the token range of its frame.
+struct PatchInfo {
+  int row, col, h, w, seg_lo, seg_hi, pad0, pad1;
+};
+constexpr int kMaxVisionGrids = 64;
+// Patch grids (t, h, w) of the images / videos of one call, by value.
+struct VisionGrids {
+  int count, merge;
+  int t[kMaxVisionGrids], h[kMaxVisionGrids], w[kMaxVisionGrids];
+};
+hipError_t launch_patch_info(const VisionGrids& grids, int n, PatchInfo* info, hipStream_t stream);
+// hidden[s] += bilinear(table [side*side, dim]) at patch s
+hipError_t launch_pos_embed(bf16_t* hidden, int ld, int n, int dim, const bf16_t* table, int side,
+                            const PatchInfo* info, hipStream_t stream);
+// qkv [n, 3 heads head_dim] (row stride ldq) -> rotated q [n, heads, 128],
+// k [heads, seq_pad(n), 128], permuted V^T [heads, 128, seq_pad(n)], zero padded
+hipError_t launch_vision_rope(const bf16_t* qkv, int ldq, int n, int heads, int head_dim,
+                              const PatchInfo* info, bf16_t* q_out, bf16_t* k_out, bf16_t* vt_out,
+                              hipStream_t stream);
+// Non-causal attention within each frame (info[s].seg_lo .. seg_hi) on the
+// layouts above: heads of head_dim (<= 128, stored padded to 128), scale
+// 1/sqrt(head_dim); o [n, heads * head_dim] with row stride ldo.
+hipError_t launch_segment_attention(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o,
+                                    int ldo, int n, int heads, int head_dim,
+                                    const PatchInfo* info, hipStream_t stream);
 
 // frontend.hip
 // Multimodal rotary positions [3, seq] (host) and optional host masks from

@@ -248,3 +248,109 @@ def feature_rows(n: int, hidden: int, seed: int, device="cpu") -> torch.Tensor:
     g = torch.Generator(device=device)
     g.manual_seed(_BASE_SEED * 1000 + _FEATURE_ID + seed)
     return torch.randn(n, hidden, generator=g, device=device).to(torch.bfloat16)
+
+
+# ---- vision tower inputs (patch pixels and random-init tower weights) ----
+
+_VISION_ID = 500
+
+
+@dataclass(frozen=True)
+class VisionDims:
+    """Vision tower sizes; `intermediate` is the stored (zero-padded) MLP width,
+    `mlp_width` the model's."""
+    hidden: int
+    n_heads: int
+    mlp_width: int
+    intermediate: int
+    depth: int
+    patch: int
+    temporal_patch: int
+    in_channels: int
+    merge: int
+    out_hidden: int
+    pos_side: int
+    deepstack: Tuple[int, ...]
+
+    @property
+    def patch_dim(self) -> int:
+        return self.in_channels * self.temporal_patch * self.patch * self.patch
+
+    @property
+    def merged_hidden(self) -> int:
+        return self.hidden * self.merge * self.merge
+
+
+# Qwen3-VL vision config (not printed on the pages): 27 blocks of width 1152,
+# 16 heads of 72, MLP 4304 (stored as 4352), 16x16x2 patches of 3 channels,
+# merge 2, 48x48 position table, DeepStack after blocks 8, 16, 24.
+VISION_FULL = VisionDims(hidden=1152, n_heads=16, mlp_width=4304, intermediate=4352, depth=27,
+                         patch=16, temporal_patch=2, in_channels=3, merge=2, out_hidden=5120,
+                         pos_side=48, deepstack=(8, 16, 24))
+# small tower with the same head_dim (72) and a padded MLP width
+VISION_TINY = VisionDims(hidden=576, n_heads=8, mlp_width=1000, intermediate=1024, depth=3,
+                         patch=8, temporal_patch=2, in_channels=3, merge=2, out_hidden=256,
+                         pos_side=8, deepstack=(0, 2))
+
+
+def _vgen(seed: int, tid: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(_BASE_SEED * 1000 + _VISION_ID + seed * 100 + tid)
+    return g
+
+
+def vision_weights(vd: VisionDims, seed: int = 0, device="cpu") -> Dict:
+    """Random-init tower: linear weights and biases N(0, 0.02), norm weights
+    U(0.5, 1.5), norm biases N(0, 0.1), position table N(0, 0.5); the MLP is
+    drawn at its model width and stored zero-padded to `intermediate`."""
+    tid = [0]
+
+    def nrm(shape, std):
+        tid[0] += 1
+        g = _vgen(seed, tid[0], device)
+        return (torch.randn(*shape, generator=g, device=device) * std).to(torch.bfloat16)
+
+    def uni(n):
+        tid[0] += 1
+        g = _vgen(seed, tid[0], device)
+        return (0.5 + torch.rand(n, generator=g, device=device)).to(torch.bfloat16)
+
+    H, I, Ipad, M = vd.hidden, vd.mlp_width, vd.intermediate, vd.merged_hidden
+
+    def padded(t, rows=None, cols=None):
+        out = torch.zeros(rows if rows is not None else t.shape[0],
+                          *(([cols] if cols is not None else list(t.shape[1:]))),
+                          dtype=t.dtype, device=t.device)
+        if t.dim() == 1:
+            out[:t.shape[0]] = t
+        elif cols is not None:
+            out[:, :t.shape[1]] = t
+        else:
+            out[:t.shape[0]] = t
+        return out
+
+    def merger(post):
+        nd = M if post else H
+        return {"norm_w": uni(nd), "norm_b": nrm((nd,), 0.1), "fc1_w": nrm((M, M), 0.02),
+                "fc1_b": nrm((M,), 0.02), "fc2_w": nrm((vd.out_hidden, M), 0.02),
+                "fc2_b": nrm((vd.out_hidden,), 0.02)}
+
+    w = {"patch_w": nrm((H, vd.patch_dim), 0.02), "patch_b": nrm((H,), 0.02),
+         "pos_table": nrm((vd.pos_side * vd.pos_side, H), 0.5), "blocks": []}
+    for _ in range(vd.depth):
+        fc1_w, fc1_b, fc2_w = nrm((I, H), 0.02), nrm((I,), 0.02), nrm((H, I), 0.02)
+        w["blocks"].append({
+            "norm1_w": uni(H), "norm1_b": nrm((H,), 0.1), "qkv_w": nrm((3 * H, H), 0.02),
+            "qkv_b": nrm((3 * H,), 0.02), "proj_w": nrm((H, H), 0.02), "proj_b": nrm((H,), 0.02),
+            "norm2_w": uni(H), "norm2_b": nrm((H,), 0.1),
+            "fc1_w": padded(fc1_w, rows=Ipad), "fc1_b": padded(fc1_b, rows=Ipad),
+            "fc2_w": padded(fc2_w, cols=Ipad), "fc2_b": nrm((H,), 0.02)})
+    w["merger"] = merger(False)
+    w["deepstack"] = [merger(True) for _ in vd.deepstack]
+    return w
+
+
+def vision_pixels(n: int, vd: VisionDims, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Patch pixels [n, patch_dim] bf16 ~ N(0, 1) (normalised image values)."""
+    g = _vgen(seed, 99, device)
+    return torch.randn(n, vd.patch_dim, generator=g, device=device).to(torch.bfloat16)
