@@ -18,6 +18,8 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                taken from HIP event pairs the library records around every
                launch of that kernel on its stream during the timed steps
   breakdown    mean milliseconds per encode of each step (a separate traced pass)
+  vision       the Qwen3-VL vision tower (27 blocks, random init) on the
+               prompt's image patches: ms per pass, TFLOP/s, MFMA util
   frontend     token-level front end of the same prompt, outside the encode:
                host position ids (ms) and the embedding gather, placeholder
                scatter and joint DeepStack kernels (us, GB/s)
@@ -178,6 +180,57 @@ def frontend_measure(wl, dev):
     return res
 
 
+def vision_flops(vd, grids):
+    """Algorithmic FLOPs of one tower pass: GEMMs as 2*M*N*K at the model's MLP
+    width, attention as 4*head_dim per (query, key) pair of a frame per head."""
+    n = sum(t * h * w for t, h, w in grids)
+    H, I, M = vd.hidden, vd.mlp_width, vd.merged_hidden
+    nm = n // (vd.merge * vd.merge)
+    blk = 2 * n * H * 3 * H + 2 * n * H * H + 2 * 2 * n * H * I
+    pairs = sum(t * (h * w) ** 2 for t, h, w in grids)
+    attn = 4 * (H // vd.n_heads) * vd.n_heads * pairs
+    merger = 2 * nm * M * M + 2 * nm * M * vd.out_hidden
+    return 2 * n * vd.patch_dim * H + vd.depth * (blk + attn) + (1 + len(vd.deepstack)) * merger
+
+
+def vision_measure(wl, dev, reps=5):
+    """The full Qwen3-VL vision tower (27 blocks, random-init weights) on the
+    patches of the workload's visual block (merged grid t x h x w = patch grid
+    t x 2h x 2w), timed with HIP events outside the encode."""
+    import torch
+    from multimodal_encoder_prefill_amd import binding as b
+    from multimodal_encoder_prefill_amd import synth
+    vd = synth.VISION_FULL
+    grids = [(int(t), 2 * int(h), 2 * int(w)) for kind, (t, h, w) in
+             ((k, s) for k, s in wl.segments if k != "text")]
+    if not grids:
+        return None
+    n = sum(t * h * w for t, h, w in grids)
+    w = synth.vision_weights(vd, 0, dev)
+    tables = b.VisionTables(w)
+    px = synth.vision_pixels(n, vd, 0, dev)
+    cfg = b.vision_config(vd)
+    nb = b.vision_workspace_bytes(cfg, n)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    nm = n // 4
+    merged = torch.empty(nm, vd.out_hidden, dtype=torch.bfloat16, device=dev)
+    ds = [torch.empty(nm, vd.out_hidden, dtype=torch.bfloat16, device=dev) for _ in vd.deepstack]
+    run = lambda: b.vision_forward(cfg, tables, px, grids, merged, ds, ws, nb)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    fl = vision_flops(vd, grids)
+    return {"grids_thw": grids, "patches": n, "blocks": vd.depth, "ms": round(ms, 3),
+            "tflops": round(fl / ms / 1e9, 1), "mfma_util": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "flops": fl, "patches_per_s": round(n / ms * 1000, 1)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +240,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-frontend", action="store_true")
+    ap.add_argument("--no-vision", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -280,6 +334,11 @@ def main():
         frontend = frontend_measure(wl, dev)
         log("front end: " + json.dumps(frontend))
 
+    vision = None
+    if not args.no_vision:
+        vision = vision_measure(wl, dev)
+        log("vision tower: " + json.dumps(vision))
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one decoder layer ...")
@@ -300,6 +359,7 @@ def main():
         "roofline": roofline,
         "breakdown_ms_per_step": breakdown,
         "frontend": frontend,
+        "vision": vision,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
