@@ -20,6 +20,9 @@ page and the class/function on it whose computation it follows:
 interpolated position embeddings, 2-D rotary, non-causal per-frame attention
 blocks, the merger and the DeepStack mergers).
 
+``oracle.fp8`` holds the online-FP8 reading of the decoder's linears
+(per-tensor E4M3 quantisation of weights and activations).
+
 ``oracle.frontend`` holds the token-level front end of the same page
 (token types, embedding gather with visual placeholder scatter, the joint
 DeepStack order and the multimodal rotary position ids).
@@ -50,3 +53,4 @@ from .qwen3vl_text import (  # noqa: F401
 from .positions import text_and_grid_positions  # noqa: F401
 from . import frontend  # noqa: F401
 from . import vision  # noqa: F401
+from . import fp8  # noqa: F401

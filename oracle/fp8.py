@@ -1,0 +1,119 @@
+"""Online FP8 variant of the decoder's linear layers, as plain reference code.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+H3 encoder page: the encoder accepts an FP8 quantisation config only when the
+checkpoint is not FP8-serialised (``_validate_encoder_quant_config``), i.e.
+weights are quantised when loaded, and every linear layer then runs through
+its quantised method (``_is_quantized_linear`` selects the fused qkv and
+gate/up GEMMs). The page does not print the method itself; the reading taken
+here is the plain per-tensor one:
+
+* FP8 is OCP E4M3 (the "fn" variant: 4 exponent bits with bias 7, 3 mantissa
+  bits, no infinities, largest finite 448);
+* a tensor x is quantised with one scale s = max|x| / 448 as
+  q = E4M3(round-to-nearest-even(clip(x * (448 / max|x|), -448, 448))), the
+  factor and the product taken in float32 (the precision of the kernel that
+  decides the code); the weights once, each activation on every call;
+* y = (q_x q_w^T) * s_x * s_w, accumulated exactly (here float64), before
+  the layer's bias / residual / SiLU epilogue.
+
+Everything else of the decoder layer is unchanged (``qwen3vl_text``).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .qwen3vl_text import (LayerWeights, ModelDims, apply_rope, causal_gqa_attention,
+                           rms_norm, silu)
+
+E4M3_MAX = 448.0
+
+
+def e4m3_values() -> np.ndarray:
+    """The 256 codes of E4M3 (fn) decoded (NaN for 0x7f and 0xff)."""
+    out = np.empty(256)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 0x7
+        if e == 0xF and m == 0x7:
+            out[c] = np.nan
+        elif e == 0:
+            out[c] = sign * m * 2.0 ** -9          # subnormals: m/8 * 2^-6
+        else:
+            out[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return out
+
+
+_VALUES = e4m3_values()
+_POS = np.sort(_VALUES[:0x7F])                       # codes 0x00..0x7e, ascending
+
+
+def round_e4m3(x) -> np.ndarray:
+    """Round to the nearest finite E4M3 value, ties to the even mantissa;
+    |x| must be <= 448 (callers clip first)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(a > E4M3_MAX):
+        raise ValueError("value beyond the E4M3 range")
+    hi = np.searchsorted(_POS, a, side="left").clip(0, len(_POS) - 1)
+    lo = (hi - 1).clip(0)
+    vlo, vhi = _POS[lo], _POS[hi]
+    dlo, dhi = a - vlo, vhi - a
+    # code of _POS[i] is i (codes 0..126 ascend with their values); even code = even mantissa
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    r = np.where(a == vhi, vhi, np.where(pick_hi, vhi, vlo))
+    return np.where(x < 0, -r, r)
+
+
+def quantize(x):
+    """(q as float64 values on the E4M3 grid, scale s) of the per-tensor scheme."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
+    if amax == 0:
+        return np.zeros(x32.shape), 1.0
+    factor = np.float32(E4M3_MAX) / amax
+    y = np.clip(x32 * factor, -E4M3_MAX, E4M3_MAX).astype(np.float64)
+    return round_e4m3(y), float(amax) / E4M3_MAX
+
+
+def linear_fp8(x, w_q, w_scale):
+    """x (float) quantised on the fly times an already-quantised weight."""
+    q_x, s_x = quantize(x)
+    return (q_x @ np.asarray(w_q, dtype=np.float64).T) * (s_x * w_scale)
+
+
+def quantize_layer(w: LayerWeights):
+    """Quantised weights of a layer: {name: (values, scale)} for the linears."""
+    return {k: quantize(getattr(w, k)) for k in ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down")}
+
+
+def decoder_layer_fp8(h, w: LayerWeights, qw, cos, sin, dims: ModelDims):
+    """The decoder layer with every linear in FP8 (qw from quantize_layer), all
+    rows (the activation scales are taken over whole tensors)."""
+    h = np.asarray(h, dtype=np.float64)
+    S = h.shape[0]
+    rows = np.arange(S)
+    need = S
+    D, Hq, Hkv = dims.head_dim, dims.n_heads, dims.n_kv_heads
+    u = rms_norm(h[:need], w.ln_in, dims.rms_eps)
+    # the fused qkv GEMM quantises its input once
+    q_u, s_u = quantize(u)
+    def lin(name):
+        qv, sv = qw[name]
+        return (q_u @ qv.T) * (s_u * sv)
+    q = lin("w_q").reshape(need, Hq, D)
+    k = lin("w_k").reshape(need, Hkv, D)
+    v = lin("w_v").reshape(need, Hkv, D)
+    q = rms_norm(q, w.q_norm, dims.rms_eps)
+    k = rms_norm(k, w.k_norm, dims.rms_eps)
+    q = apply_rope(q, cos[:need], sin[:need])
+    k = apply_rope(k, cos[:need], sin[:need])
+    o = causal_gqa_attention(q, k, v, rows)
+    x = h[rows] + linear_fp8(o.reshape(S, Hq * D), *qw["w_o"])
+    u2 = rms_norm(x, w.ln_post, dims.rms_eps)
+    q_u2, s_u2 = quantize(u2)
+    g = (q_u2 @ qw["w_gate"][0].T) * (s_u2 * qw["w_gate"][1])
+    up = (q_u2 @ qw["w_up"][0].T) * (s_u2 * qw["w_up"][1])
+    return x + linear_fp8(silu(g) * up, *qw["w_down"])
