@@ -15,6 +15,9 @@ here is the plain per-tensor one:
   q = E4M3(round-to-nearest-even(clip(x * (448 / max|x|), -448, 448))), the
   factor and the product taken in float32 (the precision of the kernel that
   decides the code); the weights once, each activation on every call;
+* the tensors are those of the page's linear layers: the fused qkv weight
+  (q, k and v rows stacked) and the fused gate_up weight (gate rows, then up
+  rows) are one tensor each, with one scale, like the o and down weights;
 * y = (q_x q_w^T) * s_x * s_w, accumulated exactly (here float64), before
   the layer's bias / residual / SiLU epilogue.
 
@@ -84,9 +87,16 @@ def linear_fp8(x, w_q, w_scale):
     return (q_x @ np.asarray(w_q, dtype=np.float64).T) * (s_x * w_scale)
 
 
+# the page's linear layers and the weight rows each one stacks
+FUSED = {"w_qkv": ("w_q", "w_k", "w_v"), "w_o": ("w_o",), "w_gate_up": ("w_gate", "w_up"),
+         "w_down": ("w_down",)}
+
+
 def quantize_layer(w: LayerWeights):
-    """Quantised weights of a layer: {name: (values, scale)} for the linears."""
-    return {k: quantize(getattr(w, k)) for k in ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down")}
+    """Quantised weights of a layer: {linear: (values, scale)}, one scale per
+    linear layer over its stacked rows."""
+    return {name: quantize(np.concatenate([np.asarray(getattr(w, p), dtype=np.float64) for p in parts]))
+            for name, parts in FUSED.items()}
 
 
 def decoder_layer_fp8(h, w: LayerWeights, qw, cos, sin, dims: ModelDims):
@@ -98,14 +108,10 @@ def decoder_layer_fp8(h, w: LayerWeights, qw, cos, sin, dims: ModelDims):
     need = S
     D, Hq, Hkv = dims.head_dim, dims.n_heads, dims.n_kv_heads
     u = rms_norm(h[:need], w.ln_in, dims.rms_eps)
-    # the fused qkv GEMM quantises its input once
-    q_u, s_u = quantize(u)
-    def lin(name):
-        qv, sv = qw[name]
-        return (q_u @ qv.T) * (s_u * sv)
-    q = lin("w_q").reshape(need, Hq, D)
-    k = lin("w_k").reshape(need, Hkv, D)
-    v = lin("w_v").reshape(need, Hkv, D)
+    qkv = linear_fp8(u, *qw["w_qkv"])
+    q = qkv[:, :Hq * D].reshape(need, Hq, D)
+    k = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(need, Hkv, D)
+    v = qkv[:, (Hq + Hkv) * D:].reshape(need, Hkv, D)
     q = rms_norm(q, w.q_norm, dims.rms_eps)
     k = rms_norm(k, w.k_norm, dims.rms_eps)
     q = apply_rope(q, cos[:need], sin[:need])
@@ -113,7 +119,6 @@ def decoder_layer_fp8(h, w: LayerWeights, qw, cos, sin, dims: ModelDims):
     o = causal_gqa_attention(q, k, v, rows)
     x = h[rows] + linear_fp8(o.reshape(S, Hq * D), *qw["w_o"])
     u2 = rms_norm(x, w.ln_post, dims.rms_eps)
-    q_u2, s_u2 = quantize(u2)
-    g = (q_u2 @ qw["w_gate"][0].T) * (s_u2 * qw["w_gate"][1])
-    up = (q_u2 @ qw["w_up"][0].T) * (s_u2 * qw["w_up"][1])
-    return x + linear_fp8(silu(g) * up, *qw["w_down"])
+    gu = linear_fp8(u2, *qw["w_gate_up"])
+    I = dims.intermediate
+    return x + linear_fp8(silu(gu[:, :I]) * gu[:, I:], *qw["w_down"])

@@ -91,26 +91,57 @@ def test_fp8_layer_structure():
     np.testing.assert_array_equal(Q.decoder_layer_fp8(h, w0, Q.quantize_layer(w0), cos, sin, d), h)
 
 
-def test_fp8_layer_scale_bookkeeping_is_equivariant():
-    # Scaling a weight by a power of two leaves its FP8 codes alone and scales its
-    # per-tensor scale: the MLP's contribution must scale by the same factor,
-    # (to fp64 rounding), for the up and for the down projection (a scale taken from the
-    # wrong tensor breaks this).
-    rng = np.random.default_rng(4)
+def _layer(rng):
     d = ModelDims(hidden=64, n_heads=4, n_kv_heads=2, head_dim=16, intermediate=96,
                   rms_eps=1e-6, rope_theta=1e4, mrope_section=(3, 3, 2))
-    S = 10
     g = lambda *sh: rng.normal(size=sh) * 0.1
     w = LayerWeights(ln_in=rng.uniform(0.5, 1.5, 64), w_q=g(64, 64), w_k=g(32, 64), w_v=g(32, 64),
                      q_norm=rng.uniform(0.5, 1.5, 16), k_norm=rng.uniform(0.5, 1.5, 16),
                      w_o=g(64, 64), ln_post=rng.uniform(0.5, 1.5, 64), w_gate=g(96, 64),
                      w_up=g(96, 64), w_down=g(64, 96))
+    return d, w
+
+
+def test_fp8_layer_scale_bookkeeping_is_equivariant():
+    # Scaling a weight by a power of two leaves its FP8 codes alone and scales its
+    # per-tensor scale: the contribution of the o projection (with the MLP switched off)
+    # and of the down projection must scale by the same factor, to fp64 rounding (a scale
+    # taken from the wrong tensor breaks this).
+    rng = np.random.default_rng(4)
+    d, w = _layer(rng)
+    S = 10
     h = rng.normal(size=(S, 64))
     cos, sin = oracle.rope_cos_sin(np.tile(np.arange(S), (3, 1)), 16, 1e4, (3, 3, 2))
     run = lambda ww: Q.decoder_layer_fp8(h, ww, Q.quantize_layer(ww), cos, sin, d)
     w_nomlp = LayerWeights(**{**w.__dict__, "w_down": np.zeros((64, 96))})
+    attn = run(w_nomlp) - h
+    w4 = LayerWeights(**{**w_nomlp.__dict__, "w_o": w.w_o * 4.0})
+    np.testing.assert_allclose(run(w4) - h, 4.0 * attn, rtol=1e-9, atol=1e-12)
     base = run(w_nomlp)
     mlp = run(w) - base
-    for name in ("w_up", "w_down"):
-        w4 = LayerWeights(**{**w.__dict__, name: getattr(w, name) * 4.0})
-        np.testing.assert_allclose(run(w4) - base, 4.0 * mlp, rtol=1e-9, atol=1e-12)
+    w4 = LayerWeights(**{**w.__dict__, "w_down": w.w_down * 4.0})
+    np.testing.assert_allclose(run(w4) - base, 4.0 * mlp, rtol=1e-9, atol=1e-12)
+
+
+def test_fused_linears_share_one_scale():
+    # Weights on the E4M3 grid whose fused tensor has max |w| = 448 quantise with scale 1
+    # and no rounding: every dequantised weight equals the original, in every part of the
+    # fused qkv and gate_up tensors. Parts quantised on their own would have smaller
+    # maxima (16 here), factors of 28 and rounded codes (3 * 28 = 84 is a tie between 80
+    # and 88).
+    rng = np.random.default_rng(5)
+    d, w = _layer(rng)
+    ints = lambda a: rng.integers(-16, 17, size=a.shape).astype(np.float64)
+    parts = {k: ints(getattr(w, k)) for k in ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down")}
+    parts["w_q"][0, 0] = 448.0
+    parts["w_gate"][0, 0] = -448.0
+    parts["w_o"][0, 0] = 448.0
+    parts["w_down"][0, 0] = 448.0
+    parts["w_k"][0, 0] = parts["w_up"][0, 0] = 3.0
+    wg = LayerWeights(**{**w.__dict__, **parts})
+    qw = Q.quantize_layer(wg)
+    for name, stacked in (("w_qkv", ("w_q", "w_k", "w_v")), ("w_gate_up", ("w_gate", "w_up")),
+                          ("w_o", ("w_o",)), ("w_down", ("w_down",))):
+        vals, s = qw[name]
+        assert s == 1.0
+        np.testing.assert_array_equal(vals, np.concatenate([parts[p] for p in stacked]))
