@@ -49,24 +49,21 @@ def e4m3_values() -> np.ndarray:
     return out
 
 
-_VALUES = e4m3_values()
-_POS = np.sort(_VALUES[:0x7F])                       # codes 0x00..0x7e, ascending
-
-
 def round_e4m3(x) -> np.ndarray:
     """Round to the nearest finite E4M3 value, ties to the even mantissa;
-    |x| must be <= 448 (callers clip first)."""
+    |x| must be <= 448 (callers clip first).
+
+    A magnitude in the binade [2^E, 2^(E+1)) lies on a grid of step
+    2^(E-3) (3 mantissa bits); below 2^-6 the subnormal step 2^-9 holds. So
+    the value is its magnitude divided by that step, rounded half to even,
+    times the step (all exact in float64)."""
     x = np.asarray(x, dtype=np.float64)
     a = np.abs(x)
     if np.any(a > E4M3_MAX):
         raise ValueError("value beyond the E4M3 range")
-    hi = np.searchsorted(_POS, a, side="left").clip(0, len(_POS) - 1)
-    lo = (hi - 1).clip(0)
-    vlo, vhi = _POS[lo], _POS[hi]
-    dlo, dhi = a - vlo, vhi - a
-    # code of _POS[i] is i (codes 0..126 ascend with their values); even code = even mantissa
-    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
-    r = np.where(a == vhi, vhi, np.where(pick_hi, vhi, vlo))
+    _, e = np.frexp(a)                                   # a = m 2^e, m in [0.5, 1)
+    step = np.ldexp(1.0, np.maximum(e - 1, -6) - 3)
+    r = np.round(a / step) * step                        # np.round: half to even
     return np.where(x < 0, -r, r)
 
 
