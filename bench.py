@@ -18,6 +18,11 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                taken from HIP event pairs the library records around every
                launch of that kernel on its stream during the timed steps
   breakdown    mean milliseconds per encode of each step (a separate traced pass)
+  fp8          the same encode with the four linears of every layer in FP8
+               (per-tensor E4M3, weights quantised once beforehand,
+               activations on every call): ms per encode, tokens/s, its
+               gate/up GEMM against the FP8 dense peak (5.0 PFLOP/s), and the
+               per-step breakdown
   vision       the Qwen3-VL vision tower (27 blocks, random init) on the
                prompt's image patches: ms per pass, TFLOP/s, MFMA util
   frontend     token-level front end of the same prompt, outside the encode:
@@ -40,6 +45,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "encoded tokens/sec, 50-layer BF16 prefill seq 4096, 1 GPU; MFMA util %"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_traffic.json")
@@ -180,6 +186,55 @@ def frontend_measure(wl, dev):
     return res
 
 
+def fp8_measure(wl, cfg, layers, emb, pos, mask, ds, dev, reps=3):
+    """mhe_encode_fp8 on the workload: weights quantised once (not timed),
+    then `reps` encodes timed with HIP events; the gate/up launches carry event
+    pairs in a separate pass, as does the per-step breakdown."""
+    import torch
+    from multimodal_encoder_prefill_amd import binding as b
+    t0 = time.perf_counter()
+    q = [b.Fp8Layer(w, cfg) for w in layers]
+    log(f"fp8: {len(q)} layers quantised in {time.perf_counter() - t0:.1f} s")
+    tables = [f.table for f in q]
+    nb = b.workspace_bytes_fp8(cfg, wl.seq)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(emb)
+    run = lambda: b.encode_fp8(cfg, tables, emb, pos, wl.seq, out, ws, nb,
+                               visual_mask=mask if wl.n_vis else None, n_vis=wl.n_vis,
+                               deepstack=ds if wl.n_vis else None)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    b.trace_enable(list(b.STEPS))
+    for s in b.STEPS:
+        b.trace_read(s)
+    run()
+    torch.cuda.synchronize()
+    bd = {}
+    for s in b.STEPS:
+        t, n = b.trace_read(s)
+        if n:
+            bd[s] = (round(t, 3), n)
+    b.trace_enable([])
+    fl = layer_flops(wl.dims, wl.seq)
+    gu_ms = bd["gate_up"][0] / bd["gate_up"][1]
+    gu_tf = fl["gate_up"] / (gu_ms / 1000.0) / 1e12
+    del q, tables, ws, out
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 3), "tokens_per_s": round(wl.seq / ms * 1000.0, 2),
+            "speedup_vs_bf16": None,
+            "gate_up": {"launch_ms": round(gu_ms, 4), "achieved": round(gu_tf, 1),
+                        "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(gu_tf / PEAK_FP8_TFLOPS, 4)},
+            "breakdown_ms_per_step": {k: v[0] for k, v in bd.items()}}
+
+
 def vision_flops(vd, grids):
     """Algorithmic FLOPs of one tower pass: GEMMs as 2*M*N*K at the model's MLP
     width, attention as 4*head_dim per (query, key) pair of a frame per head."""
@@ -241,6 +296,7 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--no-frontend", action="store_true")
     ap.add_argument("--no-vision", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -334,6 +390,12 @@ def main():
         frontend = frontend_measure(wl, dev)
         log("front end: " + json.dumps(frontend))
 
+    fp8 = None
+    if not args.no_fp8:
+        fp8 = fp8_measure(wl, cfg, layers, emb, pos, mask, ds, dev)
+        fp8["speedup_vs_bf16"] = round(ms_per_step / fp8["ms"], 3)
+        log("fp8 encode: " + json.dumps(fp8))
+
     vision = None
     if not args.no_vision:
         vision = vision_measure(wl, dev)
@@ -358,6 +420,7 @@ def main():
         "tflops_per_step": round(flops_step / 1e12, 3),
         "roofline": roofline,
         "breakdown_ms_per_step": breakdown,
+        "fp8": fp8,
         "frontend": frontend,
         "vision": vision,
         "cpu_baseline": cpu,

@@ -178,7 +178,8 @@ enum {
   MHE_STEP_GATE_UP = 6,    /* gate/up projections + SiLU*mul */
   MHE_STEP_DOWN = 7,       /* down projection + residual */
   MHE_STEP_DEEPSTACK = 8,  /* DeepStack scatter-add */
-  MHE_STEP_COUNT = 9
+  MHE_STEP_QUANTIZE = 9,   /* FP8 layers: per-tensor quantisation of a GEMM input */
+  MHE_STEP_COUNT = 10
 };
 
 /*
@@ -262,6 +263,105 @@ int32_t mhe_qk_norm_rope(const mhe_config* cfg, const void* qkv, const void* q_n
  */
 int32_t mhe_attention(const void* q, const void* k, const void* vt, void* o, int32_t seq,
                       int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, void* stream);
+
+/* ---- FP8 linears (online quantisation) ---------------------------------------
+ *
+ * H3 encoder page: the encoder accepts an FP8 quantisation config only for a
+ * checkpoint that is not FP8-serialised (_validate_encoder_quant_config), so
+ * the weights are quantised when loaded and every linear layer, among them
+ * the fused qkv and gate_up layers (_is_quantized_linear), runs through the
+ * quantised method. The page does not print that method; the one built here
+ * is per-tensor E4M3 (OCP "fn": bias 7, no infinities, largest finite 448):
+ *   s = max|x| / 448, q = E4M3_rne(clamp(x * (448 / max|x|), -448, 448)),
+ *   the factor and the product in fp32; an all-zero tensor gives zero codes
+ *   and s = 1;
+ *   y = (q_x q_w^T) * s_x * s_w accumulated in fp32, then the layer's
+ *   epilogue (residual, SiLU * up) as in the bf16 forms.
+ * A fused layer is one tensor with one scale: q | k | v rows stacked, gate
+ * rows then up rows. Weights are quantised once (mhe_quantize_fp8), the GEMM
+ * inputs on every call, inside the FP8 layer. E4M3 tensors are byte arrays;
+ * scales are device floats.
+ */
+
+/* Workspace bytes of mhe_quantize_fp8 (partial maxima). */
+size_t mhe_quantize_fp8_workspace_bytes(void);
+
+/*
+ * Quantise one bf16 tensor, stored as n_parts (1..8) row blocks parts[i]
+ * [part_rows[i], cols] (host array of device pointers; a fused weight's
+ * pieces), into q [sum part_rows, cols] E4M3 (the blocks stacked in order)
+ * with one scale written to scale[0] (device float). cols % 8 == 0.
+ * workspace: mhe_quantize_fp8_workspace_bytes() bytes, 256-byte aligned.
+ */
+int32_t mhe_quantize_fp8(const void* const* parts, const int32_t* part_rows, int32_t n_parts,
+                         int32_t cols, void* q, float* scale, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
+ * c[m, n] = scale_a[0] * scale_w[0] * sum_k a[m, k] w[n, k] (+ residual[m, n]),
+ * a [m, k] and w [n, k] E4M3, c and residual bf16 (one rounding); residual
+ * may be NULL or equal to c. k % 128 == 0, n % 32 == 0. workspace as for
+ * mhe_linear.
+ */
+int32_t mhe_linear_fp8(const void* a, const float* scale_a, const void* w, const float* scale_w,
+                       void* c, const void* residual, int32_t m, int32_t n, int32_t k,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * c[m, j] = silu(g) * u with g = sa sw sum_k a[m,k] w[j,k] and
+ * u = sa sw sum_k a[m,k] w[n + j, k] (sa = scale_a[0], sw = scale_w[0]):
+ * w_gate_up [2n, k] E4M3 is the fused gate_up weight (gate rows, then up
+ * rows). k % 128 == 0, n % 32 == 0. workspace as for mhe_linear.
+ */
+int32_t mhe_linear_swiglu_fp8(const void* a, const float* scale_a, const void* w_gate_up,
+                              const float* scale_w, void* c, int32_t m, int32_t n, int32_t k,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decoder layer's weights for the FP8 layer: norms bf16 as in
+ * mhe_layer_weights, the four linears E4M3 with their scales (device float):
+ *   w_qkv     [(n_heads + 2 n_kv_heads) head_dim, hidden]  q | k | v rows
+ *   w_o       [hidden, n_heads head_dim]
+ *   w_gate_up [2 intermediate, hidden]  gate rows, then up rows
+ *   w_down    [hidden, intermediate]
+ */
+typedef struct mhe_layer_weights_fp8 {
+  const void* ln_in;
+  const void* w_qkv;
+  const float* s_qkv;
+  const void* q_norm;
+  const void* k_norm;
+  const void* w_o;
+  const float* s_o;
+  const void* ln_post;
+  const void* w_gate_up;
+  const float* s_gate_up;
+  const void* w_down;
+  const float* s_down;
+} mhe_layer_weights_fp8;
+
+/*
+ * Workspace bytes of mhe_layer_forward_fp8 / mhe_encode_fp8 (0 for an
+ * invalid config or seq). The FP8 forms need hidden, n_heads*head_dim and
+ * intermediate to be multiples of 128.
+ */
+size_t mhe_workspace_bytes_fp8(const mhe_config* cfg, int32_t seq);
+
+/*
+ * mhe_layer_forward / mhe_encode with the four linears of every layer in FP8:
+ * before each GEMM its bf16 input (the normed hidden state, the attention
+ * output, the SiLU*up product) is quantised with its own per-tensor scale,
+ * taken over all seq rows. Everything else, arguments and errors as in the
+ * bf16 forms.
+ */
+int32_t mhe_layer_forward_fp8(const mhe_config* cfg, const mhe_layer_weights_fp8* w, void* hidden,
+                              const int32_t* positions, int32_t seq, void* workspace,
+                              size_t workspace_bytes, void* stream);
+int32_t mhe_encode_fp8(const mhe_config* cfg, const mhe_layer_weights_fp8* layers, int32_t n_layers,
+                       const void* inputs_embeds, const int32_t* positions,
+                       const uint8_t* visual_mask, int32_t n_vis, const void* const* deepstack,
+                       int32_t n_ds, int32_t seq, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream);
 
 /* ---- token-level front end (from token ids to mhe_encode's inputs) ---------- */
 

@@ -47,6 +47,15 @@ class MheLayerWeights(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in WEIGHT_FIELDS]
 
 
+FP8_WEIGHT_FIELDS = (("ln_in", False), ("w_qkv", False), ("s_qkv", True), ("q_norm", False),
+                     ("k_norm", False), ("w_o", False), ("s_o", True), ("ln_post", False),
+                     ("w_gate_up", False), ("s_gate_up", True), ("w_down", False), ("s_down", True))
+
+
+class MheLayerWeightsFp8(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name, _ in FP8_WEIGHT_FIELDS]
+
+
 class MheVisionConfig(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
                 ("intermediate", ctypes.c_int32), ("depth", ctypes.c_int32),
@@ -115,6 +124,17 @@ _SIGNATURES = {
                                 ctypes.POINTER(MheVisionMergerWeights), _i32, _vp, _i32, _vp, _vp,
                                 _sz, _vp]),
     "mhe_layer_norm": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _f32, _vp]),
+    "mhe_quantize_fp8_workspace_bytes": (_sz, []),
+    "mhe_quantize_fp8": (_i32, [ctypes.POINTER(_vp), ctypes.POINTER(_i32), _i32, _i32, _vp, _vp,
+                                _vp, _sz, _vp]),
+    "mhe_linear_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "mhe_linear_swiglu_fp8": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "mhe_workspace_bytes_fp8": (_sz, [ctypes.POINTER(MheConfig), _i32]),
+    "mhe_layer_forward_fp8": (_i32, [ctypes.POINTER(MheConfig), ctypes.POINTER(MheLayerWeightsFp8),
+                                     _vp, _vp, _i32, _vp, _sz, _vp]),
+    "mhe_encode_fp8": (_i32, [ctypes.POINTER(MheConfig), ctypes.POINTER(MheLayerWeightsFp8), _i32,
+                              _vp, _vp, _vp, _i32, ctypes.POINTER(_vp), _i32, _i32, _vp, _vp, _sz,
+                              _vp]),
     "mhe_linear_bias": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
 }
 
@@ -124,7 +144,7 @@ VIDEO_TOKEN_ID = 151656
 
 # step ids of the trace facility (MHE_STEP_* in include/mhe.h)
 STEPS = ("input_norm", "qkv", "qk_rope", "attention", "o_proj", "post_norm", "gate_up", "down",
-         "deepstack")
+         "deepstack", "quantize")
 
 
 def lib() -> ctypes.CDLL:
@@ -147,7 +167,7 @@ def header_entry_points() -> list:
     with open(HEADER) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mhe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mhe_[a-z0-9_]+)\s*\(", text)))
 
 
 def _ptr(x) -> Optional[int]:
@@ -275,6 +295,104 @@ def linear_swiglu(a, w_gate, w_up, c, m, n, k, workspace=None, stream=None):
     wp, wb = _ws(workspace)
     _check("mhe_linear_swiglu", lib().mhe_linear_swiglu(_ptr(a), _ptr(w_gate), _ptr(w_up),
                                                         _ptr(c), m, n, k, wp, wb, _stream(stream)))
+
+
+# ---- FP8 linears ----
+
+def quantize_fp8_workspace_bytes() -> int:
+    return lib().mhe_quantize_fp8_workspace_bytes()
+
+
+def quantize_fp8(parts: Sequence, part_rows: Sequence[int], cols, q, scale, workspace, stream=None):
+    """One per-tensor E4M3 quantisation of the row blocks `parts` (stacked in q)."""
+    n = len(parts)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(p) for p in parts])
+    rows = (ctypes.c_int32 * max(n, 1))(*[int(r) for r in part_rows])
+    wp, wb = _ws(workspace)
+    _check("mhe_quantize_fp8", lib().mhe_quantize_fp8(ptrs, rows, n, cols, _ptr(q), _ptr(scale),
+                                                      wp, wb, _stream(stream)))
+
+
+def linear_fp8(a, scale_a, w, scale_w, c, m, n, k, residual=None, workspace=None, stream=None):
+    wp, wb = _ws(workspace)
+    _check("mhe_linear_fp8", lib().mhe_linear_fp8(_ptr(a), _ptr(scale_a), _ptr(w), _ptr(scale_w),
+                                                  _ptr(c), _ptr(residual), m, n, k, wp, wb,
+                                                  _stream(stream)))
+
+
+def linear_swiglu_fp8(a, scale_a, w_gate_up, scale_w, c, m, n, k, workspace=None, stream=None):
+    wp, wb = _ws(workspace)
+    _check("mhe_linear_swiglu_fp8", lib().mhe_linear_swiglu_fp8(
+        _ptr(a), _ptr(scale_a), _ptr(w_gate_up), _ptr(scale_w), _ptr(c), m, n, k, wp, wb,
+        _stream(stream)))
+
+
+def layer_table_fp8(weights) -> MheLayerWeightsFp8:
+    """FP8 weight table from a mapping name -> tensor (or device address)."""
+    t = MheLayerWeightsFp8()
+    for name, _ in FP8_WEIGHT_FIELDS:
+        setattr(t, name, _ptr(weights[name]))
+    return t
+
+
+def workspace_bytes_fp8(cfg: MheConfig, seq: int) -> int:
+    n = lib().mhe_workspace_bytes_fp8(ctypes.byref(cfg), seq)
+    if n == 0:
+        raise MheError("mhe_workspace_bytes_fp8", 2, lib().mhe_last_error().decode())
+    return n
+
+
+def layer_forward_fp8(cfg, weights, hidden, positions, seq, workspace, workspace_bytes, stream=None):
+    table = weights if isinstance(weights, MheLayerWeightsFp8) else layer_table_fp8(weights)
+    _check("mhe_layer_forward_fp8", lib().mhe_layer_forward_fp8(
+        ctypes.byref(cfg), ctypes.byref(table), _ptr(hidden), _ptr(positions), seq,
+        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def encode_fp8(cfg, layers: Sequence, inputs_embeds, positions, seq, out, workspace,
+               workspace_bytes, visual_mask=None, n_vis=0, deepstack: Optional[Sequence] = None,
+               stream=None):
+    n_layers = len(layers)
+    tables = (MheLayerWeightsFp8 * max(n_layers, 1))()
+    for i, w in enumerate(layers):
+        tables[i] = w if isinstance(w, MheLayerWeightsFp8) else layer_table_fp8(w)
+    n_ds = 0 if deepstack is None else len(deepstack)
+    ds = (ctypes.c_void_p * max(n_ds, 1))()
+    for i in range(n_ds):
+        ds[i] = _ptr(deepstack[i])
+    _check("mhe_encode_fp8", lib().mhe_encode_fp8(
+        ctypes.byref(cfg), tables if n_layers else None, n_layers, _ptr(inputs_embeds),
+        _ptr(positions), _ptr(visual_mask), n_vis, ds if n_ds else None, n_ds, seq, _ptr(out),
+        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+class Fp8Layer:
+    """Device buffers of one decoder layer quantised for the FP8 forms: the
+    fused qkv and gate_up weights and the o and down weights as E4M3 tensors
+    with one scale each (mhe_quantize_fp8), the norms shared with the bf16
+    weights. `weights`: name -> bf16 device tensor as for layer_table."""
+
+    def __init__(self, weights, cfg: MheConfig, stream=None):
+        import torch
+        dev = weights["w_q"].device
+        H, I = cfg.hidden, cfg.intermediate
+        qw, kvw = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+        ws = torch.empty(quantize_fp8_workspace_bytes(), dtype=torch.uint8, device=dev)
+        self.tensors = {}
+        for name, parts, rows, cols in (
+                ("w_qkv", ("w_q", "w_k", "w_v"), (qw, kvw, kvw), H),
+                ("w_o", ("w_o",), (H,), qw),
+                ("w_gate_up", ("w_gate", "w_up"), (I, I), H),
+                ("w_down", ("w_down",), (H,), I)):
+            q = torch.empty((sum(rows), cols), dtype=torch.uint8, device=dev)
+            s = torch.empty(1, dtype=torch.float32, device=dev)
+            quantize_fp8([weights[p] for p in parts], rows, cols, q, s, ws, stream)
+            self.tensors[name] = q
+            self.tensors["s_" + name[2:]] = s
+        for name in ("ln_in", "q_norm", "k_norm", "ln_post"):
+            self.tensors[name] = weights[name]
+        torch.cuda.synchronize(dev)  # before the quantisation workspace is released
+        self.table = layer_table_fp8(self.tensors)
 
 
 def qk_norm_rope(cfg, qkv, q_norm, k_norm, positions, seq, q_out, k_out, vt_out, stream=None):

@@ -78,6 +78,20 @@ int32_t check_config(const mhe_config* c) {
   return MHE_OK;
 }
 
+// The FP8 layer's GEMMs need k % 128 == 0 for all four projections.
+int32_t check_config_fp8(const mhe_config* c) {
+  int32_t rc;
+  if ((rc = check_config(c))) return rc;
+  const int qw = c->n_heads * c->head_dim;
+  const int qkvw = (c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
+  if (!mhe::gemm_fp8_supported(qkvw, c->hidden) || !mhe::gemm_fp8_supported(c->hidden, qw) ||
+      !mhe::gemm_fp8_supported(c->intermediate, c->hidden) ||
+      !mhe::gemm_fp8_supported(c->hidden, c->intermediate))
+    return fail(MHE_ERR_UNSUPPORTED,
+                "FP8 GEMM needs hidden, n_heads*head_dim and intermediate to be multiples of 128");
+  return MHE_OK;
+}
+
 struct Workspace {
   int ld_h, ld_o, ld_i;  // row strides of hn, ao, act
   bf16_t* hn;    // [S, H] with row stride ld_h
@@ -91,10 +105,17 @@ struct Workspace {
   int32_t* cnt;  // [1]
   float* partial;  // split-K partial tiles of the GEMMs' last wave
   size_t partial_bytes;
+  // FP8 layers only: E4M3 copy of the current GEMM input (row strides in
+  // bytes ld8_h / ld8_o / ld8_i by the input), its four per-call scales and
+  // the partial maxima of the quantisation
+  uint8_t* q8;
+  int ld8_h, ld8_o, ld8_i;
+  float* scales;
+  float* amax;
   size_t total;
 };
 
-Workspace carve(const mhe_config& c, int seq, char* base) {
+Workspace carve(const mhe_config& c, int seq, char* base, bool fp8 = false) {
   const size_t S = static_cast<size_t>(seq);
   const size_t sp = static_cast<size_t>(mhe::seq_pad(seq));
   const size_t D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads;
@@ -123,8 +144,27 @@ Workspace carve(const mhe_config& c, int seq, char* base) {
   w.cnt = reinterpret_cast<int32_t*>(take(4));
   w.partial_bytes = mhe::gemm_partial_bytes();
   w.partial = reinterpret_cast<float*>(take(w.partial_bytes));
+  if (fp8) {
+    w.ld8_h = c.hidden + kActPad;
+    w.ld8_o = c.n_heads * c.head_dim + kActPad;
+    w.ld8_i = c.intermediate + kActPad;
+    w.q8 = reinterpret_cast<uint8_t*>(take(S * std::max({w.ld8_h, w.ld8_o, w.ld8_i})));
+    w.scales = reinterpret_cast<float*>(take(4 * sizeof(float)));
+    w.amax = reinterpret_cast<float*>(take(mhe::kAmaxParts * sizeof(float)));
+  }
   w.total = off;
   return w;
+}
+
+int32_t check_weights_fp8(const mhe_layer_weights_fp8* w, int layer) {
+  if (!w) return fail(MHE_ERR_NULL, "layer %d weights table is NULL", layer);
+  const void* p[] = {w->ln_in, w->w_qkv, w->s_qkv, w->q_norm, w->k_norm, w->w_o, w->s_o,
+                     w->ln_post, w->w_gate_up, w->s_gate_up, w->w_down, w->s_down};
+  const char* names[] = {"ln_in", "w_qkv", "s_qkv", "q_norm", "k_norm", "w_o", "s_o",
+                         "ln_post", "w_gate_up", "s_gate_up", "w_down", "s_down"};
+  for (int i = 0; i < 12; ++i)
+    if (!p[i]) return fail(MHE_ERR_NULL, "layer %d: %s is NULL", layer, names[i]);
+  return MHE_OK;
 }
 
 int32_t check_weights(const mhe_layer_weights* w, int layer) {
@@ -258,10 +298,165 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights& w, bf16_t* x, co
   });
 }
 
+// Per-tensor E4M3 copy of x [seq, cols] (row stride ldx) into ws.q8 (row
+// stride ldq bytes) with its scale in *scale: partial maxima, then convert.
+int32_t quantize_input(const bf16_t* x, int ldx, int seq, int cols, int ldq, float* scale,
+                       const Workspace& ws, hipStream_t st) {
+  return traced(MHE_STEP_QUANTIZE, st, "fp8 quantize", [&] {
+    const int parts = mhe::amax_parts(seq);
+    hipError_t e = mhe::launch_amax(x, ldx, seq, cols, ws.amax, parts, st);
+    if (e != hipSuccess) return e;
+    return mhe::launch_quantize_fp8(x, ldx, seq, cols, ws.amax, parts, ws.q8, ldq, scale, st);
+  });
+}
+
+// The decoder layer with its four linears in FP8 (weights quantised
+// beforehand, activations here): the launch sequence of run_layer with a
+// quantisation before each GEMM.
+int32_t run_layer(const mhe_config& c, const mhe_layer_weights_fp8& w, bf16_t* x, const int32_t* pos,
+                  int seq, const Workspace& ws, hipStream_t st) {
+  const int H = c.hidden, D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, I = c.intermediate;
+  const int qw = Hq * D, qkvw = qw + 2 * Hkv * D;
+  const uint8_t* wgu = static_cast<const uint8_t*>(w.w_gate_up);
+  int32_t rc;
+  if ((rc = traced(MHE_STEP_INPUT_NORM, st, "input rmsnorm", [&] {
+         return mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_in), ws.hn, ws.ld_h, seq, H,
+                                    c.rms_eps, st);
+       })))
+    return rc;
+  if ((rc = quantize_input(ws.hn, ws.ld_h, seq, H, ws.ld8_h, ws.scales + 0, ws, st))) return rc;
+  const mhe::F8Segments qkv{{static_cast<const uint8_t*>(w.w_qkv), nullptr, nullptr}, {qkvw, 0, 0},
+                            {w.s_qkv, nullptr, nullptr}, 1};
+  if ((rc = traced(MHE_STEP_QKV, st, "qkv projection", [&] {
+         return mhe::launch_gemm_fp8(mhe::Epilogue::kStore, ws.q8, ws.ld8_h, ws.scales + 0, qkv, H, ws.qkv,
+                                     qkvw, nullptr, seq, qkvw, H, ws.partial, ws.partial_bytes, st);
+       })))
+    return rc;
+  const mhe::RopeParams rp{Hq, Hkv, D, c.rms_eps, c.rope_theta,
+                           {c.mrope_section[0], c.mrope_section[1], c.mrope_section[2]}};
+  if ((rc = traced(MHE_STEP_QK_ROPE, st, "q/k norm + rotary", [&] {
+         return mhe::launch_qk_norm_rope(rp, ws.qkv, static_cast<const bf16_t*>(w.q_norm),
+                                         static_cast<const bf16_t*>(w.k_norm), pos, seq, ws.qn, ws.kn,
+                                         ws.vt, st);
+       })))
+    return rc;
+  if ((rc = traced(MHE_STEP_ATTENTION, st, "attention", [&] {
+         return mhe::launch_attention(ws.qn, ws.kn, ws.vt, ws.ao, ws.ld_o, seq, Hq, Hkv, D, st);
+       })))
+    return rc;
+  if ((rc = quantize_input(ws.ao, ws.ld_o, seq, qw, ws.ld8_o, ws.scales + 1, ws, st))) return rc;
+  const mhe::F8Segments wo{{static_cast<const uint8_t*>(w.w_o), nullptr, nullptr}, {H, 0, 0},
+                           {w.s_o, nullptr, nullptr}, 1};
+  if ((rc = traced(MHE_STEP_O_PROJ, st, "o projection", [&] {
+         return mhe::launch_gemm_fp8(mhe::Epilogue::kResidual, ws.q8, ws.ld8_o, ws.scales + 1, wo, qw, x, H,
+                                     x, seq, H, qw, ws.partial, ws.partial_bytes, st);
+       })))
+    return rc;
+  if ((rc = traced(MHE_STEP_POST_NORM, st, "post-attention rmsnorm", [&] {
+         return mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_post), ws.hn, ws.ld_h, seq, H,
+                                    c.rms_eps, st);
+       })))
+    return rc;
+  if ((rc = quantize_input(ws.hn, ws.ld_h, seq, H, ws.ld8_h, ws.scales + 2, ws, st))) return rc;
+  const mhe::F8Segments gu{{wgu, wgu + static_cast<size_t>(I) * H, nullptr}, {I, I, 0},
+                           {w.s_gate_up, w.s_gate_up, nullptr}, 2};
+  if ((rc = traced(MHE_STEP_GATE_UP, st, "gate/up projection", [&] {
+         return mhe::launch_gemm_fp8(mhe::Epilogue::kSwiGLU, ws.q8, ws.ld8_h, ws.scales + 2, gu, H, ws.act,
+                                     ws.ld_i, nullptr, seq, I, H, ws.partial, ws.partial_bytes, st);
+       })))
+    return rc;
+  if ((rc = quantize_input(ws.act, ws.ld_i, seq, I, ws.ld8_i, ws.scales + 3, ws, st))) return rc;
+  const mhe::F8Segments wd{{static_cast<const uint8_t*>(w.w_down), nullptr, nullptr}, {H, 0, 0},
+                           {w.s_down, nullptr, nullptr}, 1};
+  return traced(MHE_STEP_DOWN, st, "down projection", [&] {
+    return mhe::launch_gemm_fp8(mhe::Epilogue::kResidual, ws.q8, ws.ld8_i, ws.scales + 3, wd, I, x, H, x,
+                                seq, H, I, ws.partial, ws.partial_bytes, st);
+  });
+}
+
+int32_t check_weights(const mhe_layer_weights_fp8* w, int layer) { return check_weights_fp8(w, layer); }
+int32_t check_config_for(const mhe_layer_weights*, const mhe_config* c) { return check_config(c); }
+int32_t check_config_for(const mhe_layer_weights_fp8*, const mhe_config* c) { return check_config_fp8(c); }
+constexpr bool is_fp8(const mhe_layer_weights*) { return false; }
+constexpr bool is_fp8(const mhe_layer_weights_fp8*) { return true; }
+
 bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   const char* pa = static_cast<const char*>(a);
   const char* pb = static_cast<const char*>(b);
   return pa < pb + bn && pb < pa + an;
+}
+
+// mhe_layer_forward / mhe_layer_forward_fp8.
+template <class W>
+int32_t layer_forward_impl(const mhe_config* cfg, const W* w, void* hidden, const int32_t* positions,
+                           int32_t seq, void* workspace, size_t workspace_bytes, void* stream) {
+  constexpr bool fp8 = is_fp8(static_cast<const W*>(nullptr));
+  int32_t rc;
+  if ((rc = check_config_for(w, cfg))) return rc;
+  if ((rc = check_weights(w, 0))) return rc;
+  if (!hidden) return fail(MHE_ERR_NULL, "hidden is NULL");
+  if (!positions) return fail(MHE_ERR_NULL, "positions is NULL");
+  if ((rc = check_seq(seq))) return rc;
+  const Workspace need = carve(*cfg, seq, nullptr, fp8);
+  if ((rc = check_ws(workspace, workspace_bytes, need.total))) return rc;
+  const Workspace ws = carve(*cfg, seq, static_cast<char*>(workspace), fp8);
+  return run_layer(*cfg, *w, static_cast<bf16_t*>(hidden), positions, seq, ws,
+                   static_cast<hipStream_t>(stream));
+}
+
+// mhe_encode / mhe_encode_fp8 (W: the layer weight table type).
+template <class W>
+int32_t encode_impl(const mhe_config* cfg, const W* layers, int32_t n_layers,
+                    const void* inputs_embeds, const int32_t* positions,
+                    const uint8_t* visual_mask, int32_t n_vis, const void* const* deepstack,
+                    int32_t n_ds, int32_t seq, void* out, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  constexpr bool fp8 = is_fp8(static_cast<const W*>(nullptr));
+  int32_t rc;
+  if ((rc = check_config_for(layers, cfg))) return rc;
+  if ((rc = check_seq(seq))) return rc;
+  if (n_layers < 0) return fail(MHE_ERR_SHAPE, "n_layers %d < 0", n_layers);
+  if (n_ds < 0) return fail(MHE_ERR_SHAPE, "n_ds %d < 0", n_ds);
+  if (n_vis < 0 || n_vis > seq) return fail(MHE_ERR_SHAPE, "n_vis %d out of range [0, %d]", n_vis, seq);
+  if (!inputs_embeds || !out) return fail(MHE_ERR_NULL, "inputs_embeds and out are required");
+  if (!positions) return fail(MHE_ERR_NULL, "positions is NULL");
+  if (n_layers > 0 && !layers) return fail(MHE_ERR_NULL, "layers is NULL");
+  for (int l = 0; l < n_layers; ++l)
+    if ((rc = check_weights(&layers[l], l))) return rc;
+  const int used_ds = (n_vis > 0) ? (n_ds < n_layers ? n_ds : n_layers) : 0;
+  if (used_ds > 0) {
+    if (!visual_mask) return fail(MHE_ERR_NULL, "visual_mask is NULL with DeepStack levels");
+    if (!deepstack) return fail(MHE_ERR_NULL, "deepstack table is NULL");
+    for (int l = 0; l < used_ds; ++l)
+      if (!deepstack[l]) return fail(MHE_ERR_NULL, "deepstack[%d] is NULL", l);
+  }
+  const size_t act_bytes = static_cast<size_t>(seq) * cfg->hidden * 2;
+  if (overlaps(out, act_bytes, inputs_embeds, act_bytes))
+    return fail(MHE_ERR_SHAPE, "out overlaps inputs_embeds");
+  const Workspace need = carve(*cfg, seq, nullptr, fp8);
+  if ((rc = check_ws(workspace, workspace_bytes, need.total))) return rc;
+  if (overlaps(out, act_bytes, workspace, need.total))
+    return fail(MHE_ERR_SHAPE, "out overlaps the workspace");
+
+  const Workspace ws = carve(*cfg, seq, static_cast<char*>(workspace), fp8);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  bf16_t* x = static_cast<bf16_t*>(out);
+  if ((rc = hip_check(hipMemcpyAsync(x, inputs_embeds, act_bytes, hipMemcpyDeviceToDevice, st),
+                      "copy inputs_embeds")))
+    return rc;
+  if (used_ds > 0 &&
+      (rc = hip_check(mhe::launch_visual_index(visual_mask, seq, n_vis, ws.vis, ws.cnt, st),
+                      "visual index")))
+    return rc;
+  for (int l = 0; l < n_layers; ++l) {
+    if ((rc = run_layer(*cfg, layers[l], x, positions, seq, ws, st))) return rc;
+    if (l < used_ds && (rc = traced(MHE_STEP_DEEPSTACK, st, "deepstack add", [&] {
+                          return mhe::launch_deepstack_add(x, cfg->hidden, ws.vis, n_vis,
+                                                           static_cast<const bf16_t*>(deepstack[l]), st);
+                        })))
+      return rc;
+  }
+  return MHE_OK;
 }
 
 }  // namespace
@@ -326,17 +521,18 @@ size_t mhe_workspace_bytes(const mhe_config* cfg, int32_t seq) {
 int32_t mhe_layer_forward(const mhe_config* cfg, const mhe_layer_weights* w, void* hidden,
                           const int32_t* positions, int32_t seq, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  int32_t rc;
-  if ((rc = check_config(cfg))) return rc;
-  if ((rc = check_weights(w, 0))) return rc;
-  if (!hidden) return fail(MHE_ERR_NULL, "hidden is NULL");
-  if (!positions) return fail(MHE_ERR_NULL, "positions is NULL");
-  if ((rc = check_seq(seq))) return rc;
-  const Workspace need = carve(*cfg, seq, nullptr);
-  if ((rc = check_ws(workspace, workspace_bytes, need.total))) return rc;
-  const Workspace ws = carve(*cfg, seq, static_cast<char*>(workspace));
-  return run_layer(*cfg, *w, static_cast<bf16_t*>(hidden), positions, seq, ws,
-                   static_cast<hipStream_t>(stream));
+  return layer_forward_impl(cfg, w, hidden, positions, seq, workspace, workspace_bytes, stream);
+}
+
+size_t mhe_workspace_bytes_fp8(const mhe_config* cfg, int32_t seq) {
+  if (check_config_fp8(cfg) || check_seq(seq)) return 0;
+  return carve(*cfg, seq, nullptr, true).total;
+}
+
+int32_t mhe_layer_forward_fp8(const mhe_config* cfg, const mhe_layer_weights_fp8* w, void* hidden,
+                              const int32_t* positions, int32_t seq, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return layer_forward_impl(cfg, w, hidden, positions, seq, workspace, workspace_bytes, stream);
 }
 
 int32_t mhe_deepstack_inject(void* hidden, int32_t seq, int32_t hidden_dim,
@@ -365,51 +561,17 @@ int32_t mhe_encode(const mhe_config* cfg, const mhe_layer_weights* layers, int32
                    const uint8_t* visual_mask, int32_t n_vis, const void* const* deepstack,
                    int32_t n_ds, int32_t seq, void* out, void* workspace, size_t workspace_bytes,
                    void* stream) {
-  int32_t rc;
-  if ((rc = check_config(cfg))) return rc;
-  if ((rc = check_seq(seq))) return rc;
-  if (n_layers < 0) return fail(MHE_ERR_SHAPE, "n_layers %d < 0", n_layers);
-  if (n_ds < 0) return fail(MHE_ERR_SHAPE, "n_ds %d < 0", n_ds);
-  if (n_vis < 0 || n_vis > seq) return fail(MHE_ERR_SHAPE, "n_vis %d out of range [0, %d]", n_vis, seq);
-  if (!inputs_embeds || !out) return fail(MHE_ERR_NULL, "inputs_embeds and out are required");
-  if (!positions) return fail(MHE_ERR_NULL, "positions is NULL");
-  if (n_layers > 0 && !layers) return fail(MHE_ERR_NULL, "layers is NULL");
-  for (int l = 0; l < n_layers; ++l)
-    if ((rc = check_weights(&layers[l], l))) return rc;
-  const int used_ds = (n_vis > 0) ? (n_ds < n_layers ? n_ds : n_layers) : 0;
-  if (used_ds > 0) {
-    if (!visual_mask) return fail(MHE_ERR_NULL, "visual_mask is NULL with DeepStack levels");
-    if (!deepstack) return fail(MHE_ERR_NULL, "deepstack table is NULL");
-    for (int l = 0; l < used_ds; ++l)
-      if (!deepstack[l]) return fail(MHE_ERR_NULL, "deepstack[%d] is NULL", l);
-  }
-  const size_t act_bytes = static_cast<size_t>(seq) * cfg->hidden * 2;
-  if (overlaps(out, act_bytes, inputs_embeds, act_bytes))
-    return fail(MHE_ERR_SHAPE, "out overlaps inputs_embeds");
-  const Workspace need = carve(*cfg, seq, nullptr);
-  if ((rc = check_ws(workspace, workspace_bytes, need.total))) return rc;
-  if (overlaps(out, act_bytes, workspace, need.total))
-    return fail(MHE_ERR_SHAPE, "out overlaps the workspace");
+  return encode_impl(cfg, layers, n_layers, inputs_embeds, positions, visual_mask, n_vis, deepstack,
+                     n_ds, seq, out, workspace, workspace_bytes, stream);
+}
 
-  const Workspace ws = carve(*cfg, seq, static_cast<char*>(workspace));
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  bf16_t* x = static_cast<bf16_t*>(out);
-  if ((rc = hip_check(hipMemcpyAsync(x, inputs_embeds, act_bytes, hipMemcpyDeviceToDevice, st),
-                      "copy inputs_embeds")))
-    return rc;
-  if (used_ds > 0 &&
-      (rc = hip_check(mhe::launch_visual_index(visual_mask, seq, n_vis, ws.vis, ws.cnt, st),
-                      "visual index")))
-    return rc;
-  for (int l = 0; l < n_layers; ++l) {
-    if ((rc = run_layer(*cfg, layers[l], x, positions, seq, ws, st))) return rc;
-    if (l < used_ds && (rc = traced(MHE_STEP_DEEPSTACK, st, "deepstack add", [&] {
-                          return mhe::launch_deepstack_add(x, cfg->hidden, ws.vis, n_vis,
-                                                           static_cast<const bf16_t*>(deepstack[l]), st);
-                        })))
-      return rc;
-  }
-  return MHE_OK;
+int32_t mhe_encode_fp8(const mhe_config* cfg, const mhe_layer_weights_fp8* layers, int32_t n_layers,
+                       const void* inputs_embeds, const int32_t* positions,
+                       const uint8_t* visual_mask, int32_t n_vis, const void* const* deepstack,
+                       int32_t n_ds, int32_t seq, void* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return encode_impl(cfg, layers, n_layers, inputs_embeds, positions, visual_mask, n_vis, deepstack,
+                     n_ds, seq, out, workspace, workspace_bytes, stream);
 }
 
 int32_t mhe_count_visual(const uint8_t* visual_mask, int32_t seq, int32_t* count_host,
@@ -493,6 +655,96 @@ int32_t mhe_linear_swiglu(const void* a, const void* w_gate, const void* w_up, v
                                     static_cast<float*>(workspace), workspace ? workspace_bytes : 0,
                                     static_cast<hipStream_t>(stream)),
                    "linear_swiglu");
+}
+
+size_t mhe_quantize_fp8_workspace_bytes(void) { return mhe::kAmaxParts * sizeof(float); }
+
+int32_t mhe_quantize_fp8(const void* const* parts, const int32_t* part_rows, int32_t n_parts,
+                         int32_t cols, void* q, float* scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!parts || !part_rows || !q || !scale) return fail(MHE_ERR_NULL, "parts, part_rows, q and scale are required");
+  if (n_parts < 1 || n_parts > 8) return fail(MHE_ERR_SHAPE, "n_parts %d out of range [1, 8]", n_parts);
+  if (cols <= 0 || cols % 8 != 0) return fail(MHE_ERR_SHAPE, "cols %d must be a positive multiple of 8", cols);
+  int64_t rows = 0;
+  for (int i = 0; i < n_parts; ++i) {
+    if (!parts[i]) return fail(MHE_ERR_NULL, "parts[%d] is NULL", i);
+    if (part_rows[i] <= 0) return fail(MHE_ERR_SHAPE, "part_rows[%d] = %d must be > 0", i, part_rows[i]);
+    rows += part_rows[i];
+  }
+  if (rows * cols > (int64_t(1) << 40)) return fail(MHE_ERR_SHAPE, "tensor too large");
+  int32_t rc;
+  if ((rc = check_ws(workspace, workspace_bytes, mhe_quantize_fp8_workspace_bytes()))) return rc;
+  for (int i = 0; i < n_parts; ++i)
+    if (overlaps(q, static_cast<size_t>(rows) * cols, parts[i], static_cast<size_t>(part_rows[i]) * cols * 2))
+      return fail(MHE_ERR_SHAPE, "q overlaps parts[%d]", i);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* partial = static_cast<float*>(workspace);
+  // every part gets its share of the partial maxima; one scale over all parts
+  int offs[9] = {0};
+  for (int i = 0; i < n_parts; ++i)
+    offs[i + 1] = offs[i] + std::max(1, std::min(mhe::amax_parts(part_rows[i]), mhe::kAmaxParts / n_parts));
+  for (int i = 0; i < n_parts; ++i)
+    if ((rc = hip_check(mhe::launch_amax(static_cast<const bf16_t*>(parts[i]), cols, part_rows[i], cols,
+                                         partial + offs[i], offs[i + 1] - offs[i], st),
+                        "fp8 amax")))
+      return rc;
+  uint8_t* dst = static_cast<uint8_t*>(q);
+  for (int i = 0; i < n_parts; ++i) {
+    if ((rc = hip_check(mhe::launch_quantize_fp8(static_cast<const bf16_t*>(parts[i]), cols, part_rows[i],
+                                                 cols, partial, offs[n_parts], dst, cols, scale, st),
+                        "fp8 quantize")))
+      return rc;
+    dst += static_cast<size_t>(part_rows[i]) * cols;
+  }
+  return MHE_OK;
+}
+
+int32_t mhe_linear_fp8(const void* a, const float* scale_a, const void* w, const float* scale_w,
+                       void* c, const void* residual, int32_t m, int32_t n, int32_t k,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if (!a || !scale_a || !w || !scale_w || !c) return fail(MHE_ERR_NULL, "a, scale_a, w, scale_w and c are required");
+  if (m <= 0 || n <= 0 || k <= 0) return fail(MHE_ERR_SHAPE, "m, n, k must be > 0");
+  if (!mhe::gemm_fp8_supported(n, k))
+    return fail(MHE_ERR_UNSUPPORTED, "needs n %% 32 == 0 and k %% 128 == 0 (n=%d, k=%d)", n, k);
+  const size_t cb = static_cast<size_t>(m) * n * 2;
+  if (overlaps(c, cb, a, static_cast<size_t>(m) * k) || overlaps(c, cb, w, static_cast<size_t>(n) * k))
+    return fail(MHE_ERR_SHAPE, "c overlaps an operand");
+  if (residual && residual != c && overlaps(c, cb, residual, cb))
+    return fail(MHE_ERR_SHAPE, "residual partially overlaps c");
+  int32_t rc;
+  if ((rc = check_gemm_ws(workspace, workspace_bytes))) return rc;
+  if (workspace && (overlaps(workspace, workspace_bytes, c, cb) || overlaps(workspace, workspace_bytes, a, static_cast<size_t>(m) * k)))
+    return fail(MHE_ERR_SHAPE, "workspace overlaps an operand");
+  mhe::F8Segments b{{static_cast<const uint8_t*>(w), nullptr, nullptr}, {n, 0, 0}, {scale_w, nullptr, nullptr}, 1};
+  return hip_check(mhe::launch_gemm_fp8(residual ? mhe::Epilogue::kResidual : mhe::Epilogue::kStore,
+                                        static_cast<const uint8_t*>(a), k, scale_a, b, k,
+                                        static_cast<bf16_t*>(c), n, static_cast<const bf16_t*>(residual), m,
+                                        n, k, static_cast<float*>(workspace), workspace ? workspace_bytes : 0,
+                                        static_cast<hipStream_t>(stream)),
+                   "linear_fp8");
+}
+
+int32_t mhe_linear_swiglu_fp8(const void* a, const float* scale_a, const void* w_gate_up,
+                              const float* scale_w, void* c, int32_t m, int32_t n, int32_t k,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!a || !scale_a || !w_gate_up || !scale_w || !c)
+    return fail(MHE_ERR_NULL, "a, scale_a, w_gate_up, scale_w and c are required");
+  if (m <= 0 || n <= 0 || k <= 0) return fail(MHE_ERR_SHAPE, "m, n, k must be > 0");
+  if (!mhe::gemm_fp8_supported(n, k))
+    return fail(MHE_ERR_UNSUPPORTED, "needs n %% 32 == 0 and k %% 128 == 0 (n=%d, k=%d)", n, k);
+  const size_t cb = static_cast<size_t>(m) * n * 2;
+  if (overlaps(c, cb, a, static_cast<size_t>(m) * k)) return fail(MHE_ERR_SHAPE, "c overlaps a");
+  int32_t rc;
+  if ((rc = check_gemm_ws(workspace, workspace_bytes))) return rc;
+  if (workspace && overlaps(workspace, workspace_bytes, c, cb))
+    return fail(MHE_ERR_SHAPE, "workspace overlaps c");
+  const uint8_t* wg = static_cast<const uint8_t*>(w_gate_up);
+  mhe::F8Segments b{{wg, wg + static_cast<size_t>(n) * k, nullptr}, {n, n, 0}, {scale_w, scale_w, nullptr}, 2};
+  return hip_check(mhe::launch_gemm_fp8(mhe::Epilogue::kSwiGLU, static_cast<const uint8_t*>(a), k, scale_a,
+                                        b, k, static_cast<bf16_t*>(c), n, nullptr, m, n, k,
+                                        static_cast<float*>(workspace), workspace ? workspace_bytes : 0,
+                                        static_cast<hipStream_t>(stream)),
+                   "linear_swiglu_fp8");
 }
 
 int32_t mhe_qk_norm_rope(const mhe_config* cfg, const void* qkv, const void* q_norm,

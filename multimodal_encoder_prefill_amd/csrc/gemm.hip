@@ -48,12 +48,18 @@ constexpr int kThreads = 256;
 constexpr int kGroupM = 8;  // m tiles per ordering group
 constexpr int kXcds = 8;
 
-constexpr int BK = 64;  // k elements per pipeline step (one 128-byte row piece)
+constexpr int BK = 64;  // bf16 k elements per pipeline step (one 128-byte row piece)
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 struct GemmArgs {
-  const bf16_t* a;
-  const bf16_t* bptr[3];
+  const void* a;        // bf16 or (FP8 kernels) E4M3 bytes
+  const void* bptr[3];
   int brows[3];
+  // FP8 kernels: per-tensor scales (device; element 0 of each is the scale)
+  // of A and of the B segments, applied to the fp32 sums before the epilogue
+  const float* scale_a;
+  const float* scale_b[3];
   bf16_t* c;
   const bf16_t* r;
   const bf16_t* bias;
@@ -86,7 +92,7 @@ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1
 
 // Buffer resource over [p, p + bytes); the pointer and size are wave-uniform
 // and are pinned to scalar registers so loads need no per-lane descriptor.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const bf16_t* p, int bytes) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const void* p, int bytes) {
   const uint64_t u = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
@@ -123,6 +129,16 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.f + erff(x * 0.7071067811865476f));
 }
 
+// FP8 scale of the products in output column n: scale_a times the scale of
+// the weight segment that holds row n (segments are multiples of 32 rows, so
+// four consecutive columns share it).
+__device__ __forceinline__ float f8_scale(const GemmArgs& args, int n) {
+  const float sb = n < args.brows[0] ? args.scale_b[0][0]
+                   : n < args.brows[0] + args.brows[1] ? args.scale_b[1][0]
+                                                       : args.scale_b[2][0];
+  return args.scale_a[0] * sb;
+}
+
 // Non-SwiGLU epilogue of four consecutive outputs (columns n..n+3 of the row
 // at element offset `off`), rounded to bf16 once.
 template <int EPI>
@@ -152,9 +168,15 @@ __device__ __forceinline__ u32x2 finish4(float* o, const GemmArgs& args, int n, 
   return pk;
 }
 
-template <int EPI>
+// FP8: operands are E4M3 bytes, a pipeline step covers 128 k elements (the
+// same 128-byte row pieces, LDS layout and loads as bf16) in two substeps of
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales), and the sums are
+// multiplied by scale_a * scale_b before the epilogue.
+template <int EPI, bool F8>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) {
-  constexpr int kTileElems = BM * BK;           // one operand, one stage
+  constexpr int ES = F8 ? 1 : 2;                // bytes per element
+  constexpr int KSTEP = 128 / ES;               // k elements per pipeline step
+  constexpr int kTileElems = BM * BK;           // one operand, one stage (bf16 units)
   constexpr int kRowBytes = BK * 2;
   constexpr int kChunks = BK / 8;               // 16-byte chunks per row
   constexpr int kRowsPerBlk = 4096 / kRowBytes; // rows one load instruction of the 4 waves covers
@@ -190,19 +212,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   tile_coords(args.tile_begin + unit / args.ksplit, args.tiles_m, args.tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM;
   const int kt_begin = (unit % args.ksplit) * args.kt_per_split;
-  const int nk = min(kt_begin + args.kt_per_split, K / BK) - kt_begin;  // k-steps of this unit
+  const int nk = min(kt_begin + args.kt_per_split, K / KSTEP) - kt_begin;  // k-steps of this unit
 
   // ---- buffer resources over row blocks of kRowsPerBlk rows ----
   // A rows m0 + row0 .. (row0 + rows) of the tile
   auto a_block = [&](int row0, int rows) {
     const int r = m0 + row0;
     const int nrows = max(0, min(rows, M - r));
-    return scalar_rsrc(args.a + static_cast<size_t>(min(r, M - 1)) * lda,
-                       nrows > 0 ? ((nrows - 1) * lda + K) * 2 : 0);
+    return scalar_rsrc(static_cast<const char*>(args.a) + static_cast<size_t>(min(r, M - 1)) * lda * ES,
+                       nrows > 0 ? ((nrows - 1) * lda + K) * ES : 0);
   };
   // B row block i of the tile
   auto b_block = [&](int i) {
-    const bf16_t* base;
+    const void* base;
     int v, avail;
     if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
       // virtual B rows of the tile, in 32-row slots s: wave half s/4 covers
@@ -230,8 +252,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       }
     }
     const int brows = max(0, min(kRowsPerBlk, avail));
-    return scalar_rsrc(base + static_cast<size_t>(v) * ldb,
-                       brows > 0 ? ((brows - 1) * ldb + K) * 2 : 0);
+    return scalar_rsrc(static_cast<const char*>(base) + static_cast<size_t>(v) * ldb * ES,
+                       brows > 0 ? ((brows - 1) * ldb + K) * ES : 0);
   };
   __amdgpu_buffer_rsrc_t a_rsrc[kBlks], b_rsrc[kBlks];
 #pragma unroll
@@ -258,8 +280,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   //      (its zeros land in a stage that is no longer read). ----
   const int dma_row = wave * (1024 / kRowBytes) + lane / kChunks;
   const int dma_chunk = ((lane % kChunks) ^ swz(dma_row)) * 16;
-  const int dma_voff_a = dma_row * lda * 2 + dma_chunk;
-  const int dma_voff_b = dma_row * ldb * 2 + dma_chunk;
+  const int dma_voff_a = dma_row * lda * ES + dma_chunk;
+  const int dma_voff_b = dma_row * ldb * ES + dma_chunk;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // ---- L2 warm-up. The tiles running together on one XCD share operand
   //      blocks (tile_coords: 8 m-tiles x 4 n-tiles), so without help the
@@ -270,10 +292,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   //      8-row load per wavefront. (Activation rows are hits in the last-level
   //      cache and gain nothing from this.) ----
   const __amdgpu_buffer_rsrc_t warm_b = b_block((tile_m & 7) * (32 / kRowsPerBlk));
-  const int warm_voff = (8 * wave + lane / 8) * ldb * 2 + (lane % 8) * 16;
+  const int warm_voff = (8 * wave + lane / 8) * ldb * ES + (lane % 8) * 16;
   auto issue_warm = [&](int kt) {
 #if __HIP_DEVICE_COMPILE__
-    const int soff = (kt_begin + kt) * BK * 2;
+    const int soff = (kt_begin + kt) * kRowBytes;
     bf16_t* scratch = smem + 4 * kTileElems + wave_u * 512;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         kt < nk ? warm_b : null_rsrc, (__attribute__((address_space(3))) void*)scratch, 16,
@@ -287,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   auto issue_load = [&](int kt, int stage, int l) {
 #if __HIP_DEVICE_COMPILE__  // the LDS-DMA builtin exists only in the device pass
     const bool live = kt < nk;
-    const int soff = (kt_begin + kt) * BK * 2;
+    const int soff = (kt_begin + kt) * kRowBytes;
     const int i = l >> 1;
     bf16_t* dst = ((l & 1) ? Bs : As) + stage * kTileElems + wave_u * 512 + i * kRowsPerBlk * BK;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -303,22 +325,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     for (int l = 2 * b0; l < 2 * b1; ++l) issue_load(kt, stage, l);
   };
 
-  // ---- LDS -> registers and MFMA: substep s of a k-step covers k 16s..16s+15;
-  //      operands are double-buffered in two register slots ----
+  // ---- LDS -> registers and MFMA: substep s of a k-step covers the row
+  //      bytes 32s..32s+31 (bf16: 16 k) or 64s..64s+63 (FP8: 64 k); operands
+  //      are double-buffered in two register slots. For FP8 a lane holds 32
+  //      bytes of its row, chunks 4s + 2 lhalf and the next one: any
+  //      assignment of k to the operand bytes gives the same sum as long as
+  //      both operands use it. ----
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
   const int lswz = swz(lrow);
   const int a_base = (wm * 128 + lrow) * BK;  // activation rows (MFMA B operand)
   const int b_base = (wn * 128 + lrow) * BK;  // weight rows (MFMA A operand)
   bf16x8 wop[2][4], xop[2][4];
+  i32x8 wop8[2][4], xop8[2][4];
   auto fetch = [&](int stage, int s, int slot) {
     const bf16_t* as = As + stage * kTileElems;
     const bf16_t* bs = Bs + stage * kTileElems;
-    const int chunk = ((2 * s + lhalf) ^ lswz) << 3;
+    if constexpr (F8) {
+      const int c0 = ((4 * s + 2 * lhalf) ^ lswz) << 3;
+      const int c1 = ((4 * s + 2 * lhalf + 1) ^ lswz) << 3;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + chunk));
-      xop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + chunk));
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 w0 = *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + c0);
+        const u32x4 w1 = *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + c1);
+        const u32x4 x0 = *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + c0);
+        const u32x4 x1 = *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + c1);
+        wop8[slot][i] = __builtin_bit_cast(i32x8, __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7));
+        xop8[slot][i] = __builtin_bit_cast(i32x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    } else {
+      const int chunk = ((2 * s + lhalf) ^ lswz) << 3;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + chunk));
+        xop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + chunk));
+      }
     }
   };
   // blocks in order of max(i, j), so the MFMAs that need the operands read
@@ -328,7 +369,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     const int d = q < 1 ? 0 : q < 4 ? 1 : q < 9 ? 2 : 3;
     const int e = q - d * d;
     const int i = e <= d ? e : d, j = e <= d ? d : 2 * d - e;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[slot][i], xop[slot][j], acc[i][j], 0, 0, 0);
+    if constexpr (F8)
+      // E4M3 operands (format 0), block scales 127 (= 2^0)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop8[slot][i], xop8[slot][j], acc[i][j], 0, 0,
+                                                                  0, 127, 0, 127);
+    else
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[slot][i], xop[slot][j], acc[i][j], 0, 0, 0);
   };
   auto mfma = [&](int slot) {
 #pragma unroll
@@ -355,7 +401,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   //      registers: the MFMAs of that substep cover the reads of the next
   //      k-step's first operands, and the stage just finished is refilled
   //      from there on. ----
-  if (nk > 0) {
+  if constexpr (F8) {
+    // Two substeps per k-step. The barrier sits before substep 1; all loads
+    // of k-step kt+2 go out during substep 1 of kt (one per MFMA, the same
+    // issue rate as bf16), so a whole substep separates the last of them
+    // from the wait that needs them.
+    if (nk > 0) {
+      issue_dma(0, 0, 0, kBlks);
+      issue_dma(1, 1, 0, kBlks);
+      wait_vmcnt<2 * kBlks>();
+      lds_barrier();
+      fetch(0, 0, 0);
+      for (int kt = 0; kt < nk; ++kt) {
+        const int st = kt & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(st, 1, 1);
+        issue_warm(kt + kWarm);
+        mfma(0);
+        __builtin_amdgcn_sched_barrier(0);
+        // k-step kt+1 is complete in LDS and no wavefront reads stage st any more
+        wait_vmcnt<1>();
+        lds_barrier();
+        fetch(st ^ 1, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_loads(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, 2 * kBlks>());
+      }
+      wait_vmcnt<0>();
+      lds_barrier();
+    }
+  } else if (nk > 0) {
     issue_dma(0, 0, 0, kBlks);
     wait_vmcnt<0>();
     lds_barrier();
@@ -409,6 +483,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 
   // ---- epilogue: lane holds column m = lrow of each 32x32 block and rows
   //      n = 8 g + 4 lhalf + e (e < 4) for the four groups g ----
+  float sg = 1.f, su = 1.f;  // FP8 SwiGLU: scales of the gate and up products
+  if constexpr (F8 && EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+    sg = args.scale_a[0] * args.scale_b[0][0];
+    su = args.scale_a[0] * args.scale_b[1][0];
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + wm * 128 + j * 32 + lrow;
@@ -423,8 +502,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float gt = acc[i][j][4 * g + e];
-            const float up = acc[i + 2][j][4 * g + e];
+            const float gt = acc[i][j][4 * g + e] * sg;
+            const float up = acc[i + 2][j][4 * g + e] * su;
             o[e] = gt / (1.f + __expf(-gt)) * up;
           }
           u32x2 pk;
@@ -438,12 +517,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       for (int i = 0; i < 4; ++i) {
         const int nb = tile_n * BN + wn * 128 + i * 32;
         if (nb >= N) continue;
+        const float sc = F8 ? f8_scale(args, nb) : 1.f;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const size_t off = static_cast<size_t>(m) * args.ldc + nb + 8 * g + 4 * lhalf;
           float o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * g + e];
+          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * g + e] * sc;
           *reinterpret_cast<u32x2*>(args.c + off) = finish4<EPI>(o, args, nb + 8 * g + 4 * lhalf, off);
         }
       }
@@ -454,7 +534,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 // Sums the ksplit partial tiles of each split tile in a fixed order and
 // applies the epilogue. Block (t, y) handles rows 4y..4y+3 of split tile t;
 // each thread 4 consecutive virtual columns.
-template <int EPI>
+template <int EPI, bool F8>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args) {
   const int t = blockIdx.x;
   const int ml = blockIdx.y * 4 + (threadIdx.x >> 6);
@@ -480,10 +560,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args)
     for (int sidx = 1; sidx < args.ksplit; ++sidx)
       upsum += *reinterpret_cast<const f32x4*>(src + 64 + static_cast<size_t>(sidx) * BM * BN);
     n = tile_n * (BN / 2) + (vn >> 7) * 64 + slot * 32 + (vn & 31);
+    if constexpr (F8) {
+      sum *= args.scale_a[0] * args.scale_b[0][0];
+      upsum *= args.scale_a[0] * args.scale_b[1][0];
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = sum[e] / (1.f + __expf(-sum[e])) * upsum[e];
   } else {
     n = tile_n * BN + vn;
+    if constexpr (F8) {
+      if (n < N) sum *= f8_scale(args, n);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = sum[e];
   }
@@ -499,18 +586,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args)
   }
 }
 
-template <int EPI>
+template <int EPI, bool F8>
 hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
   constexpr size_t smem = static_cast<size_t>(2) * 2 * BM * BK * sizeof(bf16_t) + 4096;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_kernel<EPI>),
+        reinterpret_cast<const void*>(&gemm_kernel<EPI, F8>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<EPI>), dim3(grid), dim3(kThreads), smem,
+  hipLaunchKernelGGL((gemm_kernel<EPI, F8>), dim3(grid), dim3(kThreads), smem,
                      stream, args);
   return hipGetLastError();
 }
@@ -520,6 +607,8 @@ hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
 int gemm_segment_rows() { return 4096 / (BK * 2); }
 
 bool gemm_supported(int n, int k) { return n > 0 && k > 0 && n % 32 == 0 && k % BK == 0; }
+
+bool gemm_fp8_supported(int n, int k) { return n > 0 && k > 0 && n % 32 == 0 && k % (2 * BK) == 0; }
 
 namespace {
 
@@ -531,7 +620,7 @@ int device_cus() {
   return cus;
 }
 
-template <int EPI>
+template <int EPI, bool F8>
 hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t stream) {
   // One workgroup fills a CU (128 KB of LDS), so a launch of T tiles runs in
   // ceil(T / CUs) waves. Full waves run whole tiles; when the last wave would
@@ -539,7 +628,7 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
   // most 4 full waves before it), its R tiles are cut into ksplit k-ranges
   // (ksplit * R <= CUs) whose fp32 partials are summed by a small reduction.
   const int tiles = args.tiles_m * args.tiles_n;
-  const int nk = args.k / BK;
+  const int nk = args.k / (F8 ? 2 * BK : BK);  // k-steps (128 row bytes each)
   static const int cus = device_cus();
   const int rem = tiles % cus;
   int ksplit = 1;
@@ -558,7 +647,7 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
     a.ksplit = 1;
     a.kt_per_split = nk;
     a.partial = nullptr;
-    if ((e = launch_epi<EPI>(a, full, stream)) != hipSuccess) return e;
+    if ((e = launch_epi<EPI, F8>(a, full, stream)) != hipSuccess) return e;
   }
   if (ksplit > 1) {
     GemmArgs a = args;
@@ -567,8 +656,8 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
     a.ksplit = ksplit;
     a.kt_per_split = (nk + ksplit - 1) / ksplit;
     a.partial = partial;
-    if ((e = launch_epi<EPI>(a, a.units, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(splitk_reduce_kernel<EPI>, dim3(rem, BM / 4), dim3(256), 0, stream, a);
+    if ((e = launch_epi<EPI, F8>(a, a.units, stream)) != hipSuccess) return e;
+    hipLaunchKernelGGL((splitk_reduce_kernel<EPI, F8>), dim3(rem, BM / 4), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -578,22 +667,30 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
 
 size_t gemm_partial_bytes() { return static_cast<size_t>(320) * BM * BN * sizeof(float); }
 
-hipError_t launch_gemm(Epilogue epi, const bf16_t* a, int lda, const BSegments& b, int ldb,
-                       bf16_t* c, int ldc, const bf16_t* residual, int m, int n, int k,
-                       float* partial, size_t partial_bytes, hipStream_t stream,
-                       const bf16_t* bias) {
-  if (lda < k || ldb < k || ldc < n || lda % 8 != 0 || ldb % 8 != 0 || ldc % 4 != 0)
+namespace {
+
+// Shared set-up of the bf16 and FP8 launches; es = bytes per operand element.
+hipError_t launch_common(Epilogue epi, bool f8, const void* a, int lda, const float* scale_a,
+                         const void* const* bptr, const int* brows, const float* const* bscale,
+                         int count, int ldb, bf16_t* c, int ldc, const bf16_t* residual, int m,
+                         int n, int k, float* partial, size_t partial_bytes, hipStream_t stream,
+                         const bf16_t* bias) {
+  const int es = f8 ? 1 : 2;
+  if (lda < k || ldb < k || ldc < n || (lda * es) % 16 != 0 || (ldb * es) % 16 != 0 || ldc % 4 != 0)
     return hipErrorInvalidValue;
+  if (count < 1 || count > 3) return hipErrorInvalidValue;
   if (m <= 0) return hipSuccess;
   // a load block never straddles two weight segments
-  if (epi != Epilogue::kSwiGLU && b.count > 1)
-    for (int i = 0; i < b.count; ++i)
-      if (b.rows[i] % gemm_segment_rows() != 0) return hipErrorInvalidValue;
+  if (epi != Epilogue::kSwiGLU && count > 1)
+    for (int i = 0; i < count; ++i)
+      if (brows[i] % gemm_segment_rows() != 0) return hipErrorInvalidValue;
   GemmArgs args{};
   args.a = a;
+  args.scale_a = scale_a;
   for (int i = 0; i < 3; ++i) {
-    args.bptr[i] = i < b.count ? b.ptr[i] : b.ptr[0];
-    args.brows[i] = i < b.count ? b.rows[i] : 0;
+    args.bptr[i] = i < count ? bptr[i] : bptr[0];
+    args.brows[i] = i < count ? brows[i] : 0;
+    args.scale_b[i] = f8 ? (i < count ? bscale[i] : bscale[0]) : nullptr;
   }
   args.c = c;
   args.r = residual;
@@ -607,16 +704,47 @@ hipError_t launch_gemm(Epilogue epi, const bf16_t* a, int lda, const BSegments& 
   args.ldc = ldc;
   args.tiles_m = (m + BM - 1) / BM;
   args.tiles_n = epi == Epilogue::kSwiGLU ? (n + BN / 2 - 1) / (BN / 2) : (n + BN - 1) / BN;
+  if (f8) {
+    switch (epi) {
+      case Epilogue::kStore: return run<0, true>(args, partial, partial_bytes, stream);
+      case Epilogue::kResidual: return run<1, true>(args, partial, partial_bytes, stream);
+      case Epilogue::kSwiGLU: return run<2, true>(args, partial, partial_bytes, stream);
+      default: return hipErrorInvalidValue;  // the biased forms are bf16 only
+    }
+  }
   switch (epi) {
-    case Epilogue::kStore: return run<0>(args, partial, partial_bytes, stream);
-    case Epilogue::kResidual: return run<1>(args, partial, partial_bytes, stream);
-    case Epilogue::kSwiGLU: return run<2>(args, partial, partial_bytes, stream);
-    case Epilogue::kBias: return run<3>(args, partial, partial_bytes, stream);
-    case Epilogue::kBiasResidual: return run<4>(args, partial, partial_bytes, stream);
-    case Epilogue::kBiasGeluTanh: return run<5>(args, partial, partial_bytes, stream);
-    case Epilogue::kBiasGeluErf: return run<6>(args, partial, partial_bytes, stream);
+    case Epilogue::kStore: return run<0, false>(args, partial, partial_bytes, stream);
+    case Epilogue::kResidual: return run<1, false>(args, partial, partial_bytes, stream);
+    case Epilogue::kSwiGLU: return run<2, false>(args, partial, partial_bytes, stream);
+    case Epilogue::kBias: return run<3, false>(args, partial, partial_bytes, stream);
+    case Epilogue::kBiasResidual: return run<4, false>(args, partial, partial_bytes, stream);
+    case Epilogue::kBiasGeluTanh: return run<5, false>(args, partial, partial_bytes, stream);
+    case Epilogue::kBiasGeluErf: return run<6, false>(args, partial, partial_bytes, stream);
   }
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemm(Epilogue epi, const bf16_t* a, int lda, const BSegments& b, int ldb,
+                       bf16_t* c, int ldc, const bf16_t* residual, int m, int n, int k,
+                       float* partial, size_t partial_bytes, hipStream_t stream,
+                       const bf16_t* bias) {
+  const void* bptr[3] = {b.ptr[0], b.ptr[1], b.ptr[2]};
+  return launch_common(epi, false, a, lda, nullptr, bptr, b.rows, nullptr, b.count, ldb, c, ldc,
+                       residual, m, n, k, partial, partial_bytes, stream, bias);
+}
+
+hipError_t launch_gemm_fp8(Epilogue epi, const uint8_t* a, int lda, const float* scale_a,
+                           const F8Segments& b, int ldb, bf16_t* c, int ldc,
+                           const bf16_t* residual, int m, int n, int k, float* partial,
+                           size_t partial_bytes, hipStream_t stream) {
+  if (!scale_a) return hipErrorInvalidValue;
+  for (int i = 0; i < b.count && i < 3; ++i)
+    if (!b.scale[i]) return hipErrorInvalidValue;
+  const void* bptr[3] = {b.ptr[0], b.ptr[1], b.ptr[2]};
+  return launch_common(epi, true, a, lda, scale_a, bptr, b.rows, b.scale, b.count, ldb, c, ldc,
+                       residual, m, n, k, partial, partial_bytes, stream, nullptr);
 }
 
 }  // namespace mhe

@@ -52,6 +52,35 @@ hipError_t launch_gemm(Epilogue epi, const bf16_t* a, int lda, const BSegments& 
                        float* partial, size_t partial_bytes, hipStream_t stream,
                        const bf16_t* bias = nullptr);
 
+// FP8 (E4M3) operands with per-tensor scales: C = epilogue(scale_a * scale_b
+// * A B^T), scale pointers device floats. kStore, kResidual and kSwiGLU only;
+// k % 128 == 0; lda / ldb in bytes, multiples of 16. Segments as BSegments,
+// each with its own scale.
+struct F8Segments {
+  const uint8_t* ptr[3];
+  int rows[3];
+  const float* scale[3];
+  int count;
+};
+bool gemm_fp8_supported(int n, int k);
+hipError_t launch_gemm_fp8(Epilogue epi, const uint8_t* a, int lda, const float* scale_a,
+                           const F8Segments& b, int ldb, bf16_t* c, int ldc,
+                           const bf16_t* residual, int m, int n, int k, float* partial,
+                           size_t partial_bytes, hipStream_t stream);
+
+// quant.hip: per-tensor E4M3 quantisation in two launches. launch_amax writes
+// nparts (<= kAmaxParts; amax_parts(rows) is the usual count) partial maxima
+// of |x|; launch_quantize_fp8 reduces nparts partials (those of several
+// launch_amax calls for a tensor stored in parts) and writes the codes
+// q [rows, ldq] and the scale (max|x| / 448, 1 for an all-zero tensor).
+// cols, ldx, ldq multiples of 8.
+constexpr int kAmaxParts = 1024;
+int amax_parts(int rows);
+hipError_t launch_amax(const bf16_t* x, int ldx, int rows, int cols, float* partial, int nparts,
+                       hipStream_t stream);
+hipError_t launch_quantize_fp8(const bf16_t* x, int ldx, int rows, int cols, const float* partial,
+                               int nparts, uint8_t* q, int ldq, float* scale, hipStream_t stream);
+
 // qk_norm_rope.hip
 struct RopeParams {
   int n_heads, n_kv_heads, head_dim;

@@ -250,6 +250,21 @@ def feature_rows(n: int, hidden: int, seed: int, device="cpu") -> torch.Tensor:
     return torch.randn(n, hidden, generator=g, device=device).to(torch.bfloat16)
 
 
+_FP8_ID = 600
+
+
+def fp8_codes(shape, seed: int, device="cpu", exp_lo: int = 3, exp_hi: int = 12) -> torch.Tensor:
+    """Random E4M3 byte codes (uint8): random sign and mantissa, exponent field
+    uniform in [exp_lo, exp_hi] (magnitudes 2^(exp_lo-7) .. 2^(exp_hi-6)), so
+    the NaN codes never occur."""
+    g = torch.Generator(device=device)
+    g.manual_seed(_BASE_SEED * 1000 + _FP8_ID + seed)
+    sign = torch.randint(0, 2, shape, generator=g, device=device, dtype=torch.int32)
+    exp = torch.randint(exp_lo, exp_hi + 1, shape, generator=g, device=device, dtype=torch.int32)
+    man = torch.randint(0, 8, shape, generator=g, device=device, dtype=torch.int32)
+    return ((sign << 7) | (exp << 3) | man).to(torch.uint8)
+
+
 # ---- vision tower inputs (patch pixels and random-init tower weights) ----
 
 _VISION_ID = 500

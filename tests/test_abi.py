@@ -112,3 +112,30 @@ def test_step_entry_points_reject_before_launch():
     assert lib.mhe_attention(0x10, 0x20, 0x30, 0x40, 0, 8, 1, 128, None) == 2
     assert lib.mhe_deepstack_inject(0x10, 64, 256, 0x20, 65, 0x30, 0x40, 1 << 20, None) == 2
     assert lib.mhe_deepstack_inject(0x10, 64, 256, 0x20, 0, 0x30, 0x40, 1 << 20, None) == 0  # no-op
+
+
+def test_fp8_entry_points_reject_before_launch():
+    lib = b.lib()
+    cfg = b.config_from_dims(synth.FULL)
+    assert b.workspace_bytes_fp8(cfg, 4096) > b.workspace_bytes(cfg, 4096)
+    bad = b.config_from_dims(synth.FULL)
+    bad.hidden = 5120 + 64                        # fine for bf16, not a multiple of 128
+    assert lib.mhe_workspace_bytes(ctypes.byref(bad), 64) > 0
+    assert lib.mhe_workspace_bytes_fp8(ctypes.byref(bad), 64) == 0
+    d = 0x100000
+    # k % 128 != 0, NULL scale, NULL operand
+    assert lib.mhe_linear_fp8(d, d, d, d, d * 8, None, 64, 64, 192, None, 0, None) == 4
+    assert lib.mhe_linear_fp8(d, None, d, d, d * 8, None, 64, 64, 256, None, 0, None) == 1
+    assert lib.mhe_linear_swiglu_fp8(d, d, None, d, d * 8, 64, 64, 256, None, 0, None) == 1
+    parts = (ctypes.c_void_p * 1)(d)
+    rows = (ctypes.c_int32 * 1)(16)
+    assert lib.mhe_quantize_fp8(parts, rows, 0, 64, d * 8, d * 16, 0x10000, 1 << 20, None) == 2
+    assert lib.mhe_quantize_fp8(parts, rows, 1, 60, d * 8, d * 16, 0x10000, 1 << 20, None) == 2
+    assert lib.mhe_quantize_fp8(parts, rows, 1, 64, d * 8, None, 0x10000, 1 << 20, None) == 1
+    assert lib.mhe_quantize_fp8(parts, rows, 1, 64, d * 8, d * 16, 0x10000, 16, None) == 5
+    t = b.MheLayerWeightsFp8(*([0x1000] * 12))
+    t.s_down = None
+    tiny = b.config_from_dims(synth.TINY)
+    rc = lib.mhe_layer_forward_fp8(ctypes.byref(tiny), ctypes.byref(t), 0x2000, 0x3000, 64, 0x10000,
+                                   1 << 40, None)
+    assert rc == 1 and "s_down" in lib.mhe_last_error().decode()
