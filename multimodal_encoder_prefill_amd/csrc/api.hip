@@ -110,8 +110,9 @@ struct Workspace {
   // the partial maxima of the quantisation
   uint8_t* q8;
   int ld8_h, ld8_o, ld8_i;
-  float* scales;
-  float* amax;
+  float* scales;   // [4]: the per-call scales of the four GEMM inputs
+  float* factors;  // [4]: 448 / max|input|
+  float* amax;     // partial maxima of the input being quantised
   size_t total;
 };
 
@@ -150,7 +151,10 @@ Workspace carve(const mhe_config& c, int seq, char* base, bool fp8 = false) {
     w.ld8_i = c.intermediate + kActPad;
     w.q8 = reinterpret_cast<uint8_t*>(take(S * std::max({w.ld8_h, w.ld8_o, w.ld8_i})));
     w.scales = reinterpret_cast<float*>(take(4 * sizeof(float)));
-    w.amax = reinterpret_cast<float*>(take(mhe::kAmaxParts * sizeof(float)));
+    w.factors = reinterpret_cast<float*>(take(4 * sizeof(float)));
+    const int parts = std::max({mhe::kAmaxParts, mhe::rmsnorm_fp8_parts(seq),
+                                mhe::gemm_amax_parts(seq, c.intermediate)});
+    w.amax = reinterpret_cast<float*>(take(static_cast<size_t>(parts) * sizeof(float)));
   }
   w.total = off;
   return w;
@@ -299,20 +303,28 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights& w, bf16_t* x, co
 }
 
 // Per-tensor E4M3 copy of x [seq, cols] (row stride ldx) into ws.q8 (row
-// stride ldq bytes) with its scale in *scale: partial maxima, then convert.
-int32_t quantize_input(const bf16_t* x, int ldx, int seq, int cols, int ldq, float* scale,
+// stride ldq bytes) with its scale in ws.scales[slot]. `parts` partial maxima
+// of |x| are already in ws.amax when parts > 0; otherwise they are taken here.
+int32_t quantize_input(const bf16_t* x, int ldx, int seq, int cols, int ldq, int slot, int parts,
                        const Workspace& ws, hipStream_t st) {
   return traced(MHE_STEP_QUANTIZE, st, "fp8 quantize", [&] {
-    const int parts = mhe::amax_parts(seq);
-    hipError_t e = mhe::launch_amax(x, ldx, seq, cols, ws.amax, parts, st);
-    if (e != hipSuccess) return e;
-    return mhe::launch_quantize_fp8(x, ldx, seq, cols, ws.amax, parts, ws.q8, ldq, scale, st);
+    hipError_t e;
+    if (parts <= 0) {
+      parts = mhe::amax_parts(seq);
+      if ((e = mhe::launch_amax(x, ldx, seq, cols, ws.amax, parts, st)) != hipSuccess) return e;
+    }
+    if ((e = mhe::launch_amax_finalize(ws.amax, parts, ws.scales + slot, ws.factors + slot, st)) != hipSuccess)
+      return e;
+    return mhe::launch_quantize_fp8(x, ldx, seq, cols, ws.factors + slot, ws.q8, ldq, st);
   });
 }
 
 // The decoder layer with its four linears in FP8 (weights quantised
-// beforehand, activations here): the launch sequence of run_layer with a
-// quantisation before each GEMM.
+// beforehand, activations here): the launch sequence of run_layer with each
+// GEMM input quantised per tensor. The RMSNorm outputs go straight to E4M3
+// (the codes of the bf16 rows the bf16 layer would write); the gate/up GEMM
+// emits the partial maxima of its output, so only the attention output needs
+// a separate maximum sweep.
 int32_t run_layer(const mhe_config& c, const mhe_layer_weights_fp8& w, bf16_t* x, const int32_t* pos,
                   int seq, const Workspace& ws, hipStream_t st) {
   const int H = c.hidden, D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, I = c.intermediate;
@@ -320,11 +332,10 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights_fp8& w, bf16_t* x
   const uint8_t* wgu = static_cast<const uint8_t*>(w.w_gate_up);
   int32_t rc;
   if ((rc = traced(MHE_STEP_INPUT_NORM, st, "input rmsnorm", [&] {
-         return mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_in), ws.hn, ws.ld_h, seq, H,
-                                    c.rms_eps, st);
+         return mhe::launch_rmsnorm_fp8(x, static_cast<const bf16_t*>(w.ln_in), seq, H, c.rms_eps, ws.amax,
+                                        ws.scales + 0, ws.factors + 0, ws.q8, ws.ld8_h, st);
        })))
     return rc;
-  if ((rc = quantize_input(ws.hn, ws.ld_h, seq, H, ws.ld8_h, ws.scales + 0, ws, st))) return rc;
   const mhe::F8Segments qkv{{static_cast<const uint8_t*>(w.w_qkv), nullptr, nullptr}, {qkvw, 0, 0},
                             {w.s_qkv, nullptr, nullptr}, 1};
   if ((rc = traced(MHE_STEP_QKV, st, "qkv projection", [&] {
@@ -344,7 +355,7 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights_fp8& w, bf16_t* x
          return mhe::launch_attention(ws.qn, ws.kn, ws.vt, ws.ao, ws.ld_o, seq, Hq, Hkv, D, st);
        })))
     return rc;
-  if ((rc = quantize_input(ws.ao, ws.ld_o, seq, qw, ws.ld8_o, ws.scales + 1, ws, st))) return rc;
+  if ((rc = quantize_input(ws.ao, ws.ld_o, seq, qw, ws.ld8_o, 1, 0, ws, st))) return rc;
   const mhe::F8Segments wo{{static_cast<const uint8_t*>(w.w_o), nullptr, nullptr}, {H, 0, 0},
                            {w.s_o, nullptr, nullptr}, 1};
   if ((rc = traced(MHE_STEP_O_PROJ, st, "o projection", [&] {
@@ -353,19 +364,21 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights_fp8& w, bf16_t* x
        })))
     return rc;
   if ((rc = traced(MHE_STEP_POST_NORM, st, "post-attention rmsnorm", [&] {
-         return mhe::launch_rmsnorm(x, static_cast<const bf16_t*>(w.ln_post), ws.hn, ws.ld_h, seq, H,
-                                    c.rms_eps, st);
+         return mhe::launch_rmsnorm_fp8(x, static_cast<const bf16_t*>(w.ln_post), seq, H, c.rms_eps, ws.amax,
+                                        ws.scales + 2, ws.factors + 2, ws.q8, ws.ld8_h, st);
        })))
     return rc;
-  if ((rc = quantize_input(ws.hn, ws.ld_h, seq, H, ws.ld8_h, ws.scales + 2, ws, st))) return rc;
   const mhe::F8Segments gu{{wgu, wgu + static_cast<size_t>(I) * H, nullptr}, {I, I, 0},
                            {w.s_gate_up, w.s_gate_up, nullptr}, 2};
+  int act_parts = 0;
   if ((rc = traced(MHE_STEP_GATE_UP, st, "gate/up projection", [&] {
          return mhe::launch_gemm_fp8(mhe::Epilogue::kSwiGLU, ws.q8, ws.ld8_h, ws.scales + 2, gu, H, ws.act,
-                                     ws.ld_i, nullptr, seq, I, H, ws.partial, ws.partial_bytes, st);
+                                     ws.ld_i, nullptr, seq, I, H, ws.partial, ws.partial_bytes, st, ws.amax,
+                                     &act_parts);
        })))
     return rc;
-  if ((rc = quantize_input(ws.act, ws.ld_i, seq, I, ws.ld8_i, ws.scales + 3, ws, st))) return rc;
+  if (act_parts <= 0) return fail(MHE_ERR_HIP, "gate/up projection wrote no partial maxima");
+  if ((rc = quantize_input(ws.act, ws.ld_i, seq, I, ws.ld8_i, 3, act_parts, ws, st))) return rc;
   const mhe::F8Segments wd{{static_cast<const uint8_t*>(w.w_down), nullptr, nullptr}, {H, 0, 0},
                            {w.s_down, nullptr, nullptr}, 1};
   return traced(MHE_STEP_DOWN, st, "down projection", [&] {
@@ -657,7 +670,7 @@ int32_t mhe_linear_swiglu(const void* a, const void* w_gate, const void* w_up, v
                    "linear_swiglu");
 }
 
-size_t mhe_quantize_fp8_workspace_bytes(void) { return mhe::kAmaxParts * sizeof(float); }
+size_t mhe_quantize_fp8_workspace_bytes(void) { return (mhe::kAmaxParts + 64) * sizeof(float); }
 
 int32_t mhe_quantize_fp8(const void* const* parts, const int32_t* part_rows, int32_t n_parts,
                          int32_t cols, void* q, float* scale, void* workspace,
@@ -679,6 +692,7 @@ int32_t mhe_quantize_fp8(const void* const* parts, const int32_t* part_rows, int
       return fail(MHE_ERR_SHAPE, "q overlaps parts[%d]", i);
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* partial = static_cast<float*>(workspace);
+  float* factor = partial + mhe::kAmaxParts;
   // every part gets its share of the partial maxima; one scale over all parts
   int offs[9] = {0};
   for (int i = 0; i < n_parts; ++i)
@@ -688,10 +702,12 @@ int32_t mhe_quantize_fp8(const void* const* parts, const int32_t* part_rows, int
                                          partial + offs[i], offs[i + 1] - offs[i], st),
                         "fp8 amax")))
       return rc;
+  if ((rc = hip_check(mhe::launch_amax_finalize(partial, offs[n_parts], scale, factor, st), "fp8 scale")))
+    return rc;
   uint8_t* dst = static_cast<uint8_t*>(q);
   for (int i = 0; i < n_parts; ++i) {
     if ((rc = hip_check(mhe::launch_quantize_fp8(static_cast<const bf16_t*>(parts[i]), cols, part_rows[i],
-                                                 cols, partial, offs[n_parts], dst, cols, scale, st),
+                                                 cols, factor, dst, cols, st),
                         "fp8 quantize")))
       return rc;
     dst += static_cast<size_t>(part_rows[i]) * cols;

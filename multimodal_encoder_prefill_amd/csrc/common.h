@@ -50,6 +50,30 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
   return v;
 }
 
+// Eight floats times `factor`, clamped to +-448 and converted to E4M3 codes
+// (v_cvt_pk_fp8_f32: round to nearest even, OCP "fn" format), as 8 bytes in
+// element order. The product is a plain fp32 multiply (no fusion).
+__device__ __forceinline__ u32x2 e4m3x8(const float* f, float factor) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(__fmul_rn(f[i], factor), -448.f), 448.f);
+  u32x2 o;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h], y[4 * h + 1], 0, false));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h + 2], y[4 * h + 3], 0, false));
+    o[h] = (lo & 0xffffu) | (hi << 16);
+  }
+  return o;
+}
+
+// The same for eight bf16 values held in a 16-byte vector.
+__device__ __forceinline__ u32x2 e4m3x8(const u32x4& v, float factor) {
+  float f[8];
+  unpack8(v, f);
+  return e4m3x8(f, factor);
+}
+
 // Sum over the 64 lanes of a wavefront (every lane gets the total).
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

@@ -72,7 +72,26 @@ struct GemmArgs {
   // raw fp32 accumulators go to partial[unit] ([256][256] floats per unit).
   int tile_begin, units, ksplit, kt_per_split;
   float* partial;
+  // FP8 kSwiGLU, optional: max |C| (as stored) of each workgroup's outputs, at
+  // amax[unit] (whole tiles) or amax[split tile * 64 + row group] (the
+  // split-K reduction)
+  float* amax;
 };
+
+// max |v| over the four bf16 values of a packed pair of words
+__device__ __forceinline__ float abs_max4(const u32x2& pk) {
+  return fmaxf(fmaxf(__uint_as_float((pk[0] << 16) & 0x7fffffffu), __uint_as_float(pk[0] & 0x7fff0000u)),
+               fmaxf(__uint_as_float((pk[1] << 16) & 0x7fffffffu), __uint_as_float(pk[1] & 0x7fff0000u)));
+}
+
+// Maximum over a workgroup of 256 threads (red: 4 floats of LDS, not in use).
+__device__ __forceinline__ float workgroup_max(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
 
 // Output tile (m, n) of logical tile t: groups of kGroupM m-tiles, n-major
 // inside a group, so consecutive tiles share B panels and A panels.
@@ -483,6 +502,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 
   // ---- epilogue: lane holds column m = lrow of each 32x32 block and rows
   //      n = 8 g + 4 lhalf + e (e < 4) for the four groups g ----
+  float amx = 0.f;           // kSwiGLU: max |C| over this lane's outputs
   float sg = 1.f, su = 1.f;  // FP8 SwiGLU: scales of the gate and up products
   if constexpr (F8 && EPI == static_cast<int>(Epilogue::kSwiGLU)) {
     sg = args.scale_a[0] * args.scale_b[0][0];
@@ -510,6 +530,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
           pk[0] = pack_bf16x2(o[0], o[1]);
           pk[1] = pack_bf16x2(o[2], o[3]);
           *reinterpret_cast<u32x2*>(args.c + static_cast<size_t>(m) * args.ldc + jb + 8 * g + 4 * lhalf) = pk;
+          if constexpr (F8) amx = fmaxf(amx, abs_max4(pk));
         }
       }
     } else {
@@ -529,6 +550,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       }
     }
   }
+  if constexpr (F8 && EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+    if (args.amax) {  // uniform; LDS is free after the pipeline's last barrier
+      const float v = workgroup_max(amx, reinterpret_cast<float*>(smem));
+      if (tid == 0) args.amax[unit] = v;
+    }
+  }
 }
 
 // Sums the ksplit partial tiles of each split tile in a fixed order and
@@ -542,7 +569,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args)
   int tile_m, tile_n;
   tile_coords(args.tile_begin + t, args.tiles_m, args.tiles_n, tile_m, tile_n);
   const int m = tile_m * BM + ml;
-  if (m >= args.m) return;
+  bool live = m < args.m;  // every thread stays to the end (workgroup maximum)
   const float* src = args.partial + static_cast<size_t>(t) * args.ksplit * BM * BN + ml * BN + vn;
   f32x4 sum = *reinterpret_cast<const f32x4*>(src);
   for (int sidx = 1; sidx < args.ksplit; ++sidx)
@@ -554,11 +581,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args)
     // virtual column vn: wave half vn/128, 32-wide slot (vn%128)/32; slots 0,1
     // are gate columns whose up partner sits 64 virtual columns later
     const int slot = (vn & 127) >> 5;
-    if (slot >= 2) return;
-    const f32x4 up = *reinterpret_cast<const f32x4*>(src + 64);
+    live = live && slot < 2;
+    const f32x4 up = *reinterpret_cast<const f32x4*>(src + (slot < 2 ? 64 : 0));
     f32x4 upsum = up;
     for (int sidx = 1; sidx < args.ksplit; ++sidx)
-      upsum += *reinterpret_cast<const f32x4*>(src + 64 + static_cast<size_t>(sidx) * BM * BN);
+      upsum += *reinterpret_cast<const f32x4*>(src + (slot < 2 ? 64 : 0) + static_cast<size_t>(sidx) * BM * BN);
     n = tile_n * (BN / 2) + (vn >> 7) * 64 + slot * 32 + (vn & 31);
     if constexpr (F8) {
       sum *= args.scale_a[0] * args.scale_b[0][0];
@@ -574,15 +601,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args)
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = sum[e];
   }
-  if (n >= N) return;
+  live = live && n < N;
   const size_t off = static_cast<size_t>(m) * args.ldc + n;
   if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
     u32x2 pk;
     pk[0] = pack_bf16x2(o[0], o[1]);
     pk[1] = pack_bf16x2(o[2], o[3]);
-    *reinterpret_cast<u32x2*>(args.c + off) = pk;
+    if (live) *reinterpret_cast<u32x2*>(args.c + off) = pk;
+    if (F8 && args.amax) {
+      __shared__ float red[4];
+      const float v = workgroup_max(live ? abs_max4(pk) : 0.f, red);
+      if (threadIdx.x == 0) args.amax[t * (BM / 4) + blockIdx.y] = v;
+    }
   } else {
-    *reinterpret_cast<u32x2*>(args.c + off) = finish4<EPI>(o, args, n, off);
+    if (live) *reinterpret_cast<u32x2*>(args.c + off) = finish4<EPI>(o, args, n, off);
   }
 }
 
@@ -608,6 +640,12 @@ int gemm_segment_rows() { return 4096 / (BK * 2); }
 
 bool gemm_supported(int n, int k) { return n > 0 && k > 0 && n % 32 == 0 && k % BK == 0; }
 
+int gemm_amax_parts(int m, int n) {
+  // whole tiles (SwiGLU: 128 output columns each) plus 64 row groups of each
+  // split tile, fewer than one per CU
+  return ((m + BM - 1) / BM) * ((n + BN / 2 - 1) / (BN / 2)) + (BM / 4) * 256;
+}
+
 bool gemm_fp8_supported(int n, int k) { return n > 0 && k > 0 && n % 32 == 0 && k % (2 * BK) == 0; }
 
 namespace {
@@ -621,7 +659,7 @@ int device_cus() {
 }
 
 template <int EPI, bool F8>
-hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t stream) {
+hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t stream, int* amax_count) {
   // One workgroup fills a CU (128 KB of LDS), so a launch of T tiles runs in
   // ceil(T / CUs) waves. Full waves run whole tiles; when the last wave would
   // leave at least half the CUs idle and is a sizeable part of the launch (at
@@ -632,7 +670,9 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
   static const int cus = device_cus();
   const int rem = tiles % cus;
   int ksplit = 1;
-  if (partial && rem > 0 && rem <= cus / 2 && tiles / cus <= 4) {
+  // (with amax output, the row groups of the split tiles must fit gemm_amax_parts)
+  const bool amax_fits = !args.amax || (tiles + rem * (BM / 4) <= gemm_amax_parts(args.m, args.n));
+  if (partial && rem > 0 && rem <= cus / 2 && tiles / cus <= 4 && amax_fits) {
     ksplit = min(cus / rem, 16);
     ksplit = min(ksplit, nk / 4);
     const size_t cap = partial_bytes / (static_cast<size_t>(BM) * BN * sizeof(float));
@@ -649,6 +689,7 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
     a.partial = nullptr;
     if ((e = launch_epi<EPI, F8>(a, full, stream)) != hipSuccess) return e;
   }
+  if (amax_count) *amax_count = full + (ksplit > 1 ? rem * (BM / 4) : 0);
   if (ksplit > 1) {
     GemmArgs a = args;
     a.tile_begin = full;
@@ -656,6 +697,7 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
     a.ksplit = ksplit;
     a.kt_per_split = (nk + ksplit - 1) / ksplit;
     a.partial = partial;
+    a.amax = args.amax ? args.amax + full : nullptr;
     if ((e = launch_epi<EPI, F8>(a, a.units, stream)) != hipSuccess) return e;
     hipLaunchKernelGGL((splitk_reduce_kernel<EPI, F8>), dim3(rem, BM / 4), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -674,7 +716,7 @@ hipError_t launch_common(Epilogue epi, bool f8, const void* a, int lda, const fl
                          const void* const* bptr, const int* brows, const float* const* bscale,
                          int count, int ldb, bf16_t* c, int ldc, const bf16_t* residual, int m,
                          int n, int k, float* partial, size_t partial_bytes, hipStream_t stream,
-                         const bf16_t* bias) {
+                         const bf16_t* bias, float* amax, int* amax_count) {
   const int es = f8 ? 1 : 2;
   if (lda < k || ldb < k || ldc < n || (lda * es) % 16 != 0 || (ldb * es) % 16 != 0 || ldc % 4 != 0)
     return hipErrorInvalidValue;
@@ -695,6 +737,9 @@ hipError_t launch_common(Epilogue epi, bool f8, const void* a, int lda, const fl
   args.c = c;
   args.r = residual;
   args.bias = bias;
+  if (amax && (epi != Epilogue::kSwiGLU || !f8)) return hipErrorInvalidValue;
+  args.amax = amax;
+  if (amax_count) *amax_count = 0;
   if (static_cast<int>(epi) >= static_cast<int>(Epilogue::kBias) && !bias) return hipErrorInvalidValue;
   args.m = m;
   args.n = n;
@@ -706,20 +751,20 @@ hipError_t launch_common(Epilogue epi, bool f8, const void* a, int lda, const fl
   args.tiles_n = epi == Epilogue::kSwiGLU ? (n + BN / 2 - 1) / (BN / 2) : (n + BN - 1) / BN;
   if (f8) {
     switch (epi) {
-      case Epilogue::kStore: return run<0, true>(args, partial, partial_bytes, stream);
-      case Epilogue::kResidual: return run<1, true>(args, partial, partial_bytes, stream);
-      case Epilogue::kSwiGLU: return run<2, true>(args, partial, partial_bytes, stream);
+      case Epilogue::kStore: return run<0, true>(args, partial, partial_bytes, stream, amax_count);
+      case Epilogue::kResidual: return run<1, true>(args, partial, partial_bytes, stream, amax_count);
+      case Epilogue::kSwiGLU: return run<2, true>(args, partial, partial_bytes, stream, amax_count);
       default: return hipErrorInvalidValue;  // the biased forms are bf16 only
     }
   }
   switch (epi) {
-    case Epilogue::kStore: return run<0, false>(args, partial, partial_bytes, stream);
-    case Epilogue::kResidual: return run<1, false>(args, partial, partial_bytes, stream);
-    case Epilogue::kSwiGLU: return run<2, false>(args, partial, partial_bytes, stream);
-    case Epilogue::kBias: return run<3, false>(args, partial, partial_bytes, stream);
-    case Epilogue::kBiasResidual: return run<4, false>(args, partial, partial_bytes, stream);
-    case Epilogue::kBiasGeluTanh: return run<5, false>(args, partial, partial_bytes, stream);
-    case Epilogue::kBiasGeluErf: return run<6, false>(args, partial, partial_bytes, stream);
+    case Epilogue::kStore: return run<0, false>(args, partial, partial_bytes, stream, amax_count);
+    case Epilogue::kResidual: return run<1, false>(args, partial, partial_bytes, stream, amax_count);
+    case Epilogue::kSwiGLU: return run<2, false>(args, partial, partial_bytes, stream, amax_count);
+    case Epilogue::kBias: return run<3, false>(args, partial, partial_bytes, stream, amax_count);
+    case Epilogue::kBiasResidual: return run<4, false>(args, partial, partial_bytes, stream, amax_count);
+    case Epilogue::kBiasGeluTanh: return run<5, false>(args, partial, partial_bytes, stream, amax_count);
+    case Epilogue::kBiasGeluErf: return run<6, false>(args, partial, partial_bytes, stream, amax_count);
   }
   return hipErrorInvalidValue;
 }
@@ -732,19 +777,19 @@ hipError_t launch_gemm(Epilogue epi, const bf16_t* a, int lda, const BSegments& 
                        const bf16_t* bias) {
   const void* bptr[3] = {b.ptr[0], b.ptr[1], b.ptr[2]};
   return launch_common(epi, false, a, lda, nullptr, bptr, b.rows, nullptr, b.count, ldb, c, ldc,
-                       residual, m, n, k, partial, partial_bytes, stream, bias);
+                       residual, m, n, k, partial, partial_bytes, stream, bias, nullptr, nullptr);
 }
 
 hipError_t launch_gemm_fp8(Epilogue epi, const uint8_t* a, int lda, const float* scale_a,
                            const F8Segments& b, int ldb, bf16_t* c, int ldc,
                            const bf16_t* residual, int m, int n, int k, float* partial,
-                           size_t partial_bytes, hipStream_t stream) {
+                           size_t partial_bytes, hipStream_t stream, float* amax, int* amax_count) {
   if (!scale_a) return hipErrorInvalidValue;
   for (int i = 0; i < b.count && i < 3; ++i)
     if (!b.scale[i]) return hipErrorInvalidValue;
   const void* bptr[3] = {b.ptr[0], b.ptr[1], b.ptr[2]};
   return launch_common(epi, true, a, lda, scale_a, bptr, b.rows, b.scale, b.count, ldb, c, ldc,
-                       residual, m, n, k, partial, partial_bytes, stream, nullptr);
+                       residual, m, n, k, partial, partial_bytes, stream, nullptr, amax, amax_count);
 }
 
 }  // namespace mhe

@@ -63,23 +63,37 @@ struct F8Segments {
   int count;
 };
 bool gemm_fp8_supported(int n, int k);
+// amax (kSwiGLU only, may be NULL): partial maxima of |C| as stored, one per
+// workgroup that writes outputs, gemm_amax_parts(m, n) floats at most; the
+// count written goes to *amax_count.
+int gemm_amax_parts(int m, int n);
 hipError_t launch_gemm_fp8(Epilogue epi, const uint8_t* a, int lda, const float* scale_a,
                            const F8Segments& b, int ldb, bf16_t* c, int ldc,
                            const bf16_t* residual, int m, int n, int k, float* partial,
-                           size_t partial_bytes, hipStream_t stream);
+                           size_t partial_bytes, hipStream_t stream, float* amax = nullptr,
+                           int* amax_count = nullptr);
 
-// quant.hip: per-tensor E4M3 quantisation in two launches. launch_amax writes
-// nparts (<= kAmaxParts; amax_parts(rows) is the usual count) partial maxima
-// of |x|; launch_quantize_fp8 reduces nparts partials (those of several
-// launch_amax calls for a tensor stored in parts) and writes the codes
-// q [rows, ldq] and the scale (max|x| / 448, 1 for an all-zero tensor).
-// cols, ldx, ldq multiples of 8.
+// quant.hip: per-tensor E4M3 quantisation. launch_amax writes nparts
+// (<= kAmaxParts; amax_parts(rows) is the usual count) partial maxima of |x|;
+// launch_amax_finalize reduces nparts partials (of one tensor, possibly from
+// several launches) into scale[0] = max|x| / 448 (1 for an all-zero tensor)
+// and factor[0] = 448 / max|x|; launch_quantize_fp8 writes the codes
+// q [rows, ldq] of x times factor[0]. cols, ldx, ldq multiples of 8.
 constexpr int kAmaxParts = 1024;
 int amax_parts(int rows);
 hipError_t launch_amax(const bf16_t* x, int ldx, int rows, int cols, float* partial, int nparts,
                        hipStream_t stream);
-hipError_t launch_quantize_fp8(const bf16_t* x, int ldx, int rows, int cols, const float* partial,
-                               int nparts, uint8_t* q, int ldq, float* scale, hipStream_t stream);
+hipError_t launch_amax_finalize(const float* partial, int nparts, float* scale, float* factor,
+                                hipStream_t stream);
+hipError_t launch_quantize_fp8(const bf16_t* x, int ldx, int rows, int cols, const float* factor,
+                               uint8_t* q, int ldq, hipStream_t stream);
+// rmsnorm.hip: the RMSNorm of x quantised to E4M3 without writing it in bf16
+// (the codes of exactly the bf16 rows launch_rmsnorm would write): partial
+// maxima (rmsnorm_fp8_parts(rows) floats), finalize, quantize.
+int rmsnorm_fp8_parts(int rows);
+hipError_t launch_rmsnorm_fp8(const bf16_t* x, const bf16_t* gamma, int rows, int dim, float eps,
+                              float* partial, float* scale, float* factor, uint8_t* q, int ldq,
+                              hipStream_t stream);
 
 // qk_norm_rope.hip
 struct RopeParams {

@@ -158,3 +158,21 @@ def test_encode_no_deepstack_when_no_visual_tokens():
              visual_mask=None, n_vis=0, deepstack=None)
     torch.cuda.synchronize()
     assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("name", ["image_s4096_l50", "video_s16384_l50"])
+def test_encode_full_stack_sampled_rows(name):
+    """The two 50-layer full-width stacks in the launch configuration bench.py
+    times (one mhe_encode call): bitwise equal to layer-by-layer calls, and the
+    DeepStack layers 0-2 and the last layer teacher-forced against the oracle
+    on sampled rows (the visual block's edges, both ends, an even spread)."""
+    wl = synth.WORKLOADS[name]
+    print(f"full stack {name}: seq {wl.seq}, {wl.n_layers} layers, {wl.n_vis} visual tokens", flush=True)
+    s = _setup(wl)
+    out = _run_encode(wl, s)
+    states = _gpu_states(wl, s)
+    assert torch.equal(states[-1], out)
+    vis = np.flatnonzero(s["mask_np"])
+    rows = np.unique(np.concatenate([[0, 1, vis[0] - 1, vis[0], vis[-1], vis[-1] + 1, wl.seq - 1],
+                                     np.linspace(0, wl.seq - 1, 9).astype(int)]))
+    assert _teacher_forced(wl, s, states, rows=rows, layers=[0, 1, 2, wl.n_layers - 1]) <= 2e-2
