@@ -73,9 +73,10 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic(seq):
-    """HBM bytes per gate/up launch from the committed rocprofv3 counter runs,
-    only while the GEMM source is the one the counters were taken on."""
+def stored_traffic(seq, form="bf16"):
+    """HBM bytes per gate/up launch (bf16 or FP8 kernel) from the committed
+    rocprofv3 counter runs, only while the GEMM source is the one the counters
+    were taken on."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -83,7 +84,7 @@ def stored_traffic(seq):
         return None
     if t.get("gemm_source_sha256_16") != kernel_source_hash() or t.get("seq") != seq:
         return None
-    return t.get("bytes_per_launch")
+    return (t if form == "bf16" else t.get(form, {})).get("bytes_per_launch")
 
 
 def cpu_baseline(wl, layer0, emb, pos_np, mask_np, ds0):
@@ -229,9 +230,10 @@ def fp8_measure(wl, cfg, layers, emb, pos, mask, ds, dev, reps=3):
     torch.cuda.empty_cache()
     return {"ms": round(ms, 3), "tokens_per_s": round(wl.seq / ms * 1000.0, 2),
             "speedup_vs_bf16": None,
-            "gate_up": {"launch_ms": round(gu_ms, 4), "achieved": round(gu_tf, 1),
+            "gate_up": {"bound": "mfma", "launch_ms": round(gu_ms, 4), "achieved": round(gu_tf, 1),
                         "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(gu_tf / PEAK_FP8_TFLOPS, 4)},
+                        "frac": round(gu_tf / PEAK_FP8_TFLOPS, 4),
+                        "traffic": stored_traffic(wl.seq, "fp8")},
             "breakdown_ms_per_step": {k: v[0] for k, v in bd.items()}}
 
 
