@@ -103,6 +103,7 @@ struct Workspace {
   bf16_t* act;   // [S, I] with row stride ld_i, aliases qkv..ao (used after attention)
   int32_t* vis;  // [S]
   int32_t* cnt;  // [1]
+  float2* rope;  // [S][D/2] rotary cos/sin, formed once per call
   float* partial;  // split-K partial tiles of the GEMMs' last wave
   size_t partial_bytes;
   // FP8 layers only: E4M3 copy of the current GEMM input (row strides in
@@ -143,6 +144,7 @@ Workspace carve(const mhe_config& c, int seq, char* base, bool fp8 = false) {
   if (act_bytes > attn_bytes) off = region_start + act_bytes;
   w.vis = reinterpret_cast<int32_t*>(take(S * 4));
   w.cnt = reinterpret_cast<int32_t*>(take(4));
+  w.rope = reinterpret_cast<float2*>(take(S * (D / 2) * sizeof(float2)));
   w.partial_bytes = mhe::gemm_partial_bytes();
   w.partial = reinterpret_cast<float*>(take(w.partial_bytes));
   if (fp8) {
@@ -268,7 +270,7 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights& w, bf16_t* x, co
   if ((rc = traced(MHE_STEP_QK_ROPE, st, "q/k norm + rotary", [&] {
          return mhe::launch_qk_norm_rope(rp, ws.qkv, static_cast<const bf16_t*>(w.q_norm),
                                          static_cast<const bf16_t*>(w.k_norm), pos, seq, ws.qn, ws.kn,
-                                         ws.vt, st);
+                                         ws.vt, st, ws.rope);
        })))
     return rc;
   if ((rc = traced(MHE_STEP_ATTENTION, st, "attention", [&] {
@@ -348,7 +350,7 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights_fp8& w, bf16_t* x
   if ((rc = traced(MHE_STEP_QK_ROPE, st, "q/k norm + rotary", [&] {
          return mhe::launch_qk_norm_rope(rp, ws.qkv, static_cast<const bf16_t*>(w.q_norm),
                                          static_cast<const bf16_t*>(w.k_norm), pos, seq, ws.qn, ws.kn,
-                                         ws.vt, st);
+                                         ws.vt, st, ws.rope);
        })))
     return rc;
   if ((rc = traced(MHE_STEP_ATTENTION, st, "attention", [&] {
@@ -399,6 +401,14 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return pa < pb + bn && pb < pa + an;
 }
 
+// The rotary cos/sin of every (token, slot), shared by all layers of a call.
+int32_t rope_table(const mhe_config& c, const int32_t* pos, int seq, const Workspace& ws, hipStream_t st) {
+  const mhe::RopeParams rp{c.n_heads, c.n_kv_heads, c.head_dim, c.rms_eps, c.rope_theta,
+                           {c.mrope_section[0], c.mrope_section[1], c.mrope_section[2]}};
+  return traced(MHE_STEP_QK_ROPE, st, "rotary table",
+                [&] { return mhe::launch_rope_table(rp, pos, seq, ws.rope, st); });
+}
+
 // mhe_layer_forward / mhe_layer_forward_fp8.
 template <class W>
 int32_t layer_forward_impl(const mhe_config* cfg, const W* w, void* hidden, const int32_t* positions,
@@ -413,8 +423,9 @@ int32_t layer_forward_impl(const mhe_config* cfg, const W* w, void* hidden, cons
   const Workspace need = carve(*cfg, seq, nullptr, fp8);
   if ((rc = check_ws(workspace, workspace_bytes, need.total))) return rc;
   const Workspace ws = carve(*cfg, seq, static_cast<char*>(workspace), fp8);
-  return run_layer(*cfg, *w, static_cast<bf16_t*>(hidden), positions, seq, ws,
-                   static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = rope_table(*cfg, positions, seq, ws, st))) return rc;
+  return run_layer(*cfg, *w, static_cast<bf16_t*>(hidden), positions, seq, ws, st);
 }
 
 // mhe_encode / mhe_encode_fp8 (W: the layer weight table type).
@@ -461,6 +472,7 @@ int32_t encode_impl(const mhe_config* cfg, const W* layers, int32_t n_layers,
       (rc = hip_check(mhe::launch_visual_index(visual_mask, seq, n_vis, ws.vis, ws.cnt, st),
                       "visual index")))
     return rc;
+  if (n_layers > 0 && (rc = rope_table(*cfg, positions, seq, ws, st))) return rc;
   for (int l = 0; l < n_layers; ++l) {
     if ((rc = run_layer(*cfg, layers[l], x, positions, seq, ws, st))) return rc;
     if (l < used_ds && (rc = traced(MHE_STEP_DEEPSTACK, st, "deepstack add", [&] {

@@ -103,9 +103,15 @@ struct RopeParams {
 };
 // tokens of the K / V^T layouts: seq rounded up to a multiple of 128
 __host__ __device__ inline int seq_pad(int seq) { return (seq + 127) / 128 * 128; }
+// table (may be NULL): the rotary cos/sin of every (token, slot), [seq][D/2]
+// float pairs from launch_rope_table; without it each workgroup forms its
+// tokens' values itself (identical results).
+hipError_t launch_rope_table(const RopeParams& p, const int32_t* positions, int seq, float2* table,
+                             hipStream_t stream);
 hipError_t launch_qk_norm_rope(const RopeParams& p, const bf16_t* qkv, const bf16_t* q_norm,
                                const bf16_t* k_norm, const int32_t* positions, int seq,
-                               bf16_t* q_out, bf16_t* k_out, bf16_t* vt_out, hipStream_t stream);
+                               bf16_t* q_out, bf16_t* k_out, bf16_t* vt_out, hipStream_t stream,
+                               const float2* table = nullptr);
 
 // attention.hip
 bool attention_supported(int n_heads, int n_kv_heads, int head_dim);
