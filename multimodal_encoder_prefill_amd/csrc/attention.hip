@@ -9,8 +9,9 @@
 // the max raised lazily) and the output is rounded to bf16 once.
 //
 // One workgroup = one key/value head g and 32 query rows; its wavefronts each
-// take two query heads of the group, so every K/V tile staged in LDS serves
-// all G heads and every K or V operand read from LDS feeds the MFMAs of two
+// take HPW query heads of the group (the decoder: one, so a workgroup of 8
+// wavefronts puts two on every SIMD), so every K/V tile staged in LDS serves
+// all G heads and every K or V operand read from LDS feeds the MFMAs of HPW
 // heads. Each wavefront computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16
 // (keys are the MFMA rows, queries the columns), so a lane holds 16 scores of
 // a single query per 32-key block and the row max needs only one exchange
@@ -28,9 +29,10 @@
 // MiniMaxH3Qwen3VLVisionAttention.forward): SEG replaces the causal mask by
 // "key in the query's frame" (a [seg_lo, seg_hi) token range per query), the
 // head_dim of 72 is stored zero-padded to 128 (zero q/k columns add nothing to
-// the scores, zero V rows give output columns that are not stored), and with
-// one query head per key/value head a workgroup takes QW query blocks of one
-// head so that its QW wavefronts share every K/V tile.
+// the scores, zero V rows give output columns that are not stored; the MFMAs
+// stop at 96 dims), and with one query head per key/value head a workgroup
+// takes QW = 8 query blocks of one head so that its 8 wavefronts share every
+// K/V tile.
 #include "common.h"
 #include "internal.h"
 
@@ -53,7 +55,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const bf16_t* p, i
                                            __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-template <int D, int G, int HPW, int QW, bool SEG>
+// DU: head dims actually used (a multiple of 32, <= D); the layouts keep
+// the padded D, the MFMAs skip the columns past DU (all zero).
+template <int D, int G, int HPW, int QW, bool SEG, int DU = D>
 __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
     bf16_t* __restrict__ o, int ldo, int seq, int n_heads, int n_kv_heads, float scale_log2,
@@ -61,8 +65,9 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
   constexpr int HW = G / HPW;        // wavefronts per query block (heads of the group)
   constexpr int WAVES = HW * QW;
   constexpr int KCH = D / 8;          // 16-byte chunks per K row
-  constexpr int DS = D / 16;          // MFMA k-steps over head_dim
-  constexpr int DB = D / 32;          // 32-row blocks of O^T
+  static_assert(DU % 32 == 0 && DU <= D, "used head dims");
+  constexpr int DS = DU / 16;         // MFMA k-steps over the used head dims
+  constexpr int DB = DU / 32;         // 32-row blocks of O^T
   constexpr int KB = KT / 32;         // 32-key blocks of S^T per tile
   constexpr int PS = KT / 16;         // 16-key MFMA steps of O^T += V^T P^T
   constexpr int VCH = KT / 8;         // 16-byte chunks per V^T row
@@ -338,11 +343,18 @@ hipError_t launch_segment_attention(const bf16_t* q, const bf16_t* k, const bf16
   if (n <= 0) return hipSuccess;
   if (head_dim > 128 || head_dim % 4 != 0 || ldo < heads * head_dim || ldo % 4 != 0)
     return hipErrorInvalidValue;
-  constexpr int kQW = 4;
-  const int n_qb = (n + QB * kQW - 1) / (QB * kQW);
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(head_dim));
-  hipLaunchKernelGGL((attention_kernel<128, 1, 1, kQW, true>), dim3(n_qb * heads), dim3(64 * kQW),
-                     0, stream, q, k, vt, o, ldo, n, heads, heads, scale_log2, head_dim, info);
+  if (head_dim <= 96) {
+    // 8 query blocks (two wavefronts per SIMD), MFMAs over 96 dims
+    const int n_qb = (n + QB * 8 - 1) / (QB * 8);
+    hipLaunchKernelGGL((attention_kernel<128, 1, 1, 8, true, 96>), dim3(n_qb * heads), dim3(64 * 8), 0,
+                       stream, q, k, vt, o, ldo, n, heads, heads, scale_log2, head_dim, info);
+  } else {
+    // all 128 dims need more registers than two wavefronts per SIMD leave
+    const int n_qb = (n + QB * 4 - 1) / (QB * 4);
+    hipLaunchKernelGGL((attention_kernel<128, 1, 1, 4, true, 128>), dim3(n_qb * heads), dim3(64 * 4), 0,
+                       stream, q, k, vt, o, ldo, n, heads, heads, scale_log2, head_dim, info);
+  }
   return hipGetLastError();
 }
 

@@ -97,8 +97,15 @@ def test_vision_embed_matches_oracle(vd, grids):
     assert report(f"vision embed {vd.hidden}", f64(h), ref)[0] <= 2e-2
 
 
+# head_dim 128: the per-frame attention's all-dims path (head_dim 72 stops at 96)
+VISION_HD128 = synth.VisionDims(hidden=512, n_heads=4, mlp_width=1000, intermediate=1024, depth=2,
+                                patch=8, temporal_patch=2, in_channels=3, merge=2, out_hidden=256,
+                                pos_side=8, deepstack=(0,))
+
+
 @pytest.mark.parametrize("vd,grids,blocks", [(synth.VISION_TINY, GRIDS_TINY, [0, 1, 2]),
-                                             (synth.VISION_FULL, GRIDS_FULL, [0])])
+                                             (synth.VISION_FULL, GRIDS_FULL, [0]),
+                                             (VISION_HD128, GRIDS_TINY, [0, 1])])
 def test_vision_blocks_teacher_forced(vd, grids, blocks):
     w, tables, px, n, cfg, ws, nb = _setup(vd, grids, seed=1)
     od = _odims(vd)
