@@ -107,11 +107,17 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
   // queries' frames (SEG); per-query limits are applied as masks
   int key_lo = 0, key_hi = min(q0 + QB * QW, seq);
   int my_lo = 0, my_hi = qi + 1;
+  // SEG: keys in [in_lo, in_hi) lie in the frame of every query of the
+  // workgroup, so tiles inside that range need no mask
+  int in_lo = 0, in_hi = 0;
   if constexpr (SEG) {
-    __shared__ int range[2];
+    __shared__ int range[4];
     if (tid == 0) {
+      const int last = min(q0 + QB * QW, seq) - 1;
       range[0] = info[q0].seg_lo;
-      range[1] = info[min(q0 + QB * QW, seq) - 1].seg_hi;
+      range[1] = info[last].seg_hi;
+      range[2] = info[last].seg_lo;
+      range[3] = info[q0].seg_hi;
     }
     if (qi < seq) {
       my_lo = info[qi].seg_lo;
@@ -120,6 +126,8 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
     __syncthreads();
     key_lo = range[0];     // frames are contiguous and ascending
     key_hi = range[1];
+    in_lo = range[2];
+    in_hi = range[3];
   }
   const int t_first = key_lo / KT;
   const int n_tiles = (key_hi - 1) / KT + 1 - t_first;
@@ -215,7 +223,7 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
     //      more than 8 (p <= 2^8 meanwhile, exact once divided by the sum), so
     //      the O rescale is skipped for the whole wavefront on most tiles. ----
     // tile may hold keys past some query (causal) or outside some frame (SEG)
-    const bool edge = SEG || (t * KT + KT - 1) > q0;
+    const bool edge = SEG ? (t * KT < in_lo || t * KT + KT > in_hi) : (t * KT + KT - 1) > q0;
     bf16x8 pop[HPW][PS];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
