@@ -975,6 +975,7 @@ int32_t make_grids(const mhe_vision_config& c, const int32_t* thw, int n_grids, 
 struct VisionWs {
   int ld_u, ld_o, ld_i, ld_m;
   mhe::PatchInfo* info;
+  float2* rope;  // [n][head_dim/2] rotary cos/sin
   bf16_t* x;    // [n, H] hidden state of mhe_vision_forward
   bf16_t* u;    // [n, ld_u] norm output (dense [n, H] / [n/m^2, M] for the mergers)
   bf16_t* qkv;  // [n, 3H]
@@ -1004,6 +1005,7 @@ VisionWs vision_carve(const mhe_vision_config& c, int n, char* base) {
     return p;
   };
   w.info = reinterpret_cast<mhe::PatchInfo*>(take(N * sizeof(mhe::PatchInfo)));
+  w.rope = reinterpret_cast<float2*>(take(N * (H / heads / 2) * sizeof(float2)));
   w.x = reinterpret_cast<bf16_t*>(take(N * H * 2));
   w.u = reinterpret_cast<bf16_t*>(take(N * w.ld_u * 2));
   const size_t region = off;
@@ -1047,7 +1049,7 @@ int32_t run_vision_block(const mhe_vision_config& c, const mhe_vision_block_weig
   if ((rc = vision_gemm(mhe::Epilogue::kBias, ws.u, ws.ld_u, p.qkv_w, p.qkv_b, ws.qkv, 3 * H,
                         nullptr, n, 3 * H, H, ws, st, "qkv")))
     return rc;
-  if ((rc = hip_check(mhe::launch_vision_rope(ws.qkv, 3 * H, n, c.n_heads, dh, ws.info, ws.q, ws.k,
+  if ((rc = hip_check(mhe::launch_vision_rope(ws.qkv, 3 * H, n, c.n_heads, dh, ws.rope, ws.q, ws.k,
                                               ws.vt, st), "vision rotary")))
     return rc;
   if ((rc = hip_check(mhe::launch_segment_attention(ws.q, ws.k, ws.vt, ws.ao, ws.ld_o, n, c.n_heads,
@@ -1098,7 +1100,9 @@ int32_t vision_prelude(const mhe_vision_config* cfg, int n, const int32_t* thw, 
   const VisionWs need = vision_carve(*cfg, n, nullptr);
   if ((rc = check_ws(workspace, workspace_bytes, need.total))) return rc;
   *ws = vision_carve(*cfg, n, static_cast<char*>(workspace));
-  return hip_check(mhe::launch_patch_info(*g, n, ws->info, st), "patch info");
+  if ((rc = hip_check(mhe::launch_patch_info(*g, n, ws->info, st), "patch info"))) return rc;
+  return hip_check(mhe::launch_vision_rope_table(ws->info, n, cfg->hidden / cfg->n_heads, ws->rope, st),
+                   "vision rotary table");
 }
 
 // Patches the grids hold (0 when the list is unusable; make_grids reports why).

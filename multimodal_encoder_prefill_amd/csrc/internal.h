@@ -151,8 +151,10 @@ hipError_t launch_pos_embed(bf16_t* hidden, int ld, int n, int dim, const bf16_t
                             const PatchInfo* info, hipStream_t stream);
 // qkv [n, 3 heads head_dim] (row stride ldq) -> rotated q [n, heads, 128],
 // k [heads, seq_pad(n), 128], permuted V^T [heads, 128, seq_pad(n)], zero padded
+hipError_t launch_vision_rope_table(const PatchInfo* info, int n, int head_dim, float2* table,
+                                    hipStream_t stream);
 hipError_t launch_vision_rope(const bf16_t* qkv, int ldq, int n, int heads, int head_dim,
-                              const PatchInfo* info, bf16_t* q_out, bf16_t* k_out, bf16_t* vt_out,
+                              const float2* table, bf16_t* q_out, bf16_t* k_out, bf16_t* vt_out,
                               hipStream_t stream);
 // Non-causal attention within each frame (info[s].seg_lo .. seg_hi) on the
 // layouts above: heads of head_dim (<= 128, stored padded to 128), scale

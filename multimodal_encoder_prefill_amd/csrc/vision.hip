@@ -9,7 +9,8 @@
 //    r (side-1)/(h-1), neighbours floor and floor+1 clipped), fp32, one
 //    bf16 rounding.
 //  * vision_rope_kernel: splits the biased qkv projection into q, k, v,
-//    applies the 2-D rotary to q and k (rot_pos_emb and
+//    applies the 2-D rotary to q and k (cos/sin from vision_rope_table_kernel,
+//    formed once per call; rot_pos_emb and
 //    _apply_rotary_pos_emb_vision: angle of slot j < D/4 is row * f_j, of slot
 //    D/4 + j col * f_j, f_j = 10000^(-4j/D), the D/2 angles used twice,
 //    rotate-half) and writes the attention layouts with head_dim padded to
@@ -98,21 +99,37 @@ __global__ __launch_bounds__(256) void pos_embed_kernel(bf16_t* __restrict__ hid
 constexpr int kVT = 16;    // tokens per workgroup
 constexpr int kVD = 128;   // padded head dim of the attention layouts
 
+// cos and sin of rotary slot j (< dh/2) of every patch, formed once per call
+// (the positions are the same in every block): angle row * f_j for
+// j < dh/4, col * f_(j - dh/4) above, f_i = 10000^(-2i / (dh/2))
+__global__ __launch_bounds__(256) void vision_rope_table_kernel(const PatchInfo* __restrict__ info, int n,
+                                                               int dh, float2* __restrict__ table) {
+  const int half = dh / 2, quarter = dh / 4;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n * half) return;
+  const int s = e / half, j = e % half;
+  const float inv = powf(10000.f, -static_cast<float>(2 * (j % quarter)) / static_cast<float>(half));
+  const PatchInfo pi = info[s];
+  const float ang = static_cast<float>(j < quarter ? pi.row : pi.col) * inv;
+  float sn, cs;
+  sincosf(ang, &sn, &cs);
+  table[e] = make_float2(cs, sn);
+}
+
 // grid (n_pad / 16, heads); 128 threads = padded head dims d
 __global__ __launch_bounds__(kVD) void vision_rope_kernel(const bf16_t* __restrict__ qkv, int ldq,
                                                           int n, int n_pad, int heads, int dh,
-                                                          const PatchInfo* __restrict__ info,
+                                                          const float2* __restrict__ table,
                                                           bf16_t* __restrict__ q_out,
                                                           bf16_t* __restrict__ k_out,
                                                           bf16_t* __restrict__ vt_out) {
   const int s0 = blockIdx.x * kVT;
   const int h = blockIdx.y;
   const int d = threadIdx.x;
-  const int half = dh / 2, quarter = dh / 4;
+  const int half = dh / 2;
   const int hid = heads * dh;
-  // slot j of the D/2 angles: row * f_j (j < D/4) or col * f_(j - D/4)
+  // slot j of the D/2 angles (the angle of d and d + D/2)
   const int j = d < dh ? d % half : 0;
-  const float inv = powf(10000.f, -static_cast<float>(2 * (j % quarter)) / static_cast<float>(half));
   float vv[kVT];
 #pragma unroll
   for (int t = 0; t < kVT; ++t) {
@@ -120,10 +137,8 @@ __global__ __launch_bounds__(kVD) void vision_rope_kernel(const bf16_t* __restri
     float qo = 0.f, ko = 0.f, vo = 0.f;
     if (s < n && d < dh) {
       const bf16_t* row = qkv + static_cast<size_t>(s) * ldq + h * dh;
-      const PatchInfo pi = info[s];
-      const float ang = static_cast<float>(j < quarter ? pi.row : pi.col) * inv;
-      float sn, cs;
-      sincosf(ang, &sn, &cs);
+      const float2 c2 = table[static_cast<size_t>(s) * half + j];
+      const float cs = c2.x, sn = c2.y;
       const int pd = d < half ? d + half : d - half;
       const float sign = d < half ? -1.f : 1.f;
       const float qx = bf16_to_f32(row[d]), qp = bf16_to_f32(row[pd]);
@@ -163,14 +178,24 @@ hipError_t launch_pos_embed(bf16_t* hidden, int ld, int n, int dim, const bf16_t
   return hipGetLastError();
 }
 
+hipError_t launch_vision_rope_table(const PatchInfo* info, int n, int head_dim, float2* table,
+                                    hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (head_dim > kVD || head_dim % 4 != 0) return hipErrorInvalidValue;
+  const int e = n * (head_dim / 2);
+  hipLaunchKernelGGL(vision_rope_table_kernel, dim3((e + 255) / 256), dim3(256), 0, stream, info, n,
+                     head_dim, table);
+  return hipGetLastError();
+}
+
 hipError_t launch_vision_rope(const bf16_t* qkv, int ldq, int n, int heads, int head_dim,
-                              const PatchInfo* info, bf16_t* q_out, bf16_t* k_out, bf16_t* vt_out,
+                              const float2* table, bf16_t* q_out, bf16_t* k_out, bf16_t* vt_out,
                               hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   if (head_dim > kVD || head_dim % 4 != 0) return hipErrorInvalidValue;
   const int n_pad = seq_pad(n);
   hipLaunchKernelGGL(vision_rope_kernel, dim3(n_pad / kVT, heads), dim3(kVD), 0, stream, qkv, ldq,
-                     n, n_pad, heads, head_dim, info, q_out, k_out, vt_out);
+                     n, n_pad, heads, head_dim, table, q_out, k_out, vt_out);
   return hipGetLastError();
 }
 
