@@ -45,6 +45,21 @@ constexpr int KT = 128;  // keys per tile (the K / V^T layouts are padded to a m
 
 __device__ __forceinline__ int swz8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
+// max of three floats as one v_max3_f32. Written out because the compiler
+// otherwise precedes every max of MFMA results with a NaN-quieting copy of
+// each input; scores here are finite or -inf, never NaN.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// s + x.lo + x.hi for a pair of bf16 (v_dot2_f32_bf16 against (1, 1))
+__device__ __forceinline__ float add_pair(uint32_t x, float s) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, 0x3f803f80u),
+                                         s, false);
+}
+
 // Buffer resource over [p, p + bytes) held in scalar registers.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const bf16_t* p, int bytes) {
   const uint64_t u = reinterpret_cast<uint64_t>(p);
@@ -236,11 +251,15 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
             if (key < my_lo || key >= my_hi) sacc[hh][kb][e] = -INFINITY;
           }
       }
-      float tmax = -INFINITY;
+      float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) tmax = fmaxf(tmax, fmaxf(sacc[hh][kb][e], sacc[hh][kb][e + 1]));
+        for (int e = 0; e < 16; e += 4) {
+          m0 = max3(m0, sacc[hh][kb][e], sacc[hh][kb][e + 1]);
+          m1 = max3(m1, sacc[hh][kb][e + 2], sacc[hh][kb][e + 3]);
+        }
+      float tmax = fmaxf(m0, m1);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
       float alpha = 1.f;
       if (tmax > m_run[hh] + 8.f) {
@@ -248,20 +267,22 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
         m_run[hh] = tmax;
       }
       const float neg_m = -m_run[hh];
-      float psum = 0.f;
+      // the row sum is taken over the bf16 probabilities the PV product uses
+      float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           float pv[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
+          for (int e = 0; e < 8; ++e)
             pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[hh][kb][half * 8 + e], scale_log2, neg_m));
-            psum += pv[e];
-          }
-          pop[hh][kb * 2 + half] = __builtin_bit_cast(bf16x8, pack8(pv));
+          const u32x4 pk = pack8(pv);
+          ps0 = add_pair(pk[1], add_pair(pk[0], ps0));
+          ps1 = add_pair(pk[3], add_pair(pk[2], ps1));
+          pop[hh][kb * 2 + half] = __builtin_bit_cast(bf16x8, pk);
         }
-      l_run[hh] = l_run[hh] * alpha + psum;
+      l_run[hh] = l_run[hh] * alpha + (ps0 + ps1);
       if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
         for (int b = 0; b < DB; ++b)
