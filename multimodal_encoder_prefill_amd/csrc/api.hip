@@ -895,26 +895,10 @@ int32_t mhe_join_visual(const uint8_t* image_mask, const uint8_t* video_mask, in
     return fail(MHE_ERR_NULL, "feature array is NULL");
   if ((rc = check_ws(workspace, workspace_bytes, mhe_join_visual_workspace_bytes(seq)))) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  const size_t list = align_up(static_cast<size_t>(seq) * 4);
-  int32_t* vis_idx = reinterpret_cast<int32_t*>(ws);
-  int32_t* img_idx = reinterpret_cast<int32_t*>(ws + list);
-  int32_t* vid_idx = reinterpret_cast<int32_t*>(ws + 2 * list);
-  int32_t* cnt = reinterpret_cast<int32_t*>(ws + 3 * list);
-  const int n_total = n_image + n_video;
-  if ((rc = hip_check(mhe::launch_visual_index(image_mask, seq, n_total, vis_idx, cnt, st, video_mask),
-                      "visual index")))
-    return rc;
-  if ((rc = hip_check(mhe::launch_visual_index(image_mask, seq, n_image, img_idx, cnt + 1, st),
-                      "image index")))
-    return rc;
-  if ((rc = hip_check(mhe::launch_visual_index(video_mask, seq, n_video, vid_idx, cnt + 2, st),
-                      "video index")))
-    return rc;
-  return hip_check(mhe::launch_join_visual(vis_idx, n_total, image_mask, img_idx, n_image,
-                                           static_cast<const bf16_t*>(image_feature), vid_idx,
-                                           n_video, static_cast<const bf16_t*>(video_feature),
-                                           hidden_dim, static_cast<bf16_t*>(joint), st),
+  return hip_check(mhe::launch_join_visual(image_mask, video_mask, seq, n_image,
+                                           static_cast<const bf16_t*>(image_feature), n_video,
+                                           static_cast<const bf16_t*>(video_feature), hidden_dim,
+                                           static_cast<int32_t*>(workspace), static_cast<bf16_t*>(joint), st),
                    "visual join");
 }
 

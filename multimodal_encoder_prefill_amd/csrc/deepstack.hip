@@ -20,7 +20,6 @@ namespace {
 constexpr int kScanThreads = 1024;
 
 __global__ __launch_bounds__(kScanThreads) void visual_index_kernel(const uint8_t* __restrict__ mask,
-                                                                   const uint8_t* __restrict__ mask2,
                                                                    int seq, int n_vis,
                                                                    int32_t* __restrict__ idx,
                                                                    int32_t* __restrict__ count) {
@@ -29,8 +28,7 @@ __global__ __launch_bounds__(kScanThreads) void visual_index_kernel(const uint8_
   const int per = (seq + kScanThreads - 1) / kScanThreads;
   const int beg = min(tid * per, seq), end = min(beg + per, seq);
   int local = 0;
-  // a token counts when its byte in mask (or, if given, in mask2) is set
-  auto set = [&](int s) { return mask[s] != 0 || (mask2 && mask2[s] != 0); };
+  auto set = [&](int s) { return mask[s] != 0; };
   for (int s = beg; s < end; ++s) local += set(s);
   // inclusive scan over the workgroup: within wavefronts, then across them
   const int lane = tid & 63, wave = tid >> 6;
@@ -88,9 +86,9 @@ __global__ __launch_bounds__(256) void deepstack_add_kernel(bf16_t* __restrict__
 }  // namespace
 
 hipError_t launch_visual_index(const uint8_t* mask, int seq, int n_vis, int32_t* idx,
-                               int32_t* count, hipStream_t stream, const uint8_t* mask2) {
-  hipLaunchKernelGGL(visual_index_kernel, dim3(1), dim3(kScanThreads), 0, stream, mask, mask2,
-                     seq, n_vis, idx, count);
+                               int32_t* count, hipStream_t stream) {
+  hipLaunchKernelGGL(visual_index_kernel, dim3(1), dim3(kScanThreads), 0, stream, mask, seq, n_vis,
+                     idx, count);
   return hipGetLastError();
 }
 

@@ -9,8 +9,9 @@
 //  * embed_gather_kernel: embed_tokens, a row gather from the embedding table.
 //    Ids outside the table's row range give zero rows, which is what the
 //    page's vocab-parallel embedding does for ids outside a rank's shard.
-//  * join_kernel: _aggregate_deepstack for a prompt with images and videos:
-//    the DeepStack rows of both modalities interleaved in token order.
+//  * join_index_kernel + join_kernel: _aggregate_deepstack for a prompt with
+//    images and videos: the DeepStack rows of both modalities interleaved in
+//    token order (one scan gives every joint row its source row).
 //
 // The gather and the join are HBM-bound row copies: 2 * hidden * 2 bytes per
 // row (read one row, write one row), 16-byte loads and stores, one wavefront
@@ -121,43 +122,74 @@ __global__ __launch_bounds__(256) void embed_gather_kernel(const int32_t* __rest
   }
 }
 
-// Position of token t in the ascending index list idx[0, n) (entries past
-// the mask's popcount are -1 and compare as larger than every token), or -1.
-__device__ __forceinline__ int rank_of(const int32_t* __restrict__ idx, int n, int t) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    const int v = idx[mid];
-    if (v < 0 || v >= t) hi = mid;
-    else lo = mid + 1;
+// Source row of every joint row, by one workgroup-wide scan over the tokens:
+// the r-th visual token (image or video byte set) is the i-th image token or
+// the v-th video token, so src[r] = i, or n_image + v, or -1 when that
+// feature row does not exist (a mask with more set bytes than features).
+// Rows r past the visual-token count are -1 too.
+constexpr int kJoinThreads = 1024;
+
+__device__ __forceinline__ int block_exclusive_scan(int x, int* wave_tot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
   }
-  return (lo < n && idx[lo] == t) ? lo : -1;
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < kJoinThreads / 64; ++w) {
+    if (w < wave) before += wave_tot[w];
+    all += wave_tot[w];
+  }
+  __syncthreads();  // wave_tot is reused by the next scan
+  *total = all;
+  return before + incl - x;
 }
 
-__global__ __launch_bounds__(256) void join_kernel(const int32_t* __restrict__ vis_idx, int n_total,
-                                                   const uint8_t* __restrict__ image_mask,
-                                                   const int32_t* __restrict__ img_idx, int n_image,
+__global__ __launch_bounds__(kJoinThreads) void join_index_kernel(const uint8_t* __restrict__ image_mask,
+                                                                 const uint8_t* __restrict__ video_mask,
+                                                                 int seq, int n_total, int n_image,
+                                                                 int n_video, int32_t* __restrict__ src) {
+  __shared__ int wave_tot[kJoinThreads / 64];
+  const int tid = threadIdx.x;
+  const int per = (seq + kJoinThreads - 1) / kJoinThreads;
+  const int beg = min(tid * per, seq), end = min(beg + per, seq);
+  int li = 0, lv = 0;
+  for (int s = beg; s < end; ++s) {
+    if (image_mask[s]) ++li;
+    else if (video_mask[s]) ++lv;
+  }
+  int ti, tv;
+  int i = block_exclusive_scan(li, wave_tot, &ti);
+  int v = block_exclusive_scan(lv, wave_tot, &tv);
+  for (int s = beg; s < end; ++s) {
+    const bool img = image_mask[s] != 0, vid = !img && video_mask[s] != 0;
+    if (!img && !vid) continue;
+    const int r = i + v;
+    if (r < n_total) src[r] = img ? (i < n_image ? i : -1) : (v < n_video ? n_image + v : -1);
+    if (img) ++i;
+    else ++v;
+  }
+  for (int r = ti + tv + tid; r < n_total; r += kJoinThreads) src[r] = -1;
+}
+
+__global__ __launch_bounds__(256) void join_kernel(const int32_t* __restrict__ src, int n_total, int n_image,
                                                    const bf16_t* __restrict__ image_feature,
-                                                   const int32_t* __restrict__ vid_idx, int n_video,
                                                    const bf16_t* __restrict__ video_feature, int dim,
                                                    bf16_t* __restrict__ joint) {
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= n_total) return;
-  const int t = vis_idx[r];
-  const bf16_t* src = nullptr;
-  if (t >= 0) {
-    if (image_mask[t]) {
-      const int i = rank_of(img_idx, n_image, t);
-      if (i >= 0) src = image_feature + static_cast<size_t>(i) * dim;
-    } else {
-      const int v = rank_of(vid_idx, n_video, t);
-      if (v >= 0) src = video_feature + static_cast<size_t>(v) * dim;
-    }
-  }
+  const int k = src[r];
+  const bf16_t* from = k < 0 ? nullptr
+                       : k < n_image ? image_feature + static_cast<size_t>(k) * dim
+                                     : video_feature + static_cast<size_t>(k - n_image) * dim;
   u32x4* dst = reinterpret_cast<u32x4*>(joint + static_cast<size_t>(r) * dim);
   for (int c = lane; c < dim / 8; c += 64)
-    dst[c] = src ? reinterpret_cast<const u32x4*>(src)[c] : u32x4{0, 0, 0, 0};
+    dst[c] = from ? reinterpret_cast<const u32x4*>(from)[c] : u32x4{0, 0, 0, 0};
 }
 
 }  // namespace
@@ -171,14 +203,18 @@ hipError_t launch_embed_gather(const int32_t* ids, int seq, const bf16_t* table,
   return hipGetLastError();
 }
 
-hipError_t launch_join_visual(const int32_t* vis_idx, int n_total, const uint8_t* image_mask,
-                              const int32_t* img_idx, int n_image, const bf16_t* image_feature,
-                              const int32_t* vid_idx, int n_video, const bf16_t* video_feature,
-                              int dim, bf16_t* joint, hipStream_t stream) {
+hipError_t launch_join_visual(const uint8_t* image_mask, const uint8_t* video_mask, int seq,
+                              int n_image, const bf16_t* image_feature, int n_video,
+                              const bf16_t* video_feature, int dim, int32_t* src, bf16_t* joint,
+                              hipStream_t stream) {
+  const int n_total = n_image + n_video;
   if (n_total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(join_kernel, dim3((n_total + 3) / 4), dim3(256), 0, stream, vis_idx, n_total,
-                     image_mask, img_idx, n_image, image_feature, vid_idx, n_video, video_feature,
-                     dim, joint);
+  hipLaunchKernelGGL(join_index_kernel, dim3(1), dim3(kJoinThreads), 0, stream, image_mask, video_mask, seq,
+                     n_total, n_image, n_video, src);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(join_kernel, dim3((n_total + 3) / 4), dim3(256), 0, stream, src, n_total, n_image,
+                     image_feature, video_feature, dim, joint);
   return hipGetLastError();
 }
 

@@ -121,11 +121,10 @@ hipError_t launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* vt, 
                             hipStream_t stream);
 
 // deepstack.hip
-// Ascending list idx[0, n_vis) of the tokens whose byte in mask (or in mask2,
-// if not NULL) is set; entries past the popcount are -1; *count = popcount.
+// Ascending list idx[0, n_vis) of the tokens whose byte in mask is set;
+// entries past the popcount are -1; *count = popcount.
 hipError_t launch_visual_index(const uint8_t* mask, int seq, int n_vis, int32_t* idx,
-                               int32_t* count, hipStream_t stream,
-                               const uint8_t* mask2 = nullptr);
+                               int32_t* count, hipStream_t stream);
 // hidden[idx[r]] += feature[r] (fp32 add, one bf16 rounding), r < n_vis
 hipError_t launch_deepstack_add(bf16_t* hidden, int hidden_dim, const int32_t* idx, int n_vis,
                                 const bf16_t* feature, hipStream_t stream);
@@ -176,10 +175,11 @@ int rope_index_host(const int32_t* ids, int seq, int image_token_id, int video_t
 hipError_t launch_embed_gather(const int32_t* ids, int seq, const bf16_t* table, int row_begin,
                                int rows, int dim, bf16_t* out, int32_t* n_outside,
                                hipStream_t stream);
-// joint[r] = the feature row of the r-th visual token (image or video)
-hipError_t launch_join_visual(const int32_t* vis_idx, int n_total, const uint8_t* image_mask,
-                              const int32_t* img_idx, int n_image, const bf16_t* image_feature,
-                              const int32_t* vid_idx, int n_video, const bf16_t* video_feature,
-                              int dim, bf16_t* joint, hipStream_t stream);
+// joint[r] = the feature row of the r-th visual token (image or video); src:
+// n_image + n_video ints of scratch
+hipError_t launch_join_visual(const uint8_t* image_mask, const uint8_t* video_mask, int seq,
+                              int n_image, const bf16_t* image_feature, int n_video,
+                              const bf16_t* video_feature, int dim, int32_t* src, bf16_t* joint,
+                              hipStream_t stream);
 
 }  // namespace mhe
