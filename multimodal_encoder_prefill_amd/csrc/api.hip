@@ -155,7 +155,8 @@ Workspace carve(const mhe_config& c, int seq, char* base, bool fp8 = false) {
     w.scales = reinterpret_cast<float*>(take(4 * sizeof(float)));
     w.factors = reinterpret_cast<float*>(take(4 * sizeof(float)));
     const int parts = std::max({mhe::kAmaxParts, mhe::rmsnorm_fp8_parts(seq),
-                                mhe::gemm_amax_parts(seq, c.intermediate)});
+                                mhe::gemm_amax_parts(seq, c.intermediate),
+                                mhe::attention_amax_parts(seq, c.n_kv_heads)});
     w.amax = reinterpret_cast<float*>(take(static_cast<size_t>(parts) * sizeof(float)));
   }
   w.total = off;
@@ -324,9 +325,9 @@ int32_t quantize_input(const bf16_t* x, int ldx, int seq, int cols, int ldq, int
 // The decoder layer with its four linears in FP8 (weights quantised
 // beforehand, activations here): the launch sequence of run_layer with each
 // GEMM input quantised per tensor. The RMSNorm outputs go straight to E4M3
-// (the codes of the bf16 rows the bf16 layer would write); the gate/up GEMM
-// emits the partial maxima of its output, so only the attention output needs
-// a separate maximum sweep.
+// (the codes of the bf16 rows the bf16 layer would write); the attention and
+// gate/up kernels emit the partial maxima of their outputs, so no input
+// needs a separate maximum sweep.
 int32_t run_layer(const mhe_config& c, const mhe_layer_weights_fp8& w, bf16_t* x, const int32_t* pos,
                   int seq, const Workspace& ws, hipStream_t st) {
   const int H = c.hidden, D = c.head_dim, Hq = c.n_heads, Hkv = c.n_kv_heads, I = c.intermediate;
@@ -354,10 +355,11 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights_fp8& w, bf16_t* x
        })))
     return rc;
   if ((rc = traced(MHE_STEP_ATTENTION, st, "attention", [&] {
-         return mhe::launch_attention(ws.qn, ws.kn, ws.vt, ws.ao, ws.ld_o, seq, Hq, Hkv, D, st);
+         return mhe::launch_attention(ws.qn, ws.kn, ws.vt, ws.ao, ws.ld_o, seq, Hq, Hkv, D, st, ws.amax);
        })))
     return rc;
-  if ((rc = quantize_input(ws.ao, ws.ld_o, seq, qw, ws.ld8_o, 1, 0, ws, st))) return rc;
+  if ((rc = quantize_input(ws.ao, ws.ld_o, seq, qw, ws.ld8_o, 1, mhe::attention_amax_parts(seq, Hkv), ws, st)))
+    return rc;
   const mhe::F8Segments wo{{static_cast<const uint8_t*>(w.w_o), nullptr, nullptr}, {H, 0, 0},
                            {w.s_o, nullptr, nullptr}, 1};
   if ((rc = traced(MHE_STEP_O_PROJ, st, "o projection", [&] {

@@ -76,7 +76,7 @@ template <int D, int G, int HPW, int QW, bool SEG, int DU = D>
 __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
     bf16_t* __restrict__ o, int ldo, int seq, int n_heads, int n_kv_heads, float scale_log2,
-    int dout, const PatchInfo* __restrict__ info) {
+    int dout, const PatchInfo* __restrict__ info, float* __restrict__ amax) {
   constexpr int HW = G / HPW;        // wavefronts per query block (heads of the group)
   constexpr int WAVES = HW * QW;
   constexpr int KCH = D / 8;          // 16-byte chunks per K row
@@ -312,6 +312,7 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
   }
 
   // ---- normalise and store: lane holds query lrow, d = 32b + 8(e/4) + 4 lhalf + e%4 ----
+  float amx = 0.f;  // max |o| as stored (amax != NULL: FP8 quantisation of o)
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
     const float l_tot = l_run[hh] + __shfl_xor(l_run[hh], 32, 64);
@@ -327,15 +328,32 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
             pk[0] = pack_bf16x2(oacc[hh][b][gq * 4 + 0] * inv, oacc[hh][b][gq * 4 + 1] * inv);
             pk[1] = pack_bf16x2(oacc[hh][b][gq * 4 + 2] * inv, oacc[hh][b][gq * 4 + 3] * inv);
             *reinterpret_cast<u32x2*>(dst + b * 32 + gq * 8) = pk;
+            amx = fmaxf(amx, fmaxf(fmaxf(__uint_as_float((pk[0] << 16) & 0x7fffffffu),
+                                         __uint_as_float(pk[0] & 0x7fff0000u)),
+                                   fmaxf(__uint_as_float((pk[1] << 16) & 0x7fffffffu),
+                                         __uint_as_float(pk[1] & 0x7fff0000u))));
           }
         }
+    }
+  }
+  if (amax) {  // uniform; one partial maximum per workgroup
+    __shared__ float red[WAVES];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amx = fmaxf(amx, __shfl_xor(amx, off, 64));
+    if (lane == 0) red[wave] = amx;
+    __syncthreads();
+    if (tid == 0) {
+      float m = red[0];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) m = fmaxf(m, red[w]);
+      amax[blockIdx.x] = m;
     }
   }
 }
 
 template <int D>
 hipError_t launch_d(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o, int ldo,
-                    int seq, int n_heads, int n_kv_heads, hipStream_t stream) {
+                    int seq, int n_heads, int n_kv_heads, hipStream_t stream, float* amax) {
   const int G = n_heads / n_kv_heads;
   const int n_qb = (seq + QB - 1) / QB;
   const dim3 grid(n_qb * n_kv_heads);
@@ -345,7 +363,7 @@ hipError_t launch_d(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* 
   case GG:                                                                                    \
     hipLaunchKernelGGL((attention_kernel<D, GG, HH, 1, false>), grid, dim3(64 * (GG / HH)), 0, \
                        stream, q, k, vt, o, ldo, seq, n_heads, n_kv_heads, scale_log2, D,     \
-                       nullptr);                                                              \
+                       nullptr, amax);                                                        \
     break;
     MHE_ATTN_CASE(1, 1)
     MHE_ATTN_CASE(2, 1)
@@ -377,23 +395,25 @@ hipError_t launch_segment_attention(const bf16_t* q, const bf16_t* k, const bf16
     // 8 query blocks (two wavefronts per SIMD), MFMAs over 96 dims
     const int n_qb = (n + QB * 8 - 1) / (QB * 8);
     hipLaunchKernelGGL((attention_kernel<128, 1, 1, 8, true, 96>), dim3(n_qb * heads), dim3(64 * 8), 0,
-                       stream, q, k, vt, o, ldo, n, heads, heads, scale_log2, head_dim, info);
+                       stream, q, k, vt, o, ldo, n, heads, heads, scale_log2, head_dim, info, nullptr);
   } else {
     // all 128 dims need more registers than two wavefronts per SIMD leave
     const int n_qb = (n + QB * 4 - 1) / (QB * 4);
     hipLaunchKernelGGL((attention_kernel<128, 1, 1, 4, true, 128>), dim3(n_qb * heads), dim3(64 * 4), 0,
-                       stream, q, k, vt, o, ldo, n, heads, heads, scale_log2, head_dim, info);
+                       stream, q, k, vt, o, ldo, n, heads, heads, scale_log2, head_dim, info, nullptr);
   }
   return hipGetLastError();
 }
 
+int attention_amax_parts(int seq, int n_kv_heads) { return (seq + QB - 1) / QB * n_kv_heads; }
+
 hipError_t launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o,
                             int ldo, int seq, int n_heads, int n_kv_heads, int head_dim,
-                            hipStream_t stream) {
+                            hipStream_t stream, float* amax) {
   if (seq <= 0) return hipSuccess;
   if (ldo < n_heads * head_dim || ldo % 4 != 0) return hipErrorInvalidValue;
-  if (head_dim == 128) return launch_d<128>(q, k, vt, o, ldo, seq, n_heads, n_kv_heads, stream);
-  if (head_dim == 64) return launch_d<64>(q, k, vt, o, ldo, seq, n_heads, n_kv_heads, stream);
+  if (head_dim == 128) return launch_d<128>(q, k, vt, o, ldo, seq, n_heads, n_kv_heads, stream, amax);
+  if (head_dim == 64) return launch_d<64>(q, k, vt, o, ldo, seq, n_heads, n_kv_heads, stream, amax);
   return hipErrorInvalidValue;
 }
 

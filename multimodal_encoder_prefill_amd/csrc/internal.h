@@ -116,9 +116,13 @@ hipError_t launch_qk_norm_rope(const RopeParams& p, const bf16_t* qkv, const bf1
 // attention.hip
 bool attention_supported(int n_heads, int n_kv_heads, int head_dim);
 // o rows are ldo elements apart (>= n_heads * head_dim, multiple of 4).
+// amax (may be NULL): max |o| as stored of each workgroup, at
+// amax[0, attention_amax_parts(seq, n_kv_heads)) (the FP8 layer's input
+// maxima for the O projection).
+int attention_amax_parts(int seq, int n_kv_heads);
 hipError_t launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o,
                             int ldo, int seq, int n_heads, int n_kv_heads, int head_dim,
-                            hipStream_t stream);
+                            hipStream_t stream, float* amax = nullptr);
 
 // deepstack.hip
 // Ascending list idx[0, n_vis) of the tokens whose byte in mask is set;
