@@ -134,15 +134,23 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 constexpr bool epi_bias(int e) { return e >= static_cast<int>(Epilogue::kBias); }
+
 constexpr bool epi_residual(int e) {
   return e == static_cast<int>(Epilogue::kResidual) || e == static_cast<int>(Epilogue::kBiasResidual);
+}
+
+// silu(g) * u = g / (1 + e^-g) * u, the quotient through the hardware
+// reciprocal (v_rcp_f32, 1 ulp) instead of the IEEE division sequence: the
+// result is rounded to bf16 anyway, and the epilogue runs once per tile.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
 }
 
 // GELU, tanh form: x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), with
 // tanh(y) = 1 - 2 / (1 + e^(2y)) (saturates correctly at both ends).
 __device__ __forceinline__ float gelu_tanh(float x) {
   const float y = 0.7978845608028654f * (x + 0.044715f * x * x * x);
-  return 0.5f * x * (2.f - 2.f / (1.f + __expf(2.f * y)));
+  return 0.5f * x * (2.f - 2.f * __builtin_amdgcn_rcpf(1.f + __expf(2.f * y)));
 }
 __device__ __forceinline__ float gelu_erf(float x) {
   return 0.5f * x * (1.f + erff(x * 0.7071067811865476f));
@@ -524,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
           for (int e = 0; e < 4; ++e) {
             const float gt = acc[i][j][4 * g + e] * sg;
             const float up = acc[i + 2][j][4 * g + e] * su;
-            o[e] = gt / (1.f + __expf(-gt)) * up;
+            o[e] = silu_mul(gt, up);
           }
           u32x2 pk;
           pk[0] = pack_bf16x2(o[0], o[1]);
@@ -592,7 +600,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args)
       upsum *= args.scale_a[0] * args.scale_b[1][0];
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = sum[e] / (1.f + __expf(-sum[e])) * upsum[e];
+    for (int e = 0; e < 4; ++e) o[e] = silu_mul(sum[e], upsum[e]);
   } else {
     n = tile_n * BN + vn;
     if constexpr (F8) {
