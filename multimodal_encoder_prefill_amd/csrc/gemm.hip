@@ -457,11 +457,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       lds_barrier();
     }
   } else if (nk > 0) {
+    // k-step 0, then the first loads of k-step 1 and the warm-up of k-steps
+    // 1 .. kWarm-1 (the loop warms kWarm ahead from there) before the wait
     issue_dma(0, 0, 0, kBlks);
-    wait_vmcnt<0>();
+    for (int l = 0; l < kL0; ++l) issue_load(1, 1, l);
+    for (int kt = 1; kt < kWarm; ++kt) issue_warm(kt);
+    wait_vmcnt<kL0 + kWarm - 1>();
     lds_barrier();
     fetch(0, 0, 0);
-    for (int l = 0; l < kL0; ++l) issue_load(1, 1, l);
     for (int kt = 0; kt < nk; ++kt) {
       const int st = kt & 1;
       __builtin_amdgcn_sched_barrier(0);
