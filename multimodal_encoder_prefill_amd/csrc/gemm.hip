@@ -24,9 +24,9 @@
 // K advances 64 at a time through two LDS stages of 2 x 32 KB. Operand rows
 // are 128 bytes and their 16-byte chunks are XOR-swizzled so the ds_read_b128
 // operand fetches of 8 (or 16) consecutive lanes hit distinct banks. Tiles go
-// straight from global memory into LDS (buffer_load_dwordx4 ... lds) through
-// scalar buffer resources over 32-row blocks, so rows past M or N read as zero
-// without per-lane checks. One workgroup barrier per k-step, placed before its
+// straight from global memory into LDS (global_load_lds_dwordx4, a wave-uniform
+// base per 32-row block and one 32-bit offset per lane); lanes past the last
+// row of M or N load that row again. One workgroup barrier per k-step, placed before its
 // last k-substep: that substep's operands are already in registers, so its
 // MFMAs hide the barrier and the first operand reads of the next k-step.
 //
@@ -109,22 +109,26 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 // r..r+7 and r..r+15 map one logical chunk to distinct 16-byte bank groups.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// Buffer resource over [p, p + bytes); the pointer and size are wave-uniform
-// and are pinned to scalar registers so loads need no per-lane descriptor.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const void* p, int bytes) {
-  const uint64_t u = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
-  const uint64_t s = (static_cast<uint64_t>(hi) << 32) | lo;
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(s), (short)0,
-                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
-}
-
 // Wait until at most N vector-memory operations of this wavefront are in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// 32-bit LDS address of a pointer into the workgroup's LDS
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<size_t>((__attribute__((address_space(3))) const void*)p));
+}
+
+// global_load_lds_dwordx4 in its scalar-base form: lane L copies the 16
+// bytes at base + off (base wave-uniform, off the lane's) to LDS address
+// lds + 16 L. (The compiler builtin always forms a 64-bit address per lane.)
+// M0 carries the LDS address and needs one wait state before the load. The
+// load counts in vmcnt like any other; callers wait for it explicitly.
+__device__ __forceinline__ void global_load_lds16(const char* base, unsigned off, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
 }
 
 // Workgroup barrier that orders LDS traffic only: it waits for this
@@ -241,18 +245,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   const int kt_begin = (unit % args.ksplit) * args.kt_per_split;
   const int nk = min(kt_begin + args.kt_per_split, K / KSTEP) - kt_begin;  // k-steps of this unit
 
-  // ---- buffer resources over row blocks of kRowsPerBlk rows ----
-  // A rows m0 + row0 .. (row0 + rows) of the tile
-  auto a_block = [&](int row0, int rows) {
-    const int r = m0 + row0;
-    const int nrows = max(0, min(rows, M - r));
-    return scalar_rsrc(static_cast<const char*>(args.a) + static_cast<size_t>(min(r, M - 1)) * lda * ES,
-                       nrows > 0 ? ((nrows - 1) * lda + K) * ES : 0);
-  };
-  // B row block i of the tile
-  auto b_block = [&](int i) {
+  // ---- operand row blocks of kRowsPerBlk rows. A block i: rows
+  //      m0 + kRowsPerBlk i ..; B block i: see b_block_base. Rows past M or N
+  //      are never stored, so what is loaded for them does not matter. ----
+  // B row block i of the tile: address of its first row and the rows of its
+  // segment from there on (<= 0: the block is past N)
+  auto b_block_base = [&](int i, int& avail) -> const char* {
     const void* base;
-    int v, avail;
+    int v;
     if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
       // virtual B rows of the tile, in 32-row slots s: wave half s/4 covers
       // output columns j0 + 64 (s/4) .., slots s%4 = 0,1 gate rows, 2,3 up rows
@@ -278,19 +278,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
         avail = N - row;
       }
     }
-    const int brows = max(0, min(kRowsPerBlk, avail));
-    return scalar_rsrc(static_cast<const char*>(base) + static_cast<size_t>(v) * ldb * ES,
-                       brows > 0 ? ((brows - 1) * ldb + K) * ES : 0);
+    return static_cast<const char*>(base) + static_cast<size_t>(v) * ldb * ES;
   };
-  __amdgpu_buffer_rsrc_t a_rsrc[kBlks], b_rsrc[kBlks];
-#pragma unroll
-  for (int i = 0; i < kBlks; ++i) {
-    a_rsrc[i] = a_block(kRowsPerBlk * i, kRowsPerBlk);
-    b_rsrc[i] = b_block(i);
-  }
-  // empty range: loads through it touch no memory and return zeros
-  const __amdgpu_buffer_rsrc_t null_rsrc = scalar_rsrc(args.a, 0);
-
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -301,10 +290,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 
   // ---- global -> LDS: lane L of wave w fills 16 bytes at block row
   //      w*(1024/kRowBytes) + L/kChunks, physical chunk L%kChunks, and so
-  //      fetches the logical chunk the swizzle puts there. Blocks [b0, b1) of
-  //      both operands of k-step kt (unit-relative) go to LDS stage `stage`;
-  //      a k-step past the unit's range is loaded through the empty resource
-  //      (its zeros land in a stage that is no longer read). ----
+  //      fetches the logical chunk the swizzle puts there. ----
   const int dma_row = wave * (1024 / kRowBytes) + lane / kChunks;
   const int dma_chunk = ((lane % kChunks) ^ swz(dma_row)) * 16;
   const int dma_voff_a = dma_row * lda * ES + dma_chunk;
@@ -318,39 +304,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   //      tile_m % 8) kWarm k-steps ahead into a scratch corner of LDS, one
   //      8-row load per wavefront. (Activation rows are hits in the last-level
   //      cache and gain nothing from this.) ----
-  const __amdgpu_buffer_rsrc_t warm_b = b_block((tile_m & 7) * (32 / kRowsPerBlk));
-  const int warm_voff = (8 * wave + lane / 8) * ldb * ES + (lane % 8) * 16;
-  auto issue_warm = [&](int kt) {
-#if __HIP_DEVICE_COMPILE__
-    const int soff = (kt_begin + kt) * kRowBytes;
-    bf16_t* scratch = smem + 4 * kTileElems + wave_u * 512;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        kt < nk ? warm_b : null_rsrc, (__attribute__((address_space(3))) void*)scratch, 16,
-        warm_voff, soff, 0, 0);
-#else
-    (void)kt, (void)warm_b, (void)warm_voff;
-#endif
-  };
+  bf16_t* const warm_dst = smem + 4 * kTileElems + wave_u * 512;
 
-  // load number l of a k-step: operand l % 2 (0: A, 1: B) of row block l / 2
-  auto issue_load = [&](int kt, int stage, int l) {
-#if __HIP_DEVICE_COMPILE__  // the LDS-DMA builtin exists only in the device pass
-    const bool live = kt < nk;
-    const int soff = (kt_begin + kt) * kRowBytes;
-    const int i = l >> 1;
-    bf16_t* dst = ((l & 1) ? Bs : As) + stage * kTileElems + wave_u * 512 + i * kRowsPerBlk * BK;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        live ? ((l & 1) ? b_rsrc[i] : a_rsrc[i]) : null_rsrc,
-        (__attribute__((address_space(3))) void*)dst, 16, (l & 1) ? dma_voff_b : dma_voff_a, soff, 0, 0);
-#else
-    (void)kt, (void)stage, (void)l, (void)dma_voff_a, (void)dma_voff_b, (void)wave_u;
-    (void)null_rsrc;
-#endif
-  };
-  auto issue_dma = [&](int kt, int stage, int b0, int b1) {
+  // ---- addresses: global_load_lds_dwordx4 (a wavefront streams these 2.6x
+  //      as fast as buffer_load ... lds on gfx950, and with one wavefront per
+  //      SIMD the operand loads, not the MFMAs, set the pace). Per row block
+  //      i, the wave-uniform address of its first row and the lane's byte
+  //      offset from there, the lane's row clamped to the rows that exist:
+  //      rows past the end of A or of a B segment only feed outputs that are
+  //      never stored. ----
+  const char* a_ptr[kBlks];
+  const char* b_ptr[kBlks];
+  unsigned a_off[kBlks], b_off[kBlks];
 #pragma unroll
-    for (int l = 2 * b0; l < 2 * b1; ++l) issue_load(kt, stage, l);
-  };
+  for (int i = 0; i < kBlks; ++i) {
+    const int r = m0 + kRowsPerBlk * i;
+    a_ptr[i] = static_cast<const char*>(args.a) + static_cast<size_t>(min(r, M - 1)) * lda * ES;
+    a_off[i] = min(dma_row, max(M - r, 1) - 1) * lda * ES + dma_chunk;
+    int avail;
+    b_ptr[i] = b_block_base(i, avail);
+    b_off[i] = min(dma_row, max(avail, 1) - 1) * ldb * ES + dma_chunk;
+  }
+  // the warm-up block (computed again: a runtime index into the arrays above
+  // would put them in scratch memory); its lane offsets need no swizzle
+  int warm_avail;
+  const char* const warm_ptr = b_block_base((tile_m & 7) * (32 / kRowsPerBlk), warm_avail);
+  const unsigned warm_off = min(dma_row, max(warm_avail, 1) - 1) * ldb * ES + (lane % kChunks) * 16;
 
   // ---- LDS -> registers and MFMA: substep s of a k-step covers the row
   //      bytes 32s..32s+31 (bf16: 16 k) or 64s..64s+63 (FP8: 64 k); operands
@@ -407,10 +386,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 #pragma unroll
     for (int q = 0; q < 16; ++q) mfma_one(slot, q);
   };
+  // Load number l of k-step kt (unit-relative): operand l % 2 (0: A, 1: B)
+  // of row block l / 2, to LDS stage `stage`. The loop leaves out k-steps
+  // past the unit's range; where the prologue and the warm-up still issue
+  // one (so that the counts their waits assume hold), it loads the unit's
+  // last k-step again (a cache hit) into LDS that is not read.
+  auto koff = [&](int kt) { return static_cast<size_t>(kt_begin + min(kt, nk - 1)) * kRowBytes; };
+  auto issue_load = [&](int kt, int stage, int l) {
+    const int i = l >> 1;
+    bf16_t* dst = ((l & 1) ? Bs : As) + stage * kTileElems + wave_u * 512 + i * kRowsPerBlk * BK;
+    global_load_lds16(((l & 1) ? b_ptr[i] : a_ptr[i]) + koff(kt), (l & 1) ? b_off[i] : a_off[i], lds_addr(dst));
+  };
+  auto issue_warm = [&](int kt) { global_load_lds16(warm_ptr + koff(kt), warm_off, lds_addr(warm_dst)); };
+  auto issue_dma = [&](int kt, int stage, int b0, int b1) {
+#pragma unroll
+    for (int l = 2 * b0; l < 2 * b1; ++l) issue_load(kt, stage, l);
+  };
   // the 16 MFMAs of a substep with loads [L0, L1) of k-step kt spread evenly
-  // between them (L0, L1 compile-time: std::integral_constant)
-  auto mfma_loads = [&](int slot, int kt, int stage, auto L0, auto L1) {
-    constexpr int l0 = decltype(L0)::value, n = decltype(L1)::value - l0;
+  // between them (L0, L1 compile-time: std::integral_constant); with LIVE
+  // false (k-step kt is past the unit's range) the loads are left out
+  auto mfma_loads = [&](int slot, int kt, int stage, auto L0, auto L1, auto LIVE) {
+    constexpr int l0 = decltype(L0)::value, n = decltype(LIVE)::value ? decltype(L1)::value - l0 : 0;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       mfma_one(slot, q);
@@ -422,6 +418,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  using Live = std::true_type;
+  using Dead = std::false_type;
+
+  // The split-K output pointer is only read after the loop. Taking it into
+  // registers here completes its scalar load before the loop: a scalar load
+  // in flight at the loop entry makes every pass through the loop wait for
+  // all LDS reads (scalar loads return out of order, so the counter can only
+  // be waited to zero) before its first MFMA.
+  asm volatile("" ::"s"(args.partial));
 
   // ---- pipeline over a two-stage LDS ring. The one workgroup barrier per
   //      k-step sits before its last substep, whose operands are already in
@@ -439,7 +444,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       wait_vmcnt<2 * kBlks>();
       lds_barrier();
       fetch(0, 0, 0);
-      for (int kt = 0; kt < nk; ++kt) {
+      // one k-step; LIVE2: k-step kt+2 exists and is loaded
+      auto step = [&](int kt, auto LIVE2) {
         const int st = kt & 1;
         __builtin_amdgcn_sched_barrier(0);
         fetch(st, 1, 1);
@@ -451,8 +457,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
         lds_barrier();
         fetch(st ^ 1, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_loads(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, 2 * kBlks>());
-      }
+        mfma_loads(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, 2 * kBlks>(), LIVE2);
+      };
+      int kt = 0;
+      for (; kt < nk - 2; ++kt) step(kt, Live());
+      for (; kt < nk; ++kt) step(kt, Dead());
       wait_vmcnt<0>();
       lds_barrier();
     }
@@ -465,15 +474,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     wait_vmcnt<kL0 + kWarm - 1>();
     lds_barrier();
     fetch(0, 0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
+    // one k-step; LIVE1 / LIVE2: k-step kt+1 / kt+2 exists and is loaded
+    auto step = [&](int kt, auto LIVE1, auto LIVE2) {
       const int st = kt & 1;
       __builtin_amdgcn_sched_barrier(0);
       fetch(st, 1, 1);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_loads(0, kt + 1, st ^ 1, std::integral_constant<int, kL0>(), std::integral_constant<int, kL0 + kL1>());
+      mfma_loads(0, kt + 1, st ^ 1, std::integral_constant<int, kL0>(), std::integral_constant<int, kL0 + kL1>(),
+                 LIVE1);
       fetch(st, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_loads(1, kt + 1, st ^ 1, std::integral_constant<int, kL0 + kL1>(), std::integral_constant<int, 2 * kBlks>());
+      mfma_loads(1, kt + 1, st ^ 1, std::integral_constant<int, kL0 + kL1>(),
+                 std::integral_constant<int, 2 * kBlks>(), LIVE1);
       fetch(st, 3, 1);
       issue_warm(kt + kWarm);
       mfma(0);
@@ -484,9 +496,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       lds_barrier();
       fetch(st ^ 1, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      mfma_loads(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, kL0>());
-    }
-    // the trailing loads (empty resources) and reads have completed
+      mfma_loads(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, kL0>(), LIVE2);
+    };
+    // the last two k-steps are peeled off so that no load runs past the
+    // unit's range (the final wait would have to wait for them)
+    int kt = 0;
+    for (; kt < nk - 2; ++kt) step(kt, Live(), Live());
+    if (kt < nk - 1) step(kt++, Live(), Dead());
+    step(kt, Dead(), Dead());
+    // the trailing loads and reads have completed
     wait_vmcnt<0>();
     lds_barrier();
   }
