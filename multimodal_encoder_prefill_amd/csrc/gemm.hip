@@ -15,11 +15,13 @@
 //             VisionPatchMerger; the MLP's GELU is the tanh form, the
 //             merger's the erf form)
 //
-// Tiling: a 256 (m) x 256 (n) output tile per workgroup of 4 wavefronts, each
-// wavefront owning 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 with
-// the accumulators in AGPRs. The weight rows are the MFMA "A" operand and the
-// activation rows the "B" operand, so every lane ends up with 4 consecutive
-// output columns (8-byte stores).
+// Tiling: a 256 (m) x 64 NB (n) output tile per workgroup of 4 wavefronts, each
+// wavefront owning 128 x 32 NB as NB x 4 blocks of v_mfma_f32_32x32x16_bf16
+// (NB = 4: 256 AGPR accumulators; NB = 5: 320, the rest in VGPRs). The weight
+// rows are the MFMA "A" operand and the activation rows the "B" operand, so
+// every lane ends up with 4 consecutive output columns (8-byte stores). The
+// 320-wide form reads 10% fewer LDS bytes per MFMA and makes 4096 x 5120,
+// 4096 x 10240 and 4096 x 2 x 25600 outputs exact multiples of 256 tiles.
 //
 // K advances 64 at a time through two LDS stages of 2 x 32 KB. Operand rows
 // are 128 bytes and their 16-byte chunks are XOR-swizzled so the ds_read_b128
@@ -43,7 +45,7 @@ namespace mhe {
 namespace {
 
 constexpr int BM = 256;
-constexpr int BN = 256;
+constexpr int BN = 256;  // n extent of the NB = 4 tile (and of the FP8 kernels)
 constexpr int kThreads = 256;
 constexpr int kGroupM = 8;  // m tiles per ordering group
 constexpr int kXcds = 8;
@@ -203,27 +205,39 @@ __device__ __forceinline__ u32x2 finish4(float* o, const GemmArgs& args, int n, 
 // same 128-byte row pieces, LDS layout and loads as bf16) in two substeps of
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales), and the sums are
 // multiplied by scale_a * scale_b before the epilogue.
-template <int EPI, bool F8>
+//
+// NB: 32-row weight blocks per wavefront (4 or 5; the tile is 64 NB wide).
+template <int EPI, bool F8, int NB>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) {
+  static_assert(NB == 4 || (NB == 5 && !F8), "tile width");
   constexpr int ES = F8 ? 1 : 2;                // bytes per element
   constexpr int KSTEP = 128 / ES;               // k elements per pipeline step
-  constexpr int kTileElems = BM * BK;           // one operand, one stage (bf16 units)
+  constexpr int BNT = 64 * NB;                  // n extent of the tile (weight rows)
+  constexpr int kATile = BM * BK;               // A operand, one stage (bf16 units)
+  constexpr int kBTile = BNT * BK;              // B operand, one stage
   constexpr int kRowBytes = BK * 2;
   constexpr int kChunks = BK / 8;               // 16-byte chunks per row
   constexpr int kRowsPerBlk = 4096 / kRowBytes; // rows one load instruction of the 4 waves covers
-  constexpr int kBlks = 256 / kRowsPerBlk;      // load instructions per operand per k-step
-  // The 2 kBlks loads of k-step kt+1 are issued in up to three parts: loads
+  constexpr int kBlksA = BM / kRowsPerBlk;      // load instructions for A per k-step
+  constexpr int kBlksB = BNT / kRowsPerBlk;     // ... and for B
+  constexpr int kLoads = kBlksA + kBlksB;
+  constexpr int kMf = 4 * NB;                   // MFMAs per substep
+  // SwiGLU tiles of 320 virtual rows pair gate and up rows inside each 32-row
+  // block (8-row groups alternate gate, up), so a lane holds both factors of
+  // its outputs; the 256-row tiles pair block i with block i + 2.
+  constexpr bool kPairInBlock = EPI == static_cast<int>(Epilogue::kSwiGLU) && NB == 5;
+  // The kLoads loads of k-step kt+1 are issued in up to three parts: loads
   // [0, kL0) during the last substep of k-step kt-1, the next kL1 and the rest
   // during substeps 0 and 1 of k-step kt, each part spread evenly over the
   // substep's MFMAs. (Issuing all of them in one substep is slower, and so is
   // issuing the last ones late in substep 1.)
   constexpr int kL0 = 8, kL1 = 8;
   constexpr int kWarm = 4;  // warm-up distance in k-steps
-  static_assert(BK == 64 && kL0 + kL1 <= 2 * kBlks, "pipeline shape");
+  static_assert(BK == 64 && kL0 + kL1 <= kLoads, "pipeline shape");
 
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
-  bf16_t* As = smem;                  // [2][BM][BK]
-  bf16_t* Bs = smem + 2 * kTileElems; // [2][BN][BK], then 4 KB of warm-up scratch
+  bf16_t* As = smem;              // [2][BM][BK]
+  bf16_t* Bs = smem + 2 * kATile; // [2][BNT][BK], then 4 KB of warm-up scratch
 
   const int M = args.m, N = args.n, K = args.k;
   const int lda = args.lda, ldb = args.ldb;
@@ -249,11 +263,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   //      m0 + kRowsPerBlk i ..; B block i: see b_block_base. Rows past M or N
   //      are never stored, so what is loaded for them does not matter. ----
   // B row block i of the tile: address of its first row and the rows of its
-  // segment from there on (<= 0: the block is past N)
+  // segment from there on (<= 0: the block is past N). With kPairInBlock the
+  // address is that of this wavefront's 8-row piece of the block.
   auto b_block_base = [&](int i, int& avail) -> const char* {
     const void* base;
     int v;
-    if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+    if constexpr (kPairInBlock) {
+      // block i: wave half i / NB, block i % NB of it; the 8-row group of
+      // wavefront w is gate rows for even w, up rows for odd w, output
+      // columns j .. j+7
+      const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      const int j = tile_n * (BNT / 2) + (i / NB) * (16 * NB) + (i % NB) * 16 + (w >> 1) * 8;
+      base = (w & 1) ? args.bptr[1] : args.bptr[0];
+      v = min(j, N - 1);
+      avail = N - j;
+    } else if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
       // virtual B rows of the tile, in 32-row slots s: wave half s/4 covers
       // output columns j0 + 64 (s/4) .., slots s%4 = 0,1 gate rows, 2,3 up rows
       const int s = i * (kRowsPerBlk / 32);
@@ -262,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       v = min(j, N - 1);
       avail = N - j;
     } else {
-      const int row = tile_n * BN + kRowsPerBlk * i;
+      const int row = tile_n * BNT + kRowsPerBlk * i;
       const int rr = min(row, N - 1);
       if (rr < args.brows[0]) {
         base = args.bptr[0];
@@ -280,21 +304,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     }
     return static_cast<const char*>(base) + static_cast<size_t>(v) * ldb * ES;
   };
+  // Accumulators: weight blocks 0-3 through the MFMA builtin (the compiler
+  // keeps them in the 256 AGPRs); block 4 of the 320-wide tile in VGPRs,
+  // through inline assembly (left to itself the compiler shuffles all 320
+  // between the two register files). The compiler does not know that those
+  // assembly statements are MFMAs, so the two VALU/MFMA hazards on their
+  // results are covered by hand: a wait after zeroing them and one before
+  // they are read (see mfma_one and the end of the pipeline).
   f32x16 acc[4][4];
+  f32x16 acc4[NB > 4 ? 4 : 1];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+#pragma unroll
+  for (int j = 0; j < (NB > 4 ? 4 : 1); ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc4[j][e] = 0.f;
+  if constexpr (NB > 4)  // VALU writes, then MFMA reads of the same VGPRs
+    asm volatile("s_nop 4" : "+v"(acc4[0]), "+v"(acc4[1]), "+v"(acc4[2]), "+v"(acc4[3]));
+  // accumulator block (i, j)
+  auto A = [&](int i, int j) -> f32x16& { return i < 4 ? acc[i][j] : acc4[j]; };
 
   // ---- global -> LDS: lane L of wave w fills 16 bytes at block row
   //      w*(1024/kRowBytes) + L/kChunks, physical chunk L%kChunks, and so
   //      fetches the logical chunk the swizzle puts there. ----
   const int dma_row = wave * (1024 / kRowBytes) + lane / kChunks;
   const int dma_chunk = ((lane % kChunks) ^ swz(dma_row)) * 16;
-  const int dma_voff_a = dma_row * lda * ES + dma_chunk;
-  const int dma_voff_b = dma_row * ldb * ES + dma_chunk;
+  // the lane's row relative to the address b_block_base returns
+  const int b_lane_row = kPairInBlock ? lane / kChunks : dma_row;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // ---- L2 warm-up. The tiles running together on one XCD share operand
   //      blocks (tile_coords: 8 m-tiles x 4 n-tiles), so without help the
@@ -304,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   //      tile_m % 8) kWarm k-steps ahead into a scratch corner of LDS, one
   //      8-row load per wavefront. (Activation rows are hits in the last-level
   //      cache and gain nothing from this.) ----
-  bf16_t* const warm_dst = smem + 4 * kTileElems + wave_u * 512;
+  bf16_t* const warm_dst = smem + 2 * kATile + 2 * kBTile + wave_u * 512;
 
   // ---- addresses: global_load_lds_dwordx4 (a wavefront streams these 2.6x
   //      as fast as buffer_load ... lds on gfx950, and with one wavefront per
@@ -313,23 +353,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   //      offset from there, the lane's row clamped to the rows that exist:
   //      rows past the end of A or of a B segment only feed outputs that are
   //      never stored. ----
-  const char* a_ptr[kBlks];
-  const char* b_ptr[kBlks];
-  unsigned a_off[kBlks], b_off[kBlks];
+  const char* a_ptr[kBlksA];
+  const char* b_ptr[kBlksB];
+  unsigned a_off[kBlksA], b_off[kBlksB];
 #pragma unroll
-  for (int i = 0; i < kBlks; ++i) {
+  for (int i = 0; i < kBlksA; ++i) {
     const int r = m0 + kRowsPerBlk * i;
     a_ptr[i] = static_cast<const char*>(args.a) + static_cast<size_t>(min(r, M - 1)) * lda * ES;
     a_off[i] = min(dma_row, max(M - r, 1) - 1) * lda * ES + dma_chunk;
+  }
+#pragma unroll
+  for (int i = 0; i < kBlksB; ++i) {
     int avail;
     b_ptr[i] = b_block_base(i, avail);
-    b_off[i] = min(dma_row, max(avail, 1) - 1) * ldb * ES + dma_chunk;
+    b_off[i] = min(b_lane_row, max(avail, 1) - 1) * ldb * ES + dma_chunk;
   }
   // the warm-up block (computed again: a runtime index into the arrays above
   // would put them in scratch memory); its lane offsets need no swizzle
   int warm_avail;
   const char* const warm_ptr = b_block_base((tile_m & 7) * (32 / kRowsPerBlk), warm_avail);
-  const unsigned warm_off = min(dma_row, max(warm_avail, 1) - 1) * ldb * ES + (lane % kChunks) * 16;
+  const unsigned warm_off = min(b_lane_row, max(warm_avail, 1) - 1) * ldb * ES + (lane % kChunks) * 16;
 
   // ---- LDS -> registers and MFMA: substep s of a k-step covers the row
   //      bytes 32s..32s+31 (bf16: 16 k) or 64s..64s+63 (FP8: 64 k); operands
@@ -341,12 +384,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   const int lhalf = lane >> 5;
   const int lswz = swz(lrow);
   const int a_base = (wm * 128 + lrow) * BK;  // activation rows (MFMA B operand)
-  const int b_base = (wn * 128 + lrow) * BK;  // weight rows (MFMA A operand)
-  bf16x8 wop[2][4], xop[2][4];
+  const int b_base = (wn * 32 * NB + lrow) * BK;  // weight rows (MFMA A operand)
+  bf16x8 wop[2][NB], xop[2][4];
   i32x8 wop8[2][4], xop8[2][4];
   auto fetch = [&](int stage, int s, int slot) {
-    const bf16_t* as = As + stage * kTileElems;
-    const bf16_t* bs = Bs + stage * kTileElems;
+    const bf16_t* as = As + stage * kATile;
+    const bf16_t* bs = Bs + stage * kBTile;
     if constexpr (F8) {
       const int c0 = ((4 * s + 2 * lhalf) ^ lswz) << 3;
       const int c1 = ((4 * s + 2 * lhalf + 1) ^ lswz) << 3;
@@ -366,54 +409,62 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
         wop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + chunk));
         xop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + chunk));
       }
+#pragma unroll
+      for (int i = 4; i < NB; ++i)
+        wop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + chunk));
     }
   };
   // blocks in order of max(i, j), so the MFMAs that need the operands read
-  // last come last
+  // last come last (weight block 4, read after the others, at the end)
   auto mfma_one = [&](int slot, int q) {
-    // q-th block in that order: q = d*d + e for d = 0..3, e = 0..2d
+    // q-th block in that order: q = d*d + e for d = 0..3, e = 0..2d; then
+    // (4, q - 16)
     const int d = q < 1 ? 0 : q < 4 ? 1 : q < 9 ? 2 : 3;
     const int e = q - d * d;
-    const int i = e <= d ? e : d, j = e <= d ? d : 2 * d - e;
+    const int i = q >= 16 ? 4 : e <= d ? e : d, j = q >= 16 ? q - 16 : e <= d ? d : 2 * d - e;
     if constexpr (F8)
       // E4M3 operands (format 0), block scales 127 (= 2^0)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop8[slot][i], xop8[slot][j], acc[i][j], 0, 0,
                                                                   0, 127, 0, 127);
-    else
+    else if (i < 4)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[slot][i], xop[slot][j], acc[i][j], 0, 0, 0);
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc4[j]) : "v"(wop[slot][4]), "v"(xop[slot][j]));
   };
   auto mfma = [&](int slot) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) mfma_one(slot, q);
+    for (int q = 0; q < kMf; ++q) mfma_one(slot, q);
   };
-  // Load number l of k-step kt (unit-relative): operand l % 2 (0: A, 1: B)
-  // of row block l / 2, to LDS stage `stage`. The loop leaves out k-steps
+  // Load number l of k-step kt (unit-relative), to LDS stage `stage`: below
+  // 2 kBlksA, operand l % 2 (0: A, 1: B) of row block l / 2; from there on, B
+  // row block l - kBlksA. The loop leaves out k-steps
   // past the unit's range; where the prologue and the warm-up still issue
   // one (so that the counts their waits assume hold), it loads the unit's
   // last k-step again (a cache hit) into LDS that is not read.
   auto koff = [&](int kt) { return static_cast<size_t>(kt_begin + min(kt, nk - 1)) * kRowBytes; };
   auto issue_load = [&](int kt, int stage, int l) {
-    const int i = l >> 1;
-    bf16_t* dst = ((l & 1) ? Bs : As) + stage * kTileElems + wave_u * 512 + i * kRowsPerBlk * BK;
-    global_load_lds16(((l & 1) ? b_ptr[i] : a_ptr[i]) + koff(kt), (l & 1) ? b_off[i] : a_off[i], lds_addr(dst));
+    const bool isb = l >= 2 * kBlksA || (l & 1);
+    const int i = l >= 2 * kBlksA ? l - kBlksA : l >> 1;
+    bf16_t* dst = (isb ? Bs + stage * kBTile : As + stage * kATile) + wave_u * 512 + i * kRowsPerBlk * BK;
+    global_load_lds16((isb ? b_ptr[i] : a_ptr[i]) + koff(kt), isb ? b_off[i] : a_off[i], lds_addr(dst));
   };
   auto issue_warm = [&](int kt) { global_load_lds16(warm_ptr + koff(kt), warm_off, lds_addr(warm_dst)); };
-  auto issue_dma = [&](int kt, int stage, int b0, int b1) {
+  auto issue_dma = [&](int kt, int stage) {
 #pragma unroll
-    for (int l = 2 * b0; l < 2 * b1; ++l) issue_load(kt, stage, l);
+    for (int l = 0; l < kLoads; ++l) issue_load(kt, stage, l);
   };
-  // the 16 MFMAs of a substep with loads [L0, L1) of k-step kt spread evenly
+  // the kMf MFMAs of a substep with loads [L0, L1) of k-step kt spread evenly
   // between them (L0, L1 compile-time: std::integral_constant); with LIVE
   // false (k-step kt is past the unit's range) the loads are left out
   auto mfma_loads = [&](int slot, int kt, int stage, auto L0, auto L1, auto LIVE) {
     constexpr int l0 = decltype(L0)::value, n = decltype(LIVE)::value ? decltype(L1)::value - l0 : 0;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < kMf; ++q) {
       mfma_one(slot, q);
       if constexpr (n > 0) {
 #pragma unroll
         for (int j = 0; j < n; ++j)
-          if (j * 16 / n == q) issue_load(kt, stage, l0 + j);
+          if (j * kMf / n == q) issue_load(kt, stage, l0 + j);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -439,9 +490,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     // issue rate as bf16), so a whole substep separates the last of them
     // from the wait that needs them.
     if (nk > 0) {
-      issue_dma(0, 0, 0, kBlks);
-      issue_dma(1, 1, 0, kBlks);
-      wait_vmcnt<2 * kBlks>();
+      issue_dma(0, 0);
+      issue_dma(1, 1);
+      wait_vmcnt<kLoads>();
       lds_barrier();
       fetch(0, 0, 0);
       // one k-step; LIVE2: k-step kt+2 exists and is loaded
@@ -457,7 +508,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
         lds_barrier();
         fetch(st ^ 1, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
-        mfma_loads(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, 2 * kBlks>(), LIVE2);
+        mfma_loads(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, kLoads>(), LIVE2);
       };
       int kt = 0;
       for (; kt < nk - 2; ++kt) step(kt, Live());
@@ -468,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   } else if (nk > 0) {
     // k-step 0, then the first loads of k-step 1 and the warm-up of k-steps
     // 1 .. kWarm-1 (the loop warms kWarm ahead from there) before the wait
-    issue_dma(0, 0, 0, kBlks);
+    issue_dma(0, 0);
     for (int l = 0; l < kL0; ++l) issue_load(1, 1, l);
     for (int kt = 1; kt < kWarm; ++kt) issue_warm(kt);
     wait_vmcnt<kL0 + kWarm - 1>();
@@ -485,7 +536,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       fetch(st, 2, 0);
       __builtin_amdgcn_sched_barrier(0);
       mfma_loads(1, kt + 1, st ^ 1, std::integral_constant<int, kL0 + kL1>(),
-                 std::integral_constant<int, 2 * kBlks>(), LIVE1);
+                 std::integral_constant<int, kLoads>(), LIVE1);
       fetch(st, 3, 1);
       issue_warm(kt + kWarm);
       mfma(0);
@@ -509,21 +560,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     lds_barrier();
   }
 
+  // MFMA writes of the VGPR accumulators, then VALU reads: 32 wait states
+  // cover the longest (16-pass) MFMA
+  if constexpr (NB > 4)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+v"(acc4[0]), "+v"(acc4[1]), "+v"(acc4[2]), "+v"(acc4[3]));
+
   // ---- split-K unit: raw accumulators to the unit's partial tile, laid out
   //      [m_local][virtual n] so 4 consecutive n are one 16-byte store ----
   if (args.ksplit > 1) {
-    float* dst = args.partial + static_cast<size_t>(unit) * BM * BN;
+    float* dst = args.partial + static_cast<size_t>(unit) * BM * BNT;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ml = wm * 128 + j * 32 + lrow;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
-          *reinterpret_cast<f32x4*>(dst + ml * BN + wn * 128 + i * 32 + 8 * g + 4 * lhalf) = v;
+          for (int e = 0; e < 4; ++e) v[e] = A(i, j)[4 * g + e];
+          *reinterpret_cast<f32x4*>(dst + ml * BNT + wn * 32 * NB + i * 32 + 8 * g + 4 * lhalf) = v;
         }
     }
     return;
@@ -541,7 +598,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + wm * 128 + j * 32 + lrow;
     if (m >= M) continue;
-    if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+    if constexpr (kPairInBlock) {
+      // block i: gate rows in groups g = 0, 2, their up rows in g + 1
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          const int col = tile_n * (BNT / 2) + wn * 16 * NB + i * 16 + gp * 8 + 4 * lhalf;
+          if (col >= N) continue;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = silu_mul(A(i, j)[8 * gp + e], A(i, j)[8 * gp + 4 + e]);
+          u32x2 pk;
+          pk[0] = pack_bf16x2(o[0], o[1]);
+          pk[1] = pack_bf16x2(o[2], o[3]);
+          *reinterpret_cast<u32x2*>(args.c + static_cast<size_t>(m) * args.ldc + col) = pk;
+        }
+    } else if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int jb = tile_n * (BN / 2) + wn * 64 + i * 32;
@@ -564,8 +637,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int nb = tile_n * BN + wn * 128 + i * 32;
+      for (int i = 0; i < NB; ++i) {
+        const int nb = tile_n * BNT + wn * 32 * NB + i * 32;
         if (nb >= N) continue;
         const float sc = F8 ? f8_scale(args, nb) : 1.f;
 #pragma unroll
@@ -573,7 +646,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
           const size_t off = static_cast<size_t>(m) * args.ldc + nb + 8 * g + 4 * lhalf;
           float o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = acc[i][j][4 * g + e] * sc;
+          for (int e = 0; e < 4; ++e) o[e] = A(i, j)[4 * g + e] * sc;
           *reinterpret_cast<u32x2*>(args.c + off) = finish4<EPI>(o, args, nb + 8 * g + 4 * lhalf, off);
         }
       }
@@ -588,25 +661,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 }
 
 // Sums the ksplit partial tiles of each split tile in a fixed order and
-// applies the epilogue. Block (t, y) handles rows 4y..4y+3 of split tile t;
-// each thread 4 consecutive virtual columns.
-template <int EPI, bool F8>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args) {
+// applies the epilogue. Block (t, y) of 64 NB threads handles rows 4y..4y+3
+// of split tile t; each thread 4 consecutive virtual columns.
+template <int EPI, bool F8, int NB>
+__global__ __launch_bounds__(64 * NB) void splitk_reduce_kernel(const GemmArgs args) {
+  constexpr int BNT = 64 * NB;
+  constexpr int kRowThreads = BNT / 4;
   const int t = blockIdx.x;
-  const int ml = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int vn = (threadIdx.x & 63) * 4;
+  const int ml = blockIdx.y * 4 + threadIdx.x / kRowThreads;
+  const int vn = (threadIdx.x % kRowThreads) * 4;
   int tile_m, tile_n;
   tile_coords(args.tile_begin + t, args.tiles_m, args.tiles_n, tile_m, tile_n);
   const int m = tile_m * BM + ml;
   bool live = m < args.m;  // every thread stays to the end (workgroup maximum)
-  const float* src = args.partial + static_cast<size_t>(t) * args.ksplit * BM * BN + ml * BN + vn;
+  const float* src = args.partial + static_cast<size_t>(t) * args.ksplit * BM * BNT + ml * BNT + vn;
   f32x4 sum = *reinterpret_cast<const f32x4*>(src);
   for (int sidx = 1; sidx < args.ksplit; ++sidx)
-    sum += *reinterpret_cast<const f32x4*>(src + static_cast<size_t>(sidx) * BM * BN);
+    sum += *reinterpret_cast<const f32x4*>(src + static_cast<size_t>(sidx) * BM * BNT);
   const int N = args.n;
   float o[4];
   int n;
-  if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+  if (EPI == static_cast<int>(Epilogue::kSwiGLU) && NB == 5) {
+    // virtual column vn: wave half vn/160, block (vn%160)/32, 8-row group
+    // (vn%32)/8; even groups are gate columns whose up partner sits 8 later
+    const int r = vn % 160, grp = (r & 31) >> 3;
+    live = live && (grp & 1) == 0;
+    const int uo = (grp & 1) == 0 ? 8 : 0;
+    f32x4 upsum = *reinterpret_cast<const f32x4*>(src + uo);
+    for (int sidx = 1; sidx < args.ksplit; ++sidx)
+      upsum += *reinterpret_cast<const f32x4*>(src + uo + static_cast<size_t>(sidx) * BM * BNT);
+    n = tile_n * (BNT / 2) + (vn / 160) * 80 + (r >> 5) * 16 + (grp >> 1) * 8 + (r & 7);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = silu_mul(sum[e], upsum[e]);
+  } else if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
     // virtual column vn: wave half vn/128, 32-wide slot (vn%128)/32; slots 0,1
     // are gate columns whose up partner sits 64 virtual columns later
     const int slot = (vn & 127) >> 5;
@@ -614,7 +701,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args)
     const f32x4 up = *reinterpret_cast<const f32x4*>(src + (slot < 2 ? 64 : 0));
     f32x4 upsum = up;
     for (int sidx = 1; sidx < args.ksplit; ++sidx)
-      upsum += *reinterpret_cast<const f32x4*>(src + (slot < 2 ? 64 : 0) + static_cast<size_t>(sidx) * BM * BN);
+      upsum += *reinterpret_cast<const f32x4*>(src + (slot < 2 ? 64 : 0) + static_cast<size_t>(sidx) * BM * BNT);
     n = tile_n * (BN / 2) + (vn >> 7) * 64 + slot * 32 + (vn & 31);
     if constexpr (F8) {
       sum *= args.scale_a[0] * args.scale_b[0][0];
@@ -623,7 +710,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args)
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = silu_mul(sum[e], upsum[e]);
   } else {
-    n = tile_n * BN + vn;
+    n = tile_n * BNT + vn;
     if constexpr (F8) {
       if (n < N) sum *= f8_scale(args, n);
     }
@@ -647,18 +734,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs args)
   }
 }
 
-template <int EPI, bool F8>
+template <int EPI, bool F8, int NB>
 hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
-  constexpr size_t smem = static_cast<size_t>(2) * 2 * BM * BK * sizeof(bf16_t) + 4096;
+  // two stages of both operands, then the warm-up scratch (4 KB)
+  constexpr size_t smem = static_cast<size_t>(2) * (BM + 64 * NB) * BK * sizeof(bf16_t) + 4096;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_kernel<EPI, F8>),
+        reinterpret_cast<const void*>(&gemm_kernel<EPI, F8, NB>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<EPI, F8>), dim3(grid), dim3(kThreads), smem,
+  hipLaunchKernelGGL((gemm_kernel<EPI, F8, NB>), dim3(grid), dim3(kThreads), smem,
                      stream, args);
   return hipGetLastError();
 }
@@ -687,13 +775,17 @@ int device_cus() {
   return cus;
 }
 
-template <int EPI, bool F8>
+template <int EPI, bool F8, int NB>
 hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t stream, int* amax_count) {
-  // One workgroup fills a CU (128 KB of LDS), so a launch of T tiles runs in
-  // ceil(T / CUs) waves. Full waves run whole tiles; when the last wave would
-  // leave at least half the CUs idle and is a sizeable part of the launch (at
-  // most 4 full waves before it), its R tiles are cut into ksplit k-ranges
-  // (ksplit * R <= CUs) whose fp32 partials are summed by a small reduction.
+  // One workgroup fills a CU (128 or 144 KB of LDS), so a launch of T tiles
+  // runs in ceil(T / CUs) waves. Full waves run whole tiles; when the last
+  // wave would leave at least half the CUs idle and is a sizeable part of the
+  // launch (at most 4 full waves before it), its R tiles are cut into ksplit
+  // k-ranges (ksplit * R <= CUs) whose fp32 partials are summed by a small
+  // reduction.
+  constexpr int BNT = 64 * NB;
+  const int tn = EPI == static_cast<int>(Epilogue::kSwiGLU) ? BNT / 2 : BNT;  // output columns per tile
+  args.tiles_n = (args.n + tn - 1) / tn;
   const int tiles = args.tiles_m * args.tiles_n;
   const int nk = args.k / (F8 ? 2 * BK : BK);  // k-steps (128 row bytes each)
   static const int cus = device_cus();
@@ -704,7 +796,7 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
   if (partial && rem > 0 && rem <= cus / 2 && tiles / cus <= 4 && amax_fits) {
     ksplit = min(cus / rem, 16);
     ksplit = min(ksplit, nk / 4);
-    const size_t cap = partial_bytes / (static_cast<size_t>(BM) * BN * sizeof(float));
+    const size_t cap = partial_bytes / (static_cast<size_t>(BM) * BNT * sizeof(float));
     while (ksplit > 1 && static_cast<size_t>(ksplit) * rem > cap) --ksplit;
   }
   const int full = ksplit > 1 ? tiles - rem : tiles;
@@ -716,7 +808,7 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
     a.ksplit = 1;
     a.kt_per_split = nk;
     a.partial = nullptr;
-    if ((e = launch_epi<EPI, F8>(a, full, stream)) != hipSuccess) return e;
+    if ((e = launch_epi<EPI, F8, NB>(a, full, stream)) != hipSuccess) return e;
   }
   if (amax_count) *amax_count = full + (ksplit > 1 ? rem * (BM / 4) : 0);
   if (ksplit > 1) {
@@ -727,8 +819,8 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
     a.kt_per_split = (nk + ksplit - 1) / ksplit;
     a.partial = partial;
     a.amax = args.amax ? args.amax + full : nullptr;
-    if ((e = launch_epi<EPI, F8>(a, a.units, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL((splitk_reduce_kernel<EPI, F8>), dim3(rem, BM / 4), dim3(256), 0, stream, a);
+    if ((e = launch_epi<EPI, F8, NB>(a, a.units, stream)) != hipSuccess) return e;
+    hipLaunchKernelGGL((splitk_reduce_kernel<EPI, F8, NB>), dim3(rem, BM / 4), dim3(BNT), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -777,23 +869,33 @@ hipError_t launch_common(Epilogue epi, bool f8, const void* a, int lda, const fl
   args.ldb = ldb;
   args.ldc = ldc;
   args.tiles_m = (m + BM - 1) / BM;
-  args.tiles_n = epi == Epilogue::kSwiGLU ? (n + BN / 2 - 1) / (BN / 2) : (n + BN - 1) / BN;
   if (f8) {
     switch (epi) {
-      case Epilogue::kStore: return run<0, true>(args, partial, partial_bytes, stream, amax_count);
-      case Epilogue::kResidual: return run<1, true>(args, partial, partial_bytes, stream, amax_count);
-      case Epilogue::kSwiGLU: return run<2, true>(args, partial, partial_bytes, stream, amax_count);
+      case Epilogue::kStore: return run<0, true, 4>(args, partial, partial_bytes, stream, amax_count);
+      case Epilogue::kResidual: return run<1, true, 4>(args, partial, partial_bytes, stream, amax_count);
+      case Epilogue::kSwiGLU: return run<2, true, 4>(args, partial, partial_bytes, stream, amax_count);
       default: return hipErrorInvalidValue;  // the biased forms are bf16 only
     }
   }
+  // the decoder's bf16 linears take 320-wide tiles where those fill whole
+  // waves of the chip exactly
+  static const int cus = device_cus();
+  const int wide_cols = epi == Epilogue::kSwiGLU ? 160 : 320;  // output columns of a 320-wide tile
+  const bool wide = n % wide_cols == 0 && (args.tiles_m * (n / wide_cols)) % cus == 0;
   switch (epi) {
-    case Epilogue::kStore: return run<0, false>(args, partial, partial_bytes, stream, amax_count);
-    case Epilogue::kResidual: return run<1, false>(args, partial, partial_bytes, stream, amax_count);
-    case Epilogue::kSwiGLU: return run<2, false>(args, partial, partial_bytes, stream, amax_count);
-    case Epilogue::kBias: return run<3, false>(args, partial, partial_bytes, stream, amax_count);
-    case Epilogue::kBiasResidual: return run<4, false>(args, partial, partial_bytes, stream, amax_count);
-    case Epilogue::kBiasGeluTanh: return run<5, false>(args, partial, partial_bytes, stream, amax_count);
-    case Epilogue::kBiasGeluErf: return run<6, false>(args, partial, partial_bytes, stream, amax_count);
+    case Epilogue::kStore:
+      return wide ? run<0, false, 5>(args, partial, partial_bytes, stream, amax_count)
+                  : run<0, false, 4>(args, partial, partial_bytes, stream, amax_count);
+    case Epilogue::kResidual:
+      return wide ? run<1, false, 5>(args, partial, partial_bytes, stream, amax_count)
+                  : run<1, false, 4>(args, partial, partial_bytes, stream, amax_count);
+    case Epilogue::kSwiGLU:
+      return wide ? run<2, false, 5>(args, partial, partial_bytes, stream, amax_count)
+                  : run<2, false, 4>(args, partial, partial_bytes, stream, amax_count);
+    case Epilogue::kBias: return run<3, false, 4>(args, partial, partial_bytes, stream, amax_count);
+    case Epilogue::kBiasResidual: return run<4, false, 4>(args, partial, partial_bytes, stream, amax_count);
+    case Epilogue::kBiasGeluTanh: return run<5, false, 4>(args, partial, partial_bytes, stream, amax_count);
+    case Epilogue::kBiasGeluErf: return run<6, false, 4>(args, partial, partial_bytes, stream, amax_count);
   }
   return hipErrorInvalidValue;
 }

@@ -156,6 +156,43 @@ def test_linear_full_size_sampled_rows(name, m, n, k):
     assert report(f"{name} sampled", f64(c)[rows], ref)[0] <= 4e-3
 
 
+@pytest.mark.parametrize("m,n,k,residual", [
+    (4000, 5120, 320, True),     # 16 x 16 tiles of 256 x 320, ragged last m-tile
+    (4096, 10240, 192, False),   # 16 x 32 tiles
+])
+def test_linear_wide_tiles_dense(m, n, k, residual):
+    """Shapes whose 320-wide tiles fill whole waves of the chip, every output
+    against the oracle."""
+    print(f"linear wide m={m} n={n} k={k} residual={residual}", flush=True)
+    a = _randn((m, k), 70)
+    w = _randn((n, k), 71, 0.05)
+    c = _randn((m, n), 72) if residual else torch.empty((m, n), device=DEV, dtype=torch.bfloat16)
+    r0 = f64(c) if residual else 0.0
+    b.linear(a, w, c, m, n, k, residual=c if residual else None, workspace=_gemm_ws())
+    torch.cuda.synchronize()
+    ref = r0 + f64(a) @ f64(w).T
+    r, mx = report("linear wide", f64(c), ref)
+    assert r <= 4e-3
+    assert mx <= 2.0 ** -7 * np.max(np.abs(ref))
+
+
+def test_swiglu_wide_tiles_dense():
+    """gate/up with 320-row tiles (gate and up rows interleaved in 8-row
+    groups inside each 32-row block), every output against the oracle."""
+    m, n, k = 4000, 25600, 192
+    a = _randn((m, k), 73)
+    wg = _randn((n, k), 74, 0.1)
+    wu = _randn((n, k), 75, 0.1)
+    c = torch.empty((m, n), device=DEV, dtype=torch.bfloat16)
+    b.linear_swiglu(a, wg, wu, c, m, n, k, workspace=_gemm_ws())
+    torch.cuda.synchronize()
+    ar = f64(a)
+    ref = oracle.silu(ar @ f64(wg).T) * (ar @ f64(wu).T)
+    r, mx = report("swiglu wide", f64(c), ref)
+    assert r <= 4e-3
+    assert mx <= 2.0 ** -7 * np.max(np.abs(ref))
+
+
 def test_swiglu_full_size_sampled_rows():
     m, n, k = 4096, 25600, 5120
     a = _randn((m, k), 60)
