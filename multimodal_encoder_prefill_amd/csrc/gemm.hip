@@ -30,7 +30,10 @@
 // base per 32-row block and one 32-bit offset per lane); lanes past the last
 // row of M or N load that row again. One workgroup barrier per k-step, placed before its
 // last k-substep: that substep's operands are already in registers, so its
-// MFMAs hide the barrier and the first operand reads of the next k-step.
+// MFMAs hide the barrier and the first operand reads of the next k-step. The
+// LDS reads of a substep's operands go out one at a time between the MFMAs
+// of the substep before (a burst of all of them, from all four wavefronts at
+// once, left the MFMAs waiting on the LDS).
 //
 // Workgroups are remapped so that each XCD (workgroups are dealt round-robin
 // over the 8 XCDs) receives a contiguous run of tiles, ordered in groups of m
@@ -469,6 +472,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // the r-th operand read of fetch(stage, s, slot) (bf16): w0 x0 w1 x1 ... w4
+  constexpr int kReads = 8 + (NB - 4);
+  auto fetch_one = [&](int stage, int s, int slot, int r) {
+    const bf16_t* as = As + stage * kATile;
+    const bf16_t* bs = Bs + stage * kBTile;
+    const int chunk = ((2 * s + lhalf) ^ lswz) << 3;
+    const int i = r < 8 ? r >> 1 : 4;
+    if (r < 8 && (r & 1))
+      xop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + chunk));
+    else
+      wop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + chunk));
+  };
+  // the kMf MFMAs of a substep with loads [L0, L1) of k-step kt and the
+  // operand reads of fetch(fst, fs, fslot) spread between them
+  auto mfma_rl = [&](int slot, int kt, int stage, auto L0, auto L1, auto LIVE, int fst, int fs, int fslot) {
+    constexpr int l0 = decltype(L0)::value, n = decltype(LIVE)::value ? decltype(L1)::value - l0 : 0;
+#pragma unroll
+    for (int q = 0; q < kMf; ++q) {
+      mfma_one(slot, q);
+#pragma unroll
+      for (int r = 0; r < kReads; ++r)
+        if (r * (kMf * 3 / 4) / kReads == q) fetch_one(fst, fs, fslot, r);
+      if constexpr (n > 0) {
+#pragma unroll
+        for (int j = 0; j < n; ++j)
+          if (j * kMf / n == q) issue_load(kt, stage, l0 + j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   using Live = std::true_type;
   using Dead = std::false_type;
 
@@ -529,25 +562,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     auto step = [&](int kt, auto LIVE1, auto LIVE2) {
       const int st = kt & 1;
       __builtin_amdgcn_sched_barrier(0);
-      fetch(st, 1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_loads(0, kt + 1, st ^ 1, std::integral_constant<int, kL0>(), std::integral_constant<int, kL0 + kL1>(),
-                 LIVE1);
-      fetch(st, 2, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_loads(1, kt + 1, st ^ 1, std::integral_constant<int, kL0 + kL1>(),
-                 std::integral_constant<int, kLoads>(), LIVE1);
-      fetch(st, 3, 1);
+      mfma_rl(0, kt + 1, st ^ 1, std::integral_constant<int, kL0>(), std::integral_constant<int, kL0 + kL1>(),
+              LIVE1, st, 1, 1);
+      mfma_rl(1, kt + 1, st ^ 1, std::integral_constant<int, kL0 + kL1>(),
+              std::integral_constant<int, kLoads>(), LIVE1, st, 2, 0);
       issue_warm(kt + kWarm);
-      mfma(0);
+      mfma_rl(0, kt + 1, st ^ 1, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), Dead(), st, 3, 1);
       __builtin_amdgcn_sched_barrier(0);
       // k-step kt+1 is complete in LDS (only the warm-up load just issued may
       // still be in flight) and no wavefront reads stage st any more
       wait_vmcnt<1>();
       lds_barrier();
-      fetch(st ^ 1, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_loads(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, kL0>(), LIVE2);
+      mfma_rl(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, kL0>(), LIVE2, st ^ 1, 0, 0);
     };
     // the last two k-steps are peeled off so that no load runs past the
     // unit's range (the final wait would have to wait for them)
