@@ -233,8 +233,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   // [0, kL0) during the last substep of k-step kt-1, the next kL1 and the rest
   // during substeps 0 and 1 of k-step kt, each part spread evenly over the
   // substep's MFMAs. (Issuing all of them in one substep is slower, and so is
-  // issuing the last ones late in substep 1.)
-  constexpr int kL0 = 8, kL1 = 8;
+  // issuing the last ones late in substep 1; the 320-wide tile's 18 loads go
+  // out 10 + 8.)
+  constexpr int kL0 = NB == 5 ? 10 : 8, kL1 = 8;
   constexpr int kWarm = 4;  // warm-up distance in k-steps
   static_assert(BK == 64 && kL0 + kL1 <= kLoads, "pipeline shape");
 
@@ -390,30 +391,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   const int b_base = (wn * 32 * NB + lrow) * BK;  // weight rows (MFMA A operand)
   bf16x8 wop[2][NB], xop[2][4];
   i32x8 wop8[2][4], xop8[2][4];
-  auto fetch = [&](int stage, int s, int slot) {
+  // the r-th operand of substep s of LDS stage `stage`, into register slot
+  // `slot`: w0 x0 w1 x1 ... (w4); an FP8 operand is two 16-byte reads
+  constexpr int kReads = 8 + (NB - 4);
+  auto fetch_one = [&](int stage, int s, int slot, int r) {
     const bf16_t* as = As + stage * kATile;
     const bf16_t* bs = Bs + stage * kBTile;
+    const int i = r < 8 ? r >> 1 : 4;
     if constexpr (F8) {
       const int c0 = ((4 * s + 2 * lhalf) ^ lswz) << 3;
       const int c1 = ((4 * s + 2 * lhalf + 1) ^ lswz) << 3;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 w0 = *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + c0);
-        const u32x4 w1 = *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + c1);
-        const u32x4 x0 = *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + c0);
-        const u32x4 x1 = *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + c1);
-        wop8[slot][i] = __builtin_bit_cast(i32x8, __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7));
-        xop8[slot][i] = __builtin_bit_cast(i32x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+      const bf16_t* src = (r & 1) ? as + a_base + i * 32 * BK : bs + b_base + i * 32 * BK;
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(src + c0);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(src + c1);
+      const i32x8 v = __builtin_bit_cast(i32x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+      if (r & 1)
+        xop8[slot][i] = v;
+      else
+        wop8[slot][i] = v;
     } else {
       const int chunk = ((2 * s + lhalf) ^ lswz) << 3;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + chunk));
+      if (r < 8 && (r & 1))
         xop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + chunk));
-      }
-#pragma unroll
-      for (int i = 4; i < NB; ++i)
+      else
         wop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + chunk));
     }
   };
@@ -434,10 +434,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     else
       asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc4[j]) : "v"(wop[slot][4]), "v"(xop[slot][j]));
   };
-  auto mfma = [&](int slot) {
-#pragma unroll
-    for (int q = 0; q < kMf; ++q) mfma_one(slot, q);
-  };
   // Load number l of k-step kt (unit-relative), to LDS stage `stage`: below
   // 2 kBlksA, operand l % 2 (0: A, 1: B) of row block l / 2; from there on, B
   // row block l - kBlksA. The loop leaves out k-steps
@@ -456,36 +452,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 #pragma unroll
     for (int l = 0; l < kLoads; ++l) issue_load(kt, stage, l);
   };
-  // the kMf MFMAs of a substep with loads [L0, L1) of k-step kt spread evenly
-  // between them (L0, L1 compile-time: std::integral_constant); with LIVE
-  // false (k-step kt is past the unit's range) the loads are left out
-  auto mfma_loads = [&](int slot, int kt, int stage, auto L0, auto L1, auto LIVE) {
-    constexpr int l0 = decltype(L0)::value, n = decltype(LIVE)::value ? decltype(L1)::value - l0 : 0;
-#pragma unroll
-    for (int q = 0; q < kMf; ++q) {
-      mfma_one(slot, q);
-      if constexpr (n > 0) {
-#pragma unroll
-        for (int j = 0; j < n; ++j)
-          if (j * kMf / n == q) issue_load(kt, stage, l0 + j);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // the r-th operand read of fetch(stage, s, slot) (bf16): w0 x0 w1 x1 ... w4
-  constexpr int kReads = 8 + (NB - 4);
-  auto fetch_one = [&](int stage, int s, int slot, int r) {
-    const bf16_t* as = As + stage * kATile;
-    const bf16_t* bs = Bs + stage * kBTile;
-    const int chunk = ((2 * s + lhalf) ^ lswz) << 3;
-    const int i = r < 8 ? r >> 1 : 4;
-    if (r < 8 && (r & 1))
-      xop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + chunk));
-    else
-      wop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + chunk));
-  };
   // the kMf MFMAs of a substep with loads [L0, L1) of k-step kt and the
-  // operand reads of fetch(fst, fs, fslot) spread between them
+  // operands of substep fs of LDS stage fst (into register slot fslot) spread
+  // between them (L0, L1 compile-time: std::integral_constant; with LIVE
+  // false, k-step kt is past the unit's range and the loads are left out)
   auto mfma_rl = [&](int slot, int kt, int stage, auto L0, auto L1, auto LIVE, int fst, int fs, int fslot) {
     constexpr int l0 = decltype(L0)::value, n = decltype(LIVE)::value ? decltype(L1)::value - l0 : 0;
 #pragma unroll
@@ -527,21 +497,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       issue_dma(1, 1);
       wait_vmcnt<kLoads>();
       lds_barrier();
-      fetch(0, 0, 0);
+      for (int r = 0; r < kReads; ++r) fetch_one(0, 0, 0, r);
       // one k-step; LIVE2: k-step kt+2 exists and is loaded
       auto step = [&](int kt, auto LIVE2) {
         const int st = kt & 1;
         __builtin_amdgcn_sched_barrier(0);
-        fetch(st, 1, 1);
         issue_warm(kt + kWarm);
-        mfma(0);
+        mfma_rl(0, kt, st, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), Dead(), st, 1, 1);
         __builtin_amdgcn_sched_barrier(0);
         // k-step kt+1 is complete in LDS and no wavefront reads stage st any more
         wait_vmcnt<1>();
         lds_barrier();
-        fetch(st ^ 1, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_loads(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, kLoads>(), LIVE2);
+        mfma_rl(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, kLoads>(), LIVE2,
+                st ^ 1, 0, 0);
       };
       int kt = 0;
       for (; kt < nk - 2; ++kt) step(kt, Live());
@@ -557,7 +525,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     for (int kt = 1; kt < kWarm; ++kt) issue_warm(kt);
     wait_vmcnt<kL0 + kWarm - 1>();
     lds_barrier();
-    fetch(0, 0, 0);
+    for (int r = 0; r < kReads; ++r) fetch_one(0, 0, 0, r);
     // one k-step; LIVE1 / LIVE2: k-step kt+1 / kt+2 exists and is loaded
     auto step = [&](int kt, auto LIVE1, auto LIVE2) {
       const int st = kt & 1;
