@@ -104,7 +104,7 @@ def _gemm_ws():
     (512, 5120, 8192, True),      # 40 tiles: all split 6 ways along k
     (300, 96, 1024, False),       # ragged m, one partial n tile, 4-way split
     (1000, 2048, 1024, True),     # 32 tiles
-    (4096, 5120, 25600, True),    # down projection: 256 whole tiles + 64 tiles split 4 ways
+    (4096, 5120, 25600, True),    # down projection: 256 tiles of 256 x 320, none split
 ])
 def test_linear_split_k(m, n, k, residual):
     """The last wave of tiles is split along k into fp32 partials and reduced."""
@@ -284,6 +284,39 @@ def test_attention(seq, hq, hkv, d):
     torch.cuda.synchronize()
     ref = oracle.causal_gqa_attention(f64(q), f64(k), f64(v)).reshape(seq, hq * d)
     r, _ = report("attention", f64(o), ref)
+    assert r <= 8e-3
+
+
+@pytest.mark.parametrize("seq", [1, 32, 33, 64, 65, 96, 127, 128, 129, 191, 256])
+def test_attention_group8_tile_edges(seq):
+    """8 query heads per key/value head at head_dim 128 around the 32-query
+    block and key-tile boundaries: one to three key tiles, the masked last
+    tile at both offsets of a query block, ragged ends."""
+    print(f"attention g8 seq={seq}", flush=True)
+    hq, hkv, d = 16, 2, 128
+    q, k, v, k_l, vt_l = _attn_inputs(seq, hq, hkv, d, 300 + seq)
+    o = torch.empty((seq, hq * d), device=DEV, dtype=torch.bfloat16)
+    b.attention(q, k_l, vt_l, o, seq, hq, hkv, d)
+    torch.cuda.synchronize()
+    ref = oracle.causal_gqa_attention(f64(q), f64(k), f64(v)).reshape(seq, hq * d)
+    r, _ = report("attention g8", f64(o), ref)
+    assert r <= 8e-3
+
+
+def test_attention_rising_scores_rescale():
+    """Keys whose scale grows along the sequence, so the running maximum of
+    most queries rises by far more than the lazy threshold on later tiles and
+    the earlier output is rescaled many times."""
+    seq, hq, hkv, d = 600, 8, 1, 128
+    q, k, v, k_l, vt_l = _attn_inputs(seq, hq, hkv, d, 17)
+    ramp = torch.linspace(0.05, 20.0, seq, device=DEV).reshape(seq, 1, 1)
+    k = (k.float() * ramp).to(torch.bfloat16)
+    k_l[:, :seq] = k.transpose(0, 1)
+    o = torch.empty((seq, hq * d), device=DEV, dtype=torch.bfloat16)
+    b.attention(q, k_l, vt_l, o, seq, hq, hkv, d)
+    torch.cuda.synchronize()
+    ref = oracle.causal_gqa_attention(f64(q), f64(k), f64(v)).reshape(seq, hq * d)
+    r, _ = report("attention rising", f64(o), ref)
     assert r <= 8e-3
 
 
