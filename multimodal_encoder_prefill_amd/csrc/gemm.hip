@@ -131,10 +131,16 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 // lds + 16 L. (The compiler builtin always forms a 64-bit address per lane.)
 // M0 carries the LDS address and needs one wait state before the load. The
 // load counts in vmcnt like any other; callers wait for it explicitly.
+// clang warns that M0 is a reserved register it may not preserve across the
+// statement: nothing in this file's device code reads M0 except these loads
+// (the generated code holds no other M0 access), so the warning is silenced.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void global_load_lds16(const char* base, unsigned off, unsigned lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
                : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Workgroup barrier that orders LDS traffic only: it waits for this
 // wavefront's LDS operations but leaves global loads in flight.

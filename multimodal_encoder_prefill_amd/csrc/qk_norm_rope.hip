@@ -80,11 +80,12 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
     //      slots 4-7 / 12-15 (perm16). ----
     const int vbase = (n_heads + n_kv_heads) * D;
     const int half = threadIdx.x & 1;
+    for (int g16 = s0; g16 < s0 + kTok; g16 += 16)
     for (int c = threadIdx.x >> 1; c < n_kv_heads * D / 8; c += kThreads / 2) {
       u32x4 v[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const int s = s0 + 8 * half + t;
+        const int s = g16 + 8 * half + t;
         v[t] = s < seq ? *reinterpret_cast<const u32x4*>(qkv + static_cast<size_t>(s) * width + vbase + c * 8)
                        : u32x4{0, 0, 0, 0};
       }
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
         a[1] = e[2] | (e[3] << 16);
         b2[0] = e[4] | (e[5] << 16);
         b2[1] = e[6] | (e[7] << 16);
-        bf16_t* row = vt_out + static_cast<size_t>(col) * seq_pad + s0;
+        bf16_t* row = vt_out + static_cast<size_t>(col) * seq_pad + g16;
         *reinterpret_cast<u32x2*>(row + 4 * half) = a;
         *reinterpret_cast<u32x2*>(row + 8 + 4 * half) = b2;
       }
