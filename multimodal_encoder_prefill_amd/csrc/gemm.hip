@@ -568,7 +568,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 
   // ---- split-K unit: raw accumulators to the unit's partial tile, laid out
   //      [m_local][virtual n] so 4 consecutive n are one 16-byte store ----
-  if (args.ksplit > 1) {
+  // (320-wide tiles are only used where they fill whole waves, never split)
+  if (NB == 4 && args.ksplit > 1) {
     float* dst = args.partial + static_cast<size_t>(unit) * BM * BNT;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -588,6 +589,67 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 
   // ---- epilogue: lane holds column m = lrow of each 32x32 block and rows
   //      n = 8 g + 4 lhalf + e (e < 4) for the four groups g ----
+  if constexpr (NB == 5) {
+    // 320-wide tiles only run where N is a multiple of the tile, so only
+    // rows past M need care: buffer accesses through resources that end at
+    // row M drop those stores (and read zeros) with no branch, which keeps
+    // the accumulators in place; each 32-row block's residual loads all go
+    // out before its stores.
+    const size_t rbytes = static_cast<size_t>(M - m0) * args.ldc * sizeof(bf16_t);
+    const int nbytes = static_cast<int>(rbytes < 0x7fffffffu ? rbytes : 0x7fffffffu);
+    const size_t first = static_cast<size_t>(m0) * args.ldc;
+    const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(args.c + first, (short)0, nbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t r_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        epi_residual(EPI) ? const_cast<bf16_t*>(args.r) + first : args.c + first, (short)0, nbytes, 0x00020000);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row_bytes = (wm * 128 + j * 32 + lrow) * args.ldc * static_cast<int>(sizeof(bf16_t));
+      if constexpr (kPairInBlock) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int gp = 0; gp < 2; ++gp) {
+            const int col = tile_n * (BNT / 2) + wn * 16 * NB + i * 16 + gp * 8 + 4 * lhalf;
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = silu_mul(A(i, j)[8 * gp + e], A(i, j)[8 * gp + 4 + e]);
+            u32x2 pk;
+            pk[0] = pack_bf16x2(o[0], o[1]);
+            pk[1] = pack_bf16x2(o[2], o[3]);
+            __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + col * 2, 0, 0);
+          }
+      } else {
+        const int nbase = tile_n * BNT + wn * 32 * NB + 4 * lhalf;
+        u32x2 rv[NB][4];
+        if constexpr (epi_residual(EPI)) {
+#pragma unroll
+          for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+              rv[i][g] = __builtin_amdgcn_raw_buffer_load_b64(r_rsrc, row_bytes + (nbase + i * 32 + 8 * g) * 2, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = A(i, j)[4 * g + e];
+            if constexpr (epi_residual(EPI)) {
+              o[0] += __uint_as_float(rv[i][g][0] << 16);
+              o[1] += __uint_as_float(rv[i][g][0] & 0xffff0000u);
+              o[2] += __uint_as_float(rv[i][g][1] << 16);
+              o[3] += __uint_as_float(rv[i][g][1] & 0xffff0000u);
+            }
+            u32x2 pk;
+            pk[0] = pack_bf16x2(o[0], o[1]);
+            pk[1] = pack_bf16x2(o[2], o[3]);
+            __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + (nbase + i * 32 + 8 * g) * 2, 0, 0);
+          }
+      }
+    }
+    return;
+  }
   float amx = 0.f;           // kSwiGLU: max |C| over this lane's outputs
   float sg = 1.f, su = 1.f;  // FP8 SwiGLU: scales of the gate and up products
   if constexpr (F8 && EPI == static_cast<int>(Epilogue::kSwiGLU)) {
@@ -598,23 +660,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   for (int j = 0; j < 4; ++j) {
     const int m = m0 + wm * 128 + j * 32 + lrow;
     if (m >= M) continue;
-    if constexpr (kPairInBlock) {
-      // block i: gate rows in groups g = 0, 2, their up rows in g + 1
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-          const int col = tile_n * (BNT / 2) + wn * 16 * NB + i * 16 + gp * 8 + 4 * lhalf;
-          if (col >= N) continue;
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = silu_mul(A(i, j)[8 * gp + e], A(i, j)[8 * gp + 4 + e]);
-          u32x2 pk;
-          pk[0] = pack_bf16x2(o[0], o[1]);
-          pk[1] = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<u32x2*>(args.c + static_cast<size_t>(m) * args.ldc + col) = pk;
-        }
-    } else if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+    if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int jb = tile_n * (BN / 2) + wn * 64 + i * 32;
@@ -793,7 +839,7 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
   int ksplit = 1;
   // (with amax output, the row groups of the split tiles must fit gemm_amax_parts)
   const bool amax_fits = !args.amax || (tiles + rem * (BM / 4) <= gemm_amax_parts(args.m, args.n));
-  if (partial && rem > 0 && rem <= cus / 2 && tiles / cus <= 4 && amax_fits) {
+  if (NB == 4 && partial && rem > 0 && rem <= cus / 2 && tiles / cus <= 4 && amax_fits) {
     ksplit = min(cus / rem, 16);
     ksplit = min(ksplit, nk / 4);
     const size_t cap = partial_bytes / (static_cast<size_t>(BM) * BNT * sizeof(float));
