@@ -181,10 +181,10 @@ __device__ __forceinline__ float f8_scale(const GemmArgs& args, int n) {
   return args.scale_a[0] * sb;
 }
 
-// Non-SwiGLU epilogue of four consecutive outputs (columns n..n+3 of the row
-// at element offset `off`), rounded to bf16 once.
+// Non-SwiGLU epilogue of four consecutive outputs (columns n..n+3; rv: their
+// residual, loaded by the caller), rounded to bf16 once.
 template <int EPI>
-__device__ __forceinline__ u32x2 finish4(float* o, const GemmArgs& args, int n, size_t off) {
+__device__ __forceinline__ u32x2 finish4(float* o, const GemmArgs& args, int n, u32x2 rv) {
   if constexpr (epi_bias(EPI)) {
     const u32x2 bv = *reinterpret_cast<const u32x2*>(args.bias + n);
     o[0] += __uint_as_float(bv[0] << 16);
@@ -193,7 +193,6 @@ __device__ __forceinline__ u32x2 finish4(float* o, const GemmArgs& args, int n, 
     o[3] += __uint_as_float(bv[1] & 0xffff0000u);
   }
   if constexpr (epi_residual(EPI)) {
-    const u32x2 rv = *reinterpret_cast<const u32x2*>(args.r + off);
     o[0] += __uint_as_float(rv[0] << 16);
     o[1] += __uint_as_float(rv[0] & 0xffff0000u);
     o[2] += __uint_as_float(rv[1] << 16);
@@ -216,9 +215,13 @@ __device__ __forceinline__ u32x2 finish4(float* o, const GemmArgs& args, int n, 
 // multiplied by scale_a * scale_b before the epilogue.
 //
 // NB: 32-row weight blocks per wavefront (4 or 5; the tile is 64 NB wide).
-template <int EPI, bool F8, int NB>
+// SPLIT: the units are k-ranges of split tiles whose raw fp32 sums go to
+// `partial` (a separate instantiation, so that each kernel has one epilogue:
+// with both in one kernel the compiler read every accumulator out ahead of
+// the branch and spilled them).
+template <int EPI, bool F8, int NB, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) {
-  static_assert(NB == 4 || (NB == 5 && !F8), "tile width");
+  static_assert(NB == 4 || (NB == 5 && !F8 && !SPLIT), "tile width");
   constexpr int ES = F8 ? 1 : 2;                // bytes per element
   constexpr int KSTEP = 128 / ES;               // k elements per pipeline step
   constexpr int BNT = 64 * NB;                  // n extent of the tile (weight rows)
@@ -568,8 +571,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 
   // ---- split-K unit: raw accumulators to the unit's partial tile, laid out
   //      [m_local][virtual n] so 4 consecutive n are one 16-byte store ----
-  // (320-wide tiles are only used where they fill whole waves, never split)
-  if (NB == 4 && args.ksplit > 1) {
+  // ---- split-K unit: raw accumulators to the unit's partial tile, laid out
+  //      [m_local][virtual n] so 4 consecutive n are one 16-byte store ----
+  if constexpr (SPLIT) {
     float* dst = args.partial + static_cast<size_t>(unit) * BM * BNT;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -588,69 +592,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   }
 
   // ---- epilogue: lane holds column m = lrow of each 32x32 block and rows
-  //      n = 8 g + 4 lhalf + e (e < 4) for the four groups g ----
-  if constexpr (NB == 5) {
-    // 320-wide tiles only run where N is a multiple of the tile, so only
-    // rows past M need care: buffer accesses through resources that end at
-    // row M drop those stores (and read zeros) with no branch, which keeps
-    // the accumulators in place; each 32-row block's residual loads all go
-    // out before its stores.
-    const size_t rbytes = static_cast<size_t>(M - m0) * args.ldc * sizeof(bf16_t);
-    const int nbytes = static_cast<int>(rbytes < 0x7fffffffu ? rbytes : 0x7fffffffu);
-    const size_t first = static_cast<size_t>(m0) * args.ldc;
-    const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(args.c + first, (short)0, nbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t r_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        epi_residual(EPI) ? const_cast<bf16_t*>(args.r) + first : args.c + first, (short)0, nbytes, 0x00020000);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row_bytes = (wm * 128 + j * 32 + lrow) * args.ldc * static_cast<int>(sizeof(bf16_t));
-      if constexpr (kPairInBlock) {
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-          for (int gp = 0; gp < 2; ++gp) {
-            const int col = tile_n * (BNT / 2) + wn * 16 * NB + i * 16 + gp * 8 + 4 * lhalf;
-            float o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = silu_mul(A(i, j)[8 * gp + e], A(i, j)[8 * gp + 4 + e]);
-            u32x2 pk;
-            pk[0] = pack_bf16x2(o[0], o[1]);
-            pk[1] = pack_bf16x2(o[2], o[3]);
-            __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + col * 2, 0, 0);
-          }
-      } else {
-        const int nbase = tile_n * BNT + wn * 32 * NB + 4 * lhalf;
-        u32x2 rv[NB][4];
-        if constexpr (epi_residual(EPI)) {
-#pragma unroll
-          for (int i = 0; i < NB; ++i)
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-              rv[i][g] = __builtin_amdgcn_raw_buffer_load_b64(r_rsrc, row_bytes + (nbase + i * 32 + 8 * g) * 2, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = A(i, j)[4 * g + e];
-            if constexpr (epi_residual(EPI)) {
-              o[0] += __uint_as_float(rv[i][g][0] << 16);
-              o[1] += __uint_as_float(rv[i][g][0] & 0xffff0000u);
-              o[2] += __uint_as_float(rv[i][g][1] << 16);
-              o[3] += __uint_as_float(rv[i][g][1] & 0xffff0000u);
-            }
-            u32x2 pk;
-            pk[0] = pack_bf16x2(o[0], o[1]);
-            pk[1] = pack_bf16x2(o[2], o[3]);
-            __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + (nbase + i * 32 + 8 * g) * 2, 0, 0);
-          }
-      }
-    }
-    return;
-  }
-  float amx = 0.f;           // kSwiGLU: max |C| over this lane's outputs
+  //      n = 8 g + 4 lhalf + e (e < 4) for the four groups g. Rows past M
+  //      need no branch: C and the residual are accessed through buffer
+  //      resources that end at row M, which drop those stores and read
+  //      zeros (those rows computed from copies of row M-1, so their values
+  //      are finite and never exceed a real row's in the SwiGLU maximum).
+  //      Column blocks past N (partial n-tiles of the 256-wide form) are
+  //      skipped by wave-uniform tests. Each 32-row block's residual loads
+  //      go out before its stores. ----
+  const size_t rbytes = static_cast<size_t>(M - m0) * args.ldc * sizeof(bf16_t);
+  const int nbytes = static_cast<int>(rbytes < 0x7fffffffu ? rbytes : 0x7fffffffu);
+  const size_t first = static_cast<size_t>(m0) * args.ldc;
+  const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(args.c + first, (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t r_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      epi_residual(EPI) ? const_cast<bf16_t*>(args.r) + first : args.c + first, (short)0, nbytes, 0x00020000);
+  float amx = 0.f;           // FP8 kSwiGLU: max |C| over this lane's outputs
   float sg = 1.f, su = 1.f;  // FP8 SwiGLU: scales of the gate and up products
   if constexpr (F8 && EPI == static_cast<int>(Epilogue::kSwiGLU)) {
     sg = args.scale_a[0] * args.scale_b[0][0];
@@ -658,9 +614,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int m = m0 + wm * 128 + j * 32 + lrow;
-    if (m >= M) continue;
-    if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+    const int row_bytes = (wm * 128 + j * 32 + lrow) * args.ldc * static_cast<int>(sizeof(bf16_t));
+    if constexpr (kPairInBlock) {
+      // block i: gate rows in groups g = 0, 2, their up rows in g + 1
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          const int col = tile_n * (BNT / 2) + wn * 16 * NB + i * 16 + gp * 8 + 4 * lhalf;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = silu_mul(A(i, j)[8 * gp + e], A(i, j)[8 * gp + 4 + e]);
+          u32x2 pk;
+          pk[0] = pack_bf16x2(o[0], o[1]);
+          pk[1] = pack_bf16x2(o[2], o[3]);
+          __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + col * 2, 0, 0);
+        }
+    } else if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+      // gate block i pairs with up block i + 2
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int jb = tile_n * (BN / 2) + wn * 64 + i * 32;
@@ -669,31 +640,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
         for (int g = 0; g < 4; ++g) {
           float o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float gt = acc[i][j][4 * g + e] * sg;
-            const float up = acc[i + 2][j][4 * g + e] * su;
-            o[e] = silu_mul(gt, up);
-          }
+          for (int e = 0; e < 4; ++e) o[e] = silu_mul(acc[i][j][4 * g + e] * sg, acc[i + 2][j][4 * g + e] * su);
           u32x2 pk;
           pk[0] = pack_bf16x2(o[0], o[1]);
           pk[1] = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<u32x2*>(args.c + static_cast<size_t>(m) * args.ldc + jb + 8 * g + 4 * lhalf) = pk;
+          __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + (jb + 8 * g + 4 * lhalf) * 2, 0, 0);
           if constexpr (F8) amx = fmaxf(amx, abs_max4(pk));
         }
       }
     } else {
+      // (a residual load past N reads other columns of the buffer, or zeros
+      // past its end, for an output that is not stored)
+      const int nbase = tile_n * BNT + wn * 32 * NB;
+      u32x2 rv[NB][4];
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          rv[i][g] = epi_residual(EPI) ? __builtin_amdgcn_raw_buffer_load_b64(
+                                             r_rsrc, row_bytes + (nbase + i * 32 + 8 * g + 4 * lhalf) * 2, 0, 0)
+                                       : u32x2{0, 0};
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const int nb = tile_n * BNT + wn * 32 * NB + i * 32;
-        if (nb >= N) continue;
+        const int nb = nbase + i * 32;
+        if (NB == 4 && nb >= N) continue;  // the 320-wide form never has a partial n-tile
         const float sc = F8 ? f8_scale(args, nb) : 1.f;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const size_t off = static_cast<size_t>(m) * args.ldc + nb + 8 * g + 4 * lhalf;
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = A(i, j)[4 * g + e] * sc;
-          *reinterpret_cast<u32x2*>(args.c + off) = finish4<EPI>(o, args, nb + 8 * g + 4 * lhalf, off);
+          const u32x2 pk = finish4<EPI>(o, args, nb + 8 * g + 4 * lhalf, rv[i][g]);
+          __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + (nb + 8 * g + 4 * lhalf) * 2, 0, 0);
         }
       }
     }
@@ -775,24 +753,25 @@ __global__ __launch_bounds__(64 * NB) void splitk_reduce_kernel(const GemmArgs a
       const float v = workgroup_max(live ? abs_max4(pk) : 0.f, red);
       if (threadIdx.x == 0) args.amax[t * (BM / 4) + blockIdx.y] = v;
     }
-  } else {
-    if (live) *reinterpret_cast<u32x2*>(args.c + off) = finish4<EPI>(o, args, n, off);
+  } else if (live) {
+    const u32x2 rv = epi_residual(EPI) ? *reinterpret_cast<const u32x2*>(args.r + off) : u32x2{0, 0};
+    *reinterpret_cast<u32x2*>(args.c + off) = finish4<EPI>(o, args, n, rv);
   }
 }
 
-template <int EPI, bool F8, int NB>
+template <int EPI, bool F8, int NB, bool SPLIT>
 hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
   // two stages of both operands, then the warm-up scratch (4 KB)
   constexpr size_t smem = static_cast<size_t>(2) * (BM + 64 * NB) * BK * sizeof(bf16_t) + 4096;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_kernel<EPI, F8, NB>),
+        reinterpret_cast<const void*>(&gemm_kernel<EPI, F8, NB, SPLIT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((gemm_kernel<EPI, F8, NB>), dim3(grid), dim3(kThreads), smem,
+  hipLaunchKernelGGL((gemm_kernel<EPI, F8, NB, SPLIT>), dim3(grid), dim3(kThreads), smem,
                      stream, args);
   return hipGetLastError();
 }
@@ -854,7 +833,7 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
     a.ksplit = 1;
     a.kt_per_split = nk;
     a.partial = nullptr;
-    if ((e = launch_epi<EPI, F8, NB>(a, full, stream)) != hipSuccess) return e;
+    if ((e = launch_epi<EPI, F8, NB, false>(a, full, stream)) != hipSuccess) return e;
   }
   if (amax_count) *amax_count = full + (ksplit > 1 ? rem * (BM / 4) : 0);
   if (ksplit > 1) {
@@ -865,7 +844,9 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
     a.kt_per_split = (nk + ksplit - 1) / ksplit;
     a.partial = partial;
     a.amax = args.amax ? args.amax + full : nullptr;
-    if ((e = launch_epi<EPI, F8, NB>(a, a.units, stream)) != hipSuccess) return e;
+    if constexpr (NB == 4) {
+      if ((e = launch_epi<EPI, F8, NB, true>(a, a.units, stream)) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((splitk_reduce_kernel<EPI, F8, NB>), dim3(rem, BM / 4), dim3(BNT), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
