@@ -530,7 +530,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     // k-step 0, then the first loads of k-step 1 and the warm-up of k-steps
     // 1 .. kWarm-1 (the loop warms kWarm ahead from there) before the wait
     issue_dma(0, 0);
+#pragma unroll
     for (int l = 0; l < kL0; ++l) issue_load(1, 1, l);
+#pragma unroll
     for (int kt = 1; kt < kWarm; ++kt) issue_warm(kt);
     wait_vmcnt<kL0 + kWarm - 1>();
     lds_barrier();
