@@ -23,7 +23,8 @@
 // 320-wide form reads 10% fewer LDS bytes per MFMA and makes 4096 x 5120,
 // 4096 x 10240 and 4096 x 2 x 25600 outputs exact multiples of 256 tiles.
 //
-// K advances 64 at a time through two LDS stages of 2 x 32 KB. Operand rows
+// K advances 64 at a time through two LDS stages of (256 + 64 NB) rows of
+// 128 bytes (64 or 72 KB each). Operand rows
 // are 128 bytes and their 16-byte chunks are XOR-swizzled so the ds_read_b128
 // operand fetches of 8 (or 16) consecutive lanes hit distinct banks. Tiles go
 // straight from global memory into LDS (global_load_lds_dwordx4, a wave-uniform
@@ -38,6 +39,12 @@
 // Workgroups are remapped so that each XCD (workgroups are dealt round-robin
 // over the 8 XCDs) receives a contiguous run of tiles, ordered in groups of m
 // tiles so tiles running together on one XCD share A and B panels in its L2.
+//
+// The epilogue has no per-row branch: C and the residual are addressed
+// through buffer resources that end at row M, so the hardware drops stores
+// to (and reads zeros from) rows past it; k-split units are a separate
+// instantiation that only writes fp32 partials. (Branches there made the
+// compiler copy every accumulator out of the AGPRs up front and spill them.)
 #include <type_traits>
 
 #include "common.h"
