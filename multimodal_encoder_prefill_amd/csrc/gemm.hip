@@ -45,6 +45,9 @@
 // to (and reads zeros from) rows past it; k-split units are a separate
 // instantiation that only writes fp32 partials. (Branches there made the
 // compiler copy every accumulator out of the AGPRs up front and spill them.)
+// The plain-store and SwiGLU forms of the 320-wide tile pass their bf16
+// outputs through LDS, which is free once the pipeline ends, and store whole
+// row segments in 16-byte chunks instead of 8 bytes per row and lane.
 #include <type_traits>
 
 #include "common.h"
@@ -580,8 +583,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 
   // ---- split-K unit: raw accumulators to the unit's partial tile, laid out
   //      [m_local][virtual n] so 4 consecutive n are one 16-byte store ----
-  // ---- split-K unit: raw accumulators to the unit's partial tile, laid out
-  //      [m_local][virtual n] so 4 consecutive n are one 16-byte store ----
   if constexpr (SPLIT) {
     float* dst = args.partial + static_cast<size_t>(unit) * BM * BNT;
 #pragma unroll
@@ -621,66 +622,122 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     sg = args.scale_a[0] * args.scale_b[0][0];
     su = args.scale_a[0] * args.scale_b[1][0];
   }
+  if constexpr (kPairInBlock) {
+    // Gate rows are groups g = 0, 2 of block i, their up rows g + 1. The
+    // wave's 128 x 80 outputs pass through its own LDS region (rows of 88
+    // bf16 = 176 bytes: 16-byte aligned, and a write instruction's 32 rows
+    // spread over all 64 banks, two rows a bank) and leave as 16-byte chunks
+    // along the rows, 10 consecutive lanes per 160-byte row segment, instead
+    // of 16 bytes in each of 32 rows per store instruction.
+    constexpr int kStg = 88;
+    bf16_t* const stg = smem + wave_u * 128 * kStg;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row_bytes = (wm * 128 + j * 32 + lrow) * args.ldc * static_cast<int>(sizeof(bf16_t));
-    if constexpr (kPairInBlock) {
-      // block i: gate rows in groups g = 0, 2, their up rows in g + 1
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
-          const int col = tile_n * (BNT / 2) + wn * 16 * NB + i * 16 + gp * 8 + 4 * lhalf;
           float o[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[e] = silu_mul(A(i, j)[8 * gp + e], A(i, j)[8 * gp + 4 + e]);
           u32x2 pk;
           pk[0] = pack_bf16x2(o[0], o[1]);
           pk[1] = pack_bf16x2(o[2], o[3]);
-          __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + col * 2, 0, 0);
+          *reinterpret_cast<u32x2*>(stg + (j * 32 + lrow) * kStg + i * 16 + gp * 8 + 4 * lhalf) = pk;
         }
-    } else if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
-      // gate block i pairs with up block i + 2
+    // a wavefront's LDS operations complete in order; the wait only makes
+    // the compiler keep the reads below after the writes of other lanes
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    const int col0 = tile_n * (BNT / 2) + wn * 16 * NB;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int jb = tile_n * (BN / 2) + wn * 64 + i * 32;
-        if (jb >= N) continue;
+    for (int it = 0; it < 128 * 10 / 64; ++it) {
+      const int c = it * 64 + lane, r = c / 10, q = c - r * 10;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + q * 8);
+      const int off = (wm * 128 + r) * args.ldc * static_cast<int>(sizeof(bf16_t)) + (col0 + q * 8) * 2;
+      __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
+    }
+  } else if constexpr (NB == 5 && !epi_residual(EPI)) {
+    // Plain stores of the 320-wide tile: the wave's 128 x 160 outputs in
+    // two halves of 64 rows through its LDS region (rows of 168 bf16 = 336
+    // bytes: 16-byte aligned, each bank takes two rows of a write
+    // instruction), leaving as 16-byte chunks along the rows, 20 consecutive
+    // lanes per 320-byte row segment. (The residual form gains nothing from
+    // this: its loads and stores stay in the accumulator layout below.)
+    constexpr int kStg = 168;
+    bf16_t* const stg = smem + wave_u * 64 * kStg;
+    const int col0 = tile_n * BNT + wn * 32 * NB;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float o[4];
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = silu_mul(acc[i][j][4 * g + e] * sg, acc[i + 2][j][4 * g + e] * su);
-          u32x2 pk;
-          pk[0] = pack_bf16x2(o[0], o[1]);
-          pk[1] = pack_bf16x2(o[2], o[3]);
-          __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + (jb + 8 * g + 4 * lhalf) * 2, 0, 0);
-          if constexpr (F8) amx = fmaxf(amx, abs_max4(pk));
-        }
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = A(i, 2 * h + jj)[4 * g + e];
+            *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + i * 32 + 8 * g + 4 * lhalf) =
+                finish4<EPI>(o, args, col0 + i * 32 + 8 * g + 4 * lhalf, u32x2{0, 0});
+          }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < 64 * 20 / 64; ++it) {
+        const int c = it * 64 + lane, r = c / 20, q = c - r * 20;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + q * 8);
+        const int off = (wm * 128 + h * 64 + r) * args.ldc * static_cast<int>(sizeof(bf16_t)) + (col0 + q * 8) * 2;
+        __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
       }
-    } else {
-      // (a residual load past N reads other columns of the buffer, or zeros
-      // past its end, for an output that is not stored)
-      const int nbase = tile_n * BNT + wn * 32 * NB;
-      u32x2 rv[NB][4];
+      // the reads above have returned before the next half overwrites the region
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  } else {
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
+    for (int j = 0; j < 4; ++j) {
+      const int row_bytes = (wm * 128 + j * 32 + lrow) * args.ldc * static_cast<int>(sizeof(bf16_t));
+      if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+        // gate block i pairs with up block i + 2
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          rv[i][g] = epi_residual(EPI) ? __builtin_amdgcn_raw_buffer_load_b64(
-                                             r_rsrc, row_bytes + (nbase + i * 32 + 8 * g + 4 * lhalf) * 2, 0, 0)
-                                       : u32x2{0, 0};
+        for (int i = 0; i < 2; ++i) {
+          const int jb = tile_n * (BN / 2) + wn * 64 + i * 32;
+          if (jb >= N) continue;
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int nb = nbase + i * 32;
-        if (NB == 4 && nb >= N) continue;  // the 320-wide form never has a partial n-tile
-        const float sc = F8 ? f8_scale(args, nb) : 1.f;
+          for (int g = 0; g < 4; ++g) {
+            float o[4];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float o[4];
+            for (int e = 0; e < 4; ++e) o[e] = silu_mul(acc[i][j][4 * g + e] * sg, acc[i + 2][j][4 * g + e] * su);
+            u32x2 pk;
+            pk[0] = pack_bf16x2(o[0], o[1]);
+            pk[1] = pack_bf16x2(o[2], o[3]);
+            __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + (jb + 8 * g + 4 * lhalf) * 2, 0, 0);
+            if constexpr (F8) amx = fmaxf(amx, abs_max4(pk));
+          }
+        }
+      } else {
+        // (a residual load past N reads other columns of the buffer, or zeros
+        // past its end, for an output that is not stored)
+        const int nbase = tile_n * BNT + wn * 32 * NB;
+        u32x2 rv[NB][4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = A(i, j)[4 * g + e] * sc;
-          const u32x2 pk = finish4<EPI>(o, args, nb + 8 * g + 4 * lhalf, rv[i][g]);
-          __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + (nb + 8 * g + 4 * lhalf) * 2, 0, 0);
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            rv[i][g] = epi_residual(EPI) ? __builtin_amdgcn_raw_buffer_load_b64(
+                                               r_rsrc, row_bytes + (nbase + i * 32 + 8 * g + 4 * lhalf) * 2, 0, 0)
+                                         : u32x2{0, 0};
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          const int nb = nbase + i * 32;
+          if (NB == 4 && nb >= N) continue;  // the 320-wide form never has a partial n-tile
+          const float sc = F8 ? f8_scale(args, nb) : 1.f;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = A(i, j)[4 * g + e] * sc;
+            const u32x2 pk = finish4<EPI>(o, args, nb + 8 * g + 4 * lhalf, rv[i][g]);
+            __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + (nb + 8 * g + 4 * lhalf) * 2, 0, 0);
+          }
         }
       }
     }
