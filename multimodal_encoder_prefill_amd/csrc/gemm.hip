@@ -45,9 +45,9 @@
 // to (and reads zeros from) rows past it; k-split units are a separate
 // instantiation that only writes fp32 partials. (Branches there made the
 // compiler copy every accumulator out of the AGPRs up front and spill them.)
-// The plain-store and SwiGLU forms of the 320-wide tile pass their bf16
-// outputs through LDS, which is free once the pipeline ends, and store whole
-// row segments in 16-byte chunks instead of 8 bytes per row and lane.
+// The bf16 forms of the 320-wide tile pass their outputs through LDS, which
+// is free once the pipeline ends, and store whole row segments in 16-byte
+// chunks instead of 8 bytes per row and lane.
 #include <type_traits>
 
 #include "common.h"
@@ -656,18 +656,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       const int off = (wm * 128 + r) * args.ldc * static_cast<int>(sizeof(bf16_t)) + (col0 + q * 8) * 2;
       __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
     }
-  } else if constexpr (NB == 5 && !epi_residual(EPI)) {
-    // Plain stores of the 320-wide tile: the wave's 128 x 160 outputs in
-    // two halves of 64 rows through its LDS region (rows of 168 bf16 = 336
-    // bytes: 16-byte aligned, each bank takes two rows of a write
+  } else if constexpr (NB == 5) {
+    // Store and residual forms of the 320-wide tile: the wave's 128 x 160
+    // outputs in two halves of 64 rows through its LDS region (rows of 168
+    // bf16 = 336 bytes: 16-byte aligned, each bank takes two rows of a write
     // instruction), leaving as 16-byte chunks along the rows, 20 consecutive
-    // lanes per 320-byte row segment. (The residual form gains nothing from
-    // this: its loads and stores stay in the accumulator layout below.)
+    // lanes per 320-byte row segment. A half's residual values are loaded in
+    // the accumulator layout, all before its first add (staging them through
+    // LDS as well measured no faster).
     constexpr int kStg = 168;
     bf16_t* const stg = smem + wave_u * 64 * kStg;
     const int col0 = tile_n * BNT + wn * 32 * NB;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      u32x2 rv[2][NB][4];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            rv[jj][i][g] = epi_residual(EPI)
+                               ? __builtin_amdgcn_raw_buffer_load_b64(
+                                     r_rsrc,
+                                     (wm * 128 + (2 * h + jj) * 32 + lrow) * args.ldc * static_cast<int>(sizeof(bf16_t)) +
+                                         (col0 + i * 32 + 8 * g + 4 * lhalf) * 2,
+                                     0, 0)
+                               : u32x2{0, 0};
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -678,7 +693,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = A(i, 2 * h + jj)[4 * g + e];
             *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + i * 32 + 8 * g + 4 * lhalf) =
-                finish4<EPI>(o, args, col0 + i * 32 + 8 * g + 4 * lhalf, u32x2{0, 0});
+                finish4<EPI>(o, args, col0 + i * 32 + 8 * g + 4 * lhalf, rv[jj][i][g]);
           }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
