@@ -656,15 +656,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       const int off = (wm * 128 + r) * args.ldc * static_cast<int>(sizeof(bf16_t)) + (col0 + q * 8) * 2;
       __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
     }
-  } else if constexpr (NB == 5) {
-    // Store and residual forms of the 320-wide tile: the wave's 128 x 160
-    // outputs in two halves of 64 rows through its LDS region (rows of 168
-    // bf16 = 336 bytes: 16-byte aligned, each bank takes two rows of a write
-    // instruction), leaving as 16-byte chunks along the rows, 20 consecutive
-    // lanes per 320-byte row segment. A half's residual values are loaded in
-    // the accumulator layout, all before its first add (staging them through
-    // LDS as well measured no faster).
-    constexpr int kStg = 168;
+  } else if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+    // 256-wide SwiGLU (FP8, or bf16 where the 320-wide tile does not fit):
+    // gate block i pairs with up block i + 2, 64 outputs per row and wave,
+    // staged like the 320-wide form (rows of 72 bf16 = 144 bytes, 8 lanes
+    // per row segment). Blocks past N (a partial n-tile; N is a multiple
+    // of 32) are skipped, and so are their chunks in the stores.
+    constexpr int kStg = 72;
+    bf16_t* const stg = smem + wave_u * 128 * kStg;
+    const int col0 = tile_n * (BN / 2) + wn * 64;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (col0 + i * 32 >= N) continue;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = silu_mul(acc[i][j][4 * g + e] * sg, acc[i + 2][j][4 * g + e] * su);
+          u32x2 pk;
+          pk[0] = pack_bf16x2(o[0], o[1]);
+          pk[1] = pack_bf16x2(o[2], o[3]);
+          *reinterpret_cast<u32x2*>(stg + (j * 32 + lrow) * kStg + i * 32 + 8 * g + 4 * lhalf) = pk;
+          if constexpr (F8) amx = fmaxf(amx, abs_max4(pk));
+        }
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int it = 0; it < 128 * 8 / 64; ++it) {
+      const int c = it * 64 + lane, r = c >> 3, q = c & 7;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + q * 8);
+      const int off = (wm * 128 + r) * args.ldc * static_cast<int>(sizeof(bf16_t)) + (col0 + q * 8) * 2;
+      if (col0 + q * 8 < N) __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
+    }
+  } else {
+    // Store, residual and bias forms: the wave's 128 x 32 NB outputs in two
+    // halves of 64 rows through its LDS region (rows of 32 NB + 8 bf16: 272
+    // or 336 bytes, 16-byte aligned, each bank takes two rows of a write
+    // instruction), leaving as 16-byte chunks along the rows, 4 NB
+    // consecutive lanes per row segment. A half's residual values are
+    // loaded in the accumulator layout, all before its first add (bringing
+    // them in through LDS as well measured no faster); a residual load past
+    // N reads other columns of the buffer, or zeros past its end, for an
+    // output that is not stored. Blocks past N (256-wide tiles only) are
+    // skipped, and so are their chunks in the stores.
+    constexpr int kStg = 32 * NB + 8, kRowChunks = 4 * NB;
     bf16_t* const stg = smem + wave_u * 64 * kStg;
     const int col0 = tile_n * BNT + wn * 32 * NB;
 #pragma unroll
@@ -686,80 +723,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = A(i, 2 * h + jj)[4 * g + e];
-            *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + i * 32 + 8 * g + 4 * lhalf) =
-                finish4<EPI>(o, args, col0 + i * 32 + 8 * g + 4 * lhalf, rv[jj][i][g]);
-          }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int it = 0; it < 64 * 20 / 64; ++it) {
-        const int c = it * 64 + lane, r = c / 20, q = c - r * 20;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + q * 8);
-        const int off = (wm * 128 + h * 64 + r) * args.ldc * static_cast<int>(sizeof(bf16_t)) + (col0 + q * 8) * 2;
-        __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
-      }
-      // the reads above have returned before the next half overwrites the region
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row_bytes = (wm * 128 + j * 32 + lrow) * args.ldc * static_cast<int>(sizeof(bf16_t));
-      if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
-        // gate block i pairs with up block i + 2
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int jb = tile_n * (BN / 2) + wn * 64 + i * 32;
-          if (jb >= N) continue;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = silu_mul(acc[i][j][4 * g + e] * sg, acc[i + 2][j][4 * g + e] * su);
-            u32x2 pk;
-            pk[0] = pack_bf16x2(o[0], o[1]);
-            pk[1] = pack_bf16x2(o[2], o[3]);
-            __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + (jb + 8 * g + 4 * lhalf) * 2, 0, 0);
-            if constexpr (F8) amx = fmaxf(amx, abs_max4(pk));
-          }
-        }
-      } else {
-        // (a residual load past N reads other columns of the buffer, or zeros
-        // past its end, for an output that is not stored)
-        const int nbase = tile_n * BNT + wn * 32 * NB;
-        u32x2 rv[NB][4];
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            rv[i][g] = epi_residual(EPI) ? __builtin_amdgcn_raw_buffer_load_b64(
-                                               r_rsrc, row_bytes + (nbase + i * 32 + 8 * g + 4 * lhalf) * 2, 0, 0)
-                                         : u32x2{0, 0};
-#pragma unroll
         for (int i = 0; i < NB; ++i) {
-          const int nb = nbase + i * 32;
+          const int nb = col0 + i * 32;
           if (NB == 4 && nb >= N) continue;  // the 320-wide form never has a partial n-tile
           const float sc = F8 ? f8_scale(args, nb) : 1.f;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             float o[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = A(i, j)[4 * g + e] * sc;
-            const u32x2 pk = finish4<EPI>(o, args, nb + 8 * g + 4 * lhalf, rv[i][g]);
-            __builtin_amdgcn_raw_buffer_store_b64(pk, c_rsrc, row_bytes + (nb + 8 * g + 4 * lhalf) * 2, 0, 0);
+            for (int e = 0; e < 4; ++e) o[e] = A(i, 2 * h + jj)[4 * g + e] * sc;
+            *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + i * 32 + 8 * g + 4 * lhalf) =
+                finish4<EPI>(o, args, nb + 8 * g + 4 * lhalf, rv[jj][i][g]);
           }
         }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < kRowChunks; ++it) {
+        const int c = it * 64 + lane, r = c / kRowChunks, q = c - r * kRowChunks;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + q * 8);
+        const int off = (wm * 128 + h * 64 + r) * args.ldc * static_cast<int>(sizeof(bf16_t)) + (col0 + q * 8) * 2;
+        if (NB == 5 || col0 + q * 8 < N) __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
       }
+      // the reads above have returned before the next half overwrites the region
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
   if constexpr (F8 && EPI == static_cast<int>(Epilogue::kSwiGLU)) {
-    if (args.amax) {  // uniform; LDS is free after the pipeline's last barrier
-      const float v = workgroup_max(amx, reinterpret_cast<float*>(smem));
+    if (args.amax) {  // uniform; past the four staging regions (72 KB)
+      const float v = workgroup_max(amx, reinterpret_cast<float*>(smem + 4 * 128 * 72));
       if (tid == 0) args.amax[unit] = v;
     }
   }
