@@ -608,8 +608,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   //      zeros (those rows computed from copies of row M-1, so their values
   //      are finite and never exceed a real row's in the SwiGLU maximum).
   //      Column blocks past N (partial n-tiles of the 256-wide form) are
-  //      skipped by wave-uniform tests. Each 32-row block's residual loads
-  //      go out before its stores. ----
+  //      skipped by wave-uniform tests, their 16-byte chunks by a lane test
+  //      in the stores. Outputs leave through a per-wavefront LDS region
+  //      (the forms below). ----
   const size_t rbytes = static_cast<size_t>(M - m0) * args.ldc * sizeof(bf16_t);
   const int nbytes = static_cast<int>(rbytes < 0x7fffffffu ? rbytes : 0x7fffffffu);
   const size_t first = static_cast<size_t>(m0) * args.ldc;
