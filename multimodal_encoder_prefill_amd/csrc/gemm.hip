@@ -625,37 +625,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   }
   if constexpr (kPairInBlock) {
     // Gate rows are groups g = 0, 2 of block i, their up rows g + 1. The
-    // wave's 128 x 80 outputs pass through its own LDS region (rows of 88
-    // bf16 = 176 bytes: 16-byte aligned, and a write instruction's 32 rows
-    // spread over all 64 banks, two rows a bank) and leave as 16-byte chunks
-    // along the rows, 10 consecutive lanes per 160-byte row segment, instead
-    // of 16 bytes in each of 32 rows per store instruction.
+    // wave's 128 x 80 outputs pass through its own LDS region in two halves
+    // of 64 rows (rows of 88 bf16 = 176 bytes: 16-byte aligned, and a write
+    // instruction's 32 rows spread over all 64 banks, two rows a bank) and
+    // leave as 16-byte chunks along the rows, 10 consecutive lanes per
+    // 160-byte row segment, instead of 16 bytes in each of 32 rows per store
+    // instruction. The first half's stores overlap the second half's SiLU.
     constexpr int kStg = 88;
-    bf16_t* const stg = smem + wave_u * 128 * kStg;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = silu_mul(A(i, j)[8 * gp + e], A(i, j)[8 * gp + 4 + e]);
-          u32x2 pk;
-          pk[0] = pack_bf16x2(o[0], o[1]);
-          pk[1] = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<u32x2*>(stg + (j * 32 + lrow) * kStg + i * 16 + gp * 8 + 4 * lhalf) = pk;
-        }
-    // a wavefront's LDS operations complete in order; the wait only makes
-    // the compiler keep the reads below after the writes of other lanes
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    bf16_t* const stg = smem + wave_u * 64 * kStg;
     const int col0 = tile_n * (BNT / 2) + wn * 16 * NB;
 #pragma unroll
-    for (int it = 0; it < 128 * 10 / 64; ++it) {
-      const int c = it * 64 + lane, r = c / 10, q = c - r * 10;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + q * 8);
-      const int off = (wm * 128 + r) * args.ldc * static_cast<int>(sizeof(bf16_t)) + (col0 + q * 8) * 2;
-      __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int gp = 0; gp < 2; ++gp) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              o[e] = silu_mul(A(i, 2 * h + jj)[8 * gp + e], A(i, 2 * h + jj)[8 * gp + 4 + e]);
+            u32x2 pk;
+            pk[0] = pack_bf16x2(o[0], o[1]);
+            pk[1] = pack_bf16x2(o[2], o[3]);
+            *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + i * 16 + gp * 8 + 4 * lhalf) = pk;
+          }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < 64 * 10 / 64; ++it) {
+        const int c = it * 64 + lane, r = c / 10, q = c - r * 10;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + q * 8);
+        const int off = (wm * 128 + h * 64 + r) * args.ldc * static_cast<int>(sizeof(bf16_t)) + (col0 + q * 8) * 2;
+        __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   } else if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
     // 256-wide SwiGLU (FP8, or bf16 where the 320-wide tile does not fit):
