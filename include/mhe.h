@@ -42,7 +42,9 @@ typedef enum mhe_status {
   MHE_OK = 0,
   MHE_ERR_NULL = 1,        /* a required pointer is NULL */
   MHE_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
-  MHE_ERR_MISMATCH = 3,    /* visual-mask popcount differs from n_vis (checked mode only) */
+  MHE_ERR_MISMATCH = 3,    /* token ids and patch grids disagree (mhe_rope_index), or grids and
+                              n_patches (vision entry points); the visual-mask popcount is the
+                              caller's to check (mhe_count_visual) */
   MHE_ERR_UNSUPPORTED = 4, /* valid but not built for (head_dim, K multiple, group size) */
   MHE_ERR_WORKSPACE = 5,   /* workspace too small or misaligned */
   MHE_ERR_HIP = 6          /* the HIP runtime reported an error */
@@ -533,6 +535,25 @@ int32_t mhe_vision_blocks(const mhe_vision_config* cfg, const mhe_vision_weights
 int32_t mhe_vision_merge(const mhe_vision_config* cfg, const mhe_vision_merger_weights* m,
                          int32_t postshuffle, const void* hidden, int32_t n_patches, void* out,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The tower's per-frame attention on its own (H3 encoder page,
+ * MiniMaxH3Qwen3VLVisionAttention.forward: non-causal softmax(q k^T /
+ * sqrt(head_dim)) v within each frame, the page's cu_seqlens), for per-step
+ * checks. q [n_patches, n_heads, 128], k [n_heads, seq_pad, 128] and vt
+ * [n_heads, 128, seq_pad] in the layouts of mhe_qk_norm_rope (head dims past
+ * head_dim zero; seq_pad = n_patches rounded up to 128; V^T token-permuted in
+ * groups of 16); o [n_patches, n_heads * head_dim] bf16. The frames are those
+ * of grid_thw (HOST int32 [n_grids, 3], patch grids as for
+ * mhe_vision_forward, merge their spatial merge size). head_dim % 4 == 0,
+ * <= 128. workspace: mhe_vision_attention_workspace_bytes(n_patches) bytes,
+ * 256-byte aligned (per-patch frame ranges).
+ */
+size_t mhe_vision_attention_workspace_bytes(int32_t n_patches);
+int32_t mhe_vision_attention(const void* q, const void* k, const void* vt, void* o,
+                             int32_t n_patches, int32_t n_heads, int32_t head_dim,
+                             const int32_t* grid_thw, int32_t n_grids, int32_t merge,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* y = LayerNorm(x) * w + b over rows of dim (biased variance, fp32), one
  * bf16 rounding (nn.LayerNorm of the vision blocks). dim % 8 == 0, <= 8192;

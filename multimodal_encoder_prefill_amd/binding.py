@@ -136,6 +136,9 @@ _SIGNATURES = {
                               _vp, _vp, _vp, _i32, ctypes.POINTER(_vp), _i32, _i32, _vp, _vp, _sz,
                               _vp]),
     "mhe_linear_bias": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "mhe_vision_attention_workspace_bytes": (_sz, [_i32]),
+    "mhe_vision_attention": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _i32, _vp, _sz,
+                                    _vp]),
 }
 
 # placeholder token ids of Qwen3-VL (H3 encoder page, MiniMaxH3Qwen3VLEncoder defaults)
@@ -632,3 +635,18 @@ def linear_bias(a, w, bias, c, m, n, k, act=0, residual=None, workspace=None, st
     _check("mhe_linear_bias", lib().mhe_linear_bias(_ptr(a), _ptr(w), _ptr(bias), _ptr(c),
                                                     _ptr(residual), m, n, k, act, wp, wb,
                                                     _stream(stream)))
+
+
+def vision_attention_workspace_bytes(n_patches: int) -> int:
+    n = lib().mhe_vision_attention_workspace_bytes(n_patches)
+    if n == 0:
+        raise MheError("mhe_vision_attention_workspace_bytes", 2, lib().mhe_last_error().decode())
+    return n
+
+
+def vision_attention(q, k, vt, o, n_patches, n_heads, head_dim, grid_thw, merge, workspace,
+                     workspace_bytes, stream=None):
+    g, ng = _grids(grid_thw)
+    _check("mhe_vision_attention", lib().mhe_vision_attention(
+        _ptr(q), _ptr(k), _ptr(vt), _ptr(o), n_patches, n_heads, head_dim, g.ctypes.data, ng,
+        merge, _ptr(workspace), workspace_bytes, _stream(stream)))

@@ -497,7 +497,7 @@ const char* mhe_status_string(int32_t s) {
     case MHE_OK: return "ok";
     case MHE_ERR_NULL: return "null pointer";
     case MHE_ERR_SHAPE: return "invalid shape";
-    case MHE_ERR_MISMATCH: return "visual token count mismatch";
+    case MHE_ERR_MISMATCH: return "token / grid count mismatch";
     case MHE_ERR_UNSUPPORTED: return "unsupported configuration";
     case MHE_ERR_WORKSPACE: return "workspace too small or misaligned";
     case MHE_ERR_HIP: return "HIP runtime error";
@@ -1210,6 +1210,36 @@ int32_t mhe_vision_forward(const mhe_vision_config* cfg, const mhe_vision_weight
         return rc;
   }
   return run_vision_merge(c, w->merger, false, ws.x, n, static_cast<bf16_t*>(merged), ws, st);
+}
+
+size_t mhe_vision_attention_workspace_bytes(int32_t n_patches) {
+  if (check_seq(n_patches)) return 0;
+  return align_up(static_cast<size_t>(n_patches) * sizeof(mhe::PatchInfo));
+}
+
+int32_t mhe_vision_attention(const void* q, const void* k, const void* vt, void* o,
+                             int32_t n_patches, int32_t n_heads, int32_t head_dim,
+                             const int32_t* grid_thw, int32_t n_grids, int32_t merge,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t rc;
+  if ((rc = check_seq(n_patches))) return rc;
+  if (!q || !k || !vt || !o) return fail(MHE_ERR_NULL, "q, k, vt and o are required");
+  if (n_heads <= 0 || head_dim <= 0) return fail(MHE_ERR_SHAPE, "n_heads and head_dim must be > 0");
+  if (head_dim > 128 || head_dim % 4 != 0)
+    return fail(MHE_ERR_UNSUPPORTED, "vision head_dim %d must be a multiple of 4 and <= 128", head_dim);
+  if (merge <= 0) return fail(MHE_ERR_SHAPE, "merge %d must be > 0", merge);
+  mhe_vision_config c{};
+  c.merge = merge;
+  mhe::VisionGrids g;
+  if ((rc = make_grids(c, grid_thw, n_grids, n_patches, &g))) return rc;
+  if ((rc = check_ws(workspace, workspace_bytes, mhe_vision_attention_workspace_bytes(n_patches)))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  mhe::PatchInfo* info = static_cast<mhe::PatchInfo*>(workspace);
+  if ((rc = hip_check(mhe::launch_patch_info(g, n_patches, info, st), "patch info"))) return rc;
+  return hip_check(mhe::launch_segment_attention(static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
+                                                 static_cast<const bf16_t*>(vt), static_cast<bf16_t*>(o),
+                                                 n_heads * head_dim, n_patches, n_heads, head_dim, info, st),
+                   "vision attention");
 }
 
 int32_t mhe_layer_norm(const void* x, const void* w, const void* b, void* y, int32_t rows,

@@ -67,20 +67,52 @@ def round_e4m3(x) -> np.ndarray:
     return np.where(x < 0, -r, r)
 
 
-def quantize(x):
-    """(q as float64 values on the E4M3 grid, scale s) of the per-tensor scheme."""
+def tensor_scale(x):
+    """(float32 factor 448 / max|x|, scale s = max|x| / 448) of a whole tensor;
+    (None, 1.0) for an all-zero tensor."""
     x32 = np.asarray(x, dtype=np.float32)
     amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0)
     if amax == 0:
-        return np.zeros(x32.shape), 1.0
-    factor = np.float32(E4M3_MAX) / amax
+        return None, 1.0
+    return np.float32(E4M3_MAX) / amax, float(amax) / E4M3_MAX
+
+
+def codes(x, factor):
+    """The E4M3 values of x under a tensor's float32 factor: x * factor in
+    float32, clipped to +-448, rounded to the grid (zeros when factor is None)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    if factor is None:
+        return np.zeros(x32.shape)
     y = np.clip(x32 * factor, -E4M3_MAX, E4M3_MAX).astype(np.float64)
-    return round_e4m3(y), float(amax) / E4M3_MAX
+    return round_e4m3(y)
 
 
-def linear_fp8(x, w_q, w_scale):
+def quantize(x, threads: int = 1):
+    """(q as float64 values on the E4M3 grid, scale s) of the per-tensor scheme.
+
+    Every code depends on its own element and the tensor's factor only, so
+    with threads > 1 the codes of separate row blocks are formed on a thread
+    pool (NumPy's element-wise loops release the interpreter lock); the
+    values are the same."""
+    factor, scale = tensor_scale(x)
+    x = np.asarray(x)
+    if threads <= 1 or x.ndim < 2 or x.shape[0] < 2 * threads:
+        return codes(x, factor), scale
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty(x.shape)
+    bounds = np.linspace(0, x.shape[0], 4 * threads + 1).astype(int)
+
+    def one(i):
+        out[bounds[i]:bounds[i + 1]] = codes(x[bounds[i]:bounds[i + 1]], factor)
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, range(len(bounds) - 1)))
+    return out, scale
+
+
+def linear_fp8(x, w_q, w_scale, threads: int = 1):
     """x (float) quantised on the fly times an already-quantised weight."""
-    q_x, s_x = quantize(x)
+    q_x, s_x = quantize(x, threads)
     return (q_x @ np.asarray(w_q, dtype=np.float64).T) * (s_x * w_scale)
 
 
@@ -89,23 +121,25 @@ FUSED = {"w_qkv": ("w_q", "w_k", "w_v"), "w_o": ("w_o",), "w_gate_up": ("w_gate"
          "w_down": ("w_down",)}
 
 
-def quantize_layer(w: LayerWeights):
+def quantize_layer(w: LayerWeights, threads: int = 1):
     """Quantised weights of a layer: {linear: (values, scale)}, one scale per
     linear layer over its stacked rows."""
-    return {name: quantize(np.concatenate([np.asarray(getattr(w, p), dtype=np.float64) for p in parts]))
+    return {name: quantize(np.concatenate([np.asarray(getattr(w, p), dtype=np.float64) for p in parts]),
+                           threads)
             for name, parts in FUSED.items()}
 
 
-def decoder_layer_fp8(h, w: LayerWeights, qw, cos, sin, dims: ModelDims):
+def decoder_layer_fp8(h, w: LayerWeights, qw, cos, sin, dims: ModelDims, threads: int = 1):
     """The decoder layer with every linear in FP8 (qw from quantize_layer), all
-    rows (the activation scales are taken over whole tensors)."""
+    rows (the activation scales are taken over whole tensors). `threads`: as
+    for quantize."""
     h = np.asarray(h, dtype=np.float64)
     S = h.shape[0]
     rows = np.arange(S)
     need = S
     D, Hq, Hkv = dims.head_dim, dims.n_heads, dims.n_kv_heads
     u = rms_norm(h[:need], w.ln_in, dims.rms_eps)
-    qkv = linear_fp8(u, *qw["w_qkv"])
+    qkv = linear_fp8(u, *qw["w_qkv"], threads)
     q = qkv[:, :Hq * D].reshape(need, Hq, D)
     k = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(need, Hkv, D)
     v = qkv[:, (Hq + Hkv) * D:].reshape(need, Hkv, D)
@@ -114,8 +148,8 @@ def decoder_layer_fp8(h, w: LayerWeights, qw, cos, sin, dims: ModelDims):
     q = apply_rope(q, cos[:need], sin[:need])
     k = apply_rope(k, cos[:need], sin[:need])
     o = causal_gqa_attention(q, k, v, rows)
-    x = h[rows] + linear_fp8(o.reshape(S, Hq * D), *qw["w_o"])
+    x = h[rows] + linear_fp8(o.reshape(S, Hq * D), *qw["w_o"], threads)
     u2 = rms_norm(x, w.ln_post, dims.rms_eps)
-    gu = linear_fp8(u2, *qw["w_gate_up"])
+    gu = linear_fp8(u2, *qw["w_gate_up"], threads)
     I = dims.intermediate
-    return x + linear_fp8(silu(gu[:, :I]) * gu[:, I:], *qw["w_down"])
+    return x + linear_fp8(silu(gu[:, :I]) * gu[:, I:], *qw["w_down"], threads)

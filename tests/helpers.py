@@ -47,3 +47,24 @@ def oracle_dims(d):
 def oracle_layer(weights: dict):
     import oracle
     return oracle.LayerWeights(**{k: f64(v) for k, v in weights.items()})
+
+
+def row_rel_max(got, ref, row_len: int) -> float:
+    """Largest relative L2 error over rows of `row_len` consecutive values
+    (e.g. one (token, head) vector of a head_dim): a single wrong row shows up
+    here even when the whole-tensor rel-L2 hides it."""
+    g = np.asarray(got, np.float64).reshape(-1, row_len)
+    r = np.asarray(ref, np.float64).reshape(-1, row_len)
+    num = np.linalg.norm(g - r, axis=1)
+    den = np.linalg.norm(r, axis=1)
+    # rows whose reference is (numerically) zero are judged by the absolute error
+    rel = np.where(den > 1e-12, num / np.where(den > 1e-12, den, 1.0), num)
+    return float(np.max(rel)) if rel.size else 0.0
+
+
+def report_rows(name, got, ref, row_len: int):
+    """Whole-tensor rel-L2 and max-abs as `report`, plus the worst row's rel-L2."""
+    r, m = rel_l2(got, ref), max_abs(got, ref)
+    w = row_rel_max(got, ref, row_len)
+    print(f"{name}: rel_l2={r:.3e} max_abs={m:.3e} worst_row_rel={w:.3e}", flush=True)
+    return r, m, w

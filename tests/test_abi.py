@@ -139,3 +139,27 @@ def test_fp8_entry_points_reject_before_launch():
     rc = lib.mhe_layer_forward_fp8(ctypes.byref(tiny), ctypes.byref(t), 0x2000, 0x3000, 64, 0x10000,
                                    1 << 40, None)
     assert rc == 1 and "s_down" in lib.mhe_last_error().decode()
+
+
+def test_vision_attention_rejects_before_launch():
+    import numpy as np
+    lib = b.lib()
+    d = 0x100000
+    grids = np.array([[1, 4, 8], [2, 4, 4]], dtype=np.int32)     # 32 + 32 patches
+    g = grids.ctypes.data
+    need = b.vision_attention_workspace_bytes(64)
+    assert need >= 64 * 32
+    call = lambda **o: lib.mhe_vision_attention(
+        o.get("q", d), d, d, d * 8, o.get("n", 64), 4, o.get("hd", 72), o.get("g", g),
+        o.get("ng", 2), o.get("merge", 2), o.get("ws", 0x10000), o.get("ws_bytes", need), None)
+    assert call(q=None) == 1
+    assert call(hd=130) == 4                      # head_dim above 128
+    assert call(hd=70) == 4                       # not a multiple of 4
+    assert call(n=63) == 3                        # grids hold 64 patches
+    assert call(g=None) == 1
+    assert call(ng=0) == 2
+    assert call(merge=0) == 2
+    assert call(ws_bytes=need - 1) == 5
+    assert call(ws=0x10010) == 5                  # misaligned
+    assert b.status_string(3) != b.status_string(2)
+

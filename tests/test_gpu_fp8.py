@@ -231,14 +231,14 @@ def _gpu_states(wl, s):
     return states
 
 
-def _check_layers(wl, s, states, layers):
+def _check_layers(wl, s, states, layers, threads=1):
     dims = oracle_dims(wl.dims)
     cos, sin = oracle.rope_cos_sin(s["pos_np"], dims.head_dim, dims.rope_theta, dims.mrope_section)
     idx = np.flatnonzero(s["mask_np"])
     for l in layers:
         h_in = f64(states[l])
         w = oracle_layer(s["layers"][l])
-        ref8 = Q.decoder_layer_fp8(h_in, w, Q.quantize_layer(w), cos, sin, dims)
+        ref8 = Q.decoder_layer_fp8(h_in, w, Q.quantize_layer(w, threads), cos, sin, dims, threads)
         ref16 = oracle.decoder_layer(h_in, w, cos, sin, dims)
         if l < len(s["ds"]) and wl.n_vis > 0:
             add = np.zeros_like(ref8)
@@ -284,3 +284,25 @@ def test_encode_fp8_equals_layer_calls_and_tracks_oracle():
     states = _gpu_states(wl, s)
     assert torch.equal(states[-1], out)
     _check_layers(wl, s, states, [0, 2, 5])
+
+
+_FULL = {}
+
+
+@pytest.mark.parametrize("layer", [0, 49])
+def test_fp8_layer_full_width_s4096_teacher_forced(layer):
+    """The FP8 layer at full width in the seq-4096 image stack (the FP8
+    encode's own bf16 input of that layer, every row): layer 0 carries
+    DeepStack level 0, layer 49 is the last."""
+    import os
+    if not _FULL:
+        wl = synth.WORKLOADS["image_s4096_l50"]
+        print(f"fp8 full stack {wl.key}: seq {wl.seq}, {wl.n_layers} layers", flush=True)
+        s = _setup(wl)
+        _FULL.update(wl=wl, s=s, states=_gpu_states(wl, s))
+    wl, s, states = _FULL["wl"], _FULL["s"], _FULL["states"]
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    _check_layers(wl, s, states, [layer], threads)
+    if layer == 49:
+        _FULL.clear()
+        torch.cuda.empty_cache()

@@ -15,7 +15,12 @@ import torch
 import oracle
 from multimodal_encoder_prefill_amd import binding as b
 from multimodal_encoder_prefill_amd import synth
-from helpers import f64, report, perm16_tokens
+from helpers import f64, report, report_rows, perm16_tokens
+
+# Largest rel-L2 of any single (token, head) vector: one bf16 rounding of the
+# output (and, in attention, of the probabilities) keeps a row near 2^-9;
+# a row computed from a wrong head, position or key range is off by O(1).
+ROW_BAR = 3e-2
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -237,9 +242,12 @@ def test_qk_norm_rope(key, seq):
     dims = synth.TINY if key == "tiny" else synth.FULL
     positions = synth.random_positions(seq, 3000, seed=seq)
     q_out, k_out, vt_out, q_ref, k_ref, v_ref, sp = _qk_case(dims, seq, positions, 70 + seq)
-    assert report("q", f64(q_out), q_ref)[0] <= 4e-3
+    D = dims.head_dim
+    r, _, w = report_rows("q", f64(q_out), q_ref, D)
+    assert r <= 4e-3 and w <= ROW_BAR
     kk = f64(k_out)
-    assert report("k", kk[:, :seq].transpose(1, 0, 2), k_ref)[0] <= 4e-3
+    r, _, w = report_rows("k", kk[:, :seq].transpose(1, 0, 2), k_ref, D)
+    assert r <= 4e-3 and w <= ROW_BAR
     assert np.all(kk[:, seq:] == 0)
     vt = f64(vt_out)                          # [Hkv, D, sp], permuted columns
     tok = perm16_tokens(sp)
@@ -252,8 +260,11 @@ def test_qk_norm_rope_workload_positions():
     """Image-layout positions of the 4096-token workload (text / 1x32x64 grid / text)."""
     wl = synth.WORKLOADS["image_s4096_l50"]
     q_out, k_out, _, q_ref, k_ref, _, _ = _qk_case(wl.dims, wl.seq, synth.positions(wl), 90)
-    assert report("q image", f64(q_out), q_ref)[0] <= 4e-3
-    assert report("k image", f64(k_out)[:, :wl.seq].transpose(1, 0, 2), k_ref)[0] <= 4e-3
+    D = wl.dims.head_dim
+    r, _, w = report_rows("q image", f64(q_out), q_ref, D)
+    assert r <= 4e-3 and w <= ROW_BAR
+    r, _, w = report_rows("k image", f64(k_out)[:, :wl.seq].transpose(1, 0, 2), k_ref, D)
+    assert r <= 4e-3 and w <= ROW_BAR
 
 
 # ------------------------------------------------------------------ attention
@@ -283,8 +294,8 @@ def test_attention(seq, hq, hkv, d):
     b.attention(q, k_l, vt_l, o, seq, hq, hkv, d)
     torch.cuda.synchronize()
     ref = oracle.causal_gqa_attention(f64(q), f64(k), f64(v)).reshape(seq, hq * d)
-    r, _ = report("attention", f64(o), ref)
-    assert r <= 8e-3
+    r, _, w = report_rows("attention", f64(o), ref, d)
+    assert r <= 8e-3 and w <= ROW_BAR
 
 
 @pytest.mark.parametrize("seq", [1, 32, 33, 64, 65, 96, 127, 128, 129, 191, 256])
@@ -299,8 +310,8 @@ def test_attention_group8_tile_edges(seq):
     b.attention(q, k_l, vt_l, o, seq, hq, hkv, d)
     torch.cuda.synchronize()
     ref = oracle.causal_gqa_attention(f64(q), f64(k), f64(v)).reshape(seq, hq * d)
-    r, _ = report("attention g8", f64(o), ref)
-    assert r <= 8e-3
+    r, _, w = report_rows("attention g8", f64(o), ref, d)
+    assert r <= 8e-3 and w <= ROW_BAR
 
 
 def test_attention_rising_scores_rescale():
@@ -316,8 +327,8 @@ def test_attention_rising_scores_rescale():
     b.attention(q, k_l, vt_l, o, seq, hq, hkv, d)
     torch.cuda.synchronize()
     ref = oracle.causal_gqa_attention(f64(q), f64(k), f64(v)).reshape(seq, hq * d)
-    r, _ = report("attention rising", f64(o), ref)
-    assert r <= 8e-3
+    r, _, w = report_rows("attention rising", f64(o), ref, d)
+    assert r <= 8e-3 and w <= ROW_BAR
 
 
 def test_attention_full_size_sampled_rows():
@@ -328,7 +339,8 @@ def test_attention_full_size_sampled_rows():
     torch.cuda.synchronize()
     rows = np.array([0, 1, 63, 64, 1000, 2047, 2048, 4095])
     ref = oracle.causal_gqa_attention(f64(q), f64(k), f64(v), rows=rows).reshape(len(rows), -1)
-    assert report("attention full sampled", f64(o)[rows], ref)[0] <= 8e-3
+    r, _, w = report_rows("attention full sampled", f64(o)[rows], ref, d)
+    assert r <= 8e-3 and w <= ROW_BAR
 
 
 def test_attention_causal_bitwise():

@@ -1,8 +1,13 @@
 """Vision tower of the HIP path against the float64 oracle (oracle.vision).
 
-Bars as for the decoder: every step and every block fed the GPU's own bf16
-input agrees with the oracle to rel-L2 <= 2e-2; the free-running tower to
-<= 5e-2 at its outputs. Grids mix images and multi-frame videos so the
+Bars from the arithmetic, as for the decoder: a step that accumulates in
+fp32 and rounds its output to bf16 once (LayerNorm, the biased linears with
+their activation or residual) agrees with the oracle to rel-L2 <= 4e-3; the
+patch embedding rounds twice (the biased GEMM, then the position-table add):
+6e-3; a merger three times, two of them feeding a GEMM: 1e-2; attention
+rounds its probabilities to bf16 as well: 8e-3 (and 3e-2 for any single
+(patch, head) row). A block fed the GPU's own bf16 input (teacher-forced)
+agrees to <= 2e-2; the free-running tower to <= 5e-2 at its outputs. Grids mix images and multi-frame videos so the
 per-frame attention segments, the merge-block order and the position-table
 interpolation are all exercised; frames are checked to be independent
 bitwise.
@@ -15,7 +20,7 @@ import torch
 from oracle import vision as OV
 from multimodal_encoder_prefill_amd import binding as b
 from multimodal_encoder_prefill_amd import synth
-from helpers import f64, report
+from helpers import f64, report, report_rows, perm16_tokens
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -63,7 +68,7 @@ def test_layer_norm_matches_oracle():
         b.layer_norm(x, w, bb, y, 257, dim)
         torch.cuda.synchronize()
         ref = OV.layer_norm(f64(x), f64(w), f64(bb))
-        assert report(f"layer_norm dim {dim}", f64(y), ref)[0] <= 1e-2
+        assert report(f"layer_norm dim {dim}", f64(y), ref)[0] <= 4e-3
         # one bf16 rounding: every element within half an ulp of the fp32 result plus slack
         assert np.max(np.abs(f64(y) - ref) / (np.abs(ref) + 1e-2)) < 2e-2
 
@@ -83,7 +88,38 @@ def test_linear_bias_matches_oracle(act):
     torch.cuda.synchronize()
     y = OV.linear(f64(a), f64(w), f64(bias))
     ref = {0: y, 1: OV.gelu_tanh(y), 2: OV.gelu_erf(y), "res": y + f64(r)}[act]
-    assert report(f"linear_bias act={act}", f64(c), ref)[0] <= 1e-2
+    assert report(f"linear_bias act={act}", f64(c), ref)[0] <= 4e-3
+
+
+@pytest.mark.parametrize("grids,heads,hd", [(GRIDS_TINY, 8, 72), (GRIDS_FULL, 16, 72),
+                                           ([(1, 64, 128)], 16, 72), (GRIDS_TINY, 4, 128)])
+def test_vision_attention_per_frame(grids, heads, hd):
+    """The per-frame attention step on its own: every (patch, head) row
+    against the oracle's segment attention, frames as the grids cut them (the
+    benched single 64 x 128-patch frame included)."""
+    n = int(sum(t * h * w for t, h, w in grids))
+    print(f"vision attention n={n} heads={heads} head_dim={hd} grids={grids}", flush=True)
+    g = torch.Generator(device=DEV).manual_seed(n + hd)
+    q = torch.randn(n, heads, hd, generator=g, device=DEV).to(torch.bfloat16)
+    k = torch.randn(n, heads, hd, generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn(n, heads, hd, generator=g, device=DEV).to(torch.bfloat16)
+    sp = b.seq_pad(n)
+    q_l = torch.zeros(n, heads, 128, dtype=torch.bfloat16, device=DEV)
+    q_l[:, :, :hd] = q
+    k_l = torch.zeros(heads, sp, 128, dtype=torch.bfloat16, device=DEV)
+    k_l[:, :n, :hd] = k.transpose(0, 1)
+    v_pad = torch.zeros(sp, heads, 128, dtype=torch.bfloat16, device=DEV)
+    v_pad[:n, :, :hd] = v
+    tok = torch.from_numpy(perm16_tokens(sp)).to(DEV)
+    vt_l = v_pad[tok].permute(1, 2, 0).contiguous()
+    o = torch.full((n, heads * hd), 7.0, dtype=torch.bfloat16, device=DEV)
+    nb = b.vision_attention_workspace_bytes(n)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    b.vision_attention(q_l, k_l, vt_l, o, n, heads, hd, grids, 2, ws, nb)
+    torch.cuda.synchronize()
+    ref = OV.segment_attention(f64(q), f64(k), f64(v), OV.segments(grids))
+    r, _, w = report_rows("vision attention", f64(o), ref, hd)
+    assert r <= 8e-3 and w <= 3e-2
 
 
 @pytest.mark.parametrize("vd,grids", [(synth.VISION_TINY, GRIDS_TINY), (synth.VISION_FULL, GRIDS_FULL)])
@@ -94,7 +130,7 @@ def test_vision_embed_matches_oracle(vd, grids):
     torch.cuda.synchronize()
     ref = OV.patch_embed(f64(px), f64(w["patch_w"]), f64(w["patch_b"])) + \
         OV.pos_embed_interpolate(f64(w["pos_table"]), grids, vd.pos_side, vd.merge)
-    assert report(f"vision embed {vd.hidden}", f64(h), ref)[0] <= 2e-2
+    assert report(f"vision embed {vd.hidden}", f64(h), ref)[0] <= 6e-3
 
 
 # head_dim 128: the per-frame attention's all-dims path (head_dim 72 stops at 96)
@@ -154,7 +190,7 @@ def test_vision_merge_matches_oracle(vd, post):
     b.vision_merge(cfg, m, post, h, n, out, ws, nb)
     torch.cuda.synchronize()
     ref = OV.merger(f64(h), _omerger(m), _odims(vd), post)
-    assert report(f"vision merger post={post} hidden {vd.hidden}", f64(out), ref)[0] <= 2e-2
+    assert report(f"vision merger post={post} hidden {vd.hidden}", f64(out), ref)[0] <= 1e-2
 
 
 @pytest.mark.parametrize("vd,grids,depth", [(synth.VISION_TINY, GRIDS_TINY, None)])
@@ -173,6 +209,21 @@ def test_vision_forward_free_running(vd, grids, depth):
     assert report("vision tower merged (free-running)", f64(merged), out)[0] <= 5e-2
     for l, (got, ref) in enumerate(zip(ds, ref_ds)):
         assert report(f"vision tower DeepStack {l}", f64(got), ref)[0] <= 5e-2
+
+
+def test_vision_forward_full_depth_free_running():
+    """The full 27-block, full-width tower with its three DeepStack mergers,
+    free-running on an image and a two-frame video."""
+    print(f"vision tower full depth, grids {GRIDS_FULL}", flush=True)
+    test_vision_forward_free_running(synth.VISION_FULL, GRIDS_FULL, None)
+
+
+def test_vision_block_benched_grid_teacher_forced():
+    """One full-width block on the single 64 x 128-patch frame the bench times
+    (8192 patches attending to each other), every output against the oracle."""
+    vd, grids = synth.VISION_FULL, [(1, 64, 128)]
+    print(f"vision block on the benched grid {grids}", flush=True)
+    test_vision_blocks_teacher_forced(vd, grids, [5])
 
 
 def test_vision_forward_full_width_short_stack():

@@ -145,3 +145,20 @@ def test_fused_linears_share_one_scale():
         vals, s = qw[name]
         assert s == 1.0
         np.testing.assert_array_equal(vals, np.concatenate([parts[p] for p in stacked]))
+
+
+def test_threaded_quantisation_is_the_same_function():
+    """quantize(x, threads) forms the codes of row blocks concurrently: the
+    values and the scale equal the one-pass result bit for bit (ragged block
+    edges, an all-zero tensor and a tensor too short to split included)."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((1037, 96)) * np.exp2(rng.integers(-12, 4, size=(1037, 1)))
+    for t in (2, 7):
+        q1, s1 = Q.quantize(x)
+        qt, st = Q.quantize(x, threads=t)
+        assert st == s1 and np.array_equal(q1, qt)
+    z, sz = Q.quantize(np.zeros((50, 8)), threads=4)
+    assert sz == 1.0 and not z.any()
+    q1, _ = Q.quantize(x[:5])
+    qt, _ = Q.quantize(x[:5], threads=4)
+    assert np.array_equal(q1, qt)
