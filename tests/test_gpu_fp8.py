@@ -12,12 +12,16 @@ Bars, from the arithmetic:
   * a layer: the GPU quantises its bf16 activations, the oracle its float64
     ones, so a code whose input moved (bf16 rounding of the steps before)
     may land one E4M3 step away: the two quantisations round the same tensor
-    nearly independently. The output (residual included) must meet the bf16
-    layer's bar, rel-L2 <= 2e-2. The layer's update (output - input) may then
+    nearly independently. The layer's update (output - input) may then
     differ from the FP8 oracle's by up to sqrt(2) times the FP8 rounding
     error itself (the oracle's FP8 update against its bf16 update); the bar
     is 1.5 times that, so any error source beyond FP8 rounding (a wrong or
-    stale scale, a dropped clamp, a wrong tensor) fails it.
+    stale scale, a dropped clamp, a wrong tensor) fails it. The output
+    (residual included) meets the bf16 layer's bar, rel-L2 <= 2e-2, or, where
+    the FP8 rounding of a large update alone moves the output further (the
+    oracle's FP8 output against its bf16 output), 1.5 times that distance:
+    in the first layer of the seq-4096 stack the update is as large as the
+    output and FP8 rounding moves it by ~6.6e-2.
 Inputs are seeded (synth), bf16-valued or random E4M3 codes.
 """
 
@@ -249,7 +253,9 @@ def _check_layers(wl, s, states, layers, threads=1):
         upd_gpu = rel_l2(got - h_in, ref8 - h_in)
         upd_fp8 = rel_l2(ref8 - h_in, ref16 - h_in)
         print(f"  update: gpu vs fp8 oracle {upd_gpu:.3e}; fp8 vs bf16 oracle {upd_fp8:.3e}", flush=True)
-        assert r <= 2e-2
+        out_fp8 = rel_l2(ref8, ref16)
+        print(f"  output: fp8 vs bf16 oracle {out_fp8:.3e}", flush=True)
+        assert r <= max(2e-2, 1.5 * out_fp8)
         assert upd_gpu <= 1.5 * upd_fp8
 
 
