@@ -142,6 +142,21 @@ int32_t mhe_deepstack_inject(void* hidden, int32_t seq, int32_t hidden_dim,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mhe_deepstack_inject without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same operation, arguments and errors as
+ * mhe_deepstack_inject; the visual index list lives in a fixed scratch array
+ * inside the library (512 KiB + 256 bytes per GPU, held until the process
+ * ends), so seq is limited to 131072 (larger: MHE_ERR_SHAPE). The call itself
+ * allocates nothing; the first call on a device looks up that device's copy
+ * of the array. Calls that overlap in time on one GPU (different streams or
+ * host threads) share that array and race: serialise them.
+ */
+int32_t mhe_deepstack_inject_noalloc(void* hidden, int32_t seq, int32_t hidden_dim,
+                                     const uint8_t* visual_mask, int32_t n_vis, const void* feature,
+                                     void* stream);
+
+/*
  * The whole prefill (H3 encoder page, MiniMaxH3Qwen3VLTextModel.forward):
  * out = hidden state after n_layers decoder layers, unnormalised, bf16
  * [seq, hidden]. inputs_embeds [seq, hidden] bf16 is not written (it is

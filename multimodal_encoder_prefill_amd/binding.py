@@ -95,6 +95,7 @@ _SIGNATURES = {
     "mhe_layer_forward": (_i32, [ctypes.POINTER(MheConfig), ctypes.POINTER(MheLayerWeights), _vp,
                                  _vp, _i32, _vp, _sz, _vp]),
     "mhe_deepstack_inject": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "mhe_deepstack_inject_noalloc": (_i32, [_vp, _i32, _i32, _vp, _i32, _vp, _vp]),
     "mhe_encode": (_i32, [ctypes.POINTER(MheConfig), ctypes.POINTER(MheLayerWeights), _i32, _vp,
                           _vp, _vp, _i32, ctypes.POINTER(_vp), _i32, _i32, _vp, _vp, _sz, _vp]),
     "mhe_count_visual": (_i32, [_vp, _i32, ctypes.POINTER(_i32), _vp, _sz, _vp]),
@@ -244,6 +245,11 @@ def deepstack_inject(hidden, seq, hidden_dim, visual_mask, n_vis, feature, works
     _check("mhe_deepstack_inject", lib().mhe_deepstack_inject(
         _ptr(hidden), seq, hidden_dim, _ptr(visual_mask), n_vis, _ptr(feature),
         _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def deepstack_inject_noalloc(hidden, seq, hidden_dim, visual_mask, n_vis, feature, stream=None):
+    _check("mhe_deepstack_inject_noalloc", lib().mhe_deepstack_inject_noalloc(
+        _ptr(hidden), seq, hidden_dim, _ptr(visual_mask), n_vis, _ptr(feature), _stream(stream)))
 
 
 def encode(cfg, layers: Sequence, inputs_embeds, positions, seq, out, workspace,

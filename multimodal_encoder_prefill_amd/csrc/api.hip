@@ -583,6 +583,30 @@ int32_t mhe_deepstack_inject(void* hidden, int32_t seq, int32_t hidden_dim,
                    "deepstack add");
 }
 
+int32_t mhe_deepstack_inject_noalloc(void* hidden, int32_t seq, int32_t hidden_dim,
+                                     const uint8_t* visual_mask, int32_t n_vis, const void* feature,
+                                     void* stream) {
+  static_assert(kMaxSeq <= mhe::kStaticIndexRows, "the static index scratch covers every seq");
+  if (seq <= 0) return fail(MHE_ERR_SHAPE, "seq %d must be > 0", seq);
+  if (seq > mhe::kStaticIndexRows)
+    return fail(MHE_ERR_SHAPE, "seq %d exceeds the %d tokens the library's static scratch holds", seq,
+                mhe::kStaticIndexRows);
+  if (hidden_dim <= 0 || hidden_dim % 8 != 0)
+    return fail(MHE_ERR_SHAPE, "hidden_dim %d must be a positive multiple of 8", hidden_dim);
+  if (n_vis < 0 || n_vis > seq) return fail(MHE_ERR_SHAPE, "n_vis %d out of range [0, %d]", n_vis, seq);
+  if (n_vis == 0) return MHE_OK;
+  if (!hidden || !visual_mask || !feature) return fail(MHE_ERR_NULL, "hidden, visual_mask and feature are required");
+  int32_t *idx = nullptr, *cnt = nullptr;
+  int32_t rc;
+  if ((rc = hip_check(mhe::static_index_scratch(&idx, &cnt), "static scratch address"))) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((rc = hip_check(mhe::launch_visual_index(visual_mask, seq, n_vis, idx, cnt, st), "visual index")))
+    return rc;
+  return hip_check(mhe::launch_deepstack_add(static_cast<bf16_t*>(hidden), hidden_dim, idx, n_vis,
+                                             static_cast<const bf16_t*>(feature), st),
+                   "deepstack add");
+}
+
 int32_t mhe_encode(const mhe_config* cfg, const mhe_layer_weights* layers, int32_t n_layers,
                    const void* inputs_embeds, const int32_t* positions,
                    const uint8_t* visual_mask, int32_t n_vis, const void* const* deepstack,

@@ -10,6 +10,9 @@
 // deepstack_add_kernel is then a row gather/scatter: one wavefront per visual
 // row, 16-byte coalesced loads and stores. HBM-bound: 3 * hidden * 2 bytes
 // per visual row (read hidden, read feature, write hidden).
+#include <mutex>
+#include <vector>
+
 #include "common.h"
 #include "internal.h"
 
@@ -84,6 +87,34 @@ __global__ __launch_bounds__(256) void deepstack_add_kernel(bf16_t* __restrict__
 }
 
 }  // namespace
+
+// Scratch of the allocation-free DeepStack entry point: the visual index list
+// (kStaticIndexRows entries) and its count, 512 KiB + 256 bytes on every GPU
+// the library runs on, held until the process ends. In host code `scratch`
+// names a host-side stand-in, never the device memory: its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is handed to kernels.
+static __device__ __align__(256) int32_t scratch[kStaticIndexRows + 64];
+
+hipError_t static_index_scratch(int32_t** idx, int32_t** count) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::vector<int32_t*> per_device;
+  std::lock_guard<std::mutex> lk(mu);
+  if (dev < 0) return hipErrorInvalidDevice;
+  if (static_cast<size_t>(dev) >= per_device.size()) per_device.resize(dev + 1, nullptr);
+  if (!per_device[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    per_device[dev] = static_cast<int32_t*>(p);
+  }
+  *idx = per_device[dev];
+  *count = per_device[dev] + kStaticIndexRows;
+  return hipSuccess;
+}
 
 hipError_t launch_visual_index(const uint8_t* mask, int seq, int n_vis, int32_t* idx,
                                int32_t* count, hipStream_t stream) {

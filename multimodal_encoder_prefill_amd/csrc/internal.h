@@ -129,6 +129,12 @@ hipError_t launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* vt, 
 // entries past the popcount are -1; *count = popcount.
 hipError_t launch_visual_index(const uint8_t* mask, int seq, int n_vis, int32_t* idx,
                                int32_t* count, hipStream_t stream);
+// The library's own device scratch for the visual index list of callers that
+// cannot allocate: kStaticIndexRows entries and a count, one copy per device
+// (its address looked up on the first call on that device). Calls that
+// overlap on one device share it and race.
+constexpr int kStaticIndexRows = 1 << 17;
+hipError_t static_index_scratch(int32_t** idx, int32_t** count);
 // hidden[idx[r]] += feature[r] (fp32 add, one bf16 rounding), r < n_vis
 hipError_t launch_deepstack_add(bf16_t* hidden, int hidden_dim, const int32_t* idx, int n_vis,
                                 const bf16_t* feature, hipStream_t stream);

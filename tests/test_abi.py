@@ -163,3 +163,17 @@ def test_vision_attention_rejects_before_launch():
     assert call(ws=0x10010) == 5                  # misaligned
     assert b.status_string(3) != b.status_string(2)
 
+
+def test_deepstack_noalloc_rejects_before_launch():
+    lib = b.lib()
+    call = lambda **o: lib.mhe_deepstack_inject_noalloc(
+        o.get("h", 0x10), o.get("seq", 64), o.get("dim", 256), o.get("mask", 0x20),
+        o.get("n_vis", 8), o.get("feat", 0x30), None)
+    assert call(seq=(1 << 17) + 1, n_vis=4) == 2          # beyond the static scratch
+    assert "static scratch" in lib.mhe_last_error().decode()
+    assert call(seq=0) == 2
+    assert call(dim=100) == 2
+    assert call(n_vis=65) == 2
+    assert call(h=None) == 1
+    assert call(mask=None) == 1
+    assert call(n_vis=0) == 0                             # no-op, nothing launched
