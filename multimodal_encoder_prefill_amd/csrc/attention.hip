@@ -60,15 +60,27 @@ __device__ __forceinline__ float add_pair(uint32_t x, float s) {
                                          s, false);
 }
 
-// Buffer resource over [p, p + bytes) held in scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t scalar_rsrc(const bf16_t* p, int bytes) {
-  const uint64_t u = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
-  const uint64_t s = (static_cast<uint64_t>(hi) << 32) | lo;
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(s), (short)0,
-                                           __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+// 32-bit LDS address of a pointer into the workgroup's LDS
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<size_t>((__attribute__((address_space(3))) const void*)p));
 }
+
+// global_load_lds_dwordx4 in its scalar-base form: lane L copies the 16
+// bytes at base + off (base wave-uniform, off the lane's) to LDS address
+// lds + 16 L. Written as inline assembly so that the compiler, which does not
+// see it as a memory operation, places no wait for it before later LDS reads
+// of other stages (the builtin made every tile wait for the next tile's K
+// loads before its first score); the kernel waits for it explicitly. M0
+// carries the LDS address (one wait state before the load); nothing else in
+// this file's device code reads M0, so clang's warning about reserving it is
+// silenced.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void global_load_lds16(const char* base, unsigned off, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // DU: head dims actually used (a multiple of 32, <= D); the layouts keep
 // the padded D, the MFMAs skip the columns past DU (all zero).
@@ -147,41 +159,42 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
   const int t_first = key_lo / KT;
   const int n_tiles = (key_hi - 1) / KT + 1 - t_first;
 
-  // ---- K / V^T tiles go straight to LDS (buffer_load_dwordx4 ... lds). In
+  // ---- K / V^T tiles go straight to LDS (global_load_lds_dwordx4). In
   //      load instruction i, lane L of wavefront w fills the 16 LDS bytes at
   //      offset ((i*WAVES + w)*64 + L)*16 of the tile, i.e. some row and
   //      physical chunk, and fetches the logical chunk the swizzle puts there.
-  //      seq_pad is a multiple of the tile, so every load is in bounds. ----
+  //      seq_pad is a multiple of the tile and tiles start below key_hi <=
+  //      seq, so every address lies inside the K [sp, D] and V^T [D, sp]
+  //      blocks of head g. ----
   constexpr int K_ROW_BYTES = D * 2;
   constexpr int V_ROW_BYTES = KT * 2;
   constexpr int K_INSTR = KT * K_ROW_BYTES / (WAVES * 1024);
   constexpr int V_INSTR = D * V_ROW_BYTES / (WAVES * 1024);
-  const __amdgpu_buffer_rsrc_t k_rsrc = scalar_rsrc(kg, sp * D * 2);
-  const __amdgpu_buffer_rsrc_t v_rsrc = scalar_rsrc(vg, D * sp * 2);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  unsigned k_src[K_INSTR], v_src[V_INSTR];  // the lane's byte offsets from the tile's first row
+#pragma unroll
+  for (int i = 0; i < K_INSTR; ++i) {
+    const int off = ((i * WAVES + wave) * 64 + lane) * 16;
+    const int row = off / K_ROW_BYTES, phys = (off % K_ROW_BYTES) / 16;
+    const int ch = (KCH == 16) ? (phys ^ (row & 15)) : (phys ^ swz8(row));
+    k_src[i] = row * K_ROW_BYTES + ch * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < V_INSTR; ++i) {
+    const int off = ((i * WAVES + wave) * 64 + lane) * 16;
+    const int row = off / V_ROW_BYTES, phys = (off % V_ROW_BYTES) / 16;
+    const int ch = (VCH == 16) ? (phys ^ (row & 15)) : (phys ^ swz8(row));
+    v_src[i] = row * sp * 2 + ch * 16;
+  }
   auto issue_tile = [&](int t, int stage) {
-#if __HIP_DEVICE_COMPILE__  // the LDS-DMA builtin exists only in the device pass
+    const char* kb = reinterpret_cast<const char*>(kg) + static_cast<size_t>(t) * KT * K_ROW_BYTES;
+    const char* vb = reinterpret_cast<const char*>(vg) + static_cast<size_t>(t) * KT * 2;
 #pragma unroll
-    for (int i = 0; i < K_INSTR; ++i) {
-      const int off = ((i * WAVES + wave) * 64 + lane) * 16;
-      const int row = off / K_ROW_BYTES, phys = (off % K_ROW_BYTES) / 16;
-      const int ch = (KCH == 16) ? (phys ^ (row & 15)) : (phys ^ swz8(row));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          k_rsrc, (__attribute__((address_space(3))) void*)(&k_lds[stage][0] + (i * WAVES + wave_u) * 512),
-          16, row * K_ROW_BYTES + ch * 16, t * KT * K_ROW_BYTES, 0, 0);
-    }
+    for (int i = 0; i < K_INSTR; ++i)
+      global_load_lds16(kb, k_src[i], lds_addr(&k_lds[stage][0] + (i * WAVES + wave_u) * 512));
 #pragma unroll
-    for (int i = 0; i < V_INSTR; ++i) {
-      const int off = ((i * WAVES + wave) * 64 + lane) * 16;
-      const int row = off / V_ROW_BYTES, phys = (off % V_ROW_BYTES) / 16;
-      const int ch = (VCH == 16) ? (phys ^ (row & 15)) : (phys ^ swz8(row));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          v_rsrc, (__attribute__((address_space(3))) void*)(&v_lds[stage][0] + (i * WAVES + wave_u) * 512),
-          16, row * sp * 2 + ch * 16, t * KT * 2, 0, 0);
-    }
-#else
-    (void)t, (void)stage, (void)wave_u, (void)k_rsrc, (void)v_rsrc, (void)K_INSTR, (void)V_INSTR;
-#endif
+    for (int i = 0; i < V_INSTR; ++i)
+      global_load_lds16(vb, v_src[i], lds_addr(&v_lds[stage][0] + (i * WAVES + wave_u) * 512));
   };
 
   f32x16 oacc[HPW][DB];
@@ -199,19 +212,25 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
     l_run[hh] = 0.f;
   }
 
-  issue_tile(t_first, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  for (int ti = 0; ti < n_tiles; ++ti) {
-    const int t = t_first + ti;
-    const int cur = ti & 1;
-    if (ti + 1 < n_tiles) issue_tile(t + 1, cur ^ 1);
-    const bf16_t* kl = k_lds[cur];
-    const bf16_t* vl = v_lds[cur];
-
-    // ---- S^T for 64 keys (two 32-key blocks), every K operand used by all heads ----
-    f32x16 sacc[HPW][KB];
+  // ---- the three phases of one key tile, for this wavefront's heads ----
+  // LDS byte offsets of this lane's operand reads: row lrow of a 32-row
+  // block, logical chunk 2s + lhalf for MFMA k-step s, through the swizzle.
+  // A block of 32 rows changes none of the row bits the swizzle uses, so the
+  // block enters as an immediate offset.
+  uint32_t k_off[DS], v_off[KT / 16];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    const int ch = 2 * s + lhalf;
+    k_off[s] = lrow * K_ROW_BYTES + ((KCH == 16) ? (ch ^ (lrow & 15)) : (ch ^ swz8(lrow))) * 16;
+  }
+#pragma unroll
+  for (int s = 0; s < KT / 16; ++s) {
+    const int ch = 2 * s + lhalf;
+    v_off[s] = lrow * V_ROW_BYTES + ((VCH == 16) ? (ch ^ (lrow & 15)) : (ch ^ swz8(lrow))) * 16;
+  }
+  // scores: S^T for the tile's 128 keys (four 32-key blocks), every K operand
+  // used by all heads
+  auto scores = [&](const bf16_t* kl, f32x16 (&sacc)[HPW][KB]) {
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
@@ -220,26 +239,24 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
         for (int e = 0; e < 16; ++e) sacc[hh][kb][e] = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const int row = kb * 32 + lrow;
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
-        const int ch = 2 * s + lhalf;
-        const int phys = (KCH == 16) ? (ch ^ (row & 15)) : (ch ^ swz8(row));
-        const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kl + row * D + phys * 8));
+        const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const char*>(kl) + kb * 32 * K_ROW_BYTES + k_off[s]));
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh)
           sacc[hh][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[hh][s], sacc[hh][kb], 0, 0, 0);
       }
     }
-
-    // ---- online softmax per head. Scores stay raw; the running max m is kept
-    //      in the scaled log2 domain and p = exp2(s * scale_log2 - m) is one
-    //      FMA plus one exp. m is only raised when a tile's max exceeds it by
-    //      more than 8 (p <= 2^8 meanwhile, exact once divided by the sum), so
-    //      the O rescale is skipped for the whole wavefront on most tiles. ----
+  };
+  // softmax: online softmax of tile t per head. Scores stay raw; the running
+  // max m is kept in the scaled log2 domain and p = exp2(s * scale_log2 - m)
+  // is one FMA plus one exp. m is only raised when a tile's max exceeds it by
+  // more than 8 (p <= 2^8 meanwhile, exact once divided by the sum), so the O
+  // rescale is skipped for the whole wavefront on most tiles.
+  auto softmax = [&](int t, f32x16 (&sacc)[HPW][KB], bf16x8 (&pop)[HPW][PS]) {
     // tile may hold keys past some query (causal) or outside some frame (SEG)
     const bool edge = SEG ? (t * KT < in_lo || t * KT + KT > in_hi) : (t * KT + KT - 1) > q0;
-    bf16x8 pop[HPW][PS];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
       if (edge) {
@@ -290,22 +307,35 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
           for (int e = 0; e < 16; ++e) oacc[hh][b][e] *= alpha;
       }
     }
-
-    // ---- O^T += V^T P^T: 4 steps of 16 keys, every V operand used by all heads ----
+  };
+  // pv: O^T += V^T P^T in 16-key steps, every V operand used by all heads
+  auto pv = [&](const bf16_t* vl, bf16x8 (&pop)[HPW][PS]) {
 #pragma unroll
     for (int b = 0; b < DB; ++b) {
-      const int d = b * 32 + lrow;
 #pragma unroll
       for (int s = 0; s < KT / 16; ++s) {
-        const int ch = 2 * s + lhalf;
-        const int vphys = (VCH == 16) ? (ch ^ (d & 15)) : (ch ^ swz8(d));
-        const bf16x8 vop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(vl + d * KT + vphys * 8));
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const char*>(vl) + b * 32 * V_ROW_BYTES + v_off[s]));
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh)
           oacc[hh][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[hh][s], oacc[hh][b], 0, 0, 0);
       }
     }
+  };
 
+  f32x16 sacc[HPW][KB];
+  bf16x8 pop[HPW][PS];
+  issue_tile(t_first, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int ti = 0; ti < n_tiles; ++ti) {
+    const int t = t_first + ti;
+    const int cur = ti & 1;
+    if (ti + 1 < n_tiles) issue_tile(t + 1, cur ^ 1);
+    scores(k_lds[cur], sacc);
+    softmax(t, sacc, pop);
+    pv(v_lds[cur], pop);
     // the next tile has landed, and every wavefront is done with this one
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -337,7 +367,8 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
     }
   }
   if (amax) {  // uniform; one partial maximum per workgroup
-    __shared__ float red[WAVES];
+    // the K stages are free after the loop's last barrier
+    float* red = reinterpret_cast<float*>(&k_lds[0][0]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amx = fmaxf(amx, __shfl_xor(amx, off, 64));
     if (lane == 0) red[wave] = amx;
@@ -359,11 +390,11 @@ hipError_t launch_d(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* 
   const dim3 grid(n_qb * n_kv_heads);
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(D));
   switch (G) {
-#define MHE_ATTN_CASE(GG, HH)                                                                 \
-  case GG:                                                                                    \
-    hipLaunchKernelGGL((attention_kernel<D, GG, HH, 1, false>), grid, dim3(64 * (GG / HH)), 0, \
-                       stream, q, k, vt, o, ldo, seq, n_heads, n_kv_heads, scale_log2, D,     \
-                       nullptr, amax);                                                        \
+#define MHE_ATTN_CASE(GG, HH)                                                                      \
+  case GG:                                                                                         \
+    hipLaunchKernelGGL((attention_kernel<D, GG, HH, 1, false, D>), grid, dim3(64 * (GG / HH)),     \
+                       0, stream, q, k, vt, o, ldo, seq, n_heads, n_kv_heads, scale_log2, D,       \
+                       nullptr, amax);                                                             \
     break;
     MHE_ATTN_CASE(1, 1)
     MHE_ATTN_CASE(2, 1)

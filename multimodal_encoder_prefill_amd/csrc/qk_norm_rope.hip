@@ -110,17 +110,31 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
   }
 
   // ---- rotary cos/sin of the block's tokens into LDS: copied from the
-  //      encode's table, or formed here (every head row of a token reads them) ----
+  //      encode's table, or formed here (every head row of a token reads them).
+  //      A lane of chunk c uses the slots 8c' .. 8c'+7 (c' = c mod CH) as four
+  //      float4 (two (cos, sin) pairs each); token t's float4 number i of
+  //      chunk c' is stored at t * HALF/2 + i * CH + c', so that one read
+  //      instruction of the CH lanes of a row takes consecutive 16-byte words
+  //      (stored chunk-major, those reads were 64 bytes apart and collided
+  //      in the LDS banks). ----
+  constexpr int CH = HALF / 8;  // slot chunks of 8 per token
+  auto cs_index = [](int t, int j) {  // float4 holding slot pair (j, j+1), j even
+    return t * (HALF / 2) + ((j % 8) / 2) * CH + j / 8;
+  };
   __shared__ __attribute__((aligned(16))) float2 cs[kTok * HALF];
   if constexpr (TABLE) {
     const int n4 = kTok * HALF / 2;  // float4 = two (cos, sin) pairs
     const int valid = (min(s0 + kTok, seq) - min(s0, seq)) * HALF / 2;
     const float4* src = reinterpret_cast<const float4*>(table + static_cast<size_t>(min(s0, seq)) * HALF);
     for (int e = threadIdx.x; e < n4; e += kThreads)
-      reinterpret_cast<float4*>(cs)[e] = e < valid ? src[e] : make_float4(1.f, 0.f, 1.f, 0.f);
+      reinterpret_cast<float4*>(cs)[cs_index(e / (HALF / 2), 2 * (e % (HALF / 2)))] =
+          e < valid ? src[e] : make_float4(1.f, 0.f, 1.f, 0.f);
   } else {
-    for (int e = threadIdx.x; e < kTok * HALF; e += kThreads)
-      cs[e] = rope_angle(pos, seq, min(s0 + e / HALF, seq - 1), e % HALF, D, theta, sec1, sec2);
+    for (int e = threadIdx.x; e < kTok * HALF; e += kThreads) {
+      const int t = e / HALF, j = e % HALF;
+      cs[2 * cs_index(t, j & ~1) + (j & 1)] =
+          rope_angle(pos, seq, min(s0 + t, seq - 1), j, D, theta, sec1, sec2);
+    }
   }
   __syncthreads();
 
@@ -170,10 +184,10 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
       float gn[8];
       unpack8(*reinterpret_cast<const u32x4*>((is_q ? q_gain : k_gain) + chunk * 8), gn);
       float2 cs8[8];
-      const float4* tr = reinterpret_cast<const float4*>(cs + t * HALF + j0);
+      const float4* tr = reinterpret_cast<const float4*>(cs) + cs_index(t, j0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float4 v = tr[i];
+        const float4 v = tr[i * CH];
         cs8[2 * i] = make_float2(v.x, v.y);
         cs8[2 * i + 1] = make_float2(v.z, v.w);
       }
