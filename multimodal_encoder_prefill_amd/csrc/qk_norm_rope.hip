@@ -20,8 +20,8 @@
 //
 // The cos/sin of every (token, slot) depend only on the positions, so an
 // encode computes them once (rope_table_kernel, [seq][D/2] float pairs) and
-// every layer reads them; the single-step entry point without a table builds
-// its tokens' angles in LDS instead (same operations, same values).
+// every layer reads them; the single-step entry point without a table forms
+// each lane's angles in registers instead (same operations, same values).
 //
 // HBM-bound: per token it reads and writes (n_heads + 2 n_kv_heads) * D bf16.
 #include "common.h"
@@ -57,8 +57,38 @@ __global__ __launch_bounds__(kThreads) void rope_table_kernel(const int32_t* __r
   table[e] = rope_angle(pos, seq, e / half, e % half, D, theta, sec1, sec2);
 }
 
-// q / k head rows handled per wavefront per batch (4 rows per pass)
-constexpr int kPasses = 4;
+// Value of the lane N places further along its aligned row of 16 lanes (a DPP
+// row rotation: a plain VALU move, no LDS traffic unlike a lane permute).
+template <int N>
+__device__ __forceinline__ float row_rotate(float x) {
+  static_assert(N >= 1 && N <= 15, "row rotation by 1..15 lanes");
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
+
+// Sum over an aligned group of LPR lanes, the same bits in every lane of the
+// group. For 16-lane groups the rotations by 8, 4, 2, 1 pair the same values
+// as the xor butterfly (each step's two addends are equal across the lanes
+// that meet), through DPP instead of LDS permutes.
+template <int LPR>
+__device__ __forceinline__ float head_row_sum(float x) {
+  if constexpr (LPR == 16) {
+    x += row_rotate<8>(x);
+    x += row_rotate<4>(x);
+    x += row_rotate<2>(x);
+    x += row_rotate<1>(x);
+    return x;
+  } else {
+    return group_sum<LPR>(x);
+  }
+}
+
+// The element D/2 away in the same head row: LPR/2 lanes away, i.e. the lane
+// xor LPR/2 (for 16-lane rows the rotation by 8).
+template <int LPR>
+__device__ __forceinline__ float rotary_partner(float y) {
+  if constexpr (LPR == 16) return row_rotate<8>(y);
+  else return __shfl_xor(y, LPR / 2, 64);
+}
 
 template <int D, bool TABLE>
 __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
@@ -109,108 +139,82 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
     return;
   }
 
-  // ---- rotary cos/sin of the block's tokens into LDS: copied from the
-  //      encode's table, or formed here (every head row of a token reads them).
-  //      A lane of chunk c uses the slots 8c' .. 8c'+7 (c' = c mod CH) as four
-  //      float4 (two (cos, sin) pairs each); token t's float4 number i of
-  //      chunk c' is stored at t * HALF/2 + i * CH + c', so that one read
-  //      instruction of the CH lanes of a row takes consecutive 16-byte words
-  //      (stored chunk-major, those reads were 64 bytes apart and collided
-  //      in the LDS banks). ----
-  constexpr int CH = HALF / 8;  // slot chunks of 8 per token
-  auto cs_index = [](int t, int j) {  // float4 holding slot pair (j, j+1), j even
-    return t * (HALF / 2) + ((j % 8) / 2) * CH + j / 8;
-  };
-  __shared__ __attribute__((aligned(16))) float2 cs[kTok * HALF];
-  if constexpr (TABLE) {
-    const int n4 = kTok * HALF / 2;  // float4 = two (cos, sin) pairs
-    const int valid = (min(s0 + kTok, seq) - min(s0, seq)) * HALF / 2;
-    const float4* src = reinterpret_cast<const float4*>(table + static_cast<size_t>(min(s0, seq)) * HALF);
-    for (int e = threadIdx.x; e < n4; e += kThreads)
-      reinterpret_cast<float4*>(cs)[cs_index(e / (HALF / 2), 2 * (e % (HALF / 2)))] =
-          e < valid ? src[e] : make_float4(1.f, 0.f, 1.f, 0.f);
-  } else {
-    for (int e = threadIdx.x; e < kTok * HALF; e += kThreads) {
-      const int t = e / HALF, j = e % HALF;
-      cs[2 * cs_index(t, j & ~1) + (j & 1)] =
-          rope_angle(pos, seq, min(s0 + t, seq - 1), j, D, theta, sec1, sec2);
-    }
-  }
-  __syncthreads();
-
-  // ---- q / k head rows: D/8 lanes per row, 8 consecutive elements per lane;
-  //      element d pairs with d +- D/2, which sits D/16 lanes away ----
-  constexpr int LPR = D / 8;           // lanes per head row
-  constexpr int ROWS_PER_PASS = 64 / LPR;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int sub = lane / LPR;
-  const int chunk = lane % LPR;
+  // ---- q / k head rows: D/8 lanes per row (a row group), 8 consecutive
+  //      elements per lane; element d pairs with d +- D/2, which sits D/16
+  //      lanes away. A row group keeps one token and walks its heads, so the
+  //      lane's rotary cos/sin (8 slots) are read or formed once, in
+  //      registers: no LDS stage and no barrier, and every head row of the
+  //      group is loaded before any math. ----
+  constexpr int LPR = D / 8;              // lanes per head row
+  constexpr int RG = kThreads / LPR;      // row groups per workgroup
+  constexpr int SPLIT = RG / kTok;        // row groups per token
+  constexpr int HPR = kHeadsPerBlock / SPLIT;  // heads per row group
+  static_assert(RG % kTok == 0 && kHeadsPerBlock % SPLIT == 0, "row groups must tile the block");
+  const int rg = threadIdx.x / LPR;
+  const int chunk = threadIdx.x % LPR;
   const bool first_half = chunk < LPR / 2;
   const int j0 = (chunk % (LPR / 2)) * 8;   // rotary slot of this lane's first element
+  const int s = s0 + rg / SPLIT;
+  const int hp = (rg % SPLIT) * HPR;        // first head of the group, within the block
   const int h_first = (blockIdx.y - 1) * kHeadsPerBlock;
   const int h_count = min(kHeadsPerBlock, n_heads + n_kv_heads - h_first);
-  const int rows = kTok * h_count;
-  // kPasses row groups per batch: all their loads go out before any math
-  for (int rb = wave * ROWS_PER_PASS; rb < rows; rb += 4 * ROWS_PER_PASS * kPasses) {
-    float x[kPasses][8];
+  u32x4 raw[HPR];
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int r = rb + p * 4 * ROWS_PER_PASS + sub;
-      const int t = r < rows ? r / h_count : 0;
-      const int h = h_first + (r < rows ? r % h_count : 0);
-      const int s = s0 + t;
-      if (r < rows && s < seq) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(qkv + static_cast<size_t>(s) * width + h * D + chunk * 8);
-        unpack8(v, x[p]);
-      } else {
+  for (int i = 0; i < HPR; ++i)
+    raw[i] = (s < seq && hp + i < h_count)
+                 ? *reinterpret_cast<const u32x4*>(qkv + static_cast<size_t>(s) * width +
+                                                   (h_first + hp + i) * D + chunk * 8)
+                 : u32x4{0, 0, 0, 0};
+  // cos/sin of slots j0 .. j0+7 of the token (the last real token stands in
+  // for padding tokens, whose outputs are zeros or not stored)
+  const int sc = min(s, seq - 1);
+  float2 cs8[8];
+  if constexpr (TABLE) {
+    const float4* tr = reinterpret_cast<const float4*>(table + static_cast<size_t>(sc) * HALF + j0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[p][i] = 0.f;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float4 v = tr[i];
+      cs8[2 * i] = make_float2(v.x, v.y);
+      cs8[2 * i + 1] = make_float2(v.z, v.w);
     }
+  } else {
 #pragma unroll
-    for (int p = 0; p < kPasses; ++p) {
-      const int r = rb + p * 4 * ROWS_PER_PASS + sub;
-      const bool active = r < rows;
-      const int t = active ? r / h_count : 0;
-      const int h = h_first + (active ? r % h_count : 0);
-      const int s = s0 + t;
-      const bool is_q = h < n_heads;
-      float ss = 0.f;
+    for (int i = 0; i < 8; ++i) cs8[i] = rope_angle(pos, seq, sc, j0 + i, D, theta, sec1, sec2);
+  }
+  const u32x4 gq = *reinterpret_cast<const u32x4*>(q_gain + chunk * 8);
+  const u32x4 gk = *reinterpret_cast<const u32x4*>(k_gain + chunk * 8);
+
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ss += x[p][i] * x[p][i];
-      ss = group_sum<LPR>(ss);
-      const float rinv = rsqrtf(ss / static_cast<float>(D) + eps);
-      float gn[8];
-      unpack8(*reinterpret_cast<const u32x4*>((is_q ? q_gain : k_gain) + chunk * 8), gn);
-      float2 cs8[8];
-      const float4* tr = reinterpret_cast<const float4*>(cs) + cs_index(t, j0);
+  for (int i = 0; i < HPR; ++i) {
+    const int h = h_first + hp + i;
+    const bool is_q = h < n_heads;
+    float x[8], gn[8];
+    unpack8(raw[i], x);
+    unpack8(is_q ? gq : gk, gn);
+    float ss = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 v = tr[i * CH];
-        cs8[2 * i] = make_float2(v.x, v.y);
-        cs8[2 * i + 1] = make_float2(v.z, v.w);
-      }
-      float y[8], o[8];
+    for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+    ss = head_row_sum<LPR>(ss);
+    const float rinv = rsqrtf(ss / static_cast<float>(D) + eps);
+    float y[8], o[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] = x[p][i] * rinv * gn[i];
+    for (int e = 0; e < 8; ++e) y[e] = x[e] * rinv * gn[e];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float partner = __shfl_xor(y[i], LPR / 2, 64);
-        const float c = cs8[i].x, sn = cs8[i].y;
-        // first half: x cos - x_partner sin; second half: x cos + x_partner sin
-        o[i] = first_half ? y[i] * c - partner * sn : y[i] * c + partner * sn;
-      }
-      if (!active) continue;
-      if (is_q) {
-        if (s < seq)
-          *reinterpret_cast<u32x4*>(q_out + (static_cast<size_t>(s) * n_heads + h) * D + chunk * 8) = pack8(o);
-      } else if (s < seq_pad) {
-        const int g = h - n_heads;
-        u32x4 v = pack8(o);
-        if (s >= seq) v = u32x4{0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(k_out + (static_cast<size_t>(g) * seq_pad + s) * D + chunk * 8) = v;
-      }
+    for (int e = 0; e < 8; ++e) {
+      const float partner = rotary_partner<LPR>(y[e]);
+      const float c = cs8[e].x, sn = cs8[e].y;
+      // first half: x cos - x_partner sin; second half: x cos + x_partner sin
+      o[e] = first_half ? y[e] * c - partner * sn : y[e] * c + partner * sn;
+    }
+    if (hp + i >= h_count) continue;
+    if (is_q) {
+      if (s < seq)
+        *reinterpret_cast<u32x4*>(q_out + (static_cast<size_t>(s) * n_heads + h) * D + chunk * 8) = pack8(o);
+    } else if (s < seq_pad) {
+      const int g = h - n_heads;
+      u32x4 v = pack8(o);
+      if (s >= seq) v = u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(k_out + (static_cast<size_t>(g) * seq_pad + s) * D + chunk * 8) = v;
     }
   }
 }
