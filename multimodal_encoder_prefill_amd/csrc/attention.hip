@@ -29,8 +29,9 @@
 // MiniMaxH3Qwen3VLVisionAttention.forward): SEG replaces the causal mask by
 // "key in the query's frame" (a [seg_lo, seg_hi) token range per query), the
 // head_dim of 72 is stored zero-padded to 128 (zero q/k columns add nothing to
-// the scores, zero V rows give output columns that are not stored; the MFMAs
-// stop at 96 dims), and with one query head per key/value head a workgroup
+// the scores, zero V rows give output columns that are not stored; the score
+// MFMAs stop at 80 dims, the PV MFMAs at 96), and with one query head per
+// key/value head a workgroup
 // takes QW = 8 query blocks of one head so that its 8 wavefronts share every
 // K/V tile.
 #include "common.h"
@@ -82,9 +83,10 @@ __device__ __forceinline__ void global_load_lds16(const char* base, unsigned off
 }
 #pragma clang diagnostic pop
 
-// DU: head dims actually used (a multiple of 32, <= D); the layouts keep
-// the padded D, the MFMAs skip the columns past DU (all zero).
-template <int D, int G, int HPW, int QW, bool SEG, int DU = D>
+// DU: head dims actually used by the PV product (a multiple of 32, <= D),
+// DK: by the scores (a multiple of 16, <= DU); the layouts keep the padded D,
+// the MFMAs skip the columns past DU / DK (all zero).
+template <int D, int G, int HPW, int QW, bool SEG, int DU = D, int DK = DU>
 __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
     bf16_t* __restrict__ o, int ldo, int seq, int n_heads, int n_kv_heads, float scale_log2,
@@ -92,8 +94,8 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
   constexpr int HW = G / HPW;        // wavefronts per query block (heads of the group)
   constexpr int WAVES = HW * QW;
   constexpr int KCH = D / 8;          // 16-byte chunks per K row
-  static_assert(DU % 32 == 0 && DU <= D, "used head dims");
-  constexpr int DS = DU / 16;         // MFMA k-steps over the used head dims
+  static_assert(DU % 32 == 0 && DU <= D && DK % 16 == 0 && DK <= DU, "used head dims");
+  constexpr int DS = DK / 16;         // MFMA k-steps of the scores over the used head dims
   constexpr int DB = DU / 32;         // 32-row blocks of O^T
   constexpr int KB = KT / 32;         // 32-key blocks of S^T per tile
   constexpr int PS = KT / 16;         // 16-key MFMA steps of O^T += V^T P^T
@@ -268,6 +270,11 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
             if (key < my_lo || key >= my_hi) sacc[hh][kb][e] = -INFINITY;
           }
       }
+      // The compiler does not see the max3 assembly as a reader of MFMA
+      // results and so keeps no wait states for it; the last block's scores
+      // (the only ones whose MFMAs may still be in flight) pass through nops
+      // tied to them first (more than the 8-pass MFMA's 11 wait states).
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(sacc[hh][KB - 1]));
       float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -422,7 +429,13 @@ hipError_t launch_segment_attention(const bf16_t* q, const bf16_t* k, const bf16
   if (head_dim > 128 || head_dim % 4 != 0 || ldo < heads * head_dim || ldo % 4 != 0)
     return hipErrorInvalidValue;
   const float scale_log2 = 1.4426950408889634f / sqrtf(static_cast<float>(head_dim));
-  if (head_dim <= 96) {
+  if (head_dim <= 80) {
+    // 8 query blocks (two wavefronts per SIMD), score MFMAs over 80 dims, PV
+    // over 96
+    const int n_qb = (n + QB * 8 - 1) / (QB * 8);
+    hipLaunchKernelGGL((attention_kernel<128, 1, 1, 8, true, 96, 80>), dim3(n_qb * heads), dim3(64 * 8), 0,
+                       stream, q, k, vt, o, ldo, n, heads, heads, scale_log2, head_dim, info, nullptr);
+  } else if (head_dim <= 96) {
     // 8 query blocks (two wavefronts per SIMD), MFMAs over 96 dims
     const int n_qb = (n + QB * 8 - 1) / (QB * 8);
     hipLaunchKernelGGL((attention_kernel<128, 1, 1, 8, true, 96>), dim3(n_qb * heads), dim3(64 * 8), 0,

@@ -92,7 +92,8 @@ def test_linear_bias_matches_oracle(act):
 
 
 @pytest.mark.parametrize("grids,heads,hd", [(GRIDS_TINY, 8, 72), (GRIDS_FULL, 16, 72),
-                                           ([(1, 64, 128)], 16, 72), (GRIDS_TINY, 4, 128)])
+                                           ([(1, 64, 128)], 16, 72), (GRIDS_TINY, 4, 128),
+                                           (GRIDS_TINY, 4, 80), (GRIDS_TINY, 4, 96)])
 def test_vision_attention_per_frame(grids, heads, hd):
     """The per-frame attention step on its own: every (patch, head) row
     against the oracle's segment attention, frames as the grids cut them (the
