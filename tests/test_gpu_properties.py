@@ -1,0 +1,167 @@
+"""Property tests over random small shapes (hypothesis): the RMSNorm, q/k norm
++ rotary, attention and DeepStack kernels, through the C ABI, against the CPU
+oracle on shapes drawn at random — ragged sequence lengths, head groupings,
+head dims, position ranges, rotary sections, input scales and mask densities.
+
+The draws are derandomised (the same cases on every run) and each case prints
+its shape before its kernel runs. Bars are those of the per-step tests: one
+bf16 rounding of each output (rel-L2 <= 4e-3; attention, which also rounds
+the probabilities, 8e-3) and, per (token, head) row, <= 3e-2.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+import oracle
+from multimodal_encoder_prefill_amd import binding as b
+from multimodal_encoder_prefill_amd import synth
+from helpers import f64, perm16_tokens, report, report_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+ROW_BAR = 3e-2
+
+CASES = settings(max_examples=12, deadline=None, derandomize=True, database=None,
+                 suppress_health_check=list(HealthCheck))
+
+
+def _randn(shape, seed, std=1.0):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=DEV) * std).to(torch.bfloat16)
+
+
+def _gain(n, seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return (torch.rand(n, generator=g, device=DEV) + 0.5).to(torch.bfloat16)
+
+
+# log-uniform input scales: tiny, unit and large activations
+scales = st.sampled_from([1e-2, 0.3, 1.0, 4.0, 60.0])
+
+
+@CASES
+@given(rows=st.integers(1, 300), dim8=st.integers(1, 800), std=scales,
+       eps=st.sampled_from([1e-6, 1e-5]), seed=st.integers(0, 2**20))
+def test_rms_norm_random_shapes(rows, dim8, std, eps, seed):
+    dim = 8 * dim8
+    print(f"rms_norm rows={rows} dim={dim} std={std} eps={eps} seed={seed}", flush=True)
+    x = _randn((rows, dim), seed, std)
+    gamma = _gain(dim, seed + 1)
+    y = torch.empty_like(x)
+    b.rms_norm(x, gamma, y, rows, dim, eps)
+    torch.cuda.synchronize()
+    ref = oracle.rms_norm(f64(x), f64(gamma), eps)
+    assert report("rms_norm", f64(y), ref)[0] <= 4e-3
+    assert np.all(np.abs(f64(y) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
+
+
+@st.composite
+def qk_shapes(draw):
+    d = draw(st.sampled_from([64, 128]))
+    n_kv = draw(st.sampled_from([1, 2, 4, 8]))
+    group = draw(st.sampled_from([1, 2, 4, 8]))
+    seq = draw(st.integers(1, 300))
+    # rotary sections covering the D/2 slots in some split
+    a = draw(st.integers(0, d // 2))
+    c = draw(st.integers(0, d // 2 - a))
+    section = (d // 2 - a - c, a, c)
+    theta = draw(st.sampled_from([1e4, 1e6, 5e6]))
+    max_pos = draw(st.sampled_from([1, 50, 3000, 16384]))
+    return d, n_kv, group, seq, section, theta, max_pos
+
+
+@CASES
+@given(shape=qk_shapes(), seed=st.integers(0, 2**20))
+def test_qk_norm_rope_random_shapes(shape, seed):
+    d, n_kv, group, seq, section, theta, max_pos = shape
+    print(f"qk_norm_rope D={d} heads={n_kv * group}/{n_kv} seq={seq} section={section} "
+          f"theta={theta} max_pos={max_pos} seed={seed}", flush=True)
+    dims = dataclasses.replace(synth.TINY, hidden=n_kv * group * d, n_heads=n_kv * group,
+                               n_kv_heads=n_kv, head_dim=d, rope_theta=theta,
+                               mrope_section=section)
+    qw, kvw = dims.q_width, dims.kv_width
+    qkv = _randn((seq, qw + 2 * kvw), seed, 2.0)
+    qn, kn = _gain(d, seed + 1), _gain(d, seed + 2)
+    sp = b.seq_pad(seq)
+    q_out = torch.full((seq, dims.n_heads, d), 7.0, device=DEV, dtype=torch.bfloat16)
+    k_out = torch.full((n_kv, sp, d), 7.0, device=DEV, dtype=torch.bfloat16)
+    vt_out = torch.full((n_kv, d, sp), 7.0, device=DEV, dtype=torch.bfloat16)
+    positions = synth.random_positions(seq, max_pos, seed=seed)
+    pos = torch.from_numpy(np.ascontiguousarray(positions)).to(DEV)
+    b.qk_norm_rope(b.config_from_dims(dims), qkv, qn, kn, pos, seq, q_out, k_out, vt_out)
+    torch.cuda.synchronize()
+    x = f64(qkv)
+    cos, sin = oracle.rope_cos_sin(positions, d, theta, section)
+    q_ref = oracle.apply_rope(oracle.rms_norm(x[:, :qw].reshape(seq, -1, d), f64(qn), dims.rms_eps), cos, sin)
+    k_ref = oracle.apply_rope(oracle.rms_norm(x[:, qw:qw + kvw].reshape(seq, -1, d), f64(kn), dims.rms_eps),
+                              cos, sin)
+    r, _, w = report_rows("q", f64(q_out), q_ref, d)
+    assert r <= 4e-3 and w <= ROW_BAR
+    kk = f64(k_out)
+    r, _, w = report_rows("k", kk[:, :seq].transpose(1, 0, 2), k_ref, d)
+    assert r <= 4e-3 and w <= ROW_BAR
+    assert np.all(kk[:, seq:] == 0)
+    v_pad = np.zeros((sp, n_kv, d))
+    v_pad[:seq] = x[:, qw + kvw:].reshape(seq, n_kv, d)
+    assert np.array_equal(f64(vt_out), v_pad[perm16_tokens(sp)].transpose(1, 2, 0))
+
+
+@st.composite
+def attention_shapes(draw):
+    d = draw(st.sampled_from([64, 128]))
+    n_kv = draw(st.sampled_from([1, 2, 4, 8]))
+    group = draw(st.sampled_from([1, 2, 4, 8]))
+    seq = draw(st.integers(1, 400))
+    return d, n_kv, group, seq
+
+
+@CASES
+@given(shape=attention_shapes(), std=st.sampled_from([0.3, 1.0, 2.0, 4.0]), seed=st.integers(0, 2**20))
+def test_attention_random_shapes(shape, std, seed):
+    d, n_kv, group, seq = shape
+    hq = n_kv * group
+    print(f"attention D={d} heads={hq}/{n_kv} seq={seq} std={std} seed={seed}", flush=True)
+    q = _randn((seq, hq, d), seed, std)
+    k = _randn((seq, n_kv, d), seed + 1, std)
+    v = _randn((seq, n_kv, d), seed + 2)
+    sp = b.seq_pad(seq)
+    k_l = torch.zeros((n_kv, sp, d), device=DEV, dtype=torch.bfloat16)
+    k_l[:, :seq] = k.transpose(0, 1)
+    v_pad = torch.zeros((sp, n_kv, d), device=DEV, dtype=torch.bfloat16)
+    v_pad[:seq] = v
+    vt_l = v_pad[torch.from_numpy(perm16_tokens(sp)).to(DEV)].permute(1, 2, 0).contiguous()
+    o = torch.full((seq, hq * d), 7.0, device=DEV, dtype=torch.bfloat16)
+    b.attention(q, k_l, vt_l, o, seq, hq, n_kv, d)
+    torch.cuda.synchronize()
+    ref = oracle.causal_gqa_attention(f64(q), f64(k), f64(v)).reshape(seq, hq * d)
+    r, _, w = report_rows("attention", f64(o), ref, d)
+    assert r <= 8e-3 and w <= ROW_BAR
+
+
+@CASES
+@given(seq=st.integers(1, 2000), dim8=st.integers(1, 700), density=st.floats(0.0, 1.0),
+       seed=st.integers(0, 2**20))
+def test_deepstack_random_masks(seq, dim8, density, seed):
+    dim = 8 * dim8
+    print(f"deepstack seq={seq} dim={dim} density={density:.3f} seed={seed}", flush=True)
+    rng = np.random.default_rng(seed)
+    mask = (rng.random(seq) < density).astype(np.uint8)
+    n_vis = int(mask.sum())
+    h = _randn((seq, dim), seed)
+    feat = _randn((max(n_vis, 1), dim), seed + 1)
+    ref = oracle.deepstack_add(f64(h), mask, f64(feat)[:n_vis])
+    ws = torch.empty(seq * 4 + 512, device=DEV, dtype=torch.uint8)
+    m = torch.from_numpy(mask).to(DEV)
+    b.deepstack_inject(h, seq, dim, m, n_vis, feat, ws, ws.numel())
+    torch.cuda.synchronize()
+    got = f64(h)
+    # one rounding of the exact sum of two bf16 values: within half an ulp
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref))
+    assert np.array_equal(got[mask == 0], ref[mask == 0])
