@@ -1,7 +1,8 @@
 """Property tests over random small shapes (hypothesis): the RMSNorm, q/k norm
-+ rotary, attention and DeepStack kernels, through the C ABI, against the CPU
-oracle on shapes drawn at random — ragged sequence lengths, head groupings,
-head dims, position ranges, rotary sections, input scales and mask densities.
++ rotary, attention, DeepStack and GEMM kernels, through the C ABI, against the
+CPU oracle on shapes drawn at random — ragged sequence lengths and GEMM
+shapes, head groupings, head dims, position ranges, rotary sections, input
+scales, mask densities, with and without the split-K scratch.
 
 The draws are derandomised (the same cases on every run) and each case prints
 its shape before its kernel runs. Bars are those of the per-step tests: one
@@ -165,3 +166,50 @@ def test_deepstack_random_masks(seq, dim8, density, seed):
     # one rounding of the exact sum of two bf16 values: within half an ulp
     assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref))
     assert np.array_equal(got[mask == 0], ref[mask == 0])
+
+
+@st.composite
+def gemm_shapes(draw):
+    m = draw(st.integers(1, 1100))
+    n = 32 * draw(st.integers(1, 64))
+    k = 64 * draw(st.integers(1, 32))
+    return m, n, k
+
+
+@CASES
+@given(shape=gemm_shapes(), residual=st.booleans(), split=st.booleans(), std=st.sampled_from([0.1, 1.0, 8.0]),
+       seed=st.integers(0, 2**20))
+def test_linear_random_shapes(shape, residual, split, std, seed):
+    """C = A W^T (+ R) on ragged shapes; with the scratch, the last wave may be split along k."""
+    m, n, k = shape
+    print(f"linear m={m} n={n} k={k} residual={residual} split={split} std={std} seed={seed}", flush=True)
+    a = _randn((m, k), seed, std)
+    w = _randn((n, k), seed + 1, 0.05)
+    c = _randn((m, n), seed + 2) if residual else torch.full((m, n), 7.0, device=DEV, dtype=torch.bfloat16)
+    r0 = f64(c) if residual else 0.0
+    ws = torch.empty(b.linear_workspace_bytes(), device=DEV, dtype=torch.uint8) if split else None
+    b.linear(a, w, c, m, n, k, residual=c if residual else None, workspace=ws)
+    torch.cuda.synchronize()
+    ref = r0 + f64(a) @ f64(w).T
+    r, mx = report("linear", f64(c), ref)
+    assert r <= 4e-3
+    assert mx <= 2.0 ** -7 * np.max(np.abs(ref))
+
+
+@CASES
+@given(shape=gemm_shapes(), split=st.booleans(), seed=st.integers(0, 2**20))
+def test_swiglu_random_shapes(shape, split, seed):
+    """silu(A Wg^T) * (A Wu^T) on ragged shapes, with and without the split-K scratch."""
+    m, n, k = shape
+    print(f"swiglu m={m} n={n} k={k} split={split} seed={seed}", flush=True)
+    a = _randn((m, k), seed)
+    wg = _randn((n, k), seed + 1, 0.1)
+    wu = _randn((n, k), seed + 2, 0.1)
+    c = torch.full((m, n), 7.0, device=DEV, dtype=torch.bfloat16)
+    ws = torch.empty(b.linear_workspace_bytes(), device=DEV, dtype=torch.uint8) if split else None
+    b.linear_swiglu(a, wg, wu, c, m, n, k, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.silu(f64(a) @ f64(wg).T) * (f64(a) @ f64(wu).T)
+    r, mx = report("swiglu", f64(c), ref)
+    assert r <= 4e-3
+    assert mx <= 2.0 ** -7 * np.max(np.abs(ref))
