@@ -90,6 +90,21 @@ def test_layer_full_width_s512_teacher_forced():
     assert _teacher_forced(wl, s, states, rows=rows) <= 2e-2
 
 
+def test_layers_full_width_ragged_seq_every_row():
+    """Two full-width layers at a ragged length (seq 777: partial 256-row
+    GEMM tiles, the 256-wide tile and its split-K tail instead of the 320-wide
+    one, a partial attention tile) with an image block and its DeepStack
+    levels: every row of both layers teacher-forced against the oracle."""
+    wl = synth.custom_workload(synth.FULL, 777, 2, (("text", 201), ("visual", (1, 16, 32)), ("text", 64)),
+                               2, key="full_s777", index=77)
+    print(f"full-width layers at seq {wl.seq}, {wl.n_vis} visual tokens", flush=True)
+    s = _setup(wl)
+    out = _run_encode(wl, s)
+    states = _gpu_states(wl, s)
+    assert torch.equal(states[-1], out)
+    assert _teacher_forced(wl, s, states) <= 2e-2
+
+
 def _run_encode(wl, s, n_layers=None):
     layers = s["layers"] if n_layers is None else s["layers"][:n_layers]
     out = torch.empty_like(s["emb"])
