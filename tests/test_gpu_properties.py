@@ -1,5 +1,5 @@
 """Property tests over random small shapes (hypothesis): the RMSNorm, q/k norm
-+ rotary, attention, DeepStack and GEMM kernels, through the C ABI, against the
++ rotary, attention, DeepStack, GEMM and FP8 kernels, through the C ABI, against the
 CPU oracle on shapes drawn at random — ragged sequence lengths and GEMM
 shapes, head groupings, head dims, position ranges, rotary sections, input
 scales, mask densities, with and without the split-K scratch.
@@ -211,5 +211,57 @@ def test_swiglu_random_shapes(shape, split, seed):
     torch.cuda.synchronize()
     ref = oracle.silu(f64(a) @ f64(wg).T) * (f64(a) @ f64(wu).T)
     r, mx = report("swiglu", f64(c), ref)
+    assert r <= 4e-3
+    assert mx <= 2.0 ** -7 * np.max(np.abs(ref))
+
+
+# ------------------------------------------------------------------ FP8 (online E4M3)
+
+@CASES
+@given(rows=st.integers(1, 700), cols8=st.integers(1, 200), log_std=st.floats(-6, 6),
+       n_parts=st.integers(1, 3), outlier=st.booleans(), seed=st.integers(0, 2**20))
+def test_quantize_fp8_random_shapes_bit_exact(rows, cols8, log_std, n_parts, outlier, seed):
+    """Per-tensor E4M3 codes of 1-3 stacked row blocks at random scales: the
+    same fp32 factor, product, clamp and rounding as the oracle, so the codes
+    are bit-identical and the scale equal within one fp32 rounding."""
+    from oracle import fp8 as Q
+    cols = 8 * cols8
+    print(f"quantize_fp8 rows={rows} cols={cols} std=2^{log_std:.2f} parts={n_parts} outlier={outlier} "
+          f"seed={seed}", flush=True)
+    x = _randn((rows, cols), seed, float(2.0 ** log_std))
+    if outlier:
+        x[rows // 2, cols // 3] = float(2.0 ** (log_std + 9))
+    cuts = sorted(set([0, rows] + [int(v) for v in np.random.default_rng(seed).integers(1, rows + 1, n_parts - 1)]))
+    parts = [x[a:b_].contiguous() for a, b_ in zip(cuts, cuts[1:]) if b_ > a]
+    q = torch.empty((rows, cols), device=DEV, dtype=torch.uint8)
+    s = torch.empty(1, device=DEV, dtype=torch.float32)
+    ws = torch.empty(b.quantize_fp8_workspace_bytes(), device=DEV, dtype=torch.uint8)
+    b.quantize_fp8(parts, [p.shape[0] for p in parts], cols, q, s, ws)
+    torch.cuda.synchronize()
+    vals, scale = Q.quantize(f64(x))
+    got = Q.e4m3_values()[q.cpu().numpy()]
+    assert np.count_nonzero(got != vals) == 0
+    assert abs(s.item() - scale) <= 2.0 ** -23 * scale
+
+
+@CASES
+@given(m=st.integers(1, 1100), n32=st.integers(1, 64), k128=st.integers(1, 16), residual=st.booleans(),
+       split=st.booleans(), seed=st.integers(0, 2**20))
+def test_linear_fp8_random_shapes(m, n32, k128, residual, split, seed):
+    """(q_a q_w^T) s_a s_w (+ R) on random E4M3 codes and ragged shapes."""
+    from oracle import fp8 as Q
+    n, k = 32 * n32, 128 * k128
+    print(f"linear_fp8 m={m} n={n} k={k} residual={residual} split={split} seed={seed}", flush=True)
+    a, w = synth.fp8_codes((m, k), seed, DEV), synth.fp8_codes((n, k), seed + 1, DEV)
+    sa = torch.tensor([0.01 * (1 + seed % 7)], device=DEV, dtype=torch.float32)
+    sw = torch.tensor([1e-3 * (1 + seed % 5)], device=DEV, dtype=torch.float32)
+    c = _randn((m, n), seed + 2) if residual else torch.full((m, n), 7.0, device=DEV, dtype=torch.bfloat16)
+    r0 = f64(c) if residual else 0.0
+    ws = torch.empty(b.linear_workspace_bytes(), device=DEV, dtype=torch.uint8) if split else None
+    b.linear_fp8(a, sa, w, sw, c, m, n, k, residual=c if residual else None, workspace=ws)
+    torch.cuda.synchronize()
+    T = Q.e4m3_values()
+    ref = r0 + (T[a.cpu().numpy()] @ T[w.cpu().numpy()].T) * (float(sa.item()) * float(sw.item()))
+    r, mx = report("linear_fp8", f64(c), ref)
     assert r <= 4e-3
     assert mx <= 2.0 ** -7 * np.max(np.abs(ref))
