@@ -1,5 +1,5 @@
 """Property tests over random small shapes (hypothesis): the RMSNorm, q/k norm
-+ rotary, attention, DeepStack, GEMM and FP8 kernels, through the C ABI, against the
++ rotary, attention, DeepStack, GEMM, FP8 and vision-tower kernels, through the C ABI, against the
 CPU oracle on shapes drawn at random — ragged sequence lengths and GEMM
 shapes, head groupings, head dims, position ranges, rotary sections, input
 scales, mask densities, with and without the split-K scratch.
@@ -265,3 +265,83 @@ def test_linear_fp8_random_shapes(m, n32, k128, residual, split, seed):
     r, mx = report("linear_fp8", f64(c), ref)
     assert r <= 4e-3
     assert mx <= 2.0 ** -7 * np.max(np.abs(ref))
+
+
+# ------------------------------------------------------------------ vision tower steps
+
+@CASES
+@given(rows=st.integers(1, 300), dim8=st.integers(1, 700), std=scales, shift=st.sampled_from([0.0, 0.5, 20.0]),
+       seed=st.integers(0, 2**20))
+def test_layer_norm_random_shapes(rows, dim8, std, shift, seed):
+    """LayerNorm (weight and bias) on random widths, scales and mean offsets."""
+    from oracle import vision as OV
+    dim = 8 * dim8
+    print(f"layer_norm rows={rows} dim={dim} std={std} shift={shift} seed={seed}", flush=True)
+    x = (_randn((rows, dim), seed, std).float() + shift).to(torch.bfloat16)
+    w = _gain(dim, seed + 1)
+    bb = _randn((dim,), seed + 2, 0.1)
+    y = torch.full_like(x, 7.0)
+    b.layer_norm(x, w, bb, y, rows, dim)
+    torch.cuda.synchronize()
+    ref = OV.layer_norm(f64(x), f64(w), f64(bb))
+    assert report("layer_norm", f64(y), ref)[0] <= 4e-3
+
+
+@CASES
+@given(shape=gemm_shapes(), act=st.sampled_from([0, 1, 2, "res"]), split=st.booleans(), seed=st.integers(0, 2**20))
+def test_linear_bias_random_shapes(shape, act, split, seed):
+    """Biased GEMM with GELU (tanh or erf form) or residual on ragged shapes."""
+    from oracle import vision as OV
+    m, n, k = shape
+    print(f"linear_bias m={m} n={n} k={k} act={act} split={split} seed={seed}", flush=True)
+    a = _randn((m, k), seed)
+    w = _randn((n, k), seed + 1, 0.03)
+    bias = _randn((n,), seed + 2, 0.5)
+    r = _randn((m, n), seed + 3)
+    c = r.clone() if act == "res" else torch.full((m, n), 7.0, device=DEV, dtype=torch.bfloat16)
+    ws = torch.empty(b.linear_workspace_bytes(), device=DEV, dtype=torch.uint8) if split else None
+    b.linear_bias(a, w, bias, c, m, n, k, act=0 if act == "res" else act,
+                  residual=c if act == "res" else None, workspace=ws)
+    torch.cuda.synchronize()
+    y = OV.linear(f64(a), f64(w), f64(bias))
+    ref = {0: y, 1: OV.gelu_tanh(y), 2: OV.gelu_erf(y), "res": y + f64(r)}[act]
+    assert report(f"linear_bias act={act}", f64(c), ref)[0] <= 4e-3
+
+
+@st.composite
+def vision_grids(draw):
+    """1-4 images / videos of (t, h, w) patches, h and w even (2x2 merge)."""
+    n_grids = draw(st.integers(1, 4))
+    grids = [(draw(st.integers(1, 3)), 2 * draw(st.integers(1, 10)), 2 * draw(st.integers(1, 10)))
+             for _ in range(n_grids)]
+    heads = draw(st.integers(1, 4))
+    hd = draw(st.sampled_from([64, 72, 80, 96, 128]))
+    return grids, heads, hd
+
+
+@CASES
+@given(case=vision_grids(), seed=st.integers(0, 2**20))
+def test_vision_attention_random_grids(case, seed):
+    """Non-causal attention inside each frame, on random image / video grids,
+    head counts and head dims (every (patch, head) row checked)."""
+    from oracle import vision as OV
+    grids, heads, hd = case
+    n = int(sum(t * h * w for t, h, w in grids))
+    print(f"vision attention n={n} heads={heads} head_dim={hd} grids={grids} seed={seed}", flush=True)
+    q, k, v = (_randn((n, heads, hd), seed + i) for i in range(3))
+    sp = b.seq_pad(n)
+    q_l = torch.zeros(n, heads, 128, dtype=torch.bfloat16, device=DEV)
+    q_l[:, :, :hd] = q
+    k_l = torch.zeros(heads, sp, 128, dtype=torch.bfloat16, device=DEV)
+    k_l[:, :n, :hd] = k.transpose(0, 1)
+    v_pad = torch.zeros(sp, heads, 128, dtype=torch.bfloat16, device=DEV)
+    v_pad[:n, :, :hd] = v
+    vt_l = v_pad[torch.from_numpy(perm16_tokens(sp)).to(DEV)].permute(1, 2, 0).contiguous()
+    o = torch.full((n, heads * hd), 7.0, dtype=torch.bfloat16, device=DEV)
+    nb = b.vision_attention_workspace_bytes(n)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    b.vision_attention(q_l, k_l, vt_l, o, n, heads, hd, grids, 2, ws, nb)
+    torch.cuda.synchronize()
+    ref = OV.segment_attention(f64(q), f64(k), f64(v), OV.segments(grids))
+    r, _, w = report_rows("vision attention", f64(o), ref, hd)
+    assert r <= 8e-3 and w <= ROW_BAR
