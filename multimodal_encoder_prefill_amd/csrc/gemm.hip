@@ -48,6 +48,7 @@
 // The bf16 forms of the 320-wide tile pass their outputs through LDS, which
 // is free once the pipeline ends, and store whole row segments in 16-byte
 // chunks instead of 8 bytes per row and lane.
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -840,13 +841,17 @@ template <int EPI, bool F8, int NB, bool SPLIT>
 hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
   // two stages of both operands, then the warm-up scratch (4 KB)
   constexpr size_t smem = static_cast<size_t>(2) * (BM + 64 * NB) * BK * sizeof(bf16_t) + 4096;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&gemm_kernel<EPI, F8, NB, SPLIT>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+  // the dynamic-LDS limit is raised once per device (bit d: done on device d)
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? (1ull << dev) : 0;
+  if (!bit || !(attr_set.load(std::memory_order_acquire) & bit)) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<EPI, F8, NB, SPLIT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set.fetch_or(bit, std::memory_order_release);
   }
   hipLaunchKernelGGL((gemm_kernel<EPI, F8, NB, SPLIT>), dim3(grid), dim3(kThreads), smem,
                      stream, args);
