@@ -15,13 +15,16 @@
 //             VisionPatchMerger; the MLP's GELU is the tanh form, the
 //             merger's the erf form)
 //
-// Tiling: a 256 (m) x 64 NB (n) output tile per workgroup of 4 wavefronts, each
-// wavefront owning 128 x 32 NB as NB x 4 blocks of v_mfma_f32_32x32x16_bf16
-// (NB = 4: 256 AGPR accumulators; NB = 5: 320, the rest in VGPRs). The weight
-// rows are the MFMA "A" operand and the activation rows the "B" operand, so
-// every lane ends up with 4 consecutive output columns (8-byte stores). The
-// 320-wide form reads 10% fewer LDS bytes per MFMA and makes 4096 x 5120,
+// Tiling: a 256 (m) x 64 NB (n) output tile per workgroup of 4 wavefronts.
+// NB = 4 (gemm_kernel: the general form, FP8, and the vision tower's biased
+// linears): each wavefront owns 128 x 128 as 4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16 in the 256 AGPRs. NB = 5 (gemm16_kernel: the bf16
+// decoder linears where whole waves of tiles fill the chip): 128 x 160 per
+// wavefront as 8 x 10 blocks of v_mfma_f32_16x16x32_bf16 (see there); the
+// 320-wide tile reads 10% fewer LDS bytes per MFMA and makes 4096 x 5120,
 // 4096 x 10240 and 4096 x 2 x 25600 outputs exact multiples of 256 tiles.
+// The weight rows are the MFMA "A" operand and the activation rows the "B"
+// operand, so every lane ends up with 4 consecutive output columns.
 //
 // K advances 64 at a time through two LDS stages of (256 + 64 NB) rows of
 // 128 bytes (64 or 72 KB each). Operand rows
@@ -50,6 +53,7 @@
 // chunks instead of 8 bytes per row and lane.
 #include <atomic>
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 #include "internal.h"
@@ -130,6 +134,34 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// f(std::integral_constant<int, i>()) for i = B .. E-1, in order: loop
+// indices that select registers (accumulator blocks, operand slots) are
+// constants from the start, not only after unrolling.
+template <int B, class F, int... I>
+__device__ __forceinline__ void static_for_seq(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, B + I>()), ...);
+}
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq<B>(f, std::make_integer_sequence<int, E - B>());
+}
+// c += W X^T on v_mfma_f32_16x16x32_bf16, the accumulator in AGPRs or VGPRs
+template <bool AGPR>
+__device__ __forceinline__ void mfma16(f32x4& c, const bf16x8& w, const bf16x8& x) {
+  if constexpr (AGPR)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(w), "v"(x));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(w), "v"(x));
+}
+// accumulator block (IB, JB) of the 320-wide tile: weight blocks 0-7 in a, 8-9 in v
+template <int IB, int JB>
+__device__ __forceinline__ f32x4& acc16(f32x4 (&a)[8][8], f32x4 (&v)[2][8]) {
+  if constexpr (IB < 8)
+    return a[IB][JB];
+  else
+    return v[IB - 8][JB];
 }
 
 // 32-bit LDS address of a pointer into the workgroup's LDS
@@ -225,14 +257,14 @@ __device__ __forceinline__ u32x2 finish4(float* o, const GemmArgs& args, int n, 
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales), and the sums are
 // multiplied by scale_a * scale_b before the epilogue.
 //
-// NB: 32-row weight blocks per wavefront (4 or 5; the tile is 64 NB wide).
+// NB: 32-row weight blocks per wavefront (4 here; the tile is 64 NB wide).
 // SPLIT: the units are k-ranges of split tiles whose raw fp32 sums go to
 // `partial` (a separate instantiation, so that each kernel has one epilogue:
 // with both in one kernel the compiler read every accumulator out ahead of
 // the branch and spilled them).
 template <int EPI, bool F8, int NB, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) {
-  static_assert(NB == 4 || (NB == 5 && !F8 && !SPLIT), "tile width");
+  static_assert(NB == 4, "the 320-wide tile is gemm16_kernel");
   constexpr int ES = F8 ? 1 : 2;                // bytes per element
   constexpr int KSTEP = 128 / ES;               // k elements per pipeline step
   constexpr int BNT = 64 * NB;                  // n extent of the tile (weight rows)
@@ -245,17 +277,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   constexpr int kBlksB = BNT / kRowsPerBlk;     // ... and for B
   constexpr int kLoads = kBlksA + kBlksB;
   constexpr int kMf = 4 * NB;                   // MFMAs per substep
-  // SwiGLU tiles of 320 virtual rows pair gate and up rows inside each 32-row
-  // block (8-row groups alternate gate, up), so a lane holds both factors of
-  // its outputs; the 256-row tiles pair block i with block i + 2.
-  constexpr bool kPairInBlock = EPI == static_cast<int>(Epilogue::kSwiGLU) && NB == 5;
   // The kLoads loads of k-step kt+1 are issued in up to three parts: loads
   // [0, kL0) during the last substep of k-step kt-1, the next kL1 and the rest
   // during substeps 0 and 1 of k-step kt, each part spread evenly over the
   // substep's MFMAs. (Issuing all of them in one substep is slower, and so is
-  // issuing the last ones late in substep 1; the 320-wide tile's 18 loads go
-  // out 10 + 8.)
-  constexpr int kL0 = NB == 5 ? 10 : 8, kL1 = 8;
+  // issuing the last ones late in substep 1.)
+  constexpr int kL0 = 8, kL1 = 8;
   constexpr int kWarm = 4;  // warm-up distance in k-steps
   static_assert(BK == 64 && kL0 + kL1 <= kLoads, "pipeline shape");
 
@@ -287,21 +314,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   //      m0 + kRowsPerBlk i ..; B block i: see b_block_base. Rows past M or N
   //      are never stored, so what is loaded for them does not matter. ----
   // B row block i of the tile: address of its first row and the rows of its
-  // segment from there on (<= 0: the block is past N). With kPairInBlock the
-  // address is that of this wavefront's 8-row piece of the block.
+  // segment from there on (<= 0: the block is past N).
   auto b_block_base = [&](int i, int& avail) -> const char* {
     const void* base;
     int v;
-    if constexpr (kPairInBlock) {
-      // block i: wave half i / NB, block i % NB of it; the 8-row group of
-      // wavefront w is gate rows for even w, up rows for odd w, output
-      // columns j .. j+7
-      const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-      const int j = tile_n * (BNT / 2) + (i / NB) * (16 * NB) + (i % NB) * 16 + (w >> 1) * 8;
-      base = (w & 1) ? args.bptr[1] : args.bptr[0];
-      v = min(j, N - 1);
-      avail = N - j;
-    } else if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+    if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
       // virtual B rows of the tile, in 32-row slots s: wave half s/4 covers
       // output columns j0 + 64 (s/4) .., slots s%4 = 0,1 gate rows, 2,3 up rows
       const int s = i * (kRowsPerBlk / 32);
@@ -328,37 +345,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     }
     return static_cast<const char*>(base) + static_cast<size_t>(v) * ldb * ES;
   };
-  // Accumulators: weight blocks 0-3 through the MFMA builtin (the compiler
-  // keeps them in the 256 AGPRs); block 4 of the 320-wide tile in VGPRs,
-  // through inline assembly (left to itself the compiler shuffles all 320
-  // between the two register files). The compiler does not know that those
-  // assembly statements are MFMAs, so the two VALU/MFMA hazards on their
-  // results are covered by hand: a wait after zeroing them and one before
-  // they are read (see mfma_one and the end of the pipeline).
+  // Accumulators: the 16 blocks through the MFMA builtin (the compiler keeps
+  // them in the 256 AGPRs).
   f32x16 acc[4][4];
-  f32x16 acc4[NB > 4 ? 4 : 1];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-#pragma unroll
-  for (int j = 0; j < (NB > 4 ? 4 : 1); ++j)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc4[j][e] = 0.f;
-  if constexpr (NB > 4)  // VALU writes, then MFMA reads of the same VGPRs
-    asm volatile("s_nop 4" : "+v"(acc4[0]), "+v"(acc4[1]), "+v"(acc4[2]), "+v"(acc4[3]));
-  // accumulator block (i, j)
-  auto A = [&](int i, int j) -> f32x16& { return i < 4 ? acc[i][j] : acc4[j]; };
 
   // ---- global -> LDS: lane L of wave w fills 16 bytes at block row
   //      w*(1024/kRowBytes) + L/kChunks, physical chunk L%kChunks, and so
   //      fetches the logical chunk the swizzle puts there. ----
   const int dma_row = wave * (1024 / kRowBytes) + lane / kChunks;
   const int dma_chunk = ((lane % kChunks) ^ swz(dma_row)) * 16;
-  // the lane's row relative to the address b_block_base returns
-  const int b_lane_row = kPairInBlock ? lane / kChunks : dma_row;
+  const int b_lane_row = dma_row;  // the lane's row relative to the address b_block_base returns
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // ---- L2 warm-up. The tiles running together on one XCD share operand
   //      blocks (tile_coords: 8 m-tiles x 4 n-tiles), so without help the
@@ -412,12 +414,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   bf16x8 wop[2][NB], xop[2][4];
   i32x8 wop8[2][4], xop8[2][4];
   // the r-th operand of substep s of LDS stage `stage`, into register slot
-  // `slot`: w0 x0 w1 x1 ... (w4); an FP8 operand is two 16-byte reads
-  constexpr int kReads = 8 + (NB - 4);
+  // `slot`: w0 x0 w1 x1 ...; an FP8 operand is two 16-byte reads
+  constexpr int kReads = 8;
   auto fetch_one = [&](int stage, int s, int slot, int r) {
     const bf16_t* as = As + stage * kATile;
     const bf16_t* bs = Bs + stage * kBTile;
-    const int i = r < 8 ? r >> 1 : 4;
+    const int i = r >> 1;
     if constexpr (F8) {
       const int c0 = ((4 * s + 2 * lhalf) ^ lswz) << 3;
       const int c1 = ((4 * s + 2 * lhalf + 1) ^ lswz) << 3;
@@ -431,28 +433,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
         wop8[slot][i] = v;
     } else {
       const int chunk = ((2 * s + lhalf) ^ lswz) << 3;
-      if (r < 8 && (r & 1))
+      if (r & 1)
         xop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + chunk));
       else
         wop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + chunk));
     }
   };
   // blocks in order of max(i, j), so the MFMAs that need the operands read
-  // last come last (weight block 4, read after the others, at the end)
+  // last come last
   auto mfma_one = [&](int slot, int q) {
-    // q-th block in that order: q = d*d + e for d = 0..3, e = 0..2d; then
-    // (4, q - 16)
+    // q-th block in that order: q = d*d + e for d = 0..3, e = 0..2d
     const int d = q < 1 ? 0 : q < 4 ? 1 : q < 9 ? 2 : 3;
     const int e = q - d * d;
-    const int i = q >= 16 ? 4 : e <= d ? e : d, j = q >= 16 ? q - 16 : e <= d ? d : 2 * d - e;
+    const int i = e <= d ? e : d, j = e <= d ? d : 2 * d - e;
     if constexpr (F8)
       // E4M3 operands (format 0), block scales 127 (= 2^0)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop8[slot][i], xop8[slot][j], acc[i][j], 0, 0,
                                                                   0, 127, 0, 127);
-    else if (i < 4)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[slot][i], xop[slot][j], acc[i][j], 0, 0, 0);
     else
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc4[j]) : "v"(wop[slot][4]), "v"(xop[slot][j]));
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[slot][i], xop[slot][j], acc[i][j], 0, 0, 0);
   };
   // Load number l of k-step kt (unit-relative), to LDS stage `stage`: below
   // 2 kBlksA, operand l % 2 (0: A, 1: B) of row block l / 2; from there on, B
@@ -576,12 +575,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     lds_barrier();
   }
 
-  // MFMA writes of the VGPR accumulators, then VALU reads: 32 wait states
-  // cover the longest (16-pass) MFMA
-  if constexpr (NB > 4)
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
-                 : "+v"(acc4[0]), "+v"(acc4[1]), "+v"(acc4[2]), "+v"(acc4[3]));
-
   // ---- split-K unit: raw accumulators to the unit's partial tile, laid out
   //      [m_local][virtual n] so 4 consecutive n are one 16-byte store ----
   if constexpr (SPLIT) {
@@ -595,7 +588,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
         for (int g = 0; g < 4; ++g) {
           f32x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = A(i, j)[4 * g + e];
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
           *reinterpret_cast<f32x4*>(dst + ml * BNT + wn * 32 * NB + i * 32 + 8 * g + 4 * lhalf) = v;
         }
     }
@@ -624,46 +617,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     sg = args.scale_a[0] * args.scale_b[0][0];
     su = args.scale_a[0] * args.scale_b[1][0];
   }
-  if constexpr (kPairInBlock) {
-    // Gate rows are groups g = 0, 2 of block i, their up rows g + 1. The
-    // wave's 128 x 80 outputs pass through its own LDS region in two halves
-    // of 64 rows (rows of 88 bf16 = 176 bytes: 16-byte aligned, and a write
-    // instruction's 32 rows spread over all 64 banks, two rows a bank) and
-    // leave as 16-byte chunks along the rows, 10 consecutive lanes per
-    // 160-byte row segment, instead of 16 bytes in each of 32 rows per store
-    // instruction. The first half's stores overlap the second half's SiLU.
-    constexpr int kStg = 88;
-    bf16_t* const stg = smem + wave_u * 64 * kStg;
-    const int col0 = tile_n * (BNT / 2) + wn * 16 * NB;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-          for (int gp = 0; gp < 2; ++gp) {
-            float o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              o[e] = silu_mul(A(i, 2 * h + jj)[8 * gp + e], A(i, 2 * h + jj)[8 * gp + 4 + e]);
-            u32x2 pk;
-            pk[0] = pack_bf16x2(o[0], o[1]);
-            pk[1] = pack_bf16x2(o[2], o[3]);
-            *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + i * 16 + gp * 8 + 4 * lhalf) = pk;
-          }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int it = 0; it < 64 * 10 / 64; ++it) {
-        const int c = it * 64 + lane, r = c / 10, q = c - r * 10;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + q * 8);
-        const int off = (wm * 128 + h * 64 + r) * args.ldc * static_cast<int>(sizeof(bf16_t)) + (col0 + q * 8) * 2;
-        __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
-  } else if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
-    // 256-wide SwiGLU (FP8, or bf16 where the 320-wide tile does not fit):
+  if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+    // SwiGLU (FP8, or bf16 where the 320-wide tile does not fit):
     // gate block i pairs with up block i + 2, 64 outputs per row and wave,
     // staged like the 320-wide form (rows of 72 bf16 = 144 bytes, 8 lanes
     // per row segment). Blocks past N (a partial n-tile; N is a multiple
@@ -697,15 +652,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       if (col0 + q * 8 < N) __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
     }
   } else {
-    // Store, residual and bias forms: the wave's 128 x 32 NB outputs in two
-    // halves of 64 rows through its LDS region (rows of 32 NB + 8 bf16: 272
-    // or 336 bytes, 16-byte aligned, each bank takes two rows of a write
-    // instruction), leaving as 16-byte chunks along the rows, 4 NB
+    // Store, residual and bias forms: the wave's 128 x 128 outputs in two
+    // halves of 64 rows through its LDS region (rows of 136 bf16 = 272
+    // bytes, 16-byte aligned, each bank takes two rows of a write
+    // instruction), leaving as 16-byte chunks along the rows, 16
     // consecutive lanes per row segment. A half's residual values are
     // loaded in the accumulator layout, all before its first add (bringing
     // them in through LDS as well measured no faster); a residual load past
     // N reads other columns of the buffer, or zeros past its end, for an
-    // output that is not stored. Blocks past N (256-wide tiles only) are
+    // output that is not stored. Blocks past N (a partial n-tile) are
     // skipped, and so are their chunks in the stores.
     constexpr int kStg = 32 * NB + 8, kRowChunks = 4 * NB;
     bf16_t* const stg = smem + wave_u * 64 * kStg;
@@ -731,13 +686,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
           const int nb = col0 + i * 32;
-          if (NB == 4 && nb >= N) continue;  // the 320-wide form never has a partial n-tile
+          if (nb >= N) continue;
           const float sc = F8 ? f8_scale(args, nb) : 1.f;
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             float o[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = A(i, 2 * h + jj)[4 * g + e] * sc;
+            for (int e = 0; e < 4; ++e) o[e] = acc[i][2 * h + jj][4 * g + e] * sc;
             *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + i * 32 + 8 * g + 4 * lhalf) =
                 finish4<EPI>(o, args, nb + 8 * g + 4 * lhalf, rv[jj][i][g]);
           }
@@ -748,7 +703,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
         const int c = it * 64 + lane, r = c / kRowChunks, q = c - r * kRowChunks;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + q * 8);
         const int off = (wm * 128 + h * 64 + r) * args.ldc * static_cast<int>(sizeof(bf16_t)) + (col0 + q * 8) * 2;
-        if (NB == 5 || col0 + q * 8 < N) __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
+        if (col0 + q * 8 < N) __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
       }
       // the reads above have returned before the next half overwrites the region
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -759,6 +714,354 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       const float v = workgroup_max(amx, reinterpret_cast<float*>(smem + 4 * 128 * 72));
       if (tid == 0) args.amax[unit] = v;
     }
+  }
+}
+
+// The 320-wide bf16 tile (256 tokens x 320 weight rows) on
+// v_mfma_f32_16x16x32_bf16. Same LDS ring, LDS-DMA loads, swizzle, warm-up
+// and tile order as gemm_kernel; each wavefront owns 128 tokens x 160 weight
+// rows as 8 x 10 blocks of 16 x 16. Per MFMA the 16x16x32 form reads and
+// writes a quarter of the accumulator registers of the 32x32x16 form for half
+// the products, so the register file moves 20% fewer bytes per flop; under
+// the chip's power limit a register-only loop of it runs ~10% faster.
+//
+// A k-step (64 k) is two substeps of 32 k, 80 MFMAs each: block (ib, jb)
+// multiplies weight rows 16 ib.. by tokens 16 jb.. . A lane holds the weight
+// operand of row 16 ib + (lane & 15), k = 8 (lane >> 4).. and the activation
+// operand of token 16 jb + (lane & 15) at the same k, and ends with outputs
+// (weight row 16 ib + 4 (lane >> 4) + e, token 16 jb + (lane & 15)), e < 4:
+// four consecutive output columns of one token. The eight activation
+// operands of a substep stay in registers through it; the weight operands
+// stream through a ring of four registers, each read two blocks (16 MFMAs)
+// before its first use. The one barrier per k-step sits 16 MFMAs before its
+// end, after the last read of the stage: those MFMAs (weight blocks 8 and 9)
+// cover the barrier and the reads of the next k-step's first operands.
+//
+// All MFMAs are inline assembly: blocks 0-7 accumulate in the 256 AGPRs,
+// blocks 8-9 in VGPRs. (Through the builtin the compiler permuted the 64
+// AGPR accumulators between loop iterations with register moves.) The
+// compiler does not see these statements as MFMAs, so the VALU/MFMA hazards
+// on the accumulators are covered by explicit waits after zeroing them and
+// before the epilogue reads them.
+//
+// SwiGLU: each 32-row weight block holds 16 gate rows and then the 16 up
+// rows of the same output columns, so weight blocks 2p and 2p + 1 of a lane
+// are the two factors of the same outputs.
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args) {
+  constexpr bool kSwi = EPI == static_cast<int>(Epilogue::kSwiGLU);
+  static_assert(kSwi || EPI == static_cast<int>(Epilogue::kStore) || EPI == static_cast<int>(Epilogue::kResidual),
+                "epilogues of the 320-wide tile");
+  constexpr int BNT = 320;                       // weight rows of the tile
+  constexpr int kATile = BM * BK, kBTile = BNT * BK;
+  constexpr int kRowBytes = BK * 2, kChunks = BK / 8;
+  constexpr int kRowsPerBlk = 4096 / kRowBytes;  // rows one load instruction of the 4 waves covers
+  constexpr int kBlksA = BM / kRowsPerBlk, kBlksB = BNT / kRowsPerBlk;
+  constexpr int kLoads = kBlksA + kBlksB;        // 18 loads per k-step
+  // loads [0, kLC) of k-step kt + 2 go out after the barrier of kt, the rest
+  // over the first 40 MFMAs of kt + 1
+  constexpr int kLC = 8;
+  constexpr int kWarm = 4;  // warm-up distance in k-steps
+  static_assert(BK == 64 && kLoads == 18, "pipeline shape");
+
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+  bf16_t* As = smem;              // [2][BM][BK]
+  bf16_t* Bs = smem + 2 * kATile; // [2][BNT][BK], then 4 KB of warm-up scratch
+
+  const int M = args.m, N = args.n, K = args.k;
+  const int lda = args.lda, ldb = args.ldb;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+
+  // ---- work unit (whole tiles): contiguous per XCD ----
+  const int total = args.units;
+  const int bid = blockIdx.x;
+  const int xcd = bid % kXcds;
+  const int q = total / kXcds, rmd = total % kXcds;
+  const int unit = xcd * q + min(xcd, rmd) + bid / kXcds;
+  int tile_m, tile_n;
+  tile_coords(args.tile_begin + unit, args.tiles_m, args.tiles_n, tile_m, tile_n);
+  const int m0 = tile_m * BM;
+  const int nk = K / BK;
+
+  // B row block i (32 rows) of the tile: address of its first row, or for
+  // SwiGLU of this wavefront's 8 rows, and the rows of its segment from there
+  // on (<= 0: past N).
+  auto b_block_base = [&](int i, int& avail) -> const char* {
+    const void* base;
+    int v;
+    if constexpr (kSwi) {
+      // block i: wave half i / 5, column group p = i % 5 of it (16 output
+      // columns); wavefronts 0, 1 load its gate rows, 2, 3 its up rows, 8
+      // columns each
+      const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      const int j = tile_n * (BNT / 2) + (i / 5) * 80 + (i % 5) * 16 + (w & 1) * 8;
+      base = (w >> 1) ? args.bptr[1] : args.bptr[0];
+      v = min(j, N - 1);
+      avail = N - j;
+    } else {
+      const int row = tile_n * BNT + kRowsPerBlk * i;
+      const int rr = min(row, N - 1);
+      if (rr < args.brows[0]) {
+        base = args.bptr[0];
+        v = rr;
+        avail = args.brows[0] - row;
+      } else if (rr < args.brows[0] + args.brows[1]) {
+        base = args.bptr[1];
+        v = rr - args.brows[0];
+        avail = args.brows[0] + args.brows[1] - row;
+      } else {
+        base = args.bptr[2];
+        v = rr - args.brows[0] - args.brows[1];
+        avail = N - row;
+      }
+    }
+    return static_cast<const char*>(base) + static_cast<size_t>(v) * ldb * 2;
+  };
+
+  // ---- global -> LDS, as in gemm_kernel ----
+  const int dma_row = wave * (1024 / kRowBytes) + lane / kChunks;
+  const int dma_chunk = ((lane % kChunks) ^ swz(dma_row)) * 16;
+  const int b_lane_row = kSwi ? lane / kChunks : dma_row;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  bf16_t* const warm_dst = smem + 2 * kATile + 2 * kBTile + wave_u * 512;
+  const char* a_ptr[kBlksA];
+  const char* b_ptr[kBlksB];
+  unsigned a_off[kBlksA], b_off[kBlksB];
+#pragma unroll
+  for (int i = 0; i < kBlksA; ++i) {
+    const int r = m0 + kRowsPerBlk * i;
+    a_ptr[i] = static_cast<const char*>(args.a) + static_cast<size_t>(min(r, M - 1)) * lda * 2;
+    a_off[i] = min(dma_row, max(M - r, 1) - 1) * lda * 2 + dma_chunk;
+  }
+#pragma unroll
+  for (int i = 0; i < kBlksB; ++i) {
+    int avail;
+    b_ptr[i] = b_block_base(i, avail);
+    b_off[i] = min(b_lane_row, max(avail, 1) - 1) * ldb * 2 + dma_chunk;
+  }
+  int warm_avail;
+  const char* const warm_ptr = b_block_base((tile_m & 7) * (32 / kRowsPerBlk), warm_avail);
+  const unsigned warm_off = min(b_lane_row, max(warm_avail, 1) - 1) * ldb * 2 + (lane % kChunks) * 16;
+
+  auto koff = [&](int kt) { return static_cast<size_t>(min(kt, nk - 1)) * kRowBytes; };
+  auto issue_load = [&](int kt, int stage, int l) {
+    const bool isb = l >= 2 * kBlksA || (l & 1);
+    const int i = l >= 2 * kBlksA ? l - kBlksA : l >> 1;
+    bf16_t* dst = (isb ? Bs + stage * kBTile : As + stage * kATile) + wave_u * 512 + i * kRowsPerBlk * BK;
+    global_load_lds16((isb ? b_ptr[i] : a_ptr[i]) + koff(kt), isb ? b_off[i] : a_off[i], lds_addr(dst));
+  };
+  auto issue_warm = [&](int kt) { global_load_lds16(warm_ptr + koff(kt), warm_off, lds_addr(warm_dst)); };
+
+  // ---- LDS -> registers: 16 rows of a block, chunk 4 s + (lane >> 4) of
+  //      substep s through the swizzle (blocks start at multiples of 16 rows,
+  //      so the swizzle depends on lane & 15 only) ----
+  const int r16 = lane & 15, g16 = lane >> 4;
+  const int x_base = (wm * 128 + r16) * BK;
+  const int w_base = (wn * (BNT / 2) + r16) * BK;
+  const int c16[2] = {(g16 ^ swz(r16)) * 8, ((4 + g16) ^ swz(r16)) * 8};
+  auto rd_x = [&](int stage, int s, int jb) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(As + stage * kATile + x_base + jb * 16 * BK +
+                                                                        c16[s]));
+  };
+  auto rd_w = [&](int stage, int s, int ib) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Bs + stage * kBTile + w_base + ib * 16 * BK +
+                                                                        c16[s]));
+  };
+
+  f32x4 acc[8][8];   // weight blocks 0-7 (AGPRs)
+  f32x4 accv[2][8];  // weight blocks 8-9 (VGPRs)
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) accv[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the zeroing writes, then the first MFMA reads of the same registers
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    asm volatile("s_nop 4" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                 "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    asm volatile("s_nop 4" : "+v"(accv[i][0]), "+v"(accv[i][1]), "+v"(accv[i][2]), "+v"(accv[i][3]),
+                 "+v"(accv[i][4]), "+v"(accv[i][5]), "+v"(accv[i][6]), "+v"(accv[i][7]));
+
+  bf16x8 xo[2][8];  // activation operands of substeps 0 and 1
+  bf16x8 wo[4];     // weight operands: the 20 of a k-step (10 s + ib) in a ring of four
+  using Live = std::true_type;
+  using Dead = std::false_type;
+
+  // ---- one k-step: MFMA slot g = 80 s + 8 ib + jb, and after it the reads
+  //      and loads placed there. LIVE1 / LIVE2: k-step kt+1 / kt+2 exists
+  //      and is loaded. ----
+  auto step = [&](int kt, auto LIVE1, auto LIVE2) {
+    const int st = kt & 1;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, 144>([&](auto G) {
+      constexpr int g = decltype(G)::value;
+      constexpr int s = g / 80, ib = (g % 80) / 8, jb = g % 8;
+      mfma16<(ib < 8)>(acc16<ib, jb>(acc, accv), wo[(10 * s + ib) & 3], xo[s][jb]);
+      // weight operand 10 s' + i (i >= 2 of substep 0, all of substep 1)
+      // after slot 8 (10 s' + i) - 12, two blocks before its first use
+      if constexpr (g % 8 == 4) {
+        constexpr int idx = (g + 12) / 8;
+        wo[idx & 3] = rd_w(st, idx / 10, idx % 10);
+      }
+      // substep 1's activation operands after slots 40, 44, .., 68
+      if constexpr (g >= 40 && g < 72 && g % 4 == 0) xo[1][(g - 40) / 4] = rd_x(st, 1, (g - 40) / 4);
+      // loads [kLC, 18) of k-step kt+1 after slots 0, 4, .., 36
+      if constexpr (decltype(LIVE1)::value && g % 4 == 0 && g / 4 < kLoads - kLC)
+        issue_load(kt + 1, st ^ 1, kLC + g / 4);
+      if constexpr (g == 80) issue_warm(kt + kWarm);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // k-step kt+1 is complete in LDS (only the warm-up load may still be in
+    // flight) and no wavefront reads stage st any more
+    wait_vmcnt<1>();
+    lds_barrier();
+    static_for<144, 160>([&](auto G) {
+      constexpr int g = decltype(G)::value;
+      constexpr int ib = (g - 80) / 8, jb = g % 8;
+      mfma16<(ib < 8)>(acc16<ib, jb>(acc, accv), wo[(10 + ib) & 3], xo[1][jb]);
+      // the first operands of k-step kt+1: activations 0-7 and weights 0, 1
+      // of its substep 0, in the order they are used
+      constexpr int r = g - 144;
+      if constexpr (r == 1)
+        wo[0] = rd_w(st ^ 1, 0, 0);
+      else if constexpr (r == 9)
+        wo[1] = rd_w(st ^ 1, 0, 1);
+      else if constexpr (r < 9)
+        xo[0][r == 0 ? 0 : r - 1] = rd_x(st ^ 1, 0, r == 0 ? 0 : r - 1);
+      // loads [0, kLC) of k-step kt+2 into the stage just read
+      if constexpr (decltype(LIVE2)::value && r % 2 == 0) issue_load(kt + 2, st, r / 2);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  if (nk > 0) {
+    // k-step 0, the first loads of k-step 1 (k-step 0 again if there is no
+    // k-step 1: into a stage that is not read) and the warm-up of k-steps
+    // 1 .. kWarm-1 before the wait
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) issue_load(0, 0, l);
+#pragma unroll
+    for (int l = 0; l < kLC; ++l) issue_load(1, 1, l);
+#pragma unroll
+    for (int kt = 1; kt < kWarm; ++kt) issue_warm(kt);
+    wait_vmcnt<kLC + kWarm - 1>();
+    lds_barrier();
+    xo[0][0] = rd_x(0, 0, 0);
+    wo[0] = rd_w(0, 0, 0);
+#pragma unroll
+    for (int j = 1; j < 8; ++j) xo[0][j] = rd_x(0, 0, j);
+    wo[1] = rd_w(0, 0, 1);
+    // the last two k-steps are peeled off so that no load runs past the k-range
+    int kt = 0;
+    for (; kt < nk - 2; ++kt) step(kt, Live(), Live());
+    if (kt < nk - 1) step(kt++, Live(), Dead());
+    step(kt, Dead(), Dead());
+    // the trailing loads and reads have completed
+    wait_vmcnt<0>();
+    lds_barrier();
+  }
+
+  // MFMA writes of the accumulators, then VALU reads: 16 wait states (more
+  // than the 4-pass MFMA needs) before the first group, more before the rest
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(accv[1 - i][0]), "+v"(accv[1 - i][1]), "+v"(accv[1 - i][2]),
+                 "+v"(accv[1 - i][3]), "+v"(accv[1 - i][4]), "+v"(accv[1 - i][5]), "+v"(accv[1 - i][6]),
+                 "+v"(accv[1 - i][7]));
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    asm volatile("s_nop 1" : "+a"(acc[7 - i][0]), "+a"(acc[7 - i][1]), "+a"(acc[7 - i][2]), "+a"(acc[7 - i][3]),
+                 "+a"(acc[7 - i][4]), "+a"(acc[7 - i][5]), "+a"(acc[7 - i][6]), "+a"(acc[7 - i][7]));
+
+
+  // ---- epilogue: outputs leave through a per-wavefront LDS region in two
+  //      halves of 64 tokens, as 16-byte chunks along the rows. Rows past M:
+  //      buffer resources that end at row M drop the stores and read zeros
+  //      (see gemm_kernel). The 320-wide tile never has a partial n-tile. ----
+  const size_t rbytes = static_cast<size_t>(M - m0) * args.ldc * sizeof(bf16_t);
+  const int nbytes = static_cast<int>(rbytes < 0x7fffffffu ? rbytes : 0x7fffffffu);
+  const size_t first = static_cast<size_t>(m0) * args.ldc;
+  const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(args.c + first, (short)0, nbytes, 0x00020000);
+  const int ldc_b = args.ldc * static_cast<int>(sizeof(bf16_t));
+  if constexpr (kSwi) {
+    // 128 x 80 outputs per wavefront; staging rows of 88 bf16 (176 bytes:
+    // a write instruction's 16 rows x 4 column groups hit every bank twice)
+    constexpr int kStg = 88;
+    bf16_t* const stg = smem + wave_u * 64 * kStg;
+    const int col0 = tile_n * (BNT / 2) + wn * 80;
+    static_for<0, 2>([&](auto H) {
+      constexpr int h = decltype(H)::value;
+      static_for<0, 20>([&](auto Q) {
+        constexpr int jj = decltype(Q)::value / 5, p = decltype(Q)::value % 5;
+        const f32x4& gt = acc16<2 * p, 4 * h + jj>(acc, accv);
+        const f32x4& up = acc16<2 * p + 1, 4 * h + jj>(acc, accv);
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = silu_mul(gt[e], up[e]);
+        u32x2 pk;
+        pk[0] = pack_bf16x2(o[0], o[1]);
+        pk[1] = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<u32x2*>(stg + (jj * 16 + r16) * kStg + p * 16 + 4 * g16) = pk;
+      });
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < 10; ++it) {
+        const int c = it * 64 + lane, r = c / 10, qq = c - r * 10;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + qq * 8);
+        __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, (wm * 128 + h * 64 + r) * ldc_b + (col0 + qq * 8) * 2, 0, 0);
+      }
+      // the reads above have returned before the next half overwrites the region
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    });
+  } else {
+    // 128 x 160 outputs per wavefront; staging rows of 168 bf16 (336 bytes,
+    // each bank takes two rows of a write instruction). A half's residual
+    // values are loaded in the accumulator layout, all before its first add.
+    constexpr int kStg = 168, kRowChunks = 20;
+    bf16_t* const stg = smem + wave_u * 64 * kStg;
+    const int col0 = tile_n * BNT + wn * (BNT / 2);
+    const __amdgpu_buffer_rsrc_t r_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        epi_residual(EPI) ? const_cast<bf16_t*>(args.r) + first : args.c + first, (short)0, nbytes, 0x00020000);
+    static_for<0, 2>([&](auto H) {
+      constexpr int h = decltype(H)::value;
+      u32x2 rv[4][10];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int ib = 0; ib < 10; ++ib)
+          rv[jj][ib] = epi_residual(EPI)
+                           ? __builtin_amdgcn_raw_buffer_load_b64(
+                                 r_rsrc, (wm * 128 + (4 * h + jj) * 16 + r16) * ldc_b + (col0 + ib * 16 + 4 * g16) * 2,
+                                 0, 0)
+                           : u32x2{0, 0};
+      static_for<0, 40>([&](auto Q) {
+        constexpr int jj = decltype(Q)::value / 10, ib = decltype(Q)::value % 10;
+        const f32x4& a = acc16<ib, 4 * h + jj>(acc, accv);
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = a[e];
+        *reinterpret_cast<u32x2*>(stg + (jj * 16 + r16) * kStg + ib * 16 + 4 * g16) =
+            finish4<EPI>(o, args, col0 + ib * 16 + 4 * g16, rv[jj][ib]);
+      });
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < kRowChunks; ++it) {
+        const int c = it * 64 + lane, r = c / kRowChunks, qq = c - r * kRowChunks;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + qq * 8);
+        __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, (wm * 128 + h * 64 + r) * ldc_b + (col0 + qq * 8) * 2, 0, 0);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    });
   }
 }
 
@@ -783,19 +1086,7 @@ __global__ __launch_bounds__(64 * NB) void splitk_reduce_kernel(const GemmArgs a
   const int N = args.n;
   float o[4];
   int n;
-  if (EPI == static_cast<int>(Epilogue::kSwiGLU) && NB == 5) {
-    // virtual column vn: wave half vn/160, block (vn%160)/32, 8-row group
-    // (vn%32)/8; even groups are gate columns whose up partner sits 8 later
-    const int r = vn % 160, grp = (r & 31) >> 3;
-    live = live && (grp & 1) == 0;
-    const int uo = (grp & 1) == 0 ? 8 : 0;
-    f32x4 upsum = *reinterpret_cast<const f32x4*>(src + uo);
-    for (int sidx = 1; sidx < args.ksplit; ++sidx)
-      upsum += *reinterpret_cast<const f32x4*>(src + uo + static_cast<size_t>(sidx) * BM * BNT);
-    n = tile_n * (BNT / 2) + (vn / 160) * 80 + (r >> 5) * 16 + (grp >> 1) * 8 + (r & 7);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = silu_mul(sum[e], upsum[e]);
-  } else if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+  if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
     // virtual column vn: wave half vn/128, 32-wide slot (vn%128)/32; slots 0,1
     // are gate columns whose up partner sits 64 virtual columns later
     const int slot = (vn & 127) >> 5;
@@ -841,6 +1132,12 @@ template <int EPI, bool F8, int NB, bool SPLIT>
 hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
   // two stages of both operands, then the warm-up scratch (4 KB)
   constexpr size_t smem = static_cast<size_t>(2) * (BM + 64 * NB) * BK * sizeof(bf16_t) + 4096;
+  // NB = 5: the 320-wide bf16 tile (whole tiles only)
+  const void* kernel;
+  if constexpr (NB == 5)
+    kernel = reinterpret_cast<const void*>(&gemm16_kernel<EPI>);
+  else
+    kernel = reinterpret_cast<const void*>(&gemm_kernel<EPI, F8, NB, SPLIT>);
   // the dynamic-LDS limit is raised once per device (bit d: done on device d)
   static std::atomic<uint64_t> attr_set{0};
   int dev = 0;
@@ -848,13 +1145,16 @@ hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const uint64_t bit = dev < 64 ? (1ull << dev) : 0;
   if (!bit || !(attr_set.load(std::memory_order_acquire) & bit)) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_kernel<EPI, F8, NB, SPLIT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit, std::memory_order_release);
   }
-  hipLaunchKernelGGL((gemm_kernel<EPI, F8, NB, SPLIT>), dim3(grid), dim3(kThreads), smem,
-                     stream, args);
+  if constexpr (NB == 5) {
+    static_assert(!F8 && !SPLIT, "the 320-wide tile is bf16, whole tiles");
+    hipLaunchKernelGGL((gemm16_kernel<EPI>), dim3(grid), dim3(kThreads), smem, stream, args);
+  } else {
+    hipLaunchKernelGGL((gemm_kernel<EPI, F8, NB, SPLIT>), dim3(grid), dim3(kThreads), smem, stream, args);
+  }
   return hipGetLastError();
 }
 
@@ -918,19 +1218,19 @@ hipError_t run(GemmArgs args, float* partial, size_t partial_bytes, hipStream_t 
     if ((e = launch_epi<EPI, F8, NB, false>(a, full, stream)) != hipSuccess) return e;
   }
   if (amax_count) *amax_count = full + (ksplit > 1 ? rem * (BM / 4) : 0);
-  if (ksplit > 1) {
-    GemmArgs a = args;
-    a.tile_begin = full;
-    a.units = rem * ksplit;
-    a.ksplit = ksplit;
-    a.kt_per_split = (nk + ksplit - 1) / ksplit;
-    a.partial = partial;
-    a.amax = args.amax ? args.amax + full : nullptr;
-    if constexpr (NB == 4) {
+  if constexpr (NB == 4) {  // (the 320-wide tile is only taken for whole waves)
+    if (ksplit > 1) {
+      GemmArgs a = args;
+      a.tile_begin = full;
+      a.units = rem * ksplit;
+      a.ksplit = ksplit;
+      a.kt_per_split = (nk + ksplit - 1) / ksplit;
+      a.partial = partial;
+      a.amax = args.amax ? args.amax + full : nullptr;
       if ((e = launch_epi<EPI, F8, NB, true>(a, a.units, stream)) != hipSuccess) return e;
+      hipLaunchKernelGGL((splitk_reduce_kernel<EPI, F8, NB>), dim3(rem, BM / 4), dim3(BNT), 0, stream, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((splitk_reduce_kernel<EPI, F8, NB>), dim3(rem, BM / 4), dim3(BNT), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }
