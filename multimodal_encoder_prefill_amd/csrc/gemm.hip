@@ -727,8 +727,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 //
 // A k-step (64 k) is two substeps of 32 k, 80 MFMAs each: block (ib, jb)
 // multiplies weight rows 16 ib.. by tokens 16 jb.. . A lane holds the weight
-// operand of row 16 ib + (lane & 15), k = 8 (lane >> 4).. and the activation
-// operand of token 16 jb + (lane & 15) at the same k, and ends with outputs
+// operand of row 16 ib + (lane & 15), 8 k of the substep's 32, and the
+// activation operand of token 16 jb + (lane & 15) at the same k, and ends
+// with outputs
 // (weight row 16 ib + 4 (lane >> 4) + e, token 16 jb + (lane & 15)), e < 4:
 // four consecutive output columns of one token. The eight activation
 // operands of a substep stay in registers through it; the weight operands
@@ -856,13 +857,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
   };
   auto issue_warm = [&](int kt) { global_load_lds16(warm_ptr + koff(kt), warm_off, lds_addr(warm_dst)); };
 
-  // ---- LDS -> registers: 16 rows of a block, chunk 4 s + (lane >> 4) of
+  // ---- LDS -> registers: row 16 blk + (lane & 15), chunk 4 s + kc of
   //      substep s through the swizzle (blocks start at multiples of 16 rows,
-  //      so the swizzle depends on lane & 15 only) ----
+  //      so the swizzle depends on lane & 15 only). The MFMA takes k group
+  //      lane >> 4 from each lane; which 8-k chunk feeds which k group does
+  //      not change the sum as long as both operands agree, and kc = 0, 2,
+  //      1, 3 for lane >> 4 = 0, 1, 2, 3 has lanes L and L + 32, which the
+  //      LDS serves together, read chunks of opposite parity: with the
+  //      swizzle that puts their 16-byte reads in distinct banks (chunks kc
+  //      and kc + 2 of the same rows collide). ----
   const int r16 = lane & 15, g16 = lane >> 4;
+  const int kc = ((g16 & 1) << 1) | (g16 >> 1);
   const int x_base = (wm * 128 + r16) * BK;
   const int w_base = (wn * (BNT / 2) + r16) * BK;
-  const int c16[2] = {(g16 ^ swz(r16)) * 8, ((4 + g16) ^ swz(r16)) * 8};
+  const int c16[2] = {(kc ^ swz(r16)) * 8, ((4 + kc) ^ swz(r16)) * 8};
   auto rd_x = [&](int stage, int s, int jb) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(As + stage * kATile + x_base + jb * 16 * BK +
                                                                         c16[s]));
