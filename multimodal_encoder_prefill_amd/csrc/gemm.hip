@@ -760,7 +760,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
   constexpr int kBlksA = BM / kRowsPerBlk, kBlksB = BNT / kRowsPerBlk;
   constexpr int kLoads = kBlksA + kBlksB;        // 18 loads per k-step
   // loads [0, kLC) of k-step kt + 2 go out after the barrier of kt, the rest
-  // over the first 40 MFMAs of kt + 1
+  // over the first 80 MFMAs of kt + 1, one per 8 MFMAs (one per 4, or more
+  // of them after the barrier, measured slower: down +5%)
   constexpr int kLC = 8;
   constexpr int kWarm = 4;  // warm-up distance in k-steps
   static_assert(BK == 64 && kLoads == 18, "pipeline shape");
@@ -923,9 +924,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
       }
       // substep 1's activation operands after slots 40, 44, .., 68
       if constexpr (g >= 40 && g < 72 && g % 4 == 0) xo[1][(g - 40) / 4] = rd_x(st, 1, (g - 40) / 4);
-      // loads [kLC, 18) of k-step kt+1 after slots 0, 4, .., 36
-      if constexpr (decltype(LIVE1)::value && g % 4 == 0 && g / 4 < kLoads - kLC)
-        issue_load(kt + 1, st ^ 1, kLC + g / 4);
+      // loads [kLC, 18) of k-step kt+1 after slots 0, 8, .., 72
+      if constexpr (decltype(LIVE1)::value && g % 8 == 0 && g / 8 < kLoads - kLC)
+        issue_load(kt + 1, st ^ 1, kLC + g / 8);
       if constexpr (g == 80) issue_warm(kt + kWarm);
       __builtin_amdgcn_sched_barrier(0);
     });
