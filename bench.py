@@ -407,7 +407,7 @@ def main():
     gu_avg_ms = gu_ms / max(gu_n, 1)
     gu_tflops = fl["gate_up"] / (gu_avg_ms / 1000.0) / 1e12
     traffic = stored_traffic(wl.seq)
-    roofline = {"bound": "mfma", "kernel": "gemm_kernel<kSwiGLU> (gate/up projections + SiLU*mul)",
+    roofline = {"bound": "mfma", "kernel": "gemm16_kernel<kSwiGLU> (gate/up projections + SiLU*mul, 256 x 320 tiles)",
                 "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "launch_ms": round(gu_avg_ms, 4), "launches": gu_n,
