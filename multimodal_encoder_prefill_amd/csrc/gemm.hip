@@ -16,28 +16,26 @@
 //             merger's the erf form)
 //
 // Tiling: a 256 (m) x 64 NB (n) output tile per workgroup of 4 wavefronts.
-// NB = 4 (gemm_kernel: the general form, FP8, and the vision tower's biased
-// linears): each wavefront owns 128 x 128 as 4 x 4 blocks of
-// v_mfma_f32_32x32x16_bf16 in the 256 AGPRs. NB = 5 (gemm16_kernel: the bf16
-// decoder linears where whole waves of tiles fill the chip): 128 x 160 per
-// wavefront as 8 x 10 blocks of v_mfma_f32_16x16x32_bf16 (see there); the
-// 320-wide tile reads 10% fewer LDS bytes per MFMA and makes 4096 x 5120,
-// 4096 x 10240 and 4096 x 2 x 25600 outputs exact multiples of 256 tiles.
-// The weight rows are the MFMA "A" operand and the activation rows the "B"
-// operand, so every lane ends up with 4 consecutive output columns.
+// bf16 (gemm16_kernel): 16x16x32 MFMAs; NB = 5 (256 x 320) for the decoder
+// linears where whole waves of tiles fill the chip, NB = 4 (256 x 256, with
+// partial n-tiles and k-splits) otherwise. The 320-wide tile reads 10% fewer
+// LDS bytes per MFMA and makes 4096 x 5120, 4096 x 10240 and 4096 x 2 x 25600
+// outputs exact multiples of 256 tiles. FP8 (gemm_f8_kernel): NB = 4 on
+// 32x32x64 MFMAs. The weight rows are the MFMA "A" operand and the
+// activation rows the "B" operand, so every lane ends up with 4 consecutive
+// output columns.
 //
-// K advances 64 at a time through two LDS stages of (256 + 64 NB) rows of
-// 128 bytes (64 or 72 KB each). Operand rows
-// are 128 bytes and their 16-byte chunks are XOR-swizzled so the ds_read_b128
-// operand fetches of 8 (or 16) consecutive lanes hit distinct banks. Tiles go
-// straight from global memory into LDS (global_load_lds_dwordx4, a wave-uniform
-// base per 32-row block and one 32-bit offset per lane); lanes past the last
-// row of M or N load that row again. One workgroup barrier per k-step, placed before its
-// last k-substep: that substep's operands are already in registers, so its
-// MFMAs hide the barrier and the first operand reads of the next k-step. The
-// LDS reads of a substep's operands go out one at a time between the MFMAs
-// of the substep before (a burst of all of them, from all four wavefronts at
-// once, left the MFMAs waiting on the LDS).
+// K advances 128 row bytes at a time (64 bf16 or 128 FP8 elements) through
+// two LDS stages of (256 + 64 NB) rows of 128 bytes (64 or 72 KB each), the
+// 16-byte chunks of each row XOR-swizzled so that the ds_read_b128 operand
+// fetches hit distinct banks. Tiles go straight from global memory into LDS
+// (global_load_lds_dwordx4, a wave-uniform base per 32-row block and one
+// 32-bit offset per lane); lanes past the last row of M or N load that row
+// again. One workgroup barrier per k-step, placed where the MFMAs still to
+// come have their operands in registers, so that they hide the barrier and
+// the first operand reads of the next k-step. The LDS reads of operands go
+// out one at a time between the MFMAs (a burst of all of them, from all
+// four wavefronts at once, left the MFMAs waiting on the LDS).
 //
 // Workgroups are remapped so that each XCD (workgroups are dealt round-robin
 // over the 8 XCDs) receives a contiguous run of tiles, ordered in groups of m
@@ -48,9 +46,9 @@
 // to (and reads zeros from) rows past it; k-split units are a separate
 // instantiation that only writes fp32 partials. (Branches there made the
 // compiler copy every accumulator out of the AGPRs up front and spill them.)
-// The bf16 forms of the 320-wide tile pass their outputs through LDS, which
-// is free once the pipeline ends, and store whole row segments in 16-byte
-// chunks instead of 8 bytes per row and lane.
+// Outputs pass through LDS, which is free once the pipeline ends, and leave
+// as whole row segments in 16-byte chunks instead of 8 bytes per row and
+// lane.
 #include <atomic>
 #include <type_traits>
 #include <utility>
@@ -155,9 +153,28 @@ __device__ __forceinline__ void mfma16(f32x4& c, const bf16x8& w, const bf16x8& 
   else
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(w), "v"(x));
 }
-// accumulator block (IB, JB) of the 320-wide tile: weight blocks 0-7 in a, 8-9 in v
-template <int IB, int JB>
-__device__ __forceinline__ f32x4& acc16(f32x4 (&a)[8][8], f32x4 (&v)[2][8]) {
+// Wait states between the MFMA writes of eight accumulator blocks (AGPRs or
+// VGPRs) and their first VALU read: LONG covers a 4-pass MFMA issued just
+// before, the short form follows a long one.
+template <bool AGPR, bool LONG>
+__device__ __forceinline__ void mfma_result_wait(f32x4 (&c)[8]) {
+  if constexpr (AGPR && LONG)
+    asm volatile("s_nop 7\n\ts_nop 7" : "+a"(c[0]), "+a"(c[1]), "+a"(c[2]), "+a"(c[3]), "+a"(c[4]), "+a"(c[5]),
+                 "+a"(c[6]), "+a"(c[7]));
+  else if constexpr (AGPR)
+    asm volatile("s_nop 1" : "+a"(c[0]), "+a"(c[1]), "+a"(c[2]), "+a"(c[3]), "+a"(c[4]), "+a"(c[5]), "+a"(c[6]),
+                 "+a"(c[7]));
+  else if constexpr (LONG)
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(c[4]), "+v"(c[5]),
+                 "+v"(c[6]), "+v"(c[7]));
+  else
+    asm volatile("s_nop 1" : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(c[4]), "+v"(c[5]), "+v"(c[6]),
+                 "+v"(c[7]));
+}
+
+// accumulator block (IB, JB) of gemm16_kernel: weight blocks 0-7 in a, 8-9 in v
+template <int IB, int JB, int V>
+__device__ __forceinline__ f32x4& acc16(f32x4 (&a)[8][8], f32x4 (&v)[V][8]) {
   if constexpr (IB < 8)
     return a[IB][JB];
   else
@@ -224,12 +241,11 @@ __device__ __forceinline__ float f8_scale(const GemmArgs& args, int n) {
   return args.scale_a[0] * sb;
 }
 
-// Non-SwiGLU epilogue of four consecutive outputs (columns n..n+3; rv: their
+// Non-SwiGLU epilogue of four consecutive outputs (bv, rv: their bias and
 // residual, loaded by the caller), rounded to bf16 once.
 template <int EPI>
-__device__ __forceinline__ u32x2 finish4(float* o, const GemmArgs& args, int n, u32x2 rv) {
+__device__ __forceinline__ u32x2 finish4(float* o, u32x2 bv, u32x2 rv) {
   if constexpr (epi_bias(EPI)) {
-    const u32x2 bv = *reinterpret_cast<const u32x2*>(args.bias + n);
     o[0] += __uint_as_float(bv[0] << 16);
     o[1] += __uint_as_float(bv[0] & 0xffff0000u);
     o[2] += __uint_as_float(bv[1] << 16);
@@ -251,22 +267,32 @@ __device__ __forceinline__ u32x2 finish4(float* o, const GemmArgs& args, int n, 
   pk[1] = pack_bf16x2(o[2], o[3]);
   return pk;
 }
+// the same for columns n..n+3, loading their bias
+template <int EPI>
+__device__ __forceinline__ u32x2 finish4(float* o, const GemmArgs& args, int n, u32x2 rv) {
+  const u32x2 bv = epi_bias(EPI) ? *reinterpret_cast<const u32x2*>(args.bias + n) : u32x2{0, 0};
+  return finish4<EPI>(o, bv, rv);
+}
 
-// FP8: operands are E4M3 bytes, a pipeline step covers 128 k elements (the
-// same 128-byte row pieces, LDS layout and loads as bf16) in two substeps of
-// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales), and the sums are
-// multiplied by scale_a * scale_b before the epilogue.
+// The FP8 GEMM: operands are E4M3 bytes, a pipeline step covers 128 k
+// elements (the same 128-byte row pieces, LDS layout and loads as the bf16
+// kernel) in two substeps of v_mfma_scale_f32_32x32x64_f8f6f4 (unit block
+// scales), and the sums are multiplied by scale_a * scale_b before the
+// epilogue. 256 x 256 tile; each wavefront owns 128 tokens x 128 weight rows
+// as 4 x 4 blocks of 32 x 32 in the 256 AGPRs. (The 16x16x128 form saves
+// nothing here: with 32-byte operands per lane it moves as many register
+// bytes per flop as 32x32x64.)
 //
-// NB: 32-row weight blocks per wavefront (4 here; the tile is 64 NB wide).
 // SPLIT: the units are k-ranges of split tiles whose raw fp32 sums go to
 // `partial` (a separate instantiation, so that each kernel has one epilogue:
 // with both in one kernel the compiler read every accumulator out ahead of
 // the branch and spilled them).
-template <int EPI, bool F8, int NB, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) {
-  static_assert(NB == 4, "the 320-wide tile is gemm16_kernel");
-  constexpr int ES = F8 ? 1 : 2;                // bytes per element
-  constexpr int KSTEP = 128 / ES;               // k elements per pipeline step
+template <int EPI, bool SPLIT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_f8_kernel(const GemmArgs args) {
+  static_assert(EPI <= static_cast<int>(Epilogue::kSwiGLU), "FP8 epilogues: store, residual, SwiGLU");
+  constexpr int NB = 4;                         // 32-row weight blocks per wavefront
+  constexpr int ES = 1;                         // bytes per element
+  constexpr int KSTEP = 128;                    // k elements per pipeline step
   constexpr int BNT = 64 * NB;                  // n extent of the tile (weight rows)
   constexpr int kATile = BM * BK;               // A operand, one stage (bf16 units)
   constexpr int kBTile = BNT * BK;              // B operand, one stage
@@ -277,14 +303,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   constexpr int kBlksB = BNT / kRowsPerBlk;     // ... and for B
   constexpr int kLoads = kBlksA + kBlksB;
   constexpr int kMf = 4 * NB;                   // MFMAs per substep
-  // The kLoads loads of k-step kt+1 are issued in up to three parts: loads
-  // [0, kL0) during the last substep of k-step kt-1, the next kL1 and the rest
-  // during substeps 0 and 1 of k-step kt, each part spread evenly over the
-  // substep's MFMAs. (Issuing all of them in one substep is slower, and so is
-  // issuing the last ones late in substep 1.)
-  constexpr int kL0 = 8, kL1 = 8;
   constexpr int kWarm = 4;  // warm-up distance in k-steps
-  static_assert(BK == 64 && kL0 + kL1 <= kLoads, "pipeline shape");
+  static_assert(BK == 64, "pipeline shape");
 
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
   bf16_t* As = smem;              // [2][BM][BK]
@@ -401,43 +421,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   const unsigned warm_off = min(b_lane_row, max(warm_avail, 1) - 1) * ldb * ES + (lane % kChunks) * 16;
 
   // ---- LDS -> registers and MFMA: substep s of a k-step covers the row
-  //      bytes 32s..32s+31 (bf16: 16 k) or 64s..64s+63 (FP8: 64 k); operands
-  //      are double-buffered in two register slots. For FP8 a lane holds 32
-  //      bytes of its row, chunks 4s + 2 lhalf and the next one: any
-  //      assignment of k to the operand bytes gives the same sum as long as
-  //      both operands use it. ----
+  //      bytes 64s..64s+63 (64 k); operands are double-buffered in two
+  //      register slots. A lane holds 32 bytes of its row, chunks 4s + 2
+  //      lhalf and the next one: any assignment of k to the operand bytes
+  //      gives the same sum as long as both operands use it. ----
   const int lrow = lane & 31;
   const int lhalf = lane >> 5;
   const int lswz = swz(lrow);
   const int a_base = (wm * 128 + lrow) * BK;  // activation rows (MFMA B operand)
   const int b_base = (wn * 32 * NB + lrow) * BK;  // weight rows (MFMA A operand)
-  bf16x8 wop[2][NB], xop[2][4];
   i32x8 wop8[2][4], xop8[2][4];
   // the r-th operand of substep s of LDS stage `stage`, into register slot
-  // `slot`: w0 x0 w1 x1 ...; an FP8 operand is two 16-byte reads
+  // `slot`: w0 x0 w1 x1 ...; an operand is two 16-byte reads
   constexpr int kReads = 8;
   auto fetch_one = [&](int stage, int s, int slot, int r) {
     const bf16_t* as = As + stage * kATile;
     const bf16_t* bs = Bs + stage * kBTile;
     const int i = r >> 1;
-    if constexpr (F8) {
-      const int c0 = ((4 * s + 2 * lhalf) ^ lswz) << 3;
-      const int c1 = ((4 * s + 2 * lhalf + 1) ^ lswz) << 3;
-      const bf16_t* src = (r & 1) ? as + a_base + i * 32 * BK : bs + b_base + i * 32 * BK;
-      const u32x4 v0 = *reinterpret_cast<const u32x4*>(src + c0);
-      const u32x4 v1 = *reinterpret_cast<const u32x4*>(src + c1);
-      const i32x8 v = __builtin_bit_cast(i32x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-      if (r & 1)
-        xop8[slot][i] = v;
-      else
-        wop8[slot][i] = v;
-    } else {
-      const int chunk = ((2 * s + lhalf) ^ lswz) << 3;
-      if (r & 1)
-        xop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(as + a_base + i * 32 * BK + chunk));
-      else
-        wop[slot][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(bs + b_base + i * 32 * BK + chunk));
-    }
+    const int c0 = ((4 * s + 2 * lhalf) ^ lswz) << 3;
+    const int c1 = ((4 * s + 2 * lhalf + 1) ^ lswz) << 3;
+    const bf16_t* src = (r & 1) ? as + a_base + i * 32 * BK : bs + b_base + i * 32 * BK;
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(src + c0);
+    const u32x4 v1 = *reinterpret_cast<const u32x4*>(src + c1);
+    const i32x8 v = __builtin_bit_cast(i32x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    if (r & 1)
+      xop8[slot][i] = v;
+    else
+      wop8[slot][i] = v;
   };
   // blocks in order of max(i, j), so the MFMAs that need the operands read
   // last come last
@@ -446,12 +456,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
     const int d = q < 1 ? 0 : q < 4 ? 1 : q < 9 ? 2 : 3;
     const int e = q - d * d;
     const int i = e <= d ? e : d, j = e <= d ? d : 2 * d - e;
-    if constexpr (F8)
-      // E4M3 operands (format 0), block scales 127 (= 2^0)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop8[slot][i], xop8[slot][j], acc[i][j], 0, 0,
-                                                                  0, 127, 0, 127);
-    else
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wop[slot][i], xop[slot][j], acc[i][j], 0, 0, 0);
+    // E4M3 operands (format 0), block scales 127 (= 2^0)
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop8[slot][i], xop8[slot][j], acc[i][j], 0, 0, 0,
+                                                                127, 0, 127);
   };
   // Load number l of k-step kt (unit-relative), to LDS stage `stage`: below
   // 2 kBlksA, operand l % 2 (0: A, 1: B) of row block l / 2; from there on, B
@@ -501,76 +508,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   // be waited to zero) before its first MFMA.
   asm volatile("" ::"s"(args.partial));
 
-  // ---- pipeline over a two-stage LDS ring. The one workgroup barrier per
-  //      k-step sits before its last substep, whose operands are already in
-  //      registers: the MFMAs of that substep cover the reads of the next
-  //      k-step's first operands, and the stage just finished is refilled
-  //      from there on. ----
-  if constexpr (F8) {
-    // Two substeps per k-step. The barrier sits before substep 1; all loads
-    // of k-step kt+2 go out during substep 1 of kt (one per MFMA, the same
-    // issue rate as bf16), so a whole substep separates the last of them
-    // from the wait that needs them.
-    if (nk > 0) {
-      issue_dma(0, 0);
-      issue_dma(1, 1);
-      wait_vmcnt<kLoads>();
-      lds_barrier();
-      for (int r = 0; r < kReads; ++r) fetch_one(0, 0, 0, r);
-      // one k-step; LIVE2: k-step kt+2 exists and is loaded
-      auto step = [&](int kt, auto LIVE2) {
-        const int st = kt & 1;
-        __builtin_amdgcn_sched_barrier(0);
-        issue_warm(kt + kWarm);
-        mfma_rl(0, kt, st, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), Dead(), st, 1, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        // k-step kt+1 is complete in LDS and no wavefront reads stage st any more
-        wait_vmcnt<1>();
-        lds_barrier();
-        mfma_rl(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, kLoads>(), LIVE2,
-                st ^ 1, 0, 0);
-      };
-      int kt = 0;
-      for (; kt < nk - 2; ++kt) step(kt, Live());
-      for (; kt < nk; ++kt) step(kt, Dead());
-      wait_vmcnt<0>();
-      lds_barrier();
-    }
-  } else if (nk > 0) {
-    // k-step 0, then the first loads of k-step 1 and the warm-up of k-steps
-    // 1 .. kWarm-1 (the loop warms kWarm ahead from there) before the wait
+  // ---- pipeline over a two-stage LDS ring: two substeps per k-step. The
+  //      one workgroup barrier per k-step sits before substep 1, whose
+  //      operands are already in registers: its MFMAs cover the reads of the
+  //      next k-step's first operands. All loads of k-step kt+2 go out during
+  //      substep 1 of kt (one per MFMA), so a whole substep separates the
+  //      last of them from the wait that needs them. ----
+  if (nk > 0) {
     issue_dma(0, 0);
-#pragma unroll
-    for (int l = 0; l < kL0; ++l) issue_load(1, 1, l);
-#pragma unroll
-    for (int kt = 1; kt < kWarm; ++kt) issue_warm(kt);
-    wait_vmcnt<kL0 + kWarm - 1>();
+    issue_dma(1, 1);
+    wait_vmcnt<kLoads>();
     lds_barrier();
     for (int r = 0; r < kReads; ++r) fetch_one(0, 0, 0, r);
-    // one k-step; LIVE1 / LIVE2: k-step kt+1 / kt+2 exists and is loaded
-    auto step = [&](int kt, auto LIVE1, auto LIVE2) {
+    // one k-step; LIVE2: k-step kt+2 exists and is loaded
+    auto step = [&](int kt, auto LIVE2) {
       const int st = kt & 1;
       __builtin_amdgcn_sched_barrier(0);
-      mfma_rl(0, kt + 1, st ^ 1, std::integral_constant<int, kL0>(), std::integral_constant<int, kL0 + kL1>(),
-              LIVE1, st, 1, 1);
-      mfma_rl(1, kt + 1, st ^ 1, std::integral_constant<int, kL0 + kL1>(),
-              std::integral_constant<int, kLoads>(), LIVE1, st, 2, 0);
       issue_warm(kt + kWarm);
-      mfma_rl(0, kt + 1, st ^ 1, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), Dead(), st, 3, 1);
+      mfma_rl(0, kt, st, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), Dead(), st, 1, 1);
       __builtin_amdgcn_sched_barrier(0);
-      // k-step kt+1 is complete in LDS (only the warm-up load just issued may
-      // still be in flight) and no wavefront reads stage st any more
+      // k-step kt+1 is complete in LDS and no wavefront reads stage st any more
       wait_vmcnt<1>();
       lds_barrier();
-      mfma_rl(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, kL0>(), LIVE2, st ^ 1, 0, 0);
+      mfma_rl(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, kLoads>(), LIVE2,
+              st ^ 1, 0, 0);
     };
-    // the last two k-steps are peeled off so that no load runs past the
-    // unit's range (the final wait would have to wait for them)
     int kt = 0;
-    for (; kt < nk - 2; ++kt) step(kt, Live(), Live());
-    if (kt < nk - 1) step(kt++, Live(), Dead());
-    step(kt, Dead(), Dead());
-    // the trailing loads and reads have completed
+    for (; kt < nk - 2; ++kt) step(kt, Live());
+    for (; kt < nk; ++kt) step(kt, Dead());
     wait_vmcnt<0>();
     lds_barrier();
   }
@@ -601,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   //      resources that end at row M, which drop those stores and read
   //      zeros (those rows computed from copies of row M-1, so their values
   //      are finite and never exceed a real row's in the SwiGLU maximum).
-  //      Column blocks past N (partial n-tiles of the 256-wide form) are
+  //      Column blocks past N (partial n-tiles) are
   //      skipped by wave-uniform tests, their 16-byte chunks by a lane test
   //      in the stores. Outputs leave through a per-wavefront LDS region
   //      (the forms below). ----
@@ -611,18 +576,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(args.c + first, (short)0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t r_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       epi_residual(EPI) ? const_cast<bf16_t*>(args.r) + first : args.c + first, (short)0, nbytes, 0x00020000);
-  float amx = 0.f;           // FP8 kSwiGLU: max |C| over this lane's outputs
-  float sg = 1.f, su = 1.f;  // FP8 SwiGLU: scales of the gate and up products
-  if constexpr (F8 && EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+  float amx = 0.f;           // kSwiGLU: max |C| over this lane's outputs
+  float sg = 1.f, su = 1.f;  // SwiGLU: scales of the gate and up products
+  if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
     sg = args.scale_a[0] * args.scale_b[0][0];
     su = args.scale_a[0] * args.scale_b[1][0];
   }
   if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
-    // SwiGLU (FP8, or bf16 where the 320-wide tile does not fit):
-    // gate block i pairs with up block i + 2, 64 outputs per row and wave,
-    // staged like the 320-wide form (rows of 72 bf16 = 144 bytes, 8 lanes
-    // per row segment). Blocks past N (a partial n-tile; N is a multiple
-    // of 32) are skipped, and so are their chunks in the stores.
+    // SwiGLU: gate block i pairs with up block i + 2, 64 outputs per row and
+    // wave, staged through the wave's LDS region (rows of 72 bf16 = 144
+    // bytes, 8 lanes per row segment). Blocks past N (a partial n-tile; N is
+    // a multiple of 32) are skipped, and so are their chunks in the stores.
     constexpr int kStg = 72;
     bf16_t* const stg = smem + wave_u * 128 * kStg;
     const int col0 = tile_n * (BN / 2) + wn * 64;
@@ -640,7 +604,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
           pk[0] = pack_bf16x2(o[0], o[1]);
           pk[1] = pack_bf16x2(o[2], o[3]);
           *reinterpret_cast<u32x2*>(stg + (j * 32 + lrow) * kStg + i * 32 + 8 * g + 4 * lhalf) = pk;
-          if constexpr (F8) amx = fmaxf(amx, abs_max4(pk));
+          amx = fmaxf(amx, abs_max4(pk));
         }
       }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -652,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       if (col0 + q * 8 < N) __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
     }
   } else {
-    // Store, residual and bias forms: the wave's 128 x 128 outputs in two
+    // Store and residual forms: the wave's 128 x 128 outputs in two
     // halves of 64 rows through its LDS region (rows of 136 bf16 = 272
     // bytes, 16-byte aligned, each bank takes two rows of a write
     // instruction), leaving as 16-byte chunks along the rows, 16
@@ -687,7 +651,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
         for (int i = 0; i < NB; ++i) {
           const int nb = col0 + i * 32;
           if (nb >= N) continue;
-          const float sc = F8 ? f8_scale(args, nb) : 1.f;
+          const float sc = f8_scale(args, nb);
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             float o[4];
@@ -709,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
   }
-  if constexpr (F8 && EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+  if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
     if (args.amax) {  // uniform; past the four staging regions (72 KB)
       const float v = workgroup_max(amx, reinterpret_cast<float*>(smem + 4 * 128 * 72));
       if (tid == 0) args.amax[unit] = v;
@@ -717,15 +681,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
   }
 }
 
-// The 320-wide bf16 tile (256 tokens x 320 weight rows) on
-// v_mfma_f32_16x16x32_bf16. Same LDS ring, LDS-DMA loads, swizzle, warm-up
-// and tile order as gemm_kernel; each wavefront owns 128 tokens x 160 weight
-// rows as 8 x 10 blocks of 16 x 16. Per MFMA the 16x16x32 form reads and
-// writes a quarter of the accumulator registers of the 32x32x16 form for half
-// the products, so the register file moves 20% fewer bytes per flop; under
-// the chip's power limit a register-only loop of it runs ~10% faster.
+// The bf16 GEMMs on v_mfma_f32_16x16x32_bf16: the 256 x 320 tile (NB = 5)
+// and the 256 x 256 one (NB = 4). Same LDS ring, LDS-DMA loads, swizzle,
+// warm-up and tile order as gemm_f8_kernel; each wavefront owns 128 tokens x
+// 32 NB weight rows as 8 x WB blocks of 16 x 16 (WB = 2 NB). Per MFMA the
+// 16x16x32 form reads and writes a quarter of the accumulator registers of
+// the 32x32x16 form for half the products, so the register file moves 20%
+// fewer bytes per flop; under the chip's power limit a register-only loop of
+// it runs ~10% faster.
 //
-// A k-step (64 k) is two substeps of 32 k, 80 MFMAs each: block (ib, jb)
+// A k-step (64 k) is two substeps of 32 k, 8 WB MFMAs each: block (ib, jb)
 // multiplies weight rows 16 ib.. by tokens 16 jb.. . A lane holds the weight
 // operand of row 16 ib + (lane & 15), 8 k of the substep's 32, and the
 // activation operand of token 16 jb + (lane & 15) at the same k, and ends
@@ -735,36 +700,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(const GemmArgs args) 
 // operands of a substep stay in registers through it; the weight operands
 // stream through a ring of four registers, each read two blocks (16 MFMAs)
 // before its first use. The one barrier per k-step sits 16 MFMAs before its
-// end, after the last read of the stage: those MFMAs (weight blocks 8 and 9)
-// cover the barrier and the reads of the next k-step's first operands.
+// end, after the last read of the stage: those MFMAs (the last two weight
+// blocks) cover the barrier and the reads of the next k-step's first
+// operands.
 //
 // All MFMAs are inline assembly: blocks 0-7 accumulate in the 256 AGPRs,
-// blocks 8-9 in VGPRs. (Through the builtin the compiler permuted the 64
-// AGPR accumulators between loop iterations with register moves.) The
-// compiler does not see these statements as MFMAs, so the VALU/MFMA hazards
-// on the accumulators are covered by explicit waits after zeroing them and
-// before the epilogue reads them.
+// blocks 8-9 (NB = 5) in VGPRs. (Through the builtin the compiler permuted
+// the 64 AGPR accumulators between loop iterations with register moves.)
+// The compiler does not see these statements as MFMAs, so the VALU/MFMA
+// hazards on the accumulators are covered by explicit waits after zeroing
+// them and before the epilogue reads them.
 //
 // SwiGLU: each 32-row weight block holds 16 gate rows and then the 16 up
 // rows of the same output columns, so weight blocks 2p and 2p + 1 of a lane
 // are the two factors of the same outputs.
-template <int EPI>
+//
+// SPLIT: the unit is one k-range of a split tile; the raw fp32 sums go to
+// args.partial (laid out [m_local][virtual n], 4 consecutive n per 16-byte
+// store) for splitk_reduce_kernel, which applies the epilogue. Partial
+// n-tiles (N a multiple of 32, not of the tile): weight blocks past N are
+// loaded as copies of row N-1 and their outputs not stored.
+template <int EPI, int NB, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args) {
   constexpr bool kSwi = EPI == static_cast<int>(Epilogue::kSwiGLU);
-  static_assert(kSwi || EPI == static_cast<int>(Epilogue::kStore) || EPI == static_cast<int>(Epilogue::kResidual),
-                "epilogues of the 320-wide tile");
-  constexpr int BNT = 320;                       // weight rows of the tile
+  static_assert(NB == 4 || NB == 5, "tile width");
+  constexpr int BNT = 64 * NB;                   // weight rows of the tile
+  constexpr int WB = 2 * NB;                     // 16-row weight blocks per wavefront
+  constexpr int kSub = 8 * WB;                   // MFMAs per substep
+  constexpr int kSlots = 2 * kSub;               // MFMAs per k-step
+  constexpr int kBar = kSlots - 16;              // the barrier's slot
   constexpr int kATile = BM * BK, kBTile = BNT * BK;
   constexpr int kRowBytes = BK * 2, kChunks = BK / 8;
   constexpr int kRowsPerBlk = 4096 / kRowBytes;  // rows one load instruction of the 4 waves covers
   constexpr int kBlksA = BM / kRowsPerBlk, kBlksB = BNT / kRowsPerBlk;
-  constexpr int kLoads = kBlksA + kBlksB;        // 18 loads per k-step
+  constexpr int kLoads = kBlksA + kBlksB;        // 16 or 18 loads per k-step
   // loads [0, kLC) of k-step kt + 2 go out after the barrier of kt, the rest
   // over the first 80 MFMAs of kt + 1, one per 8 MFMAs (one per 4, or more
   // of them after the barrier, measured slower: down +5%)
   constexpr int kLC = 8;
   constexpr int kWarm = 4;  // warm-up distance in k-steps
-  static_assert(BK == 64 && kLoads == 18, "pipeline shape");
+  static_assert(BK == 64 && kLoads - kLC <= kSub / 8 && (2 * WB) % 4 == 0, "pipeline shape");
 
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
   bf16_t* As = smem;              // [2][BM][BK]
@@ -778,16 +753,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
   const int wm = wave & 1;
   const int wn = wave >> 1;
 
-  // ---- work unit (whole tiles): contiguous per XCD ----
+  // ---- work unit: contiguous per XCD, then tile and k-range ----
   const int total = args.units;
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds;
   const int q = total / kXcds, rmd = total % kXcds;
   const int unit = xcd * q + min(xcd, rmd) + bid / kXcds;
   int tile_m, tile_n;
-  tile_coords(args.tile_begin + unit, args.tiles_m, args.tiles_n, tile_m, tile_n);
+  // (whole-tile launches have ksplit 1: constants, not divisions)
+  const int ksplit = SPLIT ? args.ksplit : 1;
+  tile_coords(args.tile_begin + unit / ksplit, args.tiles_m, args.tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM;
-  const int nk = K / BK;
+  const int kt_begin = SPLIT ? (unit % ksplit) * args.kt_per_split : 0;
+  const int nk = SPLIT ? min(kt_begin + args.kt_per_split, K / BK) - kt_begin : K / BK;  // k-steps of this unit
 
   // B row block i (32 rows) of the tile: address of its first row, or for
   // SwiGLU of this wavefront's 8 rows, and the rows of its segment from there
@@ -796,11 +774,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
     const void* base;
     int v;
     if constexpr (kSwi) {
-      // block i: wave half i / 5, column group p = i % 5 of it (16 output
+      // block i: wave half i / NB, column group p = i % NB of it (16 output
       // columns); wavefronts 0, 1 load its gate rows, 2, 3 its up rows, 8
       // columns each
       const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-      const int j = tile_n * (BNT / 2) + (i / 5) * 80 + (i % 5) * 16 + (w & 1) * 8;
+      const int j = tile_n * (BNT / 2) + (i / NB) * (16 * NB) + (i % NB) * 16 + (w & 1) * 8;
       base = (w >> 1) ? args.bptr[1] : args.bptr[0];
       v = min(j, N - 1);
       avail = N - j;
@@ -824,7 +802,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
     return static_cast<const char*>(base) + static_cast<size_t>(v) * ldb * 2;
   };
 
-  // ---- global -> LDS, as in gemm_kernel ----
+  // ---- global -> LDS, as in gemm_f8_kernel ----
   const int dma_row = wave * (1024 / kRowBytes) + lane / kChunks;
   const int dma_chunk = ((lane % kChunks) ^ swz(dma_row)) * 16;
   const int b_lane_row = kSwi ? lane / kChunks : dma_row;
@@ -849,7 +827,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
   const char* const warm_ptr = b_block_base((tile_m & 7) * (32 / kRowsPerBlk), warm_avail);
   const unsigned warm_off = min(b_lane_row, max(warm_avail, 1) - 1) * ldb * 2 + (lane % kChunks) * 16;
 
-  auto koff = [&](int kt) { return static_cast<size_t>(min(kt, nk - 1)) * kRowBytes; };
+  auto koff = [&](int kt) { return static_cast<size_t>(kt_begin + min(kt, nk - 1)) * kRowBytes; };
   auto issue_load = [&](int kt, int stage, int l) {
     const bool isb = l >= 2 * kBlksA || (l & 1);
     const int i = l >= 2 * kBlksA ? l - kBlksA : l >> 1;
@@ -881,14 +859,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
                                                                         c16[s]));
   };
 
-  f32x4 acc[8][8];   // weight blocks 0-7 (AGPRs)
-  f32x4 accv[2][8];  // weight blocks 8-9 (VGPRs)
+  constexpr int kVB = WB - 8;  // weight blocks accumulating in VGPRs (0 or 2)
+  f32x4 acc[8][8];                    // weight blocks 0-7 (AGPRs)
+  f32x4 accv[kVB > 0 ? kVB : 1][8];   // weight blocks 8-9 (VGPRs)
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kVB; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) accv[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   // the zeroing writes, then the first MFMA reads of the same registers
@@ -897,12 +876,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
     asm volatile("s_nop 4" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
                  "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kVB; ++i)
     asm volatile("s_nop 4" : "+v"(accv[i][0]), "+v"(accv[i][1]), "+v"(accv[i][2]), "+v"(accv[i][3]),
                  "+v"(accv[i][4]), "+v"(accv[i][5]), "+v"(accv[i][6]), "+v"(accv[i][7]));
 
   bf16x8 xo[2][8];  // activation operands of substeps 0 and 1
-  bf16x8 wo[4];     // weight operands: the 20 of a k-step (10 s + ib) in a ring of four
+  bf16x8 wo[4];     // weight operands: the 2 WB of a k-step (WB s + ib) in a ring of four
   using Live = std::true_type;
   using Dead = std::false_type;
 
@@ -912,35 +891,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
   auto step = [&](int kt, auto LIVE1, auto LIVE2) {
     const int st = kt & 1;
     __builtin_amdgcn_sched_barrier(0);
-    static_for<0, 144>([&](auto G) {
+    static_for<0, kBar>([&](auto G) {
       constexpr int g = decltype(G)::value;
-      constexpr int s = g / 80, ib = (g % 80) / 8, jb = g % 8;
-      mfma16<(ib < 8)>(acc16<ib, jb>(acc, accv), wo[(10 * s + ib) & 3], xo[s][jb]);
-      // weight operand 10 s' + i (i >= 2 of substep 0, all of substep 1)
-      // after slot 8 (10 s' + i) - 12, two blocks before its first use
+      constexpr int s = g / kSub, ib = (g % kSub) / 8, jb = g % 8;
+      mfma16<(ib < 8)>(acc16<ib, jb>(acc, accv), wo[(WB * s + ib) & 3], xo[s][jb]);
+      // weight operand WB s' + i (i >= 2 of substep 0, all of substep 1)
+      // after slot 8 (WB s' + i) - 12, two blocks before its first use
       if constexpr (g % 8 == 4) {
         constexpr int idx = (g + 12) / 8;
-        wo[idx & 3] = rd_w(st, idx / 10, idx % 10);
+        wo[idx & 3] = rd_w(st, idx / WB, idx % WB);
       }
-      // substep 1's activation operands after slots 40, 44, .., 68
-      if constexpr (g >= 40 && g < 72 && g % 4 == 0) xo[1][(g - 40) / 4] = rd_x(st, 1, (g - 40) / 4);
-      // loads [kLC, 18) of k-step kt+1 after slots 0, 8, .., 72
+      // substep 1's activation operands, one per 4 slots, 12 or more slots
+      // before their first use
+      constexpr int x0 = kSub - 40;
+      if constexpr (g >= x0 && g < x0 + 32 && g % 4 == 0) xo[1][(g - x0) / 4] = rd_x(st, 1, (g - x0) / 4);
+      // loads [kLC, kLoads) of k-step kt+1 after slots 0, 8, 16, ..
       if constexpr (decltype(LIVE1)::value && g % 8 == 0 && g / 8 < kLoads - kLC)
         issue_load(kt + 1, st ^ 1, kLC + g / 8);
-      if constexpr (g == 80) issue_warm(kt + kWarm);
+      if constexpr (g == kSub) issue_warm(kt + kWarm);
       __builtin_amdgcn_sched_barrier(0);
     });
     // k-step kt+1 is complete in LDS (only the warm-up load may still be in
     // flight) and no wavefront reads stage st any more
     wait_vmcnt<1>();
     lds_barrier();
-    static_for<144, 160>([&](auto G) {
+    static_for<kBar, kSlots>([&](auto G) {
       constexpr int g = decltype(G)::value;
-      constexpr int ib = (g - 80) / 8, jb = g % 8;
-      mfma16<(ib < 8)>(acc16<ib, jb>(acc, accv), wo[(10 + ib) & 3], xo[1][jb]);
+      constexpr int ib = (g - kSub) / 8, jb = g % 8;
+      mfma16<(ib < 8)>(acc16<ib, jb>(acc, accv), wo[(WB + ib) & 3], xo[1][jb]);
       // the first operands of k-step kt+1: activations 0-7 and weights 0, 1
       // of its substep 0, in the order they are used
-      constexpr int r = g - 144;
+      constexpr int r = g - kBar;
       if constexpr (r == 1)
         wo[0] = rd_w(st ^ 1, 0, 0);
       else if constexpr (r == 9)
@@ -981,93 +962,123 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
   }
 
   // MFMA writes of the accumulators, then VALU reads: 16 wait states (more
-  // than the 4-pass MFMA needs) before the first group, more before the rest
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(accv[1 - i][0]), "+v"(accv[1 - i][1]), "+v"(accv[1 - i][2]),
-                 "+v"(accv[1 - i][3]), "+v"(accv[1 - i][4]), "+v"(accv[1 - i][5]), "+v"(accv[1 - i][6]),
-                 "+v"(accv[1 - i][7]));
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    asm volatile("s_nop 1" : "+a"(acc[7 - i][0]), "+a"(acc[7 - i][1]), "+a"(acc[7 - i][2]), "+a"(acc[7 - i][3]),
-                 "+a"(acc[7 - i][4]), "+a"(acc[7 - i][5]), "+a"(acc[7 - i][6]), "+a"(acc[7 - i][7]));
+  // than the 4-pass MFMA needs) before the group written last, more before
+  // the rest
+  static_for<0, kVB>([&](auto I) { mfma_result_wait<false, true>(accv[kVB - 1 - decltype(I)::value]); });
+  static_for<0, 8>([&](auto I) {
+    constexpr int i = 7 - decltype(I)::value;
+    mfma_result_wait<true, kVB == 0 && i == 7>(acc[i]);
+  });
 
+  // ---- split-K unit: raw sums to the unit's partial tile, [m_local][virtual
+  //      n] with virtual n = the tile's weight row (wave half wn, block ib) ----
+  if constexpr (SPLIT) {
+    float* dst = args.partial + static_cast<size_t>(unit) * BM * BNT;
+    static_for<0, 8 * WB>([&](auto Q) {
+      constexpr int jb = decltype(Q)::value / WB, ib = decltype(Q)::value % WB;
+      *reinterpret_cast<f32x4*>(dst + (wm * 128 + jb * 16 + r16) * BNT + wn * (BNT / 2) + ib * 16 + 4 * g16) =
+          acc16<ib, jb>(acc, accv);
+    });
+    return;
+  }
 
   // ---- epilogue: outputs leave through a per-wavefront LDS region in two
   //      halves of 64 tokens, as 16-byte chunks along the rows. Rows past M:
   //      buffer resources that end at row M drop the stores and read zeros
-  //      (see gemm_kernel). The 320-wide tile never has a partial n-tile. ----
+  //      (see gemm_f8_kernel). Weight blocks past N (a partial n-tile of the
+  //      256-wide form; N is a multiple of 32, so a 16-row block is wholly
+  //      in or out) are skipped by wave-uniform tests, their 16-byte chunks by
+  //      a lane test in the stores. ----
   const size_t rbytes = static_cast<size_t>(M - m0) * args.ldc * sizeof(bf16_t);
   const int nbytes = static_cast<int>(rbytes < 0x7fffffffu ? rbytes : 0x7fffffffu);
   const size_t first = static_cast<size_t>(m0) * args.ldc;
   const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(args.c + first, (short)0, nbytes, 0x00020000);
   const int ldc_b = args.ldc * static_cast<int>(sizeof(bf16_t));
   if constexpr (kSwi) {
-    // 128 x 80 outputs per wavefront; staging rows of 88 bf16 (176 bytes:
-    // a write instruction's 16 rows x 4 column groups hit every bank twice)
-    constexpr int kStg = 88;
+    // 128 x 16 NB outputs per wavefront (NB pairs of gate and up blocks);
+    // staging rows of 16 NB + 8 bf16 (144 or 176 bytes: a write
+    // instruction's 16 rows x 4 column groups hit every bank twice)
+    constexpr int kCols = 16 * NB, kStg = kCols + 8, kRowChunks = kCols / 8;
     bf16_t* const stg = smem + wave_u * 64 * kStg;
-    const int col0 = tile_n * (BNT / 2) + wn * 80;
+    const int col0 = tile_n * (BNT / 2) + wn * kCols;
     static_for<0, 2>([&](auto H) {
       constexpr int h = decltype(H)::value;
-      static_for<0, 20>([&](auto Q) {
-        constexpr int jj = decltype(Q)::value / 5, p = decltype(Q)::value % 5;
-        const f32x4& gt = acc16<2 * p, 4 * h + jj>(acc, accv);
-        const f32x4& up = acc16<2 * p + 1, 4 * h + jj>(acc, accv);
-        float o[4];
+      static_for<0, 4 * NB>([&](auto Q) {
+        constexpr int jj = decltype(Q)::value / NB, p = decltype(Q)::value % NB;
+        if (NB == 5 || col0 + 16 * p < N) {
+          const f32x4& gt = acc16<2 * p, 4 * h + jj>(acc, accv);
+          const f32x4& up = acc16<2 * p + 1, 4 * h + jj>(acc, accv);
+          float o[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = silu_mul(gt[e], up[e]);
-        u32x2 pk;
-        pk[0] = pack_bf16x2(o[0], o[1]);
-        pk[1] = pack_bf16x2(o[2], o[3]);
-        *reinterpret_cast<u32x2*>(stg + (jj * 16 + r16) * kStg + p * 16 + 4 * g16) = pk;
-      });
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int it = 0; it < 10; ++it) {
-        const int c = it * 64 + lane, r = c / 10, qq = c - r * 10;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + qq * 8);
-        __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, (wm * 128 + h * 64 + r) * ldc_b + (col0 + qq * 8) * 2, 0, 0);
-      }
-      // the reads above have returned before the next half overwrites the region
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    });
-  } else {
-    // 128 x 160 outputs per wavefront; staging rows of 168 bf16 (336 bytes,
-    // each bank takes two rows of a write instruction). A half's residual
-    // values are loaded in the accumulator layout, all before its first add.
-    constexpr int kStg = 168, kRowChunks = 20;
-    bf16_t* const stg = smem + wave_u * 64 * kStg;
-    const int col0 = tile_n * BNT + wn * (BNT / 2);
-    const __amdgpu_buffer_rsrc_t r_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        epi_residual(EPI) ? const_cast<bf16_t*>(args.r) + first : args.c + first, (short)0, nbytes, 0x00020000);
-    static_for<0, 2>([&](auto H) {
-      constexpr int h = decltype(H)::value;
-      u32x2 rv[4][10];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int ib = 0; ib < 10; ++ib)
-          rv[jj][ib] = epi_residual(EPI)
-                           ? __builtin_amdgcn_raw_buffer_load_b64(
-                                 r_rsrc, (wm * 128 + (4 * h + jj) * 16 + r16) * ldc_b + (col0 + ib * 16 + 4 * g16) * 2,
-                                 0, 0)
-                           : u32x2{0, 0};
-      static_for<0, 40>([&](auto Q) {
-        constexpr int jj = decltype(Q)::value / 10, ib = decltype(Q)::value % 10;
-        const f32x4& a = acc16<ib, 4 * h + jj>(acc, accv);
-        float o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = a[e];
-        *reinterpret_cast<u32x2*>(stg + (jj * 16 + r16) * kStg + ib * 16 + 4 * g16) =
-            finish4<EPI>(o, args, col0 + ib * 16 + 4 * g16, rv[jj][ib]);
+          for (int e = 0; e < 4; ++e) o[e] = silu_mul(gt[e], up[e]);
+          u32x2 pk;
+          pk[0] = pack_bf16x2(o[0], o[1]);
+          pk[1] = pack_bf16x2(o[2], o[3]);
+          *reinterpret_cast<u32x2*>(stg + (jj * 16 + r16) * kStg + p * 16 + 4 * g16) = pk;
+        }
       });
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
       for (int it = 0; it < kRowChunks; ++it) {
         const int c = it * 64 + lane, r = c / kRowChunks, qq = c - r * kRowChunks;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + qq * 8);
-        __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, (wm * 128 + h * 64 + r) * ldc_b + (col0 + qq * 8) * 2, 0, 0);
+        if (NB == 5 || col0 + qq * 8 < N)
+          __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, (wm * 128 + h * 64 + r) * ldc_b + (col0 + qq * 8) * 2, 0,
+                                                 0);
+      }
+      // the reads above have returned before the next half overwrites the region
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    });
+  } else {
+    // Store, residual and bias forms: 128 x 16 WB outputs per wavefront;
+    // staging rows of 16 WB + 8 bf16 (272 or 336 bytes, each bank takes two
+    // rows of a write instruction). The lane's bias values (one per weight
+    // block) are loaded together first, and a half's residual values in the
+    // accumulator layout, all before its first add (a load past N reads
+    // other columns of the buffer, or zeros past its end, for an output that
+    // is not stored).
+    constexpr int kCols = 16 * WB, kStg = kCols + 8, kRowChunks = kCols / 8;
+    bf16_t* const stg = smem + wave_u * 64 * kStg;
+    const int col0 = tile_n * BNT + wn * (BNT / 2);
+    u32x2 bv[WB];
+#pragma unroll
+    for (int ib = 0; ib < WB; ++ib)
+      bv[ib] = epi_bias(EPI) && col0 + ib * 16 < N
+                   ? *reinterpret_cast<const u32x2*>(args.bias + col0 + ib * 16 + 4 * g16)
+                   : u32x2{0, 0};
+    const __amdgpu_buffer_rsrc_t r_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        epi_residual(EPI) ? const_cast<bf16_t*>(args.r) + first : args.c + first, (short)0, nbytes, 0x00020000);
+    static_for<0, 2>([&](auto H) {
+      constexpr int h = decltype(H)::value;
+      u32x2 rv[4][WB];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int ib = 0; ib < WB; ++ib)
+          rv[jj][ib] = epi_residual(EPI)
+                           ? __builtin_amdgcn_raw_buffer_load_b64(
+                                 r_rsrc, (wm * 128 + (4 * h + jj) * 16 + r16) * ldc_b + (col0 + ib * 16 + 4 * g16) * 2,
+                                 0, 0)
+                           : u32x2{0, 0};
+      static_for<0, 4 * WB>([&](auto Q) {
+        constexpr int jj = decltype(Q)::value / WB, ib = decltype(Q)::value % WB;
+        if (NB == 5 || col0 + 16 * ib < N) {
+          const f32x4& a = acc16<ib, 4 * h + jj>(acc, accv);
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = a[e];
+          *reinterpret_cast<u32x2*>(stg + (jj * 16 + r16) * kStg + ib * 16 + 4 * g16) =
+              finish4<EPI>(o, bv[ib], rv[jj][ib]);
+        }
+      });
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < kRowChunks; ++it) {
+        const int c = it * 64 + lane, r = c / kRowChunks, qq = c - r * kRowChunks;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + qq * 8);
+        if (NB == 5 || col0 + qq * 8 < N)
+          __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, (wm * 128 + h * 64 + r) * ldc_b + (col0 + qq * 8) * 2, 0,
+                                                 0);
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     });
@@ -1076,7 +1087,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
 
 // Sums the ksplit partial tiles of each split tile in a fixed order and
 // applies the epilogue. Block (t, y) of 64 NB threads handles rows 4y..4y+3
-// of split tile t; each thread 4 consecutive virtual columns.
+// of split tile t; each thread 4 consecutive virtual columns. The SwiGLU
+// virtual columns follow the kernel that wrote them: gemm16_kernel (bf16)
+// pairs 16 gate and 16 up rows per 32-row block, gemm_f8_kernel block i
+// with block i + 2.
 template <int EPI, bool F8, int NB>
 __global__ __launch_bounds__(64 * NB) void splitk_reduce_kernel(const GemmArgs args) {
   constexpr int BNT = 64 * NB;
@@ -1095,7 +1109,19 @@ __global__ __launch_bounds__(64 * NB) void splitk_reduce_kernel(const GemmArgs a
   const int N = args.n;
   float o[4];
   int n;
-  if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
+  if (EPI == static_cast<int>(Epilogue::kSwiGLU) && !F8) {
+    // virtual column vn: wave half vn / (BNT/2), 16-row block (vn % (BNT/2))
+    // / 16; even blocks are gate columns whose up partner sits 16 later
+    const int r = vn % (BNT / 2), blk = r >> 4;
+    live = live && (blk & 1) == 0;
+    const int uo = (blk & 1) == 0 ? 16 : 0;
+    f32x4 upsum = *reinterpret_cast<const f32x4*>(src + uo);
+    for (int sidx = 1; sidx < args.ksplit; ++sidx)
+      upsum += *reinterpret_cast<const f32x4*>(src + uo + static_cast<size_t>(sidx) * BM * BNT);
+    n = tile_n * (BNT / 2) + (vn / (BNT / 2)) * (BNT / 4) + (blk >> 1) * 16 + (r & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = silu_mul(sum[e], upsum[e]);
+  } else if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
     // virtual column vn: wave half vn/128, 32-wide slot (vn%128)/32; slots 0,1
     // are gate columns whose up partner sits 64 virtual columns later
     const int slot = (vn & 127) >> 5;
@@ -1141,12 +1167,12 @@ template <int EPI, bool F8, int NB, bool SPLIT>
 hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
   // two stages of both operands, then the warm-up scratch (4 KB)
   constexpr size_t smem = static_cast<size_t>(2) * (BM + 64 * NB) * BK * sizeof(bf16_t) + 4096;
-  // NB = 5: the 320-wide bf16 tile (whole tiles only)
+  // bf16: gemm16_kernel (16x16x32 MFMAs); FP8: gemm_f8_kernel (256-wide)
   const void* kernel;
-  if constexpr (NB == 5)
-    kernel = reinterpret_cast<const void*>(&gemm16_kernel<EPI>);
+  if constexpr (F8)
+    kernel = reinterpret_cast<const void*>(&gemm_f8_kernel<EPI, SPLIT>);
   else
-    kernel = reinterpret_cast<const void*>(&gemm_kernel<EPI, F8, NB, SPLIT>);
+    kernel = reinterpret_cast<const void*>(&gemm16_kernel<EPI, NB, SPLIT>);
   // the dynamic-LDS limit is raised once per device (bit d: done on device d)
   static std::atomic<uint64_t> attr_set{0};
   int dev = 0;
@@ -1158,12 +1184,10 @@ hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit, std::memory_order_release);
   }
-  if constexpr (NB == 5) {
-    static_assert(!F8 && !SPLIT, "the 320-wide tile is bf16, whole tiles");
-    hipLaunchKernelGGL((gemm16_kernel<EPI>), dim3(grid), dim3(kThreads), smem, stream, args);
-  } else {
-    hipLaunchKernelGGL((gemm_kernel<EPI, F8, NB, SPLIT>), dim3(grid), dim3(kThreads), smem, stream, args);
-  }
+  if constexpr (F8)
+    hipLaunchKernelGGL((gemm_f8_kernel<EPI, SPLIT>), dim3(grid), dim3(kThreads), smem, stream, args);
+  else
+    hipLaunchKernelGGL((gemm16_kernel<EPI, NB, SPLIT>), dim3(grid), dim3(kThreads), smem, stream, args);
   return hipGetLastError();
 }
 
