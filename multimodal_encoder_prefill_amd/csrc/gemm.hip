@@ -181,6 +181,26 @@ __device__ __forceinline__ f32x4& acc16(f32x4 (&a)[8][8], f32x4 (&v)[V][8]) {
     return v[IB - 8][JB];
 }
 
+// c += W X^T on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands, both block
+// scales `scale`), the accumulator in AGPRs or VGPRs
+template <bool AGPR>
+__device__ __forceinline__ void mfma_f8(f32x16& c, const i32x8& w, const i32x8& x, int scale) {
+  if constexpr (AGPR)
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                 : "+a"(c) : "v"(w), "v"(x), "v"(scale));
+  else
+    asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                 : "+v"(c) : "v"(w), "v"(x), "v"(scale));
+}
+// accumulator block (IB, JB) of gemm_f8w_kernel: weight blocks 0-3 in a, 4 in v
+template <int IB, int JB>
+__device__ __forceinline__ f32x16& acc_f8(f32x16 (&a)[4][4], f32x16 (&v)[4]) {
+  if constexpr (IB < 4)
+    return a[IB][JB];
+  else
+    return v[JB];
+}
+
 // 32-bit LDS address of a pointer into the workgroup's LDS
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return static_cast<unsigned>(reinterpret_cast<size_t>((__attribute__((address_space(3))) const void*)p));
@@ -681,6 +701,333 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8_kernel(const GemmArgs arg
   }
 }
 
+// The FP8 GEMM in 256 x 320 tiles, for the decoder linears where whole waves
+// of such tiles fill the chip (as the bf16 gemm16_kernel's NB = 5 form): each
+// wavefront owns 128 tokens x 160 weight rows as 4 x 5 blocks of
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales; 16 blocks in the 256
+// AGPRs, the fifth weight block's 4 in VGPRs). A pipeline step covers 128 k
+// in two substeps of 64 k, 20 MFMAs each. The operands do not fit
+// double-buffered (32 bytes per lane each, 64 VGPRs of accumulators), so
+// they stream as in gemm16_kernel: a substep's four activation operands stay
+// in registers through it, the weight operands pass through a ring of five,
+// each read two blocks (8 MFMAs) ahead, and the one barrier per k-step sits
+// 8 MFMAs before its end, after the last read of the stage.
+//
+// A lane reads 32 bytes of its row (row 32 blk + (lane & 31)): chunks
+// 4 s + 2 (lane >> 5) and the next one of substep s (any assignment of k to
+// the operand bytes gives the same sum as long as both operands use it).
+// Accumulator block (ib, jb): weight rows 32 ib + 8 g + 4 (lane >> 5) + e,
+// token 32 jb + (lane & 31), for e < 4 and the four groups g. SwiGLU: the 8-row
+// groups of each 32-row weight block alternate gate and up rows of the same 8
+// output columns, so groups g and g + 1 of a lane are the two factors of the
+// same outputs.
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs args) {
+  constexpr bool kSwi = EPI == static_cast<int>(Epilogue::kSwiGLU);
+  static_assert(EPI <= static_cast<int>(Epilogue::kSwiGLU), "FP8 epilogues: store, residual, SwiGLU");
+  constexpr int NB = 5, BNT = 320;
+  constexpr int kATile = BM * BK, kBTile = BNT * BK;  // one stage, in bf16 units of the byte rows
+  constexpr int kRowBytes = BK * 2, kChunks = BK / 8;
+  constexpr int kRowsPerBlk = 4096 / kRowBytes;
+  constexpr int kBlksA = BM / kRowsPerBlk, kBlksB = BNT / kRowsPerBlk;
+  constexpr int kLoads = kBlksA + kBlksB;  // 18
+  constexpr int kSub = 4 * NB;             // MFMAs per substep
+  constexpr int kSlots = 2 * kSub;         // MFMAs per k-step
+  constexpr int kBar = kSlots - 8;         // the barrier's slot
+  // loads [0, kLC) of k-step kt + 2 go out after the barrier of kt, the rest
+  // over the first MFMAs of kt + 1, one per 2 MFMAs
+  constexpr int kLC = 8;
+  constexpr int kWarm = 4;
+  static_assert(BK == 64 && kLoads == 18 && 2 * (kLoads - kLC) <= kSub, "pipeline shape");
+
+  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+  bf16_t* As = smem;
+  bf16_t* Bs = smem + 2 * kATile;
+
+  const int M = args.m, N = args.n, K = args.k;
+  const int lda = args.lda, ldb = args.ldb;  // in bytes (one byte per element)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+
+  const int total = args.units;
+  const int bid = blockIdx.x;
+  const int xcd = bid % kXcds;
+  const int q = total / kXcds, rmd = total % kXcds;
+  const int unit = xcd * q + min(xcd, rmd) + bid / kXcds;
+  int tile_m, tile_n;
+  tile_coords(args.tile_begin + unit, args.tiles_m, args.tiles_n, tile_m, tile_n);
+  const int m0 = tile_m * BM;
+  const int nk = K / 128;  // k-steps
+
+  auto b_block_base = [&](int i, int& avail) -> const char* {
+    const void* base;
+    int v;
+    if constexpr (kSwi) {
+      // block i: wave half i / 5, block i % 5 of it; the 8-row group of
+      // wavefront w is gate rows for even w, up rows for odd w, output
+      // columns j .. j+7
+      const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      const int j = tile_n * (BNT / 2) + (i / NB) * (16 * NB) + (i % NB) * 16 + (w >> 1) * 8;
+      base = (w & 1) ? args.bptr[1] : args.bptr[0];
+      v = min(j, N - 1);
+      avail = N - j;
+    } else {
+      const int row = tile_n * BNT + kRowsPerBlk * i;
+      const int rr = min(row, N - 1);
+      if (rr < args.brows[0]) {
+        base = args.bptr[0];
+        v = rr;
+        avail = args.brows[0] - row;
+      } else if (rr < args.brows[0] + args.brows[1]) {
+        base = args.bptr[1];
+        v = rr - args.brows[0];
+        avail = args.brows[0] + args.brows[1] - row;
+      } else {
+        base = args.bptr[2];
+        v = rr - args.brows[0] - args.brows[1];
+        avail = N - row;
+      }
+    }
+    return static_cast<const char*>(base) + static_cast<size_t>(v) * ldb;
+  };
+
+  const int dma_row = wave * (1024 / kRowBytes) + lane / kChunks;
+  const int dma_chunk = ((lane % kChunks) ^ swz(dma_row)) * 16;
+  const int b_lane_row = kSwi ? lane / kChunks : dma_row;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  bf16_t* const warm_dst = smem + 2 * kATile + 2 * kBTile + wave_u * 512;
+  const char* a_ptr[kBlksA];
+  const char* b_ptr[kBlksB];
+  unsigned a_off[kBlksA], b_off[kBlksB];
+#pragma unroll
+  for (int i = 0; i < kBlksA; ++i) {
+    const int r = m0 + kRowsPerBlk * i;
+    a_ptr[i] = static_cast<const char*>(args.a) + static_cast<size_t>(min(r, M - 1)) * lda;
+    a_off[i] = min(dma_row, max(M - r, 1) - 1) * lda + dma_chunk;
+  }
+#pragma unroll
+  for (int i = 0; i < kBlksB; ++i) {
+    int avail;
+    b_ptr[i] = b_block_base(i, avail);
+    b_off[i] = min(b_lane_row, max(avail, 1) - 1) * ldb + dma_chunk;
+  }
+  int warm_avail;
+  const char* const warm_ptr = b_block_base((tile_m & 7) * (32 / kRowsPerBlk), warm_avail);
+  const unsigned warm_off = min(b_lane_row, max(warm_avail, 1) - 1) * ldb + (lane % kChunks) * 16;
+
+  auto koff = [&](int kt) { return static_cast<size_t>(min(kt, nk - 1)) * kRowBytes; };
+  auto issue_load = [&](int kt, int stage, int l) {
+    const bool isb = l >= 2 * kBlksA || (l & 1);
+    const int i = l >= 2 * kBlksA ? l - kBlksA : l >> 1;
+    bf16_t* dst = (isb ? Bs + stage * kBTile : As + stage * kATile) + wave_u * 512 + i * kRowsPerBlk * BK;
+    global_load_lds16((isb ? b_ptr[i] : a_ptr[i]) + koff(kt), isb ? b_off[i] : a_off[i], lds_addr(dst));
+  };
+  auto issue_warm = [&](int kt) { global_load_lds16(warm_ptr + koff(kt), warm_off, lds_addr(warm_dst)); };
+
+  // ---- LDS -> registers: 32 bytes of row 32 blk + lrow per operand ----
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int lswz = swz(lrow);
+  const int x_base = (wm * 128 + lrow) * BK;
+  const int w_base = (wn * (BNT / 2) + lrow) * BK;
+  const int c8[2][2] = {{((2 * lhalf) ^ lswz) * 8, ((2 * lhalf + 1) ^ lswz) * 8},
+                        {((4 + 2 * lhalf) ^ lswz) * 8, ((4 + 2 * lhalf + 1) ^ lswz) * 8}};
+  auto rd = [&](const bf16_t* p, int s) {
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(p + c8[s][0]);
+    const u32x4 v1 = *reinterpret_cast<const u32x4*>(p + c8[s][1]);
+    return __builtin_bit_cast(i32x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto rd_x = [&](int stage, int s, int jb) { return rd(As + stage * kATile + x_base + jb * 32 * BK, s); };
+  auto rd_w = [&](int stage, int s, int ib) { return rd(Bs + stage * kBTile + w_base + ib * 32 * BK, s); };
+
+  f32x16 acc[4][4];  // weight blocks 0-3 (AGPRs)
+  f32x16 accv[4];    // weight block 4 (VGPRs)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) accv[i][e] = 0.f;
+  }
+  // the zeroing writes, then the first MFMA reads of the same registers
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm volatile("s_nop 4" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]));
+  asm volatile("s_nop 4" : "+v"(accv[0]), "+v"(accv[1]), "+v"(accv[2]), "+v"(accv[3]));
+  const int unit_scale = 127;  // E8M0 block scale 2^0, in every lane
+  i32x8 xo[2][4];  // activation operands of substeps 0 and 1
+  i32x8 wo[5];     // weight operands: the 10 of a k-step (5 s + ib) in a ring of five
+  using Live = std::true_type;
+  using Dead = std::false_type;
+
+  auto step = [&](int kt, auto LIVE1, auto LIVE2) {
+    const int st = kt & 1;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, kBar>([&](auto G) {
+      constexpr int g = decltype(G)::value;
+      constexpr int s = g / kSub, ib = (g % kSub) / 4, jb = g % 4;
+      mfma_f8<(ib < 4)>(acc_f8<ib, jb>(acc, accv), wo[(NB * s + ib) % 5], xo[s][jb], unit_scale);
+      // weight operand NB s' + i (i >= 2 of substep 0, all of substep 1)
+      // after slot 4 (NB s' + i) - 7, two blocks before its first use
+      if constexpr (g % 4 == 1) {
+        constexpr int idx = (g + 7) / 4;
+        if constexpr (idx < 2 * NB) wo[idx % 5] = rd_w(st, idx / NB, idx % NB);
+      }
+      // substep 1's activation operands after slots 8, 10, 12, 14
+      if constexpr (g >= 8 && g < 16 && g % 2 == 0) xo[1][(g - 8) / 2] = rd_x(st, 1, (g - 8) / 2);
+      // loads [kLC, 18) of k-step kt+1 after slots 0, 2, 4, ..
+      if constexpr (decltype(LIVE1)::value && g % 2 == 0 && g / 2 < kLoads - kLC)
+        issue_load(kt + 1, st ^ 1, kLC + g / 2);
+      if constexpr (g == kSub) issue_warm(kt + kWarm);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    // k-step kt+1 is complete in LDS (only the warm-up load may still be in
+    // flight) and no wavefront reads stage st any more
+    wait_vmcnt<1>();
+    lds_barrier();
+    static_for<kBar, kSlots>([&](auto G) {
+      constexpr int g = decltype(G)::value;
+      constexpr int ib = (g - kSub) / 4, jb = g % 4;
+      mfma_f8<(ib < 4)>(acc_f8<ib, jb>(acc, accv), wo[(NB + ib) % 5], xo[1][jb], unit_scale);
+      // the first operands of k-step kt+1 (activations 0-3, weights 0 and 1
+      // of its substep 0) and loads [0, kLC) of k-step kt+2
+      constexpr int r = g - kBar;
+      if constexpr (r == 0 || r == 2 || r == 3 || r == 4) xo[0][r == 0 ? 0 : r - 1] = rd_x(st ^ 1, 0, r == 0 ? 0 : r - 1);
+      if constexpr (r == 1) wo[0] = rd_w(st ^ 1, 0, 0);
+      if constexpr (r == 5) wo[1] = rd_w(st ^ 1, 0, 1);
+      if constexpr (decltype(LIVE2)::value && r < kLC) issue_load(kt + 2, st, r);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  if (nk > 0) {
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) issue_load(0, 0, l);
+#pragma unroll
+    for (int l = 0; l < kLC; ++l) issue_load(1, 1, l);
+#pragma unroll
+    for (int kt = 1; kt < kWarm; ++kt) issue_warm(kt);
+    wait_vmcnt<kLC + kWarm - 1>();
+    lds_barrier();
+    xo[0][0] = rd_x(0, 0, 0);
+    wo[0] = rd_w(0, 0, 0);
+#pragma unroll
+    for (int j = 1; j < 4; ++j) xo[0][j] = rd_x(0, 0, j);
+    wo[1] = rd_w(0, 0, 1);
+    int kt = 0;
+    for (; kt < nk - 2; ++kt) step(kt, Live(), Live());
+    if (kt < nk - 1) step(kt++, Live(), Dead());
+    step(kt, Dead(), Dead());
+    wait_vmcnt<0>();
+    lds_barrier();
+  }
+
+  // MFMA writes, then VALU reads: 32 wait states before the blocks written
+  // last (weight block 4), more before the rest
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(accv[0]), "+v"(accv[1]), "+v"(accv[2]), "+v"(accv[3]));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm volatile("s_nop 1" : "+a"(acc[3 - i][0]), "+a"(acc[3 - i][1]), "+a"(acc[3 - i][2]), "+a"(acc[3 - i][3]));
+
+  // ---- epilogue, through a per-wavefront LDS region (as gemm16_kernel) ----
+  const size_t rbytes = static_cast<size_t>(M - m0) * args.ldc * sizeof(bf16_t);
+  const int nbytes = static_cast<int>(rbytes < 0x7fffffffu ? rbytes : 0x7fffffffu);
+  const size_t first = static_cast<size_t>(m0) * args.ldc;
+  const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(args.c + first, (short)0, nbytes, 0x00020000);
+  const int ldc_b = args.ldc * static_cast<int>(sizeof(bf16_t));
+  if constexpr (kSwi) {
+    // 128 x 80 outputs per wavefront in two halves of 64 tokens; staging rows
+    // of 88 bf16 (176 bytes)
+    constexpr int kStg = 88;
+    bf16_t* const stg = smem + wave_u * 64 * kStg;
+    const int col0 = tile_n * (BNT / 2) + wn * 80;
+    const float sg = args.scale_a[0] * args.scale_b[0][0];
+    const float su = args.scale_a[0] * args.scale_b[1][0];
+    float amx = 0.f;  // max |C| as stored
+    static_for<0, 2>([&](auto H) {
+      constexpr int h = decltype(H)::value;
+      static_for<0, 2 * NB>([&](auto Q) {
+        constexpr int jj = decltype(Q)::value / NB, ib = decltype(Q)::value % NB;
+        const f32x16& a = acc_f8<ib, 2 * h + jj>(acc, accv);
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = silu_mul(a[8 * gp + e] * sg, a[8 * gp + 4 + e] * su);
+          u32x2 pk;
+          pk[0] = pack_bf16x2(o[0], o[1]);
+          pk[1] = pack_bf16x2(o[2], o[3]);
+          amx = fmaxf(amx, abs_max4(pk));
+          *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + ib * 16 + gp * 8 + 4 * lhalf) = pk;
+        }
+      });
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < 10; ++it) {
+        const int c = it * 64 + lane, r = c / 10, qq = c - r * 10;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + qq * 8);
+        __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, (wm * 128 + h * 64 + r) * ldc_b + (col0 + qq * 8) * 2, 0, 0);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    });
+    if (args.amax) {  // uniform; past the four staging regions
+      const float v = workgroup_max(amx, reinterpret_cast<float*>(smem + 4 * 64 * kStg));
+      if (tid == 0) args.amax[unit] = v;
+    }
+  } else {
+    // 128 x 160 outputs per wavefront in two halves of 64 tokens; staging
+    // rows of 168 bf16 (336 bytes); a half's residual values loaded in the
+    // accumulator layout, all before its first add
+    constexpr int kStg = 168, kRowChunks = 20;
+    bf16_t* const stg = smem + wave_u * 64 * kStg;
+    const int col0 = tile_n * BNT + wn * (BNT / 2);
+    const __amdgpu_buffer_rsrc_t r_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        epi_residual(EPI) ? const_cast<bf16_t*>(args.r) + first : args.c + first, (short)0, nbytes, 0x00020000);
+    float sc[NB];  // FP8 scale of each weight block's columns (segments are multiples of 32 rows)
+#pragma unroll
+    for (int ib = 0; ib < NB; ++ib) sc[ib] = f8_scale(args, col0 + ib * 32);
+    static_for<0, 2>([&](auto H) {
+      constexpr int h = decltype(H)::value;
+      u32x2 rv[2][NB][4];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int ib = 0; ib < NB; ++ib)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq)
+            rv[jj][ib][gq] = epi_residual(EPI)
+                                 ? __builtin_amdgcn_raw_buffer_load_b64(
+                                       r_rsrc,
+                                       (wm * 128 + (2 * h + jj) * 32 + lrow) * ldc_b +
+                                           (col0 + ib * 32 + 8 * gq + 4 * lhalf) * 2,
+                                       0, 0)
+                                 : u32x2{0, 0};
+      static_for<0, 2 * NB>([&](auto Q) {
+        constexpr int jj = decltype(Q)::value / NB, ib = decltype(Q)::value % NB;
+        const f32x16& a = acc_f8<ib, 2 * h + jj>(acc, accv);
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = a[4 * gq + e] * sc[ib];
+          *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + ib * 32 + 8 * gq + 4 * lhalf) =
+              finish4<EPI>(o, u32x2{0, 0}, rv[jj][ib][gq]);
+        }
+      });
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int it = 0; it < kRowChunks; ++it) {
+        const int c = it * 64 + lane, r = c / kRowChunks, qq = c - r * kRowChunks;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + qq * 8);
+        __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, (wm * 128 + h * 64 + r) * ldc_b + (col0 + qq * 8) * 2, 0, 0);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    });
+  }
+}
+
 // The bf16 GEMMs on v_mfma_f32_16x16x32_bf16: the 256 x 320 tile (NB = 5)
 // and the 256 x 256 one (NB = 4). Same LDS ring, LDS-DMA loads, swizzle,
 // warm-up and tile order as gemm_f8_kernel; each wavefront owns 128 tokens x
@@ -1167,9 +1514,12 @@ template <int EPI, bool F8, int NB, bool SPLIT>
 hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
   // two stages of both operands, then the warm-up scratch (4 KB)
   constexpr size_t smem = static_cast<size_t>(2) * (BM + 64 * NB) * BK * sizeof(bf16_t) + 4096;
-  // bf16: gemm16_kernel (16x16x32 MFMAs); FP8: gemm_f8_kernel (256-wide)
+  // bf16: gemm16_kernel (16x16x32 MFMAs); FP8: gemm_f8w_kernel (320-wide)
+  // or gemm_f8_kernel (256-wide)
   const void* kernel;
-  if constexpr (F8)
+  if constexpr (F8 && NB == 5)
+    kernel = reinterpret_cast<const void*>(&gemm_f8w_kernel<EPI>);
+  else if constexpr (F8)
     kernel = reinterpret_cast<const void*>(&gemm_f8_kernel<EPI, SPLIT>);
   else
     kernel = reinterpret_cast<const void*>(&gemm16_kernel<EPI, NB, SPLIT>);
@@ -1184,7 +1534,9 @@ hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit, std::memory_order_release);
   }
-  if constexpr (F8)
+  if constexpr (F8 && NB == 5)
+    hipLaunchKernelGGL((gemm_f8w_kernel<EPI>), dim3(grid), dim3(kThreads), smem, stream, args);
+  else if constexpr (F8)
     hipLaunchKernelGGL((gemm_f8_kernel<EPI, SPLIT>), dim3(grid), dim3(kThreads), smem, stream, args);
   else
     hipLaunchKernelGGL((gemm16_kernel<EPI, NB, SPLIT>), dim3(grid), dim3(kThreads), smem, stream, args);
@@ -1311,19 +1663,25 @@ hipError_t launch_common(Epilogue epi, bool f8, const void* a, int lda, const fl
   args.ldb = ldb;
   args.ldc = ldc;
   args.tiles_m = (m + BM - 1) / BM;
-  if (f8) {
-    switch (epi) {
-      case Epilogue::kStore: return run<0, true, 4>(args, partial, partial_bytes, stream, amax_count);
-      case Epilogue::kResidual: return run<1, true, 4>(args, partial, partial_bytes, stream, amax_count);
-      case Epilogue::kSwiGLU: return run<2, true, 4>(args, partial, partial_bytes, stream, amax_count);
-      default: return hipErrorInvalidValue;  // the biased forms are bf16 only
-    }
-  }
-  // the decoder's bf16 linears take 320-wide tiles where those fill whole
-  // waves of the chip exactly
+  // the decoder's linears take 320-wide tiles where those fill whole waves
+  // of the chip exactly
   static const int cus = device_cus();
   const int wide_cols = epi == Epilogue::kSwiGLU ? 160 : 320;  // output columns of a 320-wide tile
   const bool wide = n % wide_cols == 0 && (args.tiles_m * (n / wide_cols)) % cus == 0;
+  if (f8) {
+    switch (epi) {
+      case Epilogue::kStore:
+        return wide ? run<0, true, 5>(args, partial, partial_bytes, stream, amax_count)
+                    : run<0, true, 4>(args, partial, partial_bytes, stream, amax_count);
+      case Epilogue::kResidual:
+        return wide ? run<1, true, 5>(args, partial, partial_bytes, stream, amax_count)
+                    : run<1, true, 4>(args, partial, partial_bytes, stream, amax_count);
+      case Epilogue::kSwiGLU:
+        return wide ? run<2, true, 5>(args, partial, partial_bytes, stream, amax_count)
+                    : run<2, true, 4>(args, partial, partial_bytes, stream, amax_count);
+      default: return hipErrorInvalidValue;  // the biased forms are bf16 only
+    }
+  }
   switch (epi) {
     case Epilogue::kStore:
       return wide ? run<0, false, 5>(args, partial, partial_bytes, stream, amax_count)
