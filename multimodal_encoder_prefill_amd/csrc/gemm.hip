@@ -20,8 +20,8 @@
 // linears where whole waves of tiles fill the chip, NB = 4 (256 x 256, with
 // partial n-tiles and k-splits) otherwise. The 320-wide tile reads 10% fewer
 // LDS bytes per MFMA and makes 4096 x 5120, 4096 x 10240 and 4096 x 2 x 25600
-// outputs exact multiples of 256 tiles. FP8 (gemm_f8_kernel): NB = 4 on
-// 32x32x64 MFMAs. The weight rows are the MFMA "A" operand and the
+// outputs exact multiples of 256 tiles. FP8 (gemm_f8w_kernel): the same two
+// widths on 32x32x64 MFMAs. The weight rows are the MFMA "A" operand and the
 // activation rows the "B" operand, so every lane ends up with 4 consecutive
 // output columns.
 //
@@ -294,424 +294,22 @@ __device__ __forceinline__ u32x2 finish4(float* o, const GemmArgs& args, int n, 
   return finish4<EPI>(o, bv, rv);
 }
 
-// The FP8 GEMM: operands are E4M3 bytes, a pipeline step covers 128 k
-// elements (the same 128-byte row pieces, LDS layout and loads as the bf16
-// kernel) in two substeps of v_mfma_scale_f32_32x32x64_f8f6f4 (unit block
-// scales), and the sums are multiplied by scale_a * scale_b before the
-// epilogue. 256 x 256 tile; each wavefront owns 128 tokens x 128 weight rows
-// as 4 x 4 blocks of 32 x 32 in the 256 AGPRs. (The 16x16x128 form saves
-// nothing here: with 32-byte operands per lane it moves as many register
-// bytes per flop as 32x32x64.)
-//
-// SPLIT: the units are k-ranges of split tiles whose raw fp32 sums go to
-// `partial` (a separate instantiation, so that each kernel has one epilogue:
-// with both in one kernel the compiler read every accumulator out ahead of
-// the branch and spilled them).
-template <int EPI, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 1) void gemm_f8_kernel(const GemmArgs args) {
-  static_assert(EPI <= static_cast<int>(Epilogue::kSwiGLU), "FP8 epilogues: store, residual, SwiGLU");
-  constexpr int NB = 4;                         // 32-row weight blocks per wavefront
-  constexpr int ES = 1;                         // bytes per element
-  constexpr int KSTEP = 128;                    // k elements per pipeline step
-  constexpr int BNT = 64 * NB;                  // n extent of the tile (weight rows)
-  constexpr int kATile = BM * BK;               // A operand, one stage (bf16 units)
-  constexpr int kBTile = BNT * BK;              // B operand, one stage
-  constexpr int kRowBytes = BK * 2;
-  constexpr int kChunks = BK / 8;               // 16-byte chunks per row
-  constexpr int kRowsPerBlk = 4096 / kRowBytes; // rows one load instruction of the 4 waves covers
-  constexpr int kBlksA = BM / kRowsPerBlk;      // load instructions for A per k-step
-  constexpr int kBlksB = BNT / kRowsPerBlk;     // ... and for B
-  constexpr int kLoads = kBlksA + kBlksB;
-  constexpr int kMf = 4 * NB;                   // MFMAs per substep
-  constexpr int kWarm = 4;  // warm-up distance in k-steps
-  static_assert(BK == 64, "pipeline shape");
-
-  extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
-  bf16_t* As = smem;              // [2][BM][BK]
-  bf16_t* Bs = smem + 2 * kATile; // [2][BNT][BK], then 4 KB of warm-up scratch
-
-  const int M = args.m, N = args.n, K = args.k;
-  const int lda = args.lda, ldb = args.ldb;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
-
-  // ---- work unit: contiguous per XCD, then tile and k-range ----
-  const int total = args.units;
-  const int bid = blockIdx.x;
-  const int xcd = bid % kXcds;
-  const int q = total / kXcds, rmd = total % kXcds;
-  const int unit = xcd * q + min(xcd, rmd) + bid / kXcds;
-  int tile_m, tile_n;
-  tile_coords(args.tile_begin + unit / args.ksplit, args.tiles_m, args.tiles_n, tile_m, tile_n);
-  const int m0 = tile_m * BM;
-  const int kt_begin = (unit % args.ksplit) * args.kt_per_split;
-  const int nk = min(kt_begin + args.kt_per_split, K / KSTEP) - kt_begin;  // k-steps of this unit
-
-  // ---- operand row blocks of kRowsPerBlk rows. A block i: rows
-  //      m0 + kRowsPerBlk i ..; B block i: see b_block_base. Rows past M or N
-  //      are never stored, so what is loaded for them does not matter. ----
-  // B row block i of the tile: address of its first row and the rows of its
-  // segment from there on (<= 0: the block is past N).
-  auto b_block_base = [&](int i, int& avail) -> const char* {
-    const void* base;
-    int v;
-    if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
-      // virtual B rows of the tile, in 32-row slots s: wave half s/4 covers
-      // output columns j0 + 64 (s/4) .., slots s%4 = 0,1 gate rows, 2,3 up rows
-      const int s = i * (kRowsPerBlk / 32);
-      const int j = tile_n * (BN / 2) + (s >> 2) * 64 + (s & 1) * 32;
-      base = ((s & 3) < 2) ? args.bptr[0] : args.bptr[1];
-      v = min(j, N - 1);
-      avail = N - j;
-    } else {
-      const int row = tile_n * BNT + kRowsPerBlk * i;
-      const int rr = min(row, N - 1);
-      if (rr < args.brows[0]) {
-        base = args.bptr[0];
-        v = rr;
-        avail = args.brows[0] - row;
-      } else if (rr < args.brows[0] + args.brows[1]) {
-        base = args.bptr[1];
-        v = rr - args.brows[0];
-        avail = args.brows[0] + args.brows[1] - row;
-      } else {
-        base = args.bptr[2];
-        v = rr - args.brows[0] - args.brows[1];
-        avail = N - row;
-      }
-    }
-    return static_cast<const char*>(base) + static_cast<size_t>(v) * ldb * ES;
-  };
-  // Accumulators: the 16 blocks through the MFMA builtin (the compiler keeps
-  // them in the 256 AGPRs).
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  // ---- global -> LDS: lane L of wave w fills 16 bytes at block row
-  //      w*(1024/kRowBytes) + L/kChunks, physical chunk L%kChunks, and so
-  //      fetches the logical chunk the swizzle puts there. ----
-  const int dma_row = wave * (1024 / kRowBytes) + lane / kChunks;
-  const int dma_chunk = ((lane % kChunks) ^ swz(dma_row)) * 16;
-  const int b_lane_row = dma_row;  // the lane's row relative to the address b_block_base returns
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // ---- L2 warm-up. The tiles running together on one XCD share operand
-  //      blocks (tile_coords: 8 m-tiles x 4 n-tiles), so without help the
-  //      first request for a k-step block misses the L2 for all of its sharers
-  //      at once. For the weight rows, which come from HBM, each tile
-  //      therefore loads its share of its B block (32 rows, chosen by
-  //      tile_m % 8) kWarm k-steps ahead into a scratch corner of LDS, one
-  //      8-row load per wavefront. (Activation rows are hits in the last-level
-  //      cache and gain nothing from this.) ----
-  bf16_t* const warm_dst = smem + 2 * kATile + 2 * kBTile + wave_u * 512;
-
-  // ---- addresses: global_load_lds_dwordx4 (a wavefront streams these 2.6x
-  //      as fast as buffer_load ... lds on gfx950, and with one wavefront per
-  //      SIMD the operand loads, not the MFMAs, set the pace). Per row block
-  //      i, the wave-uniform address of its first row and the lane's byte
-  //      offset from there, the lane's row clamped to the rows that exist:
-  //      rows past the end of A or of a B segment only feed outputs that are
-  //      never stored. ----
-  const char* a_ptr[kBlksA];
-  const char* b_ptr[kBlksB];
-  unsigned a_off[kBlksA], b_off[kBlksB];
-#pragma unroll
-  for (int i = 0; i < kBlksA; ++i) {
-    const int r = m0 + kRowsPerBlk * i;
-    a_ptr[i] = static_cast<const char*>(args.a) + static_cast<size_t>(min(r, M - 1)) * lda * ES;
-    a_off[i] = min(dma_row, max(M - r, 1) - 1) * lda * ES + dma_chunk;
-  }
-#pragma unroll
-  for (int i = 0; i < kBlksB; ++i) {
-    int avail;
-    b_ptr[i] = b_block_base(i, avail);
-    b_off[i] = min(b_lane_row, max(avail, 1) - 1) * ldb * ES + dma_chunk;
-  }
-  // the warm-up block (computed again: a runtime index into the arrays above
-  // would put them in scratch memory); its lane offsets need no swizzle
-  int warm_avail;
-  const char* const warm_ptr = b_block_base((tile_m & 7) * (32 / kRowsPerBlk), warm_avail);
-  const unsigned warm_off = min(b_lane_row, max(warm_avail, 1) - 1) * ldb * ES + (lane % kChunks) * 16;
-
-  // ---- LDS -> registers and MFMA: substep s of a k-step covers the row
-  //      bytes 64s..64s+63 (64 k); operands are double-buffered in two
-  //      register slots. A lane holds 32 bytes of its row, chunks 4s + 2
-  //      lhalf and the next one: any assignment of k to the operand bytes
-  //      gives the same sum as long as both operands use it. ----
-  const int lrow = lane & 31;
-  const int lhalf = lane >> 5;
-  const int lswz = swz(lrow);
-  const int a_base = (wm * 128 + lrow) * BK;  // activation rows (MFMA B operand)
-  const int b_base = (wn * 32 * NB + lrow) * BK;  // weight rows (MFMA A operand)
-  i32x8 wop8[2][4], xop8[2][4];
-  // the r-th operand of substep s of LDS stage `stage`, into register slot
-  // `slot`: w0 x0 w1 x1 ...; an operand is two 16-byte reads
-  constexpr int kReads = 8;
-  auto fetch_one = [&](int stage, int s, int slot, int r) {
-    const bf16_t* as = As + stage * kATile;
-    const bf16_t* bs = Bs + stage * kBTile;
-    const int i = r >> 1;
-    const int c0 = ((4 * s + 2 * lhalf) ^ lswz) << 3;
-    const int c1 = ((4 * s + 2 * lhalf + 1) ^ lswz) << 3;
-    const bf16_t* src = (r & 1) ? as + a_base + i * 32 * BK : bs + b_base + i * 32 * BK;
-    const u32x4 v0 = *reinterpret_cast<const u32x4*>(src + c0);
-    const u32x4 v1 = *reinterpret_cast<const u32x4*>(src + c1);
-    const i32x8 v = __builtin_bit_cast(i32x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-    if (r & 1)
-      xop8[slot][i] = v;
-    else
-      wop8[slot][i] = v;
-  };
-  // blocks in order of max(i, j), so the MFMAs that need the operands read
-  // last come last
-  auto mfma_one = [&](int slot, int q) {
-    // q-th block in that order: q = d*d + e for d = 0..3, e = 0..2d
-    const int d = q < 1 ? 0 : q < 4 ? 1 : q < 9 ? 2 : 3;
-    const int e = q - d * d;
-    const int i = e <= d ? e : d, j = e <= d ? d : 2 * d - e;
-    // E4M3 operands (format 0), block scales 127 (= 2^0)
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop8[slot][i], xop8[slot][j], acc[i][j], 0, 0, 0,
-                                                                127, 0, 127);
-  };
-  // Load number l of k-step kt (unit-relative), to LDS stage `stage`: below
-  // 2 kBlksA, operand l % 2 (0: A, 1: B) of row block l / 2; from there on, B
-  // row block l - kBlksA. The loop leaves out k-steps
-  // past the unit's range; where the prologue and the warm-up still issue
-  // one (so that the counts their waits assume hold), it loads the unit's
-  // last k-step again (a cache hit) into LDS that is not read.
-  auto koff = [&](int kt) { return static_cast<size_t>(kt_begin + min(kt, nk - 1)) * kRowBytes; };
-  auto issue_load = [&](int kt, int stage, int l) {
-    const bool isb = l >= 2 * kBlksA || (l & 1);
-    const int i = l >= 2 * kBlksA ? l - kBlksA : l >> 1;
-    bf16_t* dst = (isb ? Bs + stage * kBTile : As + stage * kATile) + wave_u * 512 + i * kRowsPerBlk * BK;
-    global_load_lds16((isb ? b_ptr[i] : a_ptr[i]) + koff(kt), isb ? b_off[i] : a_off[i], lds_addr(dst));
-  };
-  auto issue_warm = [&](int kt) { global_load_lds16(warm_ptr + koff(kt), warm_off, lds_addr(warm_dst)); };
-  auto issue_dma = [&](int kt, int stage) {
-#pragma unroll
-    for (int l = 0; l < kLoads; ++l) issue_load(kt, stage, l);
-  };
-  // the kMf MFMAs of a substep with loads [L0, L1) of k-step kt and the
-  // operands of substep fs of LDS stage fst (into register slot fslot) spread
-  // between them (L0, L1 compile-time: std::integral_constant; with LIVE
-  // false, k-step kt is past the unit's range and the loads are left out)
-  auto mfma_rl = [&](int slot, int kt, int stage, auto L0, auto L1, auto LIVE, int fst, int fs, int fslot) {
-    constexpr int l0 = decltype(L0)::value, n = decltype(LIVE)::value ? decltype(L1)::value - l0 : 0;
-#pragma unroll
-    for (int q = 0; q < kMf; ++q) {
-      mfma_one(slot, q);
-#pragma unroll
-      for (int r = 0; r < kReads; ++r)
-        if (r * (kMf * 3 / 4) / kReads == q) fetch_one(fst, fs, fslot, r);
-      if constexpr (n > 0) {
-#pragma unroll
-        for (int j = 0; j < n; ++j)
-          if (j * kMf / n == q) issue_load(kt, stage, l0 + j);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  using Live = std::true_type;
-  using Dead = std::false_type;
-
-  // The split-K output pointer is only read after the loop. Taking it into
-  // registers here completes its scalar load before the loop: a scalar load
-  // in flight at the loop entry makes every pass through the loop wait for
-  // all LDS reads (scalar loads return out of order, so the counter can only
-  // be waited to zero) before its first MFMA.
-  asm volatile("" ::"s"(args.partial));
-
-  // ---- pipeline over a two-stage LDS ring: two substeps per k-step. The
-  //      one workgroup barrier per k-step sits before substep 1, whose
-  //      operands are already in registers: its MFMAs cover the reads of the
-  //      next k-step's first operands. All loads of k-step kt+2 go out during
-  //      substep 1 of kt (one per MFMA), so a whole substep separates the
-  //      last of them from the wait that needs them. ----
-  if (nk > 0) {
-    issue_dma(0, 0);
-    issue_dma(1, 1);
-    wait_vmcnt<kLoads>();
-    lds_barrier();
-    for (int r = 0; r < kReads; ++r) fetch_one(0, 0, 0, r);
-    // one k-step; LIVE2: k-step kt+2 exists and is loaded
-    auto step = [&](int kt, auto LIVE2) {
-      const int st = kt & 1;
-      __builtin_amdgcn_sched_barrier(0);
-      issue_warm(kt + kWarm);
-      mfma_rl(0, kt, st, std::integral_constant<int, 0>(), std::integral_constant<int, 0>(), Dead(), st, 1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      // k-step kt+1 is complete in LDS and no wavefront reads stage st any more
-      wait_vmcnt<1>();
-      lds_barrier();
-      mfma_rl(1, kt + 2, st, std::integral_constant<int, 0>(), std::integral_constant<int, kLoads>(), LIVE2,
-              st ^ 1, 0, 0);
-    };
-    int kt = 0;
-    for (; kt < nk - 2; ++kt) step(kt, Live());
-    for (; kt < nk; ++kt) step(kt, Dead());
-    wait_vmcnt<0>();
-    lds_barrier();
-  }
-
-  // ---- split-K unit: raw accumulators to the unit's partial tile, laid out
-  //      [m_local][virtual n] so 4 consecutive n are one 16-byte store ----
-  if constexpr (SPLIT) {
-    float* dst = args.partial + static_cast<size_t>(unit) * BM * BNT;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ml = wm * 128 + j * 32 + lrow;
-#pragma unroll
-      for (int i = 0; i < NB; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
-          *reinterpret_cast<f32x4*>(dst + ml * BNT + wn * 32 * NB + i * 32 + 8 * g + 4 * lhalf) = v;
-        }
-    }
-    return;
-  }
-
-  // ---- epilogue: lane holds column m = lrow of each 32x32 block and rows
-  //      n = 8 g + 4 lhalf + e (e < 4) for the four groups g. Rows past M
-  //      need no branch: C and the residual are accessed through buffer
-  //      resources that end at row M, which drop those stores and read
-  //      zeros (those rows computed from copies of row M-1, so their values
-  //      are finite and never exceed a real row's in the SwiGLU maximum).
-  //      Column blocks past N (partial n-tiles) are
-  //      skipped by wave-uniform tests, their 16-byte chunks by a lane test
-  //      in the stores. Outputs leave through a per-wavefront LDS region
-  //      (the forms below). ----
-  const size_t rbytes = static_cast<size_t>(M - m0) * args.ldc * sizeof(bf16_t);
-  const int nbytes = static_cast<int>(rbytes < 0x7fffffffu ? rbytes : 0x7fffffffu);
-  const size_t first = static_cast<size_t>(m0) * args.ldc;
-  const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(args.c + first, (short)0, nbytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t r_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      epi_residual(EPI) ? const_cast<bf16_t*>(args.r) + first : args.c + first, (short)0, nbytes, 0x00020000);
-  float amx = 0.f;           // kSwiGLU: max |C| over this lane's outputs
-  float sg = 1.f, su = 1.f;  // SwiGLU: scales of the gate and up products
-  if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
-    sg = args.scale_a[0] * args.scale_b[0][0];
-    su = args.scale_a[0] * args.scale_b[1][0];
-  }
-  if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
-    // SwiGLU: gate block i pairs with up block i + 2, 64 outputs per row and
-    // wave, staged through the wave's LDS region (rows of 72 bf16 = 144
-    // bytes, 8 lanes per row segment). Blocks past N (a partial n-tile; N is
-    // a multiple of 32) are skipped, and so are their chunks in the stores.
-    constexpr int kStg = 72;
-    bf16_t* const stg = smem + wave_u * 128 * kStg;
-    const int col0 = tile_n * (BN / 2) + wn * 64;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (col0 + i * 32 >= N) continue;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = silu_mul(acc[i][j][4 * g + e] * sg, acc[i + 2][j][4 * g + e] * su);
-          u32x2 pk;
-          pk[0] = pack_bf16x2(o[0], o[1]);
-          pk[1] = pack_bf16x2(o[2], o[3]);
-          *reinterpret_cast<u32x2*>(stg + (j * 32 + lrow) * kStg + i * 32 + 8 * g + 4 * lhalf) = pk;
-          amx = fmaxf(amx, abs_max4(pk));
-        }
-      }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int it = 0; it < 128 * 8 / 64; ++it) {
-      const int c = it * 64 + lane, r = c >> 3, q = c & 7;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + q * 8);
-      const int off = (wm * 128 + r) * args.ldc * static_cast<int>(sizeof(bf16_t)) + (col0 + q * 8) * 2;
-      if (col0 + q * 8 < N) __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
-    }
-  } else {
-    // Store and residual forms: the wave's 128 x 128 outputs in two
-    // halves of 64 rows through its LDS region (rows of 136 bf16 = 272
-    // bytes, 16-byte aligned, each bank takes two rows of a write
-    // instruction), leaving as 16-byte chunks along the rows, 16
-    // consecutive lanes per row segment. A half's residual values are
-    // loaded in the accumulator layout, all before its first add (bringing
-    // them in through LDS as well measured no faster); a residual load past
-    // N reads other columns of the buffer, or zeros past its end, for an
-    // output that is not stored. Blocks past N (a partial n-tile) are
-    // skipped, and so are their chunks in the stores.
-    constexpr int kStg = 32 * NB + 8, kRowChunks = 4 * NB;
-    bf16_t* const stg = smem + wave_u * 64 * kStg;
-    const int col0 = tile_n * BNT + wn * 32 * NB;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x2 rv[2][NB][4];
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-            rv[jj][i][g] = epi_residual(EPI)
-                               ? __builtin_amdgcn_raw_buffer_load_b64(
-                                     r_rsrc,
-                                     (wm * 128 + (2 * h + jj) * 32 + lrow) * args.ldc * static_cast<int>(sizeof(bf16_t)) +
-                                         (col0 + i * 32 + 8 * g + 4 * lhalf) * 2,
-                                     0, 0)
-                               : u32x2{0, 0};
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          const int nb = col0 + i * 32;
-          if (nb >= N) continue;
-          const float sc = f8_scale(args, nb);
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float o[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = acc[i][2 * h + jj][4 * g + e] * sc;
-            *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + i * 32 + 8 * g + 4 * lhalf) =
-                finish4<EPI>(o, args, nb + 8 * g + 4 * lhalf, rv[jj][i][g]);
-          }
-        }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int it = 0; it < kRowChunks; ++it) {
-        const int c = it * 64 + lane, r = c / kRowChunks, q = c - r * kRowChunks;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + q * 8);
-        const int off = (wm * 128 + h * 64 + r) * args.ldc * static_cast<int>(sizeof(bf16_t)) + (col0 + q * 8) * 2;
-        if (col0 + q * 8 < N) __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, off, 0, 0);
-      }
-      // the reads above have returned before the next half overwrites the region
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
-  }
-  if constexpr (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
-    if (args.amax) {  // uniform; past the four staging regions (72 KB)
-      const float v = workgroup_max(amx, reinterpret_cast<float*>(smem + 4 * 128 * 72));
-      if (tid == 0) args.amax[unit] = v;
-    }
-  }
-}
-
-// The FP8 GEMM in 256 x 320 tiles, for the decoder linears where whole waves
-// of such tiles fill the chip (as the bf16 gemm16_kernel's NB = 5 form): each
-// wavefront owns 128 tokens x 160 weight rows as 4 x 5 blocks of
-// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales; 16 blocks in the 256
-// AGPRs, the fifth weight block's 4 in VGPRs). A pipeline step covers 128 k
-// in two substeps of 64 k, 20 MFMAs each. The operands do not fit
-// double-buffered (32 bytes per lane each, 64 VGPRs of accumulators), so
-// they stream as in gemm16_kernel: a substep's four activation operands stay
-// in registers through it, the weight operands pass through a ring of five,
-// each read two blocks (8 MFMAs) ahead, and the one barrier per k-step sits
-// 8 MFMAs before its end, after the last read of the stage.
+// The FP8 GEMMs: operands are E4M3 bytes in the same 128-byte LDS rows as
+// the bf16 kernels', a pipeline step covers 128 k in two substeps of 64 k on
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales), and the sums are
+// multiplied by scale_a * scale_b before the epilogue. NB = 5 (256 x 320)
+// for the decoder linears where whole waves of such tiles fill the chip (as
+// for bf16), NB = 4 (256 x 256, partial n-tiles and k-splits) otherwise:
+// each wavefront owns 128 tokens x 32 NB weight rows as 4 x NB blocks of
+// 32 x 32, 4 NB MFMAs per substep (16 blocks in the 256 AGPRs, the fifth
+// weight block's 4 in VGPRs). The operands do not fit double-buffered (32
+// bytes per lane each), so they stream as in gemm16_kernel: a substep's
+// four activation operands stay in registers through it, the weight
+// operands pass through a ring of NB, each read two blocks (8 MFMAs) ahead,
+// and the one barrier per k-step sits 8 MFMAs before its end, after the
+// last read of the stage. (The 16x16x128 FP8 form would save nothing: with
+// 32-byte operands per lane it moves as many register bytes per flop as
+// 32x32x64.)
 //
 // A lane reads 32 bytes of its row (row 32 blk + (lane & 31)): chunks
 // 4 s + 2 (lane >> 5) and the next one of substep s (any assignment of k to
@@ -721,16 +319,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8_kernel(const GemmArgs arg
 // groups of each 32-row weight block alternate gate and up rows of the same 8
 // output columns, so groups g and g + 1 of a lane are the two factors of the
 // same outputs.
-template <int EPI>
+//
+// SPLIT: the unit is one k-range of a split tile; the raw fp32 sums (before
+// the scales) go to args.partial, [m_local][virtual n], for
+// splitk_reduce_kernel. (A separate instantiation, so that each kernel has
+// one epilogue: with both in one kernel the compiler read every accumulator
+// out ahead of the branch and spilled them.)
+template <int EPI, int NB, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs args) {
   constexpr bool kSwi = EPI == static_cast<int>(Epilogue::kSwiGLU);
   static_assert(EPI <= static_cast<int>(Epilogue::kSwiGLU), "FP8 epilogues: store, residual, SwiGLU");
-  constexpr int NB = 5, BNT = 320;
+  static_assert(NB == 4 || NB == 5, "tile width");
+  constexpr int BNT = 64 * NB;
   constexpr int kATile = BM * BK, kBTile = BNT * BK;  // one stage, in bf16 units of the byte rows
   constexpr int kRowBytes = BK * 2, kChunks = BK / 8;
   constexpr int kRowsPerBlk = 4096 / kRowBytes;
   constexpr int kBlksA = BM / kRowsPerBlk, kBlksB = BNT / kRowsPerBlk;
-  constexpr int kLoads = kBlksA + kBlksB;  // 18
+  constexpr int kLoads = kBlksA + kBlksB;  // 16 or 18
   constexpr int kSub = 4 * NB;             // MFMAs per substep
   constexpr int kSlots = 2 * kSub;         // MFMAs per k-step
   constexpr int kBar = kSlots - 8;         // the barrier's slot
@@ -738,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs ar
   // over the first MFMAs of kt + 1, one per 2 MFMAs
   constexpr int kLC = 8;
   constexpr int kWarm = 4;
-  static_assert(BK == 64 && kLoads == 18 && 2 * (kLoads - kLC) <= kSub, "pipeline shape");
+  static_assert(BK == 64 && 2 * (kLoads - kLC) <= kSub, "pipeline shape");
 
   extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
   bf16_t* As = smem;
@@ -758,15 +363,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs ar
   const int q = total / kXcds, rmd = total % kXcds;
   const int unit = xcd * q + min(xcd, rmd) + bid / kXcds;
   int tile_m, tile_n;
-  tile_coords(args.tile_begin + unit, args.tiles_m, args.tiles_n, tile_m, tile_n);
+  // (whole-tile launches have ksplit 1: constants, not divisions)
+  const int ksplit = SPLIT ? args.ksplit : 1;
+  tile_coords(args.tile_begin + unit / ksplit, args.tiles_m, args.tiles_n, tile_m, tile_n);
   const int m0 = tile_m * BM;
-  const int nk = K / 128;  // k-steps
+  const int kt_begin = SPLIT ? (unit % ksplit) * args.kt_per_split : 0;
+  const int nk = SPLIT ? min(kt_begin + args.kt_per_split, K / 128) - kt_begin : K / 128;  // k-steps
 
   auto b_block_base = [&](int i, int& avail) -> const char* {
     const void* base;
     int v;
     if constexpr (kSwi) {
-      // block i: wave half i / 5, block i % 5 of it; the 8-row group of
+      // block i: wave half i / NB, block i % NB of it; the 8-row group of
       // wavefront w is gate rows for even w, up rows for odd w, output
       // columns j .. j+7
       const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -818,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs ar
   const char* const warm_ptr = b_block_base((tile_m & 7) * (32 / kRowsPerBlk), warm_avail);
   const unsigned warm_off = min(b_lane_row, max(warm_avail, 1) - 1) * ldb + (lane % kChunks) * 16;
 
-  auto koff = [&](int kt) { return static_cast<size_t>(min(kt, nk - 1)) * kRowBytes; };
+  auto koff = [&](int kt) { return static_cast<size_t>(kt_begin + min(kt, nk - 1)) * kRowBytes; };
   auto issue_load = [&](int kt, int stage, int l) {
     const bool isb = l >= 2 * kBlksA || (l & 1);
     const int i = l >= 2 * kBlksA ? l - kBlksA : l >> 1;
@@ -843,23 +451,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs ar
   auto rd_w = [&](int stage, int s, int ib) { return rd(Bs + stage * kBTile + w_base + ib * 32 * BK, s); };
 
   f32x16 acc[4][4];  // weight blocks 0-3 (AGPRs)
-  f32x16 accv[4];    // weight block 4 (VGPRs)
+  f32x16 accv[4];    // weight block 4 (VGPRs; NB = 5)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    if constexpr (NB == 5)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) accv[i][e] = 0.f;
+      for (int e = 0; e < 16; ++e) accv[i][e] = 0.f;
   }
   // the zeroing writes, then the first MFMA reads of the same registers
 #pragma unroll
   for (int i = 0; i < 4; ++i) asm volatile("s_nop 4" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]));
-  asm volatile("s_nop 4" : "+v"(accv[0]), "+v"(accv[1]), "+v"(accv[2]), "+v"(accv[3]));
+  if constexpr (NB == 5) asm volatile("s_nop 4" : "+v"(accv[0]), "+v"(accv[1]), "+v"(accv[2]), "+v"(accv[3]));
   const int unit_scale = 127;  // E8M0 block scale 2^0, in every lane
   i32x8 xo[2][4];  // activation operands of substeps 0 and 1
-  i32x8 wo[5];     // weight operands: the 10 of a k-step (5 s + ib) in a ring of five
+  i32x8 wo[NB];    // weight operands: the 2 NB of a k-step (NB s + ib) in a ring of NB
   using Live = std::true_type;
   using Dead = std::false_type;
 
@@ -869,12 +478,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs ar
     static_for<0, kBar>([&](auto G) {
       constexpr int g = decltype(G)::value;
       constexpr int s = g / kSub, ib = (g % kSub) / 4, jb = g % 4;
-      mfma_f8<(ib < 4)>(acc_f8<ib, jb>(acc, accv), wo[(NB * s + ib) % 5], xo[s][jb], unit_scale);
+      mfma_f8<(ib < 4)>(acc_f8<ib, jb>(acc, accv), wo[ib], xo[s][jb], unit_scale);
       // weight operand NB s' + i (i >= 2 of substep 0, all of substep 1)
       // after slot 4 (NB s' + i) - 7, two blocks before its first use
       if constexpr (g % 4 == 1) {
         constexpr int idx = (g + 7) / 4;
-        if constexpr (idx < 2 * NB) wo[idx % 5] = rd_w(st, idx / NB, idx % NB);
+        if constexpr (idx < 2 * NB) wo[idx % NB] = rd_w(st, idx / NB, idx % NB);
       }
       // substep 1's activation operands after slots 8, 10, 12, 14
       if constexpr (g >= 8 && g < 16 && g % 2 == 0) xo[1][(g - 8) / 2] = rd_x(st, 1, (g - 8) / 2);
@@ -891,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs ar
     static_for<kBar, kSlots>([&](auto G) {
       constexpr int g = decltype(G)::value;
       constexpr int ib = (g - kSub) / 4, jb = g % 4;
-      mfma_f8<(ib < 4)>(acc_f8<ib, jb>(acc, accv), wo[(NB + ib) % 5], xo[1][jb], unit_scale);
+      mfma_f8<(ib < 4)>(acc_f8<ib, jb>(acc, accv), wo[ib], xo[1][jb], unit_scale);
       // the first operands of k-step kt+1 (activations 0-3, weights 0 and 1
       // of its substep 0) and loads [0, kLC) of k-step kt+2
       constexpr int r = g - kBar;
@@ -926,10 +535,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs ar
   }
 
   // MFMA writes, then VALU reads: 32 wait states before the blocks written
-  // last (weight block 4), more before the rest
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(accv[0]), "+v"(accv[1]), "+v"(accv[2]), "+v"(accv[3]));
+  // last (the last weight block), more before the rest
+  if constexpr (NB == 5)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(accv[0]), "+v"(accv[1]), "+v"(accv[2]), "+v"(accv[3]));
+  else
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[3][0]), "+a"(acc[3][1]), "+a"(acc[3][2]), "+a"(acc[3][3]));
 #pragma unroll
   for (int i = 0; i < 4; ++i) asm volatile("s_nop 1" : "+a"(acc[3 - i][0]), "+a"(acc[3 - i][1]), "+a"(acc[3 - i][2]), "+a"(acc[3 - i][3]));
+
+  // ---- split-K unit: raw accumulators to the unit's partial tile ----
+  if constexpr (SPLIT) {
+    float* dst = args.partial + static_cast<size_t>(unit) * BM * BNT;
+    static_for<0, 4 * NB>([&](auto Q) {
+      constexpr int jb = decltype(Q)::value / NB, ib = decltype(Q)::value % NB;
+      const f32x16& a = acc_f8<ib, jb>(acc, accv);
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = a[4 * gq + e];
+        *reinterpret_cast<f32x4*>(dst + (wm * 128 + jb * 32 + lrow) * BNT + wn * (BNT / 2) + ib * 32 + 8 * gq +
+                                  4 * lhalf) = v;
+      }
+    });
+    return;
+  }
 
   // ---- epilogue, through a per-wavefront LDS region (as gemm16_kernel) ----
   const size_t rbytes = static_cast<size_t>(M - m0) * args.ldc * sizeof(bf16_t);
@@ -937,12 +567,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs ar
   const size_t first = static_cast<size_t>(m0) * args.ldc;
   const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(args.c + first, (short)0, nbytes, 0x00020000);
   const int ldc_b = args.ldc * static_cast<int>(sizeof(bf16_t));
+  // Weight blocks past N (a partial n-tile of the 256-wide form; N is a
+  // multiple of 32) are skipped by wave-uniform tests, their 16-byte chunks
+  // by a lane test in the stores.
   if constexpr (kSwi) {
-    // 128 x 80 outputs per wavefront in two halves of 64 tokens; staging rows
-    // of 88 bf16 (176 bytes)
-    constexpr int kStg = 88;
+    // 128 x 16 NB outputs per wavefront in two halves of 64 tokens; staging
+    // rows of 16 NB + 8 bf16 (144 or 176 bytes)
+    constexpr int kCols = 16 * NB, kStg = kCols + 8, kRowChunks = kCols / 8;
     bf16_t* const stg = smem + wave_u * 64 * kStg;
-    const int col0 = tile_n * (BNT / 2) + wn * 80;
+    const int col0 = tile_n * (BNT / 2) + wn * kCols;
     const float sg = args.scale_a[0] * args.scale_b[0][0];
     const float su = args.scale_a[0] * args.scale_b[1][0];
     float amx = 0.f;  // max |C| as stored
@@ -950,25 +583,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs ar
       constexpr int h = decltype(H)::value;
       static_for<0, 2 * NB>([&](auto Q) {
         constexpr int jj = decltype(Q)::value / NB, ib = decltype(Q)::value % NB;
-        const f32x16& a = acc_f8<ib, 2 * h + jj>(acc, accv);
+        if (NB == 5 || col0 + ib * 16 < N) {
+          const f32x16& a = acc_f8<ib, 2 * h + jj>(acc, accv);
 #pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-          float o[4];
+          for (int gp = 0; gp < 2; ++gp) {
+            float o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = silu_mul(a[8 * gp + e] * sg, a[8 * gp + 4 + e] * su);
-          u32x2 pk;
-          pk[0] = pack_bf16x2(o[0], o[1]);
-          pk[1] = pack_bf16x2(o[2], o[3]);
-          amx = fmaxf(amx, abs_max4(pk));
-          *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + ib * 16 + gp * 8 + 4 * lhalf) = pk;
+            for (int e = 0; e < 4; ++e) o[e] = silu_mul(a[8 * gp + e] * sg, a[8 * gp + 4 + e] * su);
+            u32x2 pk;
+            pk[0] = pack_bf16x2(o[0], o[1]);
+            pk[1] = pack_bf16x2(o[2], o[3]);
+            amx = fmaxf(amx, abs_max4(pk));
+            *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + ib * 16 + gp * 8 + 4 * lhalf) = pk;
+          }
         }
       });
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-      for (int it = 0; it < 10; ++it) {
-        const int c = it * 64 + lane, r = c / 10, qq = c - r * 10;
+      for (int it = 0; it < kRowChunks; ++it) {
+        const int c = it * 64 + lane, r = c / kRowChunks, qq = c - r * kRowChunks;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + qq * 8);
-        __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, (wm * 128 + h * 64 + r) * ldc_b + (col0 + qq * 8) * 2, 0, 0);
+        if (NB == 5 || col0 + qq * 8 < N)
+          __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, (wm * 128 + h * 64 + r) * ldc_b + (col0 + qq * 8) * 2, 0,
+                                                 0);
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     });
@@ -977,17 +614,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs ar
       if (tid == 0) args.amax[unit] = v;
     }
   } else {
-    // 128 x 160 outputs per wavefront in two halves of 64 tokens; staging
-    // rows of 168 bf16 (336 bytes); a half's residual values loaded in the
-    // accumulator layout, all before its first add
-    constexpr int kStg = 168, kRowChunks = 20;
+    // 128 x 32 NB outputs per wavefront in two halves of 64 tokens; staging
+    // rows of 32 NB + 8 bf16 (272 or 336 bytes); a half's residual values
+    // loaded in the accumulator layout, all before its first add (a load past
+    // N reads other columns of the buffer, or zeros past its end, for an
+    // output that is not stored)
+    constexpr int kCols = 32 * NB, kStg = kCols + 8, kRowChunks = kCols / 8;
     bf16_t* const stg = smem + wave_u * 64 * kStg;
     const int col0 = tile_n * BNT + wn * (BNT / 2);
     const __amdgpu_buffer_rsrc_t r_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         epi_residual(EPI) ? const_cast<bf16_t*>(args.r) + first : args.c + first, (short)0, nbytes, 0x00020000);
     float sc[NB];  // FP8 scale of each weight block's columns (segments are multiples of 32 rows)
 #pragma unroll
-    for (int ib = 0; ib < NB; ++ib) sc[ib] = f8_scale(args, col0 + ib * 32);
+    for (int ib = 0; ib < NB; ++ib) sc[ib] = NB == 5 || col0 + ib * 32 < N ? f8_scale(args, col0 + ib * 32) : 0.f;
     static_for<0, 2>([&](auto H) {
       constexpr int h = decltype(H)::value;
       u32x2 rv[2][NB][4];
@@ -1006,14 +645,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs ar
                                  : u32x2{0, 0};
       static_for<0, 2 * NB>([&](auto Q) {
         constexpr int jj = decltype(Q)::value / NB, ib = decltype(Q)::value % NB;
-        const f32x16& a = acc_f8<ib, 2 * h + jj>(acc, accv);
+        if (NB == 5 || col0 + ib * 32 < N) {
+          const f32x16& a = acc_f8<ib, 2 * h + jj>(acc, accv);
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          float o[4];
+          for (int gq = 0; gq < 4; ++gq) {
+            float o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = a[4 * gq + e] * sc[ib];
-          *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + ib * 32 + 8 * gq + 4 * lhalf) =
-              finish4<EPI>(o, u32x2{0, 0}, rv[jj][ib][gq]);
+            for (int e = 0; e < 4; ++e) o[e] = a[4 * gq + e] * sc[ib];
+            *reinterpret_cast<u32x2*>(stg + (jj * 32 + lrow) * kStg + ib * 32 + 8 * gq + 4 * lhalf) =
+                finish4<EPI>(o, u32x2{0, 0}, rv[jj][ib][gq]);
+          }
         }
       });
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -1021,7 +662,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs ar
       for (int it = 0; it < kRowChunks; ++it) {
         const int c = it * 64 + lane, r = c / kRowChunks, qq = c - r * kRowChunks;
         const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * kStg + qq * 8);
-        __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, (wm * 128 + h * 64 + r) * ldc_b + (col0 + qq * 8) * 2, 0, 0);
+        if (NB == 5 || col0 + qq * 8 < N)
+          __builtin_amdgcn_raw_buffer_store_b128(v, c_rsrc, (wm * 128 + h * 64 + r) * ldc_b + (col0 + qq * 8) * 2, 0,
+                                                 0);
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     });
@@ -1030,7 +673,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_f8w_kernel(const GemmArgs ar
 
 // The bf16 GEMMs on v_mfma_f32_16x16x32_bf16: the 256 x 320 tile (NB = 5)
 // and the 256 x 256 one (NB = 4). Same LDS ring, LDS-DMA loads, swizzle,
-// warm-up and tile order as gemm_f8_kernel; each wavefront owns 128 tokens x
+// warm-up and tile order as gemm_f8w_kernel; each wavefront owns 128 tokens x
 // 32 NB weight rows as 8 x WB blocks of 16 x 16 (WB = 2 NB). Per MFMA the
 // 16x16x32 form reads and writes a quarter of the accumulator registers of
 // the 32x32x16 form for half the products, so the register file moves 20%
@@ -1149,7 +792,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
     return static_cast<const char*>(base) + static_cast<size_t>(v) * ldb * 2;
   };
 
-  // ---- global -> LDS, as in gemm_f8_kernel ----
+  // ---- global -> LDS, as in gemm_f8w_kernel ----
   const int dma_row = wave * (1024 / kRowBytes) + lane / kChunks;
   const int dma_chunk = ((lane % kChunks) ^ swz(dma_row)) * 16;
   const int b_lane_row = kSwi ? lane / kChunks : dma_row;
@@ -1332,7 +975,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
   // ---- epilogue: outputs leave through a per-wavefront LDS region in two
   //      halves of 64 tokens, as 16-byte chunks along the rows. Rows past M:
   //      buffer resources that end at row M drop the stores and read zeros
-  //      (see gemm_f8_kernel). Weight blocks past N (a partial n-tile of the
+  //      (see gemm_f8w_kernel). Weight blocks past N (a partial n-tile of the
   //      256-wide form; N is a multiple of 32, so a 16-row block is wholly
   //      in or out) are skipped by wave-uniform tests, their 16-byte chunks by
   //      a lane test in the stores. ----
@@ -1436,8 +1079,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm16_kernel(const GemmArgs args
 // applies the epilogue. Block (t, y) of 64 NB threads handles rows 4y..4y+3
 // of split tile t; each thread 4 consecutive virtual columns. The SwiGLU
 // virtual columns follow the kernel that wrote them: gemm16_kernel (bf16)
-// pairs 16 gate and 16 up rows per 32-row block, gemm_f8_kernel block i
-// with block i + 2.
+// pairs 16 gate and 16 up rows per 32-row block, gemm_f8w_kernel (FP8)
+// alternates 8 gate and 8 up rows.
 template <int EPI, bool F8, int NB>
 __global__ __launch_bounds__(64 * NB) void splitk_reduce_kernel(const GemmArgs args) {
   constexpr int BNT = 64 * NB;
@@ -1469,19 +1112,18 @@ __global__ __launch_bounds__(64 * NB) void splitk_reduce_kernel(const GemmArgs a
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = silu_mul(sum[e], upsum[e]);
   } else if (EPI == static_cast<int>(Epilogue::kSwiGLU)) {
-    // virtual column vn: wave half vn/128, 32-wide slot (vn%128)/32; slots 0,1
-    // are gate columns whose up partner sits 64 virtual columns later
-    const int slot = (vn & 127) >> 5;
-    live = live && slot < 2;
-    const f32x4 up = *reinterpret_cast<const f32x4*>(src + (slot < 2 ? 64 : 0));
-    f32x4 upsum = up;
+    // virtual column vn: 32-row block vn / 32 (16 outputs each), 8-row group
+    // (vn % 32) / 8; even groups are gate columns whose up partner sits 8
+    // later
+    const int blk = vn >> 5, grp = (vn & 31) >> 3;
+    live = live && (grp & 1) == 0;
+    const int uo = (grp & 1) == 0 ? 8 : 0;
+    f32x4 upsum = *reinterpret_cast<const f32x4*>(src + uo);
     for (int sidx = 1; sidx < args.ksplit; ++sidx)
-      upsum += *reinterpret_cast<const f32x4*>(src + (slot < 2 ? 64 : 0) + static_cast<size_t>(sidx) * BM * BNT);
-    n = tile_n * (BN / 2) + (vn >> 7) * 64 + slot * 32 + (vn & 31);
-    if constexpr (F8) {
-      sum *= args.scale_a[0] * args.scale_b[0][0];
-      upsum *= args.scale_a[0] * args.scale_b[1][0];
-    }
+      upsum += *reinterpret_cast<const f32x4*>(src + uo + static_cast<size_t>(sidx) * BM * BNT);
+    n = tile_n * (BNT / 2) + blk * 16 + (grp >> 1) * 8 + (vn & 7);
+    sum *= args.scale_a[0] * args.scale_b[0][0];
+    upsum *= args.scale_a[0] * args.scale_b[1][0];
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[e] = silu_mul(sum[e], upsum[e]);
   } else {
@@ -1514,13 +1156,10 @@ template <int EPI, bool F8, int NB, bool SPLIT>
 hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
   // two stages of both operands, then the warm-up scratch (4 KB)
   constexpr size_t smem = static_cast<size_t>(2) * (BM + 64 * NB) * BK * sizeof(bf16_t) + 4096;
-  // bf16: gemm16_kernel (16x16x32 MFMAs); FP8: gemm_f8w_kernel (320-wide)
-  // or gemm_f8_kernel (256-wide)
+  // bf16: gemm16_kernel (16x16x32 MFMAs); FP8: gemm_f8w_kernel (32x32x64)
   const void* kernel;
-  if constexpr (F8 && NB == 5)
-    kernel = reinterpret_cast<const void*>(&gemm_f8w_kernel<EPI>);
-  else if constexpr (F8)
-    kernel = reinterpret_cast<const void*>(&gemm_f8_kernel<EPI, SPLIT>);
+  if constexpr (F8)
+    kernel = reinterpret_cast<const void*>(&gemm_f8w_kernel<EPI, NB, SPLIT>);
   else
     kernel = reinterpret_cast<const void*>(&gemm16_kernel<EPI, NB, SPLIT>);
   // the dynamic-LDS limit is raised once per device (bit d: done on device d)
@@ -1534,10 +1173,8 @@ hipError_t launch_epi(const GemmArgs& args, int grid, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set.fetch_or(bit, std::memory_order_release);
   }
-  if constexpr (F8 && NB == 5)
-    hipLaunchKernelGGL((gemm_f8w_kernel<EPI>), dim3(grid), dim3(kThreads), smem, stream, args);
-  else if constexpr (F8)
-    hipLaunchKernelGGL((gemm_f8_kernel<EPI, SPLIT>), dim3(grid), dim3(kThreads), smem, stream, args);
+  if constexpr (F8)
+    hipLaunchKernelGGL((gemm_f8w_kernel<EPI, NB, SPLIT>), dim3(grid), dim3(kThreads), smem, stream, args);
   else
     hipLaunchKernelGGL((gemm16_kernel<EPI, NB, SPLIT>), dim3(grid), dim3(kThreads), smem, stream, args);
   return hipGetLastError();

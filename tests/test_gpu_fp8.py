@@ -182,6 +182,28 @@ def test_linear_fp8_split_k(m, n, k, residual):
     assert r <= 2e-3 and mx <= 2.0 ** -6 * np.max(np.abs(f64(c_plain)))
 
 
+@pytest.mark.parametrize("m,n,k", [
+    (512, 1280, 4096),   # 20 tiles, all split along k
+    (300, 96, 1024),     # ragged m, partial n tile, split
+])
+def test_linear_swiglu_fp8_split_k(m, n, k):
+    print(f"swiglu_fp8 split-k m={m} n={n} k={k}", flush=True)
+    a, wgu = _codes((m, k), 15 + m), _codes((2 * n, k), 16 + n)
+    sa, sw = _scale(0.002), _scale(4e-4)
+    c = torch.empty((m, n), device=DEV, dtype=torch.bfloat16)
+    c_plain = torch.empty_like(c)
+    b.linear_swiglu_fp8(a, sa, wgu, sw, c, m, n, k, workspace=_gemm_ws())
+    b.linear_swiglu_fp8(a, sa, wgu, sw, c_plain, m, n, k)
+    torch.cuda.synchronize()
+    prod = (_decode(a) @ _decode(wgu).T) * (float(sa.item()) * float(sw.item()))
+    ref = oracle.silu(prod[:, :n]) * prod[:, n:]
+    r, mx = report("swiglu_fp8 split-k", f64(c), ref)
+    assert r <= 4e-3
+    assert mx <= 2.0 ** -7 * np.max(np.abs(ref))
+    r, mx = report("split vs unsplit", f64(c), f64(c_plain))
+    assert r <= 2e-3 and mx <= 2.0 ** -6 * np.max(np.abs(f64(c_plain)))
+
+
 def test_swiglu_fp8_full_size_sampled_rows():
     m, n, k = 4096, 25600, 5120
     a, wgu = _codes((m, k), 7), _codes((2 * n, k), 8)
