@@ -281,6 +281,26 @@ int32_t mhe_qk_norm_rope(const mhe_config* cfg, const void* qkv, const void* q_n
 int32_t mhe_attention(const void* q, const void* k, const void* vt, void* o, int32_t seq,
                       int32_t n_heads, int32_t n_kv_heads, int32_t head_dim, void* stream);
 
+/*
+ * The attention step as the decoder layer runs it (H3 encoder page,
+ * MiniMaxH3Qwen3VLTextAttention.forward from the q/k/v split to SDPA): the
+ * query heads are read raw from the q/k/v projection output and RMS-normalised
+ * (gain q_norm) and rotated as they are loaded, i.e. the q half of
+ * mhe_qk_norm_rope fused into mhe_attention, with the same arithmetic (fp32,
+ * one bf16 rounding of q) and the same outputs up to that rounding.
+ * qkv, q_norm, positions as for mhe_qk_norm_rope (only the q columns of qkv
+ * are read); k, vt in the layouts mhe_qk_norm_rope writes; o as for
+ * mhe_attention. workspace: mhe_qnorm_attention_workspace_bytes(cfg, seq)
+ * bytes, 256-byte aligned (the rotary cos/sin of every token and slot).
+ * Errors: MHE_ERR_NULL, MHE_ERR_SHAPE (config or seq), MHE_ERR_UNSUPPORTED
+ * (head_dim other than 64 / 128, or other than 1, 2, 4, 8 query heads per kv
+ * head), MHE_ERR_WORKSPACE; nothing is launched then.
+ */
+size_t mhe_qnorm_attention_workspace_bytes(const mhe_config* cfg, int32_t seq);
+int32_t mhe_qnorm_attention(const mhe_config* cfg, const void* qkv, const void* q_norm,
+                            const int32_t* positions, const void* k, const void* vt, void* o,
+                            int32_t seq, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- FP8 linears (online quantisation) ---------------------------------------
  *
  * H3 encoder page: the encoder accepts an FP8 quantisation config only for a

@@ -106,6 +106,8 @@ _SIGNATURES = {
     "mhe_qk_norm_rope": (_i32, [ctypes.POINTER(MheConfig), _vp, _vp, _vp, _vp, _i32, _vp, _vp,
                                 _vp, _vp]),
     "mhe_attention": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "mhe_qnorm_attention_workspace_bytes": (_sz, [ctypes.POINTER(MheConfig), _i32]),
+    "mhe_qnorm_attention": (_i32, [ctypes.POINTER(MheConfig), _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]),
     "mhe_trace_enable": (_i32, [ctypes.c_uint32]),
     "mhe_trace_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "mhe_rope_index": (_i32, [_vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _i32, _vp, _vp, _vp,
@@ -413,6 +415,16 @@ def qk_norm_rope(cfg, qkv, q_norm, k_norm, positions, seq, q_out, k_out, vt_out,
 def attention(q, k, vt, o, seq, n_heads, n_kv_heads, head_dim, stream=None):
     _check("mhe_attention", lib().mhe_attention(_ptr(q), _ptr(k), _ptr(vt), _ptr(o), seq,
                                                 n_heads, n_kv_heads, head_dim, _stream(stream)))
+
+
+def qnorm_attention_workspace_bytes(cfg, seq) -> int:
+    return int(lib().mhe_qnorm_attention_workspace_bytes(ctypes.byref(cfg), seq))
+
+
+def qnorm_attention(cfg, qkv, q_norm, positions, k, vt, o, seq, workspace, workspace_bytes, stream=None):
+    _check("mhe_qnorm_attention", lib().mhe_qnorm_attention(
+        ctypes.byref(cfg), _ptr(qkv), _ptr(q_norm), _ptr(positions), _ptr(k), _ptr(vt), _ptr(o), seq,
+        _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def trace_enable(steps) -> None:

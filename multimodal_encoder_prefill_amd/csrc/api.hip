@@ -96,7 +96,6 @@ struct Workspace {
   int ld_h, ld_o, ld_i;  // row strides of hn, ao, act
   bf16_t* hn;    // [S, H] with row stride ld_h
   bf16_t* qkv;   // [S, (Hq + 2 Hkv) D]
-  bf16_t* qn;    // [S, Hq, D]
   bf16_t* kn;    // [Hkv, Sp, D]
   bf16_t* vt;    // [Hkv, D, Sp]
   bf16_t* ao;    // [S, Hq D] with row stride ld_o
@@ -134,7 +133,6 @@ Workspace carve(const mhe_config& c, int seq, char* base, bool fp8 = false) {
   w.hn = reinterpret_cast<bf16_t*>(take(S * w.ld_h * 2));
   const size_t region_start = off;
   w.qkv = reinterpret_cast<bf16_t*>(take(S * (Hq + 2 * Hkv) * D * 2));
-  w.qn = reinterpret_cast<bf16_t*>(take(S * Hq * D * 2));
   w.kn = reinterpret_cast<bf16_t*>(take(Hkv * sp * D * 2));
   w.vt = reinterpret_cast<bf16_t*>(take(Hkv * D * sp * 2));
   w.ao = reinterpret_cast<bf16_t*>(take(S * w.ld_o * 2));
@@ -265,17 +263,17 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights& w, bf16_t* x, co
                                 ws.partial, ws.partial_bytes, st);
        })))
     return rc;
-  // q/k norm + rotary, K and V relayout
+  // k norm + rotary, K and V relayout; q norm + rotary inside the attention
   const mhe::RopeParams rp{Hq, Hkv, D, c.rms_eps, c.rope_theta,
                            {c.mrope_section[0], c.mrope_section[1], c.mrope_section[2]}};
-  if ((rc = traced(MHE_STEP_QK_ROPE, st, "q/k norm + rotary", [&] {
-         return mhe::launch_qk_norm_rope(rp, ws.qkv, static_cast<const bf16_t*>(w.q_norm),
-                                         static_cast<const bf16_t*>(w.k_norm), pos, seq, ws.qn, ws.kn,
-                                         ws.vt, st, ws.rope);
+  if ((rc = traced(MHE_STEP_QK_ROPE, st, "k norm + rotary", [&] {
+         return mhe::launch_k_norm_rope(rp, ws.qkv, static_cast<const bf16_t*>(w.k_norm), pos, seq, ws.kn,
+                                        ws.vt, st, ws.rope);
        })))
     return rc;
   if ((rc = traced(MHE_STEP_ATTENTION, st, "attention", [&] {
-         return mhe::launch_attention(ws.qn, ws.kn, ws.vt, ws.ao, ws.ld_o, seq, Hq, Hkv, D, st);
+         return mhe::launch_attention_qnorm(ws.qkv, qw + 2 * kvw, static_cast<const bf16_t*>(w.q_norm), ws.rope,
+                                            c.rms_eps, ws.kn, ws.vt, ws.ao, ws.ld_o, seq, Hq, Hkv, D, st);
        })))
     return rc;
   // O projection + residual, in place on x
@@ -348,14 +346,15 @@ int32_t run_layer(const mhe_config& c, const mhe_layer_weights_fp8& w, bf16_t* x
     return rc;
   const mhe::RopeParams rp{Hq, Hkv, D, c.rms_eps, c.rope_theta,
                            {c.mrope_section[0], c.mrope_section[1], c.mrope_section[2]}};
-  if ((rc = traced(MHE_STEP_QK_ROPE, st, "q/k norm + rotary", [&] {
-         return mhe::launch_qk_norm_rope(rp, ws.qkv, static_cast<const bf16_t*>(w.q_norm),
-                                         static_cast<const bf16_t*>(w.k_norm), pos, seq, ws.qn, ws.kn,
-                                         ws.vt, st, ws.rope);
+  if ((rc = traced(MHE_STEP_QK_ROPE, st, "k norm + rotary", [&] {
+         return mhe::launch_k_norm_rope(rp, ws.qkv, static_cast<const bf16_t*>(w.k_norm), pos, seq, ws.kn,
+                                        ws.vt, st, ws.rope);
        })))
     return rc;
   if ((rc = traced(MHE_STEP_ATTENTION, st, "attention", [&] {
-         return mhe::launch_attention(ws.qn, ws.kn, ws.vt, ws.ao, ws.ld_o, seq, Hq, Hkv, D, st, ws.amax);
+         return mhe::launch_attention_qnorm(ws.qkv, qkvw, static_cast<const bf16_t*>(w.q_norm), ws.rope,
+                                            c.rms_eps, ws.kn, ws.vt, ws.ao, ws.ld_o, seq, Hq, Hkv, D, st,
+                                            ws.amax);
        })))
     return rc;
   if ((rc = quantize_input(ws.ao, ws.ld_o, seq, qw, ws.ld8_o, 1, mhe::attention_amax_parts(seq, Hkv), ws, st)))
@@ -834,6 +833,34 @@ int32_t mhe_attention(const void* q, const void* k, const void* vt, void* o, int
                                          n_heads, n_kv_heads, head_dim,
                                          static_cast<hipStream_t>(stream)),
                    "attention");
+}
+
+size_t mhe_qnorm_attention_workspace_bytes(const mhe_config* cfg, int32_t seq) {
+  if (!cfg || seq <= 0 || cfg->head_dim <= 0) return 0;
+  return align_up(static_cast<size_t>(seq) * (cfg->head_dim / 2) * sizeof(float2));
+}
+
+int32_t mhe_qnorm_attention(const mhe_config* cfg, const void* qkv, const void* q_norm,
+                            const int32_t* positions, const void* k, const void* vt, void* o,
+                            int32_t seq, void* workspace, size_t workspace_bytes, void* stream) {
+  int32_t rc;
+  if ((rc = check_config(cfg))) return rc;
+  if ((rc = check_seq(seq))) return rc;
+  if (!qkv || !q_norm || !positions || !k || !vt || !o) return fail(MHE_ERR_NULL, "all buffers are required");
+  const int D = cfg->head_dim, Hq = cfg->n_heads, Hkv = cfg->n_kv_heads;
+  if (!mhe::attention_supported(Hq, Hkv, D))
+    return fail(MHE_ERR_UNSUPPORTED, "head_dim 64/128 and 1, 2, 4 or 8 query heads per kv head");
+  if ((rc = check_ws(workspace, workspace_bytes, mhe_qnorm_attention_workspace_bytes(cfg, seq)))) return rc;
+  const mhe::RopeParams rp{Hq, Hkv, D, cfg->rms_eps, cfg->rope_theta,
+                           {cfg->mrope_section[0], cfg->mrope_section[1], cfg->mrope_section[2]}};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float2* table = static_cast<float2*>(workspace);
+  if ((rc = hip_check(mhe::launch_rope_table(rp, positions, seq, table, st), "rotary table"))) return rc;
+  return hip_check(mhe::launch_attention_qnorm(static_cast<const bf16_t*>(qkv), (Hq + 2 * Hkv) * D,
+                                               static_cast<const bf16_t*>(q_norm), table, cfg->rms_eps,
+                                               static_cast<const bf16_t*>(k), static_cast<const bf16_t*>(vt),
+                                               static_cast<bf16_t*>(o), Hq * D, seq, Hq, Hkv, D, st),
+                   "attention with q norm + rotary");
 }
 
 // ---- token-level front end ----

@@ -25,6 +25,12 @@
 // own L2. Query blocks are issued longest-first (causal work grows with the
 // block index).
 //
+// In the decoder layer (QN) the query rows come straight from the q/k/v
+// projection's output and the kernel applies the per-head q RMSNorm and the
+// multimodal rotary itself as it loads them (the same arithmetic as
+// qk_norm_rope.hip: fp32, one bf16 rounding), so q never makes a round trip
+// through HBM between the two steps; K and V^T still come from that kernel.
+//
 // The same kernel serves the vision tower's attention (H3 encoder page,
 // MiniMaxH3Qwen3VLVisionAttention.forward): SEG replaces the causal mask by
 // "key in the query's frame" (a [seg_lo, seg_hi) token range per query), the
@@ -86,11 +92,17 @@ __device__ __forceinline__ void global_load_lds16(const char* base, unsigned off
 // DU: head dims actually used by the PV product (a multiple of 32, <= D),
 // DK: by the scores (a multiple of 16, <= DU); the layouts keep the padded D,
 // the MFMAs skip the columns past DU / DK (all zero).
-template <int D, int G, int HPW, int QW, bool SEG, int DU = D, int DK = DU>
+// QN: q holds the raw projection rows (row stride ldq), normalised with
+// q_gain [D] and eps and rotated with the cos/sin table rope [seq][D/2] here;
+// otherwise q is already normalised and rotated ([seq][n_heads][D], ldq =
+// n_heads * D) and q_gain / rope are unused.
+template <int D, int G, int HPW, int QW, bool SEG, bool QN, int DU = D, int DK = DU>
 __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ vt,
-    bf16_t* __restrict__ o, int ldo, int seq, int n_heads, int n_kv_heads, float scale_log2,
-    int dout, const PatchInfo* __restrict__ info, float* __restrict__ amax) {
+    const bf16_t* q, int ldq, const bf16_t* q_gain, const float2* rope, float eps,
+    const bf16_t* __restrict__ k,
+    const bf16_t* __restrict__ vt, bf16_t* __restrict__ o, int ldo, int seq, int n_heads,
+    int n_kv_heads, float scale_log2, int dout, const PatchInfo* __restrict__ info,
+    float* __restrict__ amax) {
   constexpr int HW = G / HPW;        // wavefronts per query block (heads of the group)
   constexpr int WAVES = HW * QW;
   constexpr int KCH = D / 8;          // 16-byte chunks per K row
@@ -103,6 +115,12 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
 
   __shared__ __attribute__((aligned(16))) bf16_t k_lds[2][KT * D];
   __shared__ __attribute__((aligned(16))) bf16_t v_lds[2][D * KT];
+  // QN: the cos/sin rows of the workgroup's QB queries ([QB][D/2] float2,
+  // the 16-byte chunks of row r XOR-swizzled by r % 16, so the 32 rows of a
+  // read spread over the banks) and the q gain, one copy for all wavefronts
+  constexpr int CS_CH = D / 4;   // 16-byte chunks per cos/sin row
+  __shared__ __attribute__((aligned(16))) float cs_lds[QN ? QB * D : 4];
+  __shared__ __attribute__((aligned(16))) bf16_t g_lds[QN ? D : 8];
 
   const int sp = seq_pad(seq);
   const int n_qb = (seq + QB * QW - 1) / (QB * QW);
@@ -117,19 +135,18 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
   const int lhalf = lane >> 5;
   const int qi = q0 + (wave / HW) * QB + lrow;
 
-  // ---- Q rows of the wavefront's heads as MFMA B operands, kept in registers ----
+  // ---- Q rows of the wavefront's heads as MFMA B operands, kept in registers:
+  //      lane (lrow, lhalf) holds dims 16 s + 8 lhalf + [0, 8) of query qi for
+  //      k-step s (queries past seq: zeros, set once the first K/V tile is
+  //      on its way) ----
   bf16x8 qreg[HPW][DS];
+  const int qs = min(qi, seq - 1);
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    const bf16_t* src = q + (static_cast<size_t>(min(qi, seq - 1)) * n_heads + h0 + hh) * D + lhalf * 8;
+    const bf16_t* src = q + static_cast<size_t>(qs) * ldq + (h0 + hh) * D + lhalf * 8;
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(src + s * 16);
-      if (qi >= seq) v = u32x4{0, 0, 0, 0};
-      qreg[hh][s] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int s = 0; s < DS; ++s) qreg[hh][s] = *reinterpret_cast<const bf16x8*>(src + s * 16);
   }
-
   const bf16_t* kg = k + static_cast<size_t>(g) * sp * D;
   const bf16_t* vg = vt + static_cast<size_t>(g) * D * sp;
   // key range of the workgroup: [0, last query] (causal) or the union of its
@@ -332,9 +349,88 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
 
   f32x16 sacc[HPW][KB];
   bf16x8 pop[HPW][PS];
+  if constexpr (QN) {
+    // the queries' cos/sin rows and the q gain, by LDS-DMA beside the first
+    // tile: lane L of load instruction n fills 16-byte chunk L % CS_CH of
+    // row (n WAVES + w) * (64 / CS_CH) + L / CS_CH with the logical chunk
+    // the swizzle puts there
+    static_assert(QW == 1 && DK == D && DS == D / 16, "the fused q norm: one query block, every head dim");
+    constexpr int ROWS_PER_INSTR = 64 / CS_CH;
+    constexpr int CS_INSTR = QB / ROWS_PER_INSTR;
+#pragma unroll
+    for (int n = 0; n * WAVES < CS_INSTR; ++n) {
+      const int ins = n * WAVES + wave_u;
+      if (ins < CS_INSTR) {
+        const int r = ins * ROWS_PER_INSTR + lane / CS_CH, ph = lane % CS_CH;
+        const int tok = min(q0 + r, seq - 1);
+        global_load_lds16(reinterpret_cast<const char*>(rope),
+                          static_cast<unsigned>(tok * (D / 2) * 8 + (ph ^ (r & 15)) * 16),
+                          lds_addr(&cs_lds[0] + ins * 256));
+      }
+    }
+    if (wave_u == WAVES - 1 && lane < D / 8)
+      global_load_lds16(reinterpret_cast<const char*>(q_gain), 0u + lane * 16, lds_addr(&g_lds[0]));
+  }
   issue_tile(t_first, 0);
+  // The q values pass through empty assembly here, after the tiles' load
+  // instructions, so that no arithmetic on them (and no wait for them) is
+  // scheduled ahead of those instructions.
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+    for (int s = 0; s < DS; ++s) asm volatile("" : "+v"(qreg[hh][s]));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  if constexpr (QN) {
+    // Per-head RMSNorm (gain q_gain, mean over the D dims: this lane's half
+    // plus lane ^ 32's) and rotate-half rotary: dims d and d + D/2 are k-steps
+    // s and s + DS/2 of the same lane, and their rotary slot j = d is the
+    // table entry 16 s + 8 lhalf + e of the query's row.
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        float x[8];
+        unpack8(__builtin_bit_cast(u32x4, qreg[hh][s]), x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+      }
+      ss += __shfl_xor(ss, 32, 64);
+      const float rinv = rsqrtf(ss / static_cast<float>(D) + eps);
+#pragma unroll
+      for (int s = 0; s < DS / 2; ++s) {
+        float xl[8], xh[8], gl[8], gh[8], ol[8], oh[8];
+        unpack8(__builtin_bit_cast(u32x4, qreg[hh][s]), xl);
+        unpack8(__builtin_bit_cast(u32x4, qreg[hh][s + DS / 2]), xh);
+        unpack8(*reinterpret_cast<const u32x4*>(&g_lds[s * 16 + lhalf * 8]), gl);
+        unpack8(*reinterpret_cast<const u32x4*>(&g_lds[(s + DS / 2) * 16 + lhalf * 8]), gh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // (cos, sin) of slots e = 2i, 2i + 1: logical chunk 8 s + 4 lhalf + i of row lrow
+          const f32x4 cs = *reinterpret_cast<const f32x4*>(
+              &cs_lds[lrow * D + ((8 * s + 4 * lhalf + i) ^ (lrow & 15)) * 4]);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int e = 2 * i + u;
+            const float c = cs[2 * u], sn = cs[2 * u + 1];
+            const float yl = xl[e] * rinv * gl[e], yh = xh[e] * rinv * gh[e];
+            // first half: y cos - y_partner sin; second half: y cos + y_partner sin
+            ol[e] = yl * c - yh * sn;
+            oh[e] = yh * c + yl * sn;
+          }
+        }
+        qreg[hh][s] = __builtin_bit_cast(bf16x8, pack8(ol));
+        qreg[hh][s + DS / 2] = __builtin_bit_cast(bf16x8, pack8(oh));
+      }
+    }
+  }
+  if (qi >= seq) {
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+      for (int s = 0; s < DS; ++s) qreg[hh][s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  }
 
   for (int ti = 0; ti < n_tiles; ++ti) {
     const int t = t_first + ti;
@@ -389,9 +485,10 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
   }
 }
 
-template <int D>
-hipError_t launch_d(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o, int ldo,
-                    int seq, int n_heads, int n_kv_heads, hipStream_t stream, float* amax) {
+template <int D, bool QN>
+hipError_t launch_d(const bf16_t* q, int ldq, const bf16_t* q_gain, const float2* rope, float eps,
+                    const bf16_t* k, const bf16_t* vt, bf16_t* o, int ldo, int seq, int n_heads,
+                    int n_kv_heads, hipStream_t stream, float* amax) {
   const int G = n_heads / n_kv_heads;
   const int n_qb = (seq + QB - 1) / QB;
   const dim3 grid(n_qb * n_kv_heads);
@@ -399,9 +496,9 @@ hipError_t launch_d(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* 
   switch (G) {
 #define MHE_ATTN_CASE(GG, HH)                                                                      \
   case GG:                                                                                         \
-    hipLaunchKernelGGL((attention_kernel<D, GG, HH, 1, false, D>), grid, dim3(64 * (GG / HH)),     \
-                       0, stream, q, k, vt, o, ldo, seq, n_heads, n_kv_heads, scale_log2, D,       \
-                       nullptr, amax);                                                             \
+    hipLaunchKernelGGL((attention_kernel<D, GG, HH, 1, false, QN, D>), grid, dim3(64 * (GG / HH)), \
+                       0, stream, q, ldq, q_gain, rope, eps, k, vt, o, ldo, seq, n_heads,          \
+                       n_kv_heads, scale_log2, D, nullptr, amax);                                  \
     break;
     MHE_ATTN_CASE(1, 1)
     MHE_ATTN_CASE(2, 1)
@@ -433,18 +530,21 @@ hipError_t launch_segment_attention(const bf16_t* q, const bf16_t* k, const bf16
     // 8 query blocks (two wavefronts per SIMD), score MFMAs over 80 dims, PV
     // over 96
     const int n_qb = (n + QB * 8 - 1) / (QB * 8);
-    hipLaunchKernelGGL((attention_kernel<128, 1, 1, 8, true, 96, 80>), dim3(n_qb * heads), dim3(64 * 8), 0,
-                       stream, q, k, vt, o, ldo, n, heads, heads, scale_log2, head_dim, info, nullptr);
+    hipLaunchKernelGGL((attention_kernel<128, 1, 1, 8, true, false, 96, 80>), dim3(n_qb * heads), dim3(64 * 8), 0,
+                       stream, q, heads * 128, nullptr, nullptr, 0.f, k, vt, o, ldo, n, heads, heads, scale_log2,
+                       head_dim, info, nullptr);
   } else if (head_dim <= 96) {
     // 8 query blocks (two wavefronts per SIMD), MFMAs over 96 dims
     const int n_qb = (n + QB * 8 - 1) / (QB * 8);
-    hipLaunchKernelGGL((attention_kernel<128, 1, 1, 8, true, 96>), dim3(n_qb * heads), dim3(64 * 8), 0,
-                       stream, q, k, vt, o, ldo, n, heads, heads, scale_log2, head_dim, info, nullptr);
+    hipLaunchKernelGGL((attention_kernel<128, 1, 1, 8, true, false, 96>), dim3(n_qb * heads), dim3(64 * 8), 0,
+                       stream, q, heads * 128, nullptr, nullptr, 0.f, k, vt, o, ldo, n, heads, heads, scale_log2,
+                       head_dim, info, nullptr);
   } else {
     // all 128 dims need more registers than two wavefronts per SIMD leave
     const int n_qb = (n + QB * 4 - 1) / (QB * 4);
-    hipLaunchKernelGGL((attention_kernel<128, 1, 1, 4, true, 128>), dim3(n_qb * heads), dim3(64 * 4), 0,
-                       stream, q, k, vt, o, ldo, n, heads, heads, scale_log2, head_dim, info, nullptr);
+    hipLaunchKernelGGL((attention_kernel<128, 1, 1, 4, true, false, 128>), dim3(n_qb * heads), dim3(64 * 4), 0,
+                       stream, q, heads * 128, nullptr, nullptr, 0.f, k, vt, o, ldo, n, heads, heads, scale_log2,
+                       head_dim, info, nullptr);
   }
   return hipGetLastError();
 }
@@ -456,8 +556,24 @@ hipError_t launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* vt, 
                             hipStream_t stream, float* amax) {
   if (seq <= 0) return hipSuccess;
   if (ldo < n_heads * head_dim || ldo % 4 != 0) return hipErrorInvalidValue;
-  if (head_dim == 128) return launch_d<128>(q, k, vt, o, ldo, seq, n_heads, n_kv_heads, stream, amax);
-  if (head_dim == 64) return launch_d<64>(q, k, vt, o, ldo, seq, n_heads, n_kv_heads, stream, amax);
+  const int ldq = n_heads * head_dim;
+  if (head_dim == 128)
+    return launch_d<128, false>(q, ldq, nullptr, nullptr, 0.f, k, vt, o, ldo, seq, n_heads, n_kv_heads, stream, amax);
+  if (head_dim == 64)
+    return launch_d<64, false>(q, ldq, nullptr, nullptr, 0.f, k, vt, o, ldo, seq, n_heads, n_kv_heads, stream, amax);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attention_qnorm(const bf16_t* q_raw, int ldq, const bf16_t* q_gain, const float2* rope,
+                                  float eps, const bf16_t* k, const bf16_t* vt, bf16_t* o, int ldo, int seq,
+                                  int n_heads, int n_kv_heads, int head_dim, hipStream_t stream, float* amax) {
+  if (seq <= 0) return hipSuccess;
+  if (ldo < n_heads * head_dim || ldo % 4 != 0 || ldq < n_heads * head_dim || ldq % 8 != 0)
+    return hipErrorInvalidValue;
+  if (head_dim == 128)
+    return launch_d<128, true>(q_raw, ldq, q_gain, rope, eps, k, vt, o, ldo, seq, n_heads, n_kv_heads, stream, amax);
+  if (head_dim == 64)
+    return launch_d<64, true>(q_raw, ldq, q_gain, rope, eps, k, vt, o, ldo, seq, n_heads, n_kv_heads, stream, amax);
   return hipErrorInvalidValue;
 }
 

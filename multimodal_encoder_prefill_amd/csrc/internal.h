@@ -112,6 +112,11 @@ hipError_t launch_qk_norm_rope(const RopeParams& p, const bf16_t* qkv, const bf1
                                const bf16_t* k_norm, const int32_t* positions, int seq,
                                bf16_t* q_out, bf16_t* k_out, bf16_t* vt_out, hipStream_t stream,
                                const float2* table = nullptr);
+// The k heads and the V relayout only (the decoder layer: q is normalised and
+// rotated by launch_attention_qnorm); k_out and vt_out as above.
+hipError_t launch_k_norm_rope(const RopeParams& p, const bf16_t* qkv, const bf16_t* k_norm,
+                              const int32_t* positions, int seq, bf16_t* k_out, bf16_t* vt_out,
+                              hipStream_t stream, const float2* table);
 
 // attention.hip
 bool attention_supported(int n_heads, int n_kv_heads, int head_dim);
@@ -123,6 +128,14 @@ int attention_amax_parts(int seq, int n_kv_heads);
 hipError_t launch_attention(const bf16_t* q, const bf16_t* k, const bf16_t* vt, bf16_t* o,
                             int ldo, int seq, int n_heads, int n_kv_heads, int head_dim,
                             hipStream_t stream, float* amax = nullptr);
+// The same attention with q taken raw from the q/k/v projection output
+// (q_raw rows ldq elements apart, q heads first) and normalised (gain q_gain
+// [head_dim], eps) and rotated (cos/sin table rope from launch_rope_table) as
+// it is loaded: the q half of launch_qk_norm_rope fused into the attention.
+hipError_t launch_attention_qnorm(const bf16_t* q_raw, int ldq, const bf16_t* q_gain, const float2* rope,
+                                  float eps, const bf16_t* k, const bf16_t* vt, bf16_t* o, int ldo, int seq,
+                                  int n_heads, int n_kv_heads, int head_dim, hipStream_t stream,
+                                  float* amax = nullptr);
 
 // deepstack.hip
 // Ascending list idx[0, n_vis) of the tokens whose byte in mask is set;

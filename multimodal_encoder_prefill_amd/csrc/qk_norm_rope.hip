@@ -10,6 +10,9 @@
 // fp32 (inverse frequency and position product as on the page) and cos/sin
 // are kept in fp32; each output is rounded to bf16 once.
 //
+// A launch covers the q and k heads, or (in the decoder layer, where the
+// attention kernel normalises and rotates q as it loads it) the k heads only.
+//
 // The kernel also writes K as [kv_head][seq_pad][D] and V transposed as
 // [kv_head][D][seq_pad] with tokens permuted inside every aligned group of 16
 // (0 1 2 3 8 9 10 11 4 5 6 7 12 13 14 15), which is the order in which one
@@ -95,8 +98,8 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ q_gain,
     const bf16_t* __restrict__ k_gain, const int32_t* __restrict__ pos,
     const float2* __restrict__ table, int seq, int seq_pad, int n_heads, int n_kv_heads, float eps,
-    float theta, int sec1, int sec2, bf16_t* __restrict__ q_out, bf16_t* __restrict__ k_out,
-    bf16_t* __restrict__ vt_out) {
+    float theta, int sec1, int sec2, int first_head, bf16_t* __restrict__ q_out,
+    bf16_t* __restrict__ k_out, bf16_t* __restrict__ vt_out) {
   constexpr int HALF = D / 2;
   const int s0 = blockIdx.x * kTok;
   const int width = (n_heads + 2 * n_kv_heads) * D;
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void qk_norm_rope_kernel(
   const int j0 = (chunk % (LPR / 2)) * 8;   // rotary slot of this lane's first element
   const int s = s0 + rg / SPLIT;
   const int hp = (rg % SPLIT) * HPR;        // first head of the group, within the block
-  const int h_first = (blockIdx.y - 1) * kHeadsPerBlock;
+  const int h_first = first_head + (blockIdx.y - 1) * kHeadsPerBlock;
   const int h_count = min(kHeadsPerBlock, n_heads + n_kv_heads - h_first);
   u32x4 raw[HPR];
 #pragma unroll
@@ -230,18 +233,21 @@ hipError_t launch_rope_table(const RopeParams& p, const int32_t* positions, int 
   return hipGetLastError();
 }
 
-hipError_t launch_qk_norm_rope(const RopeParams& p, const bf16_t* qkv, const bf16_t* q_norm,
-                               const bf16_t* k_norm, const int32_t* positions, int seq,
-                               bf16_t* q_out, bf16_t* k_out, bf16_t* vt_out, hipStream_t stream,
-                               const float2* table) {
+namespace {
+
+// Heads [first_head, n_heads + n_kv_heads) of every token plus the V relayout.
+hipError_t launch_heads(const RopeParams& p, const bf16_t* qkv, const bf16_t* q_norm,
+                        const bf16_t* k_norm, const int32_t* positions, int seq, int first_head,
+                        bf16_t* q_out, bf16_t* k_out, bf16_t* vt_out, hipStream_t stream,
+                        const float2* table) {
   if (seq <= 0) return hipSuccess;
   const int sp = seq_pad(seq);
-  const int n_chunks = (p.n_heads + p.n_kv_heads + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  const int n_chunks = (p.n_heads + p.n_kv_heads - first_head + kHeadsPerBlock - 1) / kHeadsPerBlock;
   dim3 grid(sp / kTok, n_chunks + 1);
 #define MHE_QK_LAUNCH(DD, TT)                                                                        \
   hipLaunchKernelGGL((qk_norm_rope_kernel<DD, TT>), grid, dim3(kThreads), 0, stream, qkv, q_norm,   \
                      k_norm, positions, table, seq, sp, p.n_heads, p.n_kv_heads, p.eps, p.theta,   \
-                     p.section[1], p.section[2], q_out, k_out, vt_out)
+                     p.section[1], p.section[2], first_head, q_out, k_out, vt_out)
   if (p.head_dim == 128) {
     if (table) MHE_QK_LAUNCH(128, true);
     else MHE_QK_LAUNCH(128, false);
@@ -253,6 +259,23 @@ hipError_t launch_qk_norm_rope(const RopeParams& p, const bf16_t* qkv, const bf1
   }
 #undef MHE_QK_LAUNCH
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_qk_norm_rope(const RopeParams& p, const bf16_t* qkv, const bf16_t* q_norm,
+                               const bf16_t* k_norm, const int32_t* positions, int seq,
+                               bf16_t* q_out, bf16_t* k_out, bf16_t* vt_out, hipStream_t stream,
+                               const float2* table) {
+  return launch_heads(p, qkv, q_norm, k_norm, positions, seq, 0, q_out, k_out, vt_out, stream, table);
+}
+
+hipError_t launch_k_norm_rope(const RopeParams& p, const bf16_t* qkv, const bf16_t* k_norm,
+                              const int32_t* positions, int seq, bf16_t* k_out, bf16_t* vt_out,
+                              hipStream_t stream, const float2* table) {
+  // no q head is visited, so q_norm and q_out are never read or written
+  return launch_heads(p, qkv, k_norm, k_norm, positions, seq, p.n_heads, nullptr, k_out, vt_out, stream,
+                      table);
 }
 
 }  // namespace mhe

@@ -31,9 +31,10 @@ def test_workspace_bytes_scales_and_validates():
     w1 = b.workspace_bytes(cfg, 512)
     w2 = b.workspace_bytes(cfg, 4096)
     assert w2 - part > 7 * (w1 - part)
-    # hidden + max(attention buffers, MLP activation) + index list, 256-byte aligned pieces
+    # hidden + max(attention buffers: q|k|v, K, V^T, attention output; MLP
+    # activation) + index list, 256-byte aligned pieces
     S = 4096
-    attn = S * 10240 * 2 + S * 8192 * 2 + 2 * 8 * 4096 * 128 * 2 + S * 8192 * 2
+    attn = S * 10240 * 2 + 2 * 8 * 4096 * 128 * 2 + S * 8192 * 2
     assert w2 >= S * 5120 * 2 + max(attn, S * 25600 * 2) + S * 4 + part
     with pytest.raises(b.MheError):
         b.workspace_bytes(cfg, 0)
@@ -139,6 +140,24 @@ def test_fp8_entry_points_reject_before_launch():
     rc = lib.mhe_layer_forward_fp8(ctypes.byref(tiny), ctypes.byref(t), 0x2000, 0x3000, 64, 0x10000,
                                    1 << 40, None)
     assert rc == 1 and "s_down" in lib.mhe_last_error().decode()
+
+
+def test_qnorm_attention_rejects_before_launch():
+    lib = b.lib()
+    d = 0x100000
+    cfg = b.config_from_dims(synth.FULL)
+    need = b.qnorm_attention_workspace_bytes(cfg, 64)
+    assert need >= 64 * 64 * 8                    # cos/sin of 64 slots per token
+    call = lambda c=cfg, **o: lib.mhe_qnorm_attention(
+        ctypes.byref(c), o.get("qkv", d), d, d, d, d, d, o.get("seq", 64), o.get("ws", 0x10000),
+        o.get("ws_bytes", need), None)
+    assert call(qkv=None) == 1
+    assert call(seq=0) == 2
+    assert call(ws_bytes=need - 1) == 5
+    assert call(ws=0x10010) == 5                  # misaligned
+    bad = b.config_from_dims(synth.FULL)
+    bad.n_heads = 96                              # 12 query heads per kv head
+    assert call(bad) == 4
 
 
 def test_vision_attention_rejects_before_launch():

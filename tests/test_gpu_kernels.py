@@ -233,6 +233,7 @@ def _qk_case(dims, seq, positions, seed):
     q_ref = oracle.apply_rope(oracle.rms_norm(x[:, :qw].reshape(seq, -1, D), f64(qn), dims.rms_eps), cos, sin)
     k_ref = oracle.apply_rope(oracle.rms_norm(x[:, qw:qw + kvw].reshape(seq, -1, D), f64(kn), dims.rms_eps), cos, sin)
     v_ref = x[:, qw + kvw:].reshape(seq, -1, D)
+    _qk_case.inputs = dict(qkv=qkv, qn=qn, pos=pos, cfg=cfg)
     return q_out, k_out, vt_out, q_ref, k_ref, v_ref, sp
 
 
@@ -359,6 +360,54 @@ def test_attention_causal_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(o1[:cut], o2[:cut])
     assert not torch.equal(o1[cut:], o2[cut:])
+
+
+# ------------------------------------------------------------------ attention, q norm + rotary fused
+
+def _qnorm_attention_case(dims, seq, positions, seed, rows=None):
+    """The decoder layer's form of the attention step (q read raw from the
+    q/k/v projection output, normalised and rotated in the attention kernel)
+    next to the two-step chain, and the oracle's q/k norm, rotary and causal
+    GQA attention on the same q/k/v rows."""
+    q_out, k_out, vt_out, q_ref, k_ref, v_ref, _ = _qk_case(dims, seq, positions, seed)
+    inp = _qk_case.inputs
+    D, hq, hkv = dims.head_dim, dims.n_heads, dims.n_kv_heads
+    nbytes = b.qnorm_attention_workspace_bytes(inp["cfg"], seq)
+    ws = torch.empty(nbytes, device=DEV, dtype=torch.uint8)
+    o = torch.full((seq, hq * D), 7.0, device=DEV, dtype=torch.bfloat16)
+    b.qnorm_attention(inp["cfg"], inp["qkv"], inp["qn"], inp["pos"], k_out, vt_out, o, seq, ws, nbytes)
+    o_chain = torch.empty_like(o)
+    b.attention(q_out, k_out, vt_out, o_chain, seq, hq, hkv, D)
+    torch.cuda.synchronize()
+    r = np.arange(seq) if rows is None else rows
+    ref = oracle.causal_gqa_attention(q_ref, k_ref, v_ref, rows=rows).reshape(len(r), hq * D)
+    return f64(o)[r], f64(o_chain)[r], ref
+
+
+@pytest.mark.parametrize("key,seq", [("tiny", 64), ("tiny", 77), ("full", 100), ("full", 700)])
+def test_qnorm_attention(key, seq):
+    print(f"qnorm_attention {key} seq={seq}", flush=True)
+    dims = synth.TINY if key == "tiny" else synth.FULL
+    positions = synth.random_positions(seq, 3000, seed=seq + 5)
+    got, chain, ref = _qnorm_attention_case(dims, seq, positions, 500 + seq)
+    r, _, w = report_rows("qnorm attention", got, ref, dims.head_dim)
+    assert r <= 8e-3 and w <= ROW_BAR
+    # the two-step chain rounds the same q once too; only the order of the
+    # q row's sum of squares differs
+    assert report("qnorm attention vs chain", got, chain)[0] <= 4e-3
+
+
+def test_qnorm_attention_workload_sampled_rows():
+    """4096 tokens, 64/8 heads of 128, the image workload's positions, rows
+    sampled over the sequence and at the image block's edges."""
+    wl = synth.WORKLOADS["image_s4096_l50"]
+    vis = np.flatnonzero(synth.visual_mask(wl))
+    rows = np.unique(np.array([0, 1, 63, 64, vis[0] - 1, vis[0], vis[0] + 64, vis[-1], vis[-1] + 1,
+                               3000, wl.seq - 1]))
+    got, chain, ref = _qnorm_attention_case(wl.dims, wl.seq, synth.positions(wl), 95, rows)
+    r, _, w = report_rows("qnorm attention image sampled", got, ref, wl.dims.head_dim)
+    assert r <= 8e-3 and w <= ROW_BAR
+    assert report("qnorm attention image vs chain", got, chain)[0] <= 4e-3
 
 
 # ------------------------------------------------------------------ DeepStack
