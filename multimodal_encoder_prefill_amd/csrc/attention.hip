@@ -257,15 +257,25 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[hh][kb][e] = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int s = 0; s < DS; ++s) {
 #pragma unroll
-      for (int s = 0; s < DS; ++s) {
+      for (int kb = 0; kb < KB; ++kb) {
         const bf16x8 kop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
             reinterpret_cast<const char*>(kl) + kb * 32 * K_ROW_BYTES + k_off[s]));
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh)
           sacc[hh][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qreg[hh][s], sacc[hh][kb], 0, 0, 0);
       }
+    }
+    if constexpr (HPW == 1) {
+      // keep eight K reads in flight ahead of the score MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < KB * DS - 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
   };
   // softmax: online softmax of tile t per head. Scores stay raw; the running
