@@ -355,6 +355,17 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
           oacc[hh][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pop[hh][s], oacc[hh][b], 0, 0, 0);
       }
     }
+    if constexpr (HPW == 1) {
+      // eight V reads in flight ahead of the PV MFMAs as well (the
+      // exponentials are left to the compiler's placement)
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < DB * PS - 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
   };
 
   f32x16 sacc[HPW][KB];
