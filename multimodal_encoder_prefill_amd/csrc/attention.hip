@@ -61,6 +61,18 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
   return r;
 }
 
+// x combined with its value in lane ^ 32 (v_permlane32_swap: a VALU lane
+// exchange, no LDS round trip as with a lane permute); both orders give the
+// same bits, so every lane holds the same result
+__device__ __forceinline__ float max_lane32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_lane32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // s + x.lo + x.hi for a pair of bf16 (v_dot2_f32_bf16 against (1, 1))
 __device__ __forceinline__ float add_pair(uint32_t x, float s) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, 0x3f803f80u),
@@ -311,7 +323,7 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
           m1 = max3(m1, sacc[hh][kb][e + 2], sacc[hh][kb][e + 3]);
         }
       float tmax = fmaxf(m0, m1);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * scale_log2;
+      tmax = max_lane32(tmax) * scale_log2;
       float alpha = 1.f;
       if (tmax > m_run[hh] + 8.f) {
         alpha = __builtin_amdgcn_exp2f(m_run[hh] - tmax);  // 0 on the first tile
@@ -417,7 +429,7 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
       }
-      ss += __shfl_xor(ss, 32, 64);
+      ss = sum_lane32(ss);
       const float rinv = rsqrtf(ss / static_cast<float>(D) + eps);
 #pragma unroll
       for (int s = 0; s < DS / 2; ++s) {
@@ -469,7 +481,7 @@ __global__ __launch_bounds__(64 * (G / HPW) * QW) void attention_kernel(
   float amx = 0.f;  // max |o| as stored (amax != NULL: FP8 quantisation of o)
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    const float l_tot = l_run[hh] + __shfl_xor(l_run[hh], 32, 64);
+    const float l_tot = sum_lane32(l_run[hh]);
     if (qi < seq) {
       const float inv = 1.f / l_tot;
       bf16_t* dst = o + static_cast<size_t>(qi) * ldo + (h0 + hh) * dout + lhalf * 4;

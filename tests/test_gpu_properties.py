@@ -114,6 +114,44 @@ def test_qk_norm_rope_random_shapes(shape, seed):
     assert np.array_equal(f64(vt_out), v_pad[perm16_tokens(sp)].transpose(1, 2, 0))
 
 
+@CASES
+@given(shape=qk_shapes(), seed=st.integers(0, 2**20))
+def test_qnorm_attention_random_shapes(shape, seed):
+    """The decoder layer's attention step (q RMSNorm and rotary applied as the
+    attention kernel loads the raw q rows) on the same random shapes, rotary
+    sections and positions, against the oracle's norm, rotary and attention."""
+    d, n_kv, group, seq, section, theta, max_pos = shape
+    print(f"qnorm_attention D={d} heads={n_kv * group}/{n_kv} seq={seq} section={section} "
+          f"theta={theta} max_pos={max_pos} seed={seed}", flush=True)
+    dims = dataclasses.replace(synth.TINY, hidden=n_kv * group * d, n_heads=n_kv * group,
+                               n_kv_heads=n_kv, head_dim=d, rope_theta=theta,
+                               mrope_section=section)
+    qw, kvw = dims.q_width, dims.kv_width
+    qkv = _randn((seq, qw + 2 * kvw), seed, 2.0)
+    qn, kn = _gain(d, seed + 1), _gain(d, seed + 2)
+    sp = b.seq_pad(seq)
+    q_out = torch.empty((seq, dims.n_heads, d), device=DEV, dtype=torch.bfloat16)
+    k_out = torch.empty((n_kv, sp, d), device=DEV, dtype=torch.bfloat16)
+    vt_out = torch.empty((n_kv, d, sp), device=DEV, dtype=torch.bfloat16)
+    positions = synth.random_positions(seq, max_pos, seed=seed)
+    pos = torch.from_numpy(np.ascontiguousarray(positions)).to(DEV)
+    cfg = b.config_from_dims(dims)
+    b.qk_norm_rope(cfg, qkv, qn, kn, pos, seq, q_out, k_out, vt_out)
+    nbytes = b.qnorm_attention_workspace_bytes(cfg, seq)
+    ws = torch.empty(nbytes, device=DEV, dtype=torch.uint8)
+    o = torch.full((seq, dims.n_heads * d), 7.0, device=DEV, dtype=torch.bfloat16)
+    b.qnorm_attention(cfg, qkv, qn, pos, k_out, vt_out, o, seq, ws, nbytes)
+    torch.cuda.synchronize()
+    x = f64(qkv)
+    cos, sin = oracle.rope_cos_sin(positions, d, theta, section)
+    q_ref = oracle.apply_rope(oracle.rms_norm(x[:, :qw].reshape(seq, -1, d), f64(qn), dims.rms_eps), cos, sin)
+    k_ref = oracle.apply_rope(oracle.rms_norm(x[:, qw:qw + kvw].reshape(seq, -1, d), f64(kn), dims.rms_eps),
+                              cos, sin)
+    ref = oracle.causal_gqa_attention(q_ref, k_ref, x[:, qw + kvw:].reshape(seq, n_kv, d))
+    r, _, w = report_rows("qnorm attention", f64(o), ref.reshape(seq, -1), d)
+    assert r <= 8e-3 and w <= ROW_BAR
+
+
 @st.composite
 def attention_shapes(draw):
     d = draw(st.sampled_from([64, 128]))
