@@ -18,7 +18,10 @@
 // with lane^32; the row sum stays lane-local until the end. O^T = V^T P^T is
 // accumulated the same way; V arrives pre-transposed and token-permuted
 // (qk_norm_rope.hip) so the probabilities produced by the first product are
-// directly the second product's B operand.
+// directly the second product's B operand. Both products keep eight 16-byte
+// LDS operand reads in flight ahead of the MFMA that consumes them (the score
+// MFMAs step the head dims outermost, so four independent accumulators take
+// turns), and the lane ^ 32 exchanges are v_permlane32_swap, not LDS permutes.
 //
 // Workgroups are numbered so that the key/value head is blockIdx % n_kv_heads:
 // with 8 key/value heads, each XCD serves one head and keeps its K/V in its
