@@ -105,6 +105,30 @@ def test_layers_full_width_ragged_seq_every_row():
     assert _teacher_forced(wl, s, states) <= 2e-2
 
 
+_EDGE_DIMS = {
+    "d128_g8": synth.Dims(hidden=1024, n_heads=8, n_kv_heads=1, head_dim=128, intermediate=2048),
+    "d64_g2": synth.Dims(hidden=256, n_heads=4, n_kv_heads=2, head_dim=64, intermediate=1024,
+                         rope_theta=1e6),
+}
+
+
+@pytest.mark.parametrize("seq", [1, 2, 31, 33, 127, 129, 255])
+@pytest.mark.parametrize("key", sorted(_EDGE_DIMS))
+def test_layers_edge_lengths_every_row(key, seq):
+    """Two layers at lengths around the 32-query block and the 128-key tile
+    (one token, a partial query block, one key tile plus one key): the layer
+    path's q norm and rotary inside the attention, the k-only norm kernel and
+    the padded K / V^T layouts, every row teacher-forced against the oracle;
+    mhe_encode equals the layer-by-layer calls."""
+    wl = synth.custom_workload(_EDGE_DIMS[key], seq, 2, key=f"edge_{key}_{seq}", index=60 + seq % 30)
+    print(f"edge layers {key} seq={seq}", flush=True)
+    s = _setup(wl)
+    out = _run_encode(wl, s)
+    states = _gpu_states(wl, s)
+    assert torch.equal(states[-1], out)
+    assert _teacher_forced(wl, s, states) <= 2e-2
+
+
 def _run_encode(wl, s, n_layers=None):
     layers = s["layers"] if n_layers is None else s["layers"][:n_layers]
     out = torch.empty_like(s["emb"])
