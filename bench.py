@@ -19,6 +19,11 @@ Prints ONE JSON line on stdout (everything else goes to stderr):
                launch of that kernel on its stream, in two encodes run after
                the timed steps (the timed steps carry no events)
   breakdown    mean milliseconds per encode of each step (a separate traced pass)
+  per_step_roofline
+               each step of that traced pass per launch against its own
+               roofline: the GEMMs and attention in TFLOP/s of algorithmic
+               flops (dense bf16 peak), norms, k rotary and DeepStack in GB/s
+               of algorithmic bytes (8 TB/s HBM)
   fp8          the same encode with the four linears of every layer in FP8
                (per-tensor E4M3, weights quantised once beforehand,
                activations on every call): ms per encode, tokens/s, its
@@ -428,6 +433,34 @@ def main():
         b.trace_enable([])
         log("breakdown ms/encode: " + json.dumps(breakdown))
 
+    # every kernel of the hot path against its own roofline, from the traced
+    # encode (event pairs around each launch): MFMA steps in TFLOP/s of
+    # their algorithmic flops, HBM-bound steps in GB/s of their algorithmic
+    # bytes; per launch = per encode / n_layers (DeepStack: / its levels)
+    per_step = None
+    if breakdown:
+        bytes_act = wl.seq * d.hidden * 2
+        kv = wl.seq * d.n_kv_heads * d.head_dim * 2
+        work = {"qkv": ("mfma", fl["qkv"]), "attention": ("mfma", fl["attention"]),
+                "o_proj": ("mfma", fl["o_proj"]), "gate_up": ("mfma", fl["gate_up"]),
+                "down": ("mfma", fl["down"]), "input_norm": ("hbm", 2 * bytes_act),
+                "post_norm": ("hbm", 2 * bytes_act), "qk_rope": ("hbm", 4 * kv),
+                "deepstack": ("hbm", 3 * wl.n_vis * d.hidden * 2)}
+        per_step = {}
+        for s_name, (bound, amount) in work.items():
+            launches = (min(wl.n_ds, wl.n_layers) if s_name == "deepstack" else wl.n_layers)
+            if s_name not in breakdown or not launches or not amount:
+                continue
+            us = breakdown[s_name] * 1000.0 / launches
+            if bound == "mfma":
+                rate = amount / (us * 1e-6) / 1e12
+                per_step[s_name] = {"us": round(us, 1), "tflops": round(rate, 1),
+                                    "frac": round(rate / PEAK_BF16_TFLOPS, 4)}
+            else:
+                rate = amount / (us * 1e-6) / 1e9
+                per_step[s_name] = {"us": round(us, 1), "gb_s": round(rate, 1),
+                                    "frac": round(rate / PEAK_HBM_GBS, 4)}
+
     frontend = None
     if not args.no_frontend:
         frontend = frontend_measure(wl, dev)
@@ -463,6 +496,7 @@ def main():
         "tflops_per_step": round(flops_step / 1e12, 3),
         "roofline": roofline,
         "breakdown_ms_per_step": breakdown,
+        "per_step_roofline": per_step,
         "fp8": fp8,
         "frontend": frontend,
         "vision": vision,
