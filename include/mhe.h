@@ -12,6 +12,11 @@
  *  - Tensors are dense row-major device buffers. "bf16" means IEEE bfloat16
  *    stored as uint16; the library rounds to nearest-even wherever it
  *    produces bf16. Linear weights follow y = x W^T with W stored [out, in].
+ *  - Every tensor starts on a 16-byte boundary (the kernels move 16-byte
+ *    vectors; PyTorch allocations are 256-byte aligned). The layer, encode and
+ *    fused-attention entry points reject misaligned weights and activations
+ *    with MHE_ERR_SHAPE; scales and the device position / mask arrays only
+ *    need their element alignment.
  *  - The caller owns every device buffer, the workspace and the stream. The
  *    library allocates and frees nothing; host pointer arrays (layer weight
  *    tables, DeepStack feature tables) are read only during the call.

@@ -161,14 +161,22 @@ Workspace carve(const mhe_config& c, int seq, char* base, bool fp8 = false) {
   return w;
 }
 
+// The kernels move tensors in 16-byte vectors (and 16-byte LDS-DMA loads),
+// so every tensor starts on a 16-byte boundary; scales are single floats.
+bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
 int32_t check_weights_fp8(const mhe_layer_weights_fp8* w, int layer) {
   if (!w) return fail(MHE_ERR_NULL, "layer %d weights table is NULL", layer);
   const void* p[] = {w->ln_in, w->w_qkv, w->s_qkv, w->q_norm, w->k_norm, w->w_o, w->s_o,
                      w->ln_post, w->w_gate_up, w->s_gate_up, w->w_down, w->s_down};
   const char* names[] = {"ln_in", "w_qkv", "s_qkv", "q_norm", "k_norm", "w_o", "s_o",
                          "ln_post", "w_gate_up", "s_gate_up", "w_down", "s_down"};
-  for (int i = 0; i < 12; ++i)
+  const bool is_scale[] = {false, false, true, false, false, false, true, false, false, true, false, true};
+  for (int i = 0; i < 12; ++i) {
     if (!p[i]) return fail(MHE_ERR_NULL, "layer %d: %s is NULL", layer, names[i]);
+    if (!is_scale[i] && misaligned16(p[i]))
+      return fail(MHE_ERR_SHAPE, "layer %d: %s is not 16-byte aligned", layer, names[i]);
+  }
   return MHE_OK;
 }
 
@@ -178,8 +186,10 @@ int32_t check_weights(const mhe_layer_weights* w, int layer) {
                      w->w_o, w->ln_post, w->w_gate, w->w_up, w->w_down};
   const char* names[] = {"ln_in", "w_q", "w_k", "w_v", "q_norm", "k_norm",
                          "w_o", "ln_post", "w_gate", "w_up", "w_down"};
-  for (int i = 0; i < 11; ++i)
+  for (int i = 0; i < 11; ++i) {
     if (!p[i]) return fail(MHE_ERR_NULL, "layer %d: %s is NULL", layer, names[i]);
+    if (misaligned16(p[i])) return fail(MHE_ERR_SHAPE, "layer %d: %s is not 16-byte aligned", layer, names[i]);
+  }
   return MHE_OK;
 }
 
@@ -420,6 +430,7 @@ int32_t layer_forward_impl(const mhe_config* cfg, const W* w, void* hidden, cons
   if ((rc = check_weights(w, 0))) return rc;
   if (!hidden) return fail(MHE_ERR_NULL, "hidden is NULL");
   if (!positions) return fail(MHE_ERR_NULL, "positions is NULL");
+  if (misaligned16(hidden)) return fail(MHE_ERR_SHAPE, "hidden is not 16-byte aligned");
   if ((rc = check_seq(seq))) return rc;
   const Workspace need = carve(*cfg, seq, nullptr, fp8);
   if ((rc = check_ws(workspace, workspace_bytes, need.total))) return rc;
@@ -445,6 +456,8 @@ int32_t encode_impl(const mhe_config* cfg, const W* layers, int32_t n_layers,
   if (n_vis < 0 || n_vis > seq) return fail(MHE_ERR_SHAPE, "n_vis %d out of range [0, %d]", n_vis, seq);
   if (!inputs_embeds || !out) return fail(MHE_ERR_NULL, "inputs_embeds and out are required");
   if (!positions) return fail(MHE_ERR_NULL, "positions is NULL");
+  if (misaligned16(inputs_embeds) || misaligned16(out))
+    return fail(MHE_ERR_SHAPE, "inputs_embeds and out must be 16-byte aligned");
   if (n_layers > 0 && !layers) return fail(MHE_ERR_NULL, "layers is NULL");
   for (int l = 0; l < n_layers; ++l)
     if ((rc = check_weights(&layers[l], l))) return rc;
@@ -452,8 +465,10 @@ int32_t encode_impl(const mhe_config* cfg, const W* layers, int32_t n_layers,
   if (used_ds > 0) {
     if (!visual_mask) return fail(MHE_ERR_NULL, "visual_mask is NULL with DeepStack levels");
     if (!deepstack) return fail(MHE_ERR_NULL, "deepstack table is NULL");
-    for (int l = 0; l < used_ds; ++l)
+    for (int l = 0; l < used_ds; ++l) {
       if (!deepstack[l]) return fail(MHE_ERR_NULL, "deepstack[%d] is NULL", l);
+      if (misaligned16(deepstack[l])) return fail(MHE_ERR_SHAPE, "deepstack[%d] is not 16-byte aligned", l);
+    }
   }
   const size_t act_bytes = static_cast<size_t>(seq) * cfg->hidden * 2;
   if (overlaps(out, act_bytes, inputs_embeds, act_bytes))
@@ -847,6 +862,8 @@ int32_t mhe_qnorm_attention(const mhe_config* cfg, const void* qkv, const void* 
   if ((rc = check_config(cfg))) return rc;
   if ((rc = check_seq(seq))) return rc;
   if (!qkv || !q_norm || !positions || !k || !vt || !o) return fail(MHE_ERR_NULL, "all buffers are required");
+  for (const void* p : {qkv, q_norm, k, vt, static_cast<const void*>(o)})
+    if (misaligned16(p)) return fail(MHE_ERR_SHAPE, "qkv, q_norm, k, vt and o must be 16-byte aligned");
   const int D = cfg->head_dim, Hq = cfg->n_heads, Hkv = cfg->n_kv_heads;
   if (!mhe::attention_supported(Hq, Hkv, D))
     return fail(MHE_ERR_UNSUPPORTED, "head_dim 64/128 and 1, 2, 4 or 8 query heads per kv head");

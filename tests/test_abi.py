@@ -78,6 +78,10 @@ def test_layer_forward_rejects_before_launch():
     t.w_down = None
     assert _layer_call(w=ctypes.byref(t)) == 1
     assert "w_down" in b.lib().mhe_last_error().decode()
+    t.w_down = 0x1008                             # not on a 16-byte boundary
+    assert _layer_call(w=ctypes.byref(t)) == 2
+    assert "w_down" in b.lib().mhe_last_error().decode()
+    assert _layer_call(hidden=0x2004) == 2
 
 
 def test_encode_rejects_before_launch():
@@ -97,6 +101,8 @@ def test_encode_rejects_before_launch():
     assert call(out=0x2000) == 2             # out overlaps inputs_embeds
     assert call(ws_bytes=16) == 5
     assert call(layers=None) == 1
+    assert call(emb=0x2002) == 2             # inputs_embeds not 16-byte aligned
+    assert call(ds=(ctypes.c_void_p * 1)(0x5008)) == 2
 
 
 def test_step_entry_points_reject_before_launch():
@@ -152,6 +158,7 @@ def test_qnorm_attention_rejects_before_launch():
         ctypes.byref(c), o.get("qkv", d), d, d, d, d, d, o.get("seq", 64), o.get("ws", 0x10000),
         o.get("ws_bytes", need), None)
     assert call(qkv=None) == 1
+    assert call(qkv=d + 8) == 2                   # not 16-byte aligned
     assert call(seq=0) == 2
     assert call(ws_bytes=need - 1) == 5
     assert call(ws=0x10010) == 5                  # misaligned
