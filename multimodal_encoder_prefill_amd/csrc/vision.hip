@@ -116,50 +116,75 @@ __global__ __launch_bounds__(256) void vision_rope_table_kernel(const PatchInfo*
   table[e] = make_float2(cs, sn);
 }
 
-// grid (n_pad / 16, heads); 128 threads = padded head dims d
-__global__ __launch_bounds__(kVD) void vision_rope_kernel(const bf16_t* __restrict__ qkv, int ldq,
-                                                          int n, int n_pad, int heads, int dh,
-                                                          const float2* __restrict__ table,
-                                                          bf16_t* __restrict__ q_out,
-                                                          bf16_t* __restrict__ k_out,
-                                                          bf16_t* __restrict__ vt_out) {
+// grid (n_pad / 16, heads); one wavefront, lane l = padded head dims 2l and
+// 2l + 1 (the rotate-half partner of an even dim is even: dh % 4 == 0), so
+// every load and store moves a pair and the pair's two cos/sin come as one
+// 16-byte table read
+__global__ __launch_bounds__(64) void vision_rope_kernel(const bf16_t* __restrict__ qkv, int ldq,
+                                                         int n, int n_pad, int heads, int dh,
+                                                         const float2* __restrict__ table,
+                                                         bf16_t* __restrict__ q_out,
+                                                         bf16_t* __restrict__ k_out,
+                                                         bf16_t* __restrict__ vt_out) {
   const int s0 = blockIdx.x * kVT;
   const int h = blockIdx.y;
-  const int d = threadIdx.x;
+  const int d = 2 * threadIdx.x;
   const int half = dh / 2;
   const int hid = heads * dh;
-  // slot j of the D/2 angles (the angle of d and d + D/2)
-  const int j = d < dh ? d % half : 0;
-  float vv[kVT];
+  const bool used = d < dh;
+  // slot j of the D/2 angles (the angle of d and d + D/2), and the partner dim
+  const int j = used ? d % half : 0;
+  const int pd = d < half ? d + half : d - half;
+  const float sign = d < half ? -1.f : 1.f;
+  auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+  auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
+  // loads from in-range addresses for every lane and token (the last patch
+  // and dim 0 stand in for padding), so all of them can go out together;
+  // results outside the patches or the head dims are zeroed afterwards
+  const int du = used ? d : 0, pu = used ? pd : 0;
+  f32x4 cs[kVT];
+  uint32_t w[kVT][5];
+#pragma unroll
+  for (int t = 0; t < kVT; ++t) {
+    const int su = min(s0 + t, n - 1);
+    const bf16_t* row = qkv + static_cast<size_t>(su) * ldq + h * dh;
+    cs[t] = *reinterpret_cast<const f32x4*>(table + static_cast<size_t>(su) * half + j);
+    w[t][0] = *reinterpret_cast<const uint32_t*>(row + du);
+    w[t][1] = *reinterpret_cast<const uint32_t*>(row + pu);
+    w[t][2] = *reinterpret_cast<const uint32_t*>(row + hid + du);
+    w[t][3] = *reinterpret_cast<const uint32_t*>(row + hid + pu);
+    w[t][4] = *reinterpret_cast<const uint32_t*>(row + 2 * hid + du);
+  }
+  float va[kVT], vb[kVT];
 #pragma unroll
   for (int t = 0; t < kVT; ++t) {
     const int s = s0 + t;
-    float qo = 0.f, ko = 0.f, vo = 0.f;
-    if (s < n && d < dh) {
-      const bf16_t* row = qkv + static_cast<size_t>(s) * ldq + h * dh;
-      const float2 c2 = table[static_cast<size_t>(s) * half + j];
-      const float cs = c2.x, sn = c2.y;
-      const int pd = d < half ? d + half : d - half;
-      const float sign = d < half ? -1.f : 1.f;
-      const float qx = bf16_to_f32(row[d]), qp = bf16_to_f32(row[pd]);
-      const float kx = bf16_to_f32(row[hid + d]), kp = bf16_to_f32(row[hid + pd]);
-      qo = qx * cs + sign * qp * sn;
-      ko = kx * cs + sign * kp * sn;
-      vo = bf16_to_f32(row[2 * hid + d]);
-    }
-    if (s < n) q_out[(static_cast<size_t>(s) * heads + h) * kVD + d] = f32_to_bf16(qo);
-    k_out[(static_cast<size_t>(h) * n_pad + s) * kVD + d] = f32_to_bf16(ko);
-    vv[t] = vo;
+    const bool real = s < n && used;
+    const f32x4 c4 = cs[t];
+    const uint32_t qx = w[t][0], qp = w[t][1], kx = w[t][2], kp = w[t][3], vx = w[t][4];
+    uint32_t qo = pack_bf16x2(lo(qx) * c4[0] + sign * lo(qp) * c4[1], hi(qx) * c4[2] + sign * hi(qp) * c4[3]);
+    uint32_t ko = pack_bf16x2(lo(kx) * c4[0] + sign * lo(kp) * c4[1], hi(kx) * c4[2] + sign * hi(kp) * c4[3]);
+    qo = real ? qo : 0u;
+    ko = real ? ko : 0u;
+    va[t] = real ? lo(vx) : 0.f;
+    vb[t] = real ? hi(vx) : 0.f;
+    if (s < n) *reinterpret_cast<uint32_t*>(q_out + (static_cast<size_t>(s) * heads + h) * kVD + d) = qo;
+    *reinterpret_cast<uint32_t*>(k_out + (static_cast<size_t>(h) * n_pad + s) * kVD + d) = ko;
   }
-  u32x4 lo, hi;
+  // V^T rows d and d + 1: the 16 tokens in the permuted order
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    lo[p] = pack_bf16x2(vv[perm16v(2 * p)], vv[perm16v(2 * p + 1)]);
-    hi[p] = pack_bf16x2(vv[perm16v(8 + 2 * p)], vv[perm16v(8 + 2 * p + 1)]);
+  for (int r = 0; r < 2; ++r) {
+    const float* vv = r ? vb : va;
+    u32x4 w0, w1;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      w0[p] = pack_bf16x2(vv[perm16v(2 * p)], vv[perm16v(2 * p + 1)]);
+      w1[p] = pack_bf16x2(vv[perm16v(8 + 2 * p)], vv[perm16v(8 + 2 * p + 1)]);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(vt_out + (static_cast<size_t>(h) * kVD + d + r) * n_pad + s0);
+    dst[0] = w0;
+    dst[1] = w1;
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(vt_out + (static_cast<size_t>(h) * kVD + d) * n_pad + s0);
-  dst[0] = lo;
-  dst[1] = hi;
 }
 
 }  // namespace
@@ -194,7 +219,8 @@ hipError_t launch_vision_rope(const bf16_t* qkv, int ldq, int n, int heads, int 
   if (n <= 0) return hipSuccess;
   if (head_dim > kVD || head_dim % 4 != 0) return hipErrorInvalidValue;
   const int n_pad = seq_pad(n);
-  hipLaunchKernelGGL(vision_rope_kernel, dim3(n_pad / kVT, heads), dim3(kVD), 0, stream, qkv, ldq,
+  if (ldq % 2 != 0) return hipErrorInvalidValue;  // pairs of bf16 are read as one word
+  hipLaunchKernelGGL(vision_rope_kernel, dim3(n_pad / kVT, heads), dim3(kVD / 2), 0, stream, qkv, ldq,
                      n, n_pad, heads, head_dim, table, q_out, k_out, vt_out);
   return hipGetLastError();
 }
