@@ -99,31 +99,40 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const bf16_t* x, int ldx
   const int nchunks = dim >> 3;
   const u32x4* xr = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(row) * ldx);
   u32x4 v[kMaxChunks];
-  float s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunks; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nchunks) v[i] = xr[c];
+  }
+  // mean and variance in one pass over the row, on data shifted by its first
+  // element (the shifted-data form of the sums: the shift keeps the squares
+  // near the variance's scale, so no cancellation against a large mean),
+  // and one wavefront reduction carrying both sums
+  const float shift = __uint_as_float(__builtin_amdgcn_readfirstlane(v[0][0] << 16));  // x[row][0] (lane 0)
+  float s1 = 0.f, s2 = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxChunks; ++i) {
     const int c = lane + 64 * i;
     if (c < nchunks) {
-      v[i] = xr[c];
       float f[8];
       unpack8(v[i], f);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s1 += f[j];
+      for (int j = 0; j < 8; ++j) {
+        const float z = f[j] - shift;
+        s1 += z;
+        s2 += z * z;
+      }
     }
   }
-  const float mean = wave_sum(s1) / static_cast<float>(dim);
-  float s2 = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMaxChunks; ++i) {
-    const int c = lane + 64 * i;
-    if (c < nchunks) {
-      float f[8];
-      unpack8(v[i], f);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s2 += (f[j] - mean) * (f[j] - mean);
-    }
+  for (int off = 32; off >= 1; off >>= 1) {
+    s1 += __shfl_xor(s1, off, 64);
+    s2 += __shfl_xor(s2, off, 64);
   }
-  const float r = rsqrtf(wave_sum(s2) / static_cast<float>(dim) + eps);
+  const float inv_n = 1.f / static_cast<float>(dim);
+  const float zmean = s1 * inv_n;
+  const float mean = shift + zmean;
+  const float r = rsqrtf(fmaxf(s2 * inv_n - zmean * zmean, 0.f) + eps);
   const u32x4* wr = reinterpret_cast<const u32x4*>(w);
   const u32x4* br = reinterpret_cast<const u32x4*>(bias);
   u32x4* yr = reinterpret_cast<u32x4*>(y + static_cast<size_t>(row) * ldy);

@@ -58,10 +58,14 @@ GRIDS_TINY = [(1, 8, 8), (2, 4, 8), (1, 6, 4)]
 GRIDS_FULL = [(1, 32, 32), (2, 16, 16)]
 
 
-def test_layer_norm_matches_oracle():
+@pytest.mark.parametrize("offset", [0.5, 300.0, -2000.0])
+def test_layer_norm_matches_oracle(offset):
+    """Rows of N(offset, 4): the large offsets check that the statistics do
+    not cancel against a mean far from zero (bf16 keeps only ~3 significant
+    digits of the offset, so the rows' spread survives as bf16 steps)."""
     for dim in (576, 1152, 4608):
         g = torch.Generator(device=DEV).manual_seed(dim)
-        x = (torch.randn(257, dim, generator=g, device=DEV) * 2 + 0.5).to(torch.bfloat16)
+        x = (torch.randn(257, dim, generator=g, device=DEV) * 2 + offset).to(torch.bfloat16)
         w = (0.5 + torch.rand(dim, generator=g, device=DEV)).to(torch.bfloat16)
         bb = (0.1 * torch.randn(dim, generator=g, device=DEV)).to(torch.bfloat16)
         y = torch.empty_like(x)
