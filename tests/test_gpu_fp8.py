@@ -287,6 +287,19 @@ def test_fp8_layer_tiny_teacher_forced():
     _check_layers(wl, s, _gpu_states(wl, s), range(wl.n_layers))
 
 
+@pytest.mark.parametrize("seq", [1, 33, 129])
+def test_fp8_layers_edge_lengths(seq):
+    """The FP8 layer (quantised inputs, the attention with the q norm inside
+    it emitting the maxima of its output) at a single token, a partial query
+    block and one key tile plus one key, head dim 128 with 8 query heads per
+    key/value head: every row of two layers against the oracle's FP8 layer."""
+    dims = synth.Dims(hidden=1024, n_heads=8, n_kv_heads=1, head_dim=128, intermediate=2048)
+    wl = synth.custom_workload(dims, seq, 2, key=f"fp8_edge_{seq}", index=70 + seq % 20)
+    print(f"fp8 edge layers seq={seq}", flush=True)
+    s = _setup(wl)
+    _check_layers(wl, s, _gpu_states(wl, s), range(wl.n_layers))
+
+
 def test_fp8_weights_match_oracle_quantisation():
     """The load-time quantisation of a layer (fused qkv and gate_up) is the oracle's, bit for bit."""
     wl = synth.WORKLOADS["tiny"]
